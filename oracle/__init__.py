@@ -1,0 +1,31 @@
+"""CPU oracle for the fine-grained MoE layer forward.
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package; the product path
+(``sparse_moe_layer_04_amd``) never does and shares no code with it.
+
+The arithmetic lives in ``moe_oracle.c`` (plain C, fp64, built by
+``oracle/build.py``); this module only marshals numpy arrays through ctypes.
+Parity unpinned: the clamp form (symmetric vs gate-above-only), the shared
+expert's form and the init-std reading are readings of what the pages leave
+open; they are configurable, and every other step is pinned by the tests.
+"""
+from .oracle import (  # noqa: F401
+    MODE_TOPK,
+    MODE_HASH,
+    FLAG_BAD_INPUT_ID,
+    FLAG_BAD_EXPERT_ID,
+    library_path,
+    load,
+    f64_to_bf16,
+    score,
+    gate_logits,
+    route,
+    permute,
+    gather,
+    expert_ffn,
+    expert_ffn_rows,
+    combine,
+    tokens_forward,
+    forward,
+)

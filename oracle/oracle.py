@@ -1,0 +1,240 @@
+"""ctypes marshalling for the C oracle (moe_oracle.c).  TEST INFRASTRUCTURE ONLY.
+
+Arrays are numpy; bf16 tensors travel as their uint16 bit patterns.  No
+arithmetic of the method lives here: every function forwards to the C
+definition of the same name (``orc_*``), except ``forward``, which only
+chains those calls in the pages' order (route -> permute -> gather -> expert
+FFN -> shared FFN -> combine).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+MODE_TOPK = 0
+MODE_HASH = 1
+FLAG_BAD_INPUT_ID = 1
+FLAG_BAD_EXPERT_ID = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libmoe_oracle.so")
+
+
+def load():
+    """Load (building first if absent) the oracle shared library."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    I64 = ctypes.c_int64
+    F = ctypes.c_float
+    D = ctypes.c_double
+    lib.orc_f64_to_bf16.argtypes = [D]
+    lib.orc_f64_to_bf16.restype = ctypes.c_uint16
+    lib.orc_score.argtypes = [F]
+    lib.orc_score.restype = F
+    lib.orc_score_array.argtypes = [P, P, I64]
+    lib.orc_score_array.restype = None
+    lib.orc_gate_logits.argtypes = [P, P, P, I, I, I, P]
+    lib.orc_gate_logits.restype = None
+    lib.orc_route.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, P]
+    lib.orc_route.restype = ctypes.c_uint
+    lib.orc_permute.argtypes = [P, I, I, I, P, P, P, P]
+    lib.orc_permute.restype = ctypes.c_uint
+    lib.orc_gather.argtypes = [P, P, I64, I, P]
+    lib.orc_gather.restype = None
+    lib.orc_expert_ffn.argtypes = [P, P, I, I, I, P, P, P, D, I, P, P]
+    lib.orc_expert_ffn.restype = None
+    lib.orc_expert_ffn_rows.argtypes = [P, P, P, I, I, I, P, P, P, D, I, P, P]
+    lib.orc_expert_ffn_rows.restype = None
+    lib.orc_combine.argtypes = [P, P, P, P, I, I, I, P]
+    lib.orc_combine.restype = None
+    lib.orc_tokens_forward.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, P, I, D, I, P]
+    lib.orc_tokens_forward.restype = None
+    _LIB = lib
+    return lib
+
+
+def _c(a, dtype):
+    """Contiguous array of the given dtype (None passes through)."""
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _bf16(a):
+    """bf16 payload as uint16 bits (accepts uint16 arrays or torch bf16 tensors)."""
+    if a is None:
+        return None
+    if hasattr(a, "view") and hasattr(a, "dtype") and str(a.dtype) == "torch.bfloat16":
+        import torch
+        return a.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    a = np.asarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bf16 arrays are passed as uint16 bit patterns")
+    return np.ascontiguousarray(a)
+
+
+def f64_to_bf16(v: float) -> int:
+    return int(load().orc_f64_to_bf16(float(v)))
+
+
+def score(x):
+    """Pinned binary32 sigmoid S(x), elementwise."""
+    x = _c(x, np.float32)
+    out = np.empty_like(x)
+    load().orc_score_array(_p(x), _p(out), x.size)
+    return out
+
+
+def gate_logits(x, wg, off=None):
+    x, wg, off = _bf16(x), _bf16(wg), _c(off, np.float32)
+    T, d = x.shape
+    E = wg.shape[0]
+    out = np.empty((T, E), np.float32)
+    load().orc_gate_logits(_p(x), _p(wg), _p(off), T, d, E, _p(out))
+    return out
+
+
+def route(logits, k, scale, bias=None, modality=None, input_ids=None, tid2eid=None,
+          mode=MODE_TOPK):
+    """Returns (ids[T,k] int32, w[T,k] float32, flags)."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    bias = _c(bias, np.float32)
+    if bias is not None:
+        bias = bias.reshape(-1, E)
+    n_bias = 0 if bias is None else bias.shape[0]
+    modality = _c(modality, np.uint8)
+    input_ids = _c(input_ids, np.int32)
+    tid2eid = _c(tid2eid, np.int32)
+    V = 0 if tid2eid is None else tid2eid.shape[0]
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    flags = load().orc_route(_p(logits), _p(bias), _p(modality), _p(input_ids), _p(tid2eid),
+                             T, E, k, n_bias, V, mode, float(scale), _p(ids), _p(w))
+    return ids, w, int(flags)
+
+
+def permute(ids, E):
+    """Returns (counts[E], offsets[E+1], dest[T*k], src[T*k], flags)."""
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    dest = np.empty(T * k, np.int32)
+    src = np.empty(T * k, np.int32)
+    flags = load().orc_permute(_p(ids), T, k, E, _p(counts), _p(offsets), _p(dest), _p(src))
+    return counts, offsets, dest, src, int(flags)
+
+
+def gather(x, src):
+    x = _bf16(x)
+    src = _c(src, np.int32)
+    rows = src.shape[0]
+    d = x.shape[1]
+    out = np.zeros((rows, d), np.uint16)
+    load().orc_gather(_p(x), _p(src), rows, d, _p(out))
+    return out
+
+
+def expert_ffn(a, offsets, w_gate, w_up, w_down, clamp_limit, clamp_mode=0):
+    """Grouped FFN. Returns (h[rows,F] uint16 bf16 bits, y[rows,d] float64)."""
+    a = _bf16(a)
+    offsets = _c(offsets, np.int32)
+    w_gate, w_up, w_down = _bf16(w_gate), _bf16(w_up), _bf16(w_down)
+    G = offsets.shape[0] - 1
+    rows, d = a.shape
+    F = w_gate.shape[-2]
+    h = np.zeros((rows, F), np.uint16)
+    y = np.zeros((rows, d), np.float64)
+    load().orc_expert_ffn(_p(a), _p(offsets), G, d, F, _p(w_gate), _p(w_up), _p(w_down),
+                          float(clamp_limit), int(clamp_mode), _p(h), _p(y))
+    return h, y
+
+
+def expert_ffn_rows(a, rows, experts, w_gate, w_up, w_down, clamp_limit, clamp_mode=0):
+    """FFN of a[rows[i]] through expert experts[i]; returns packed (h, y)."""
+    a = _bf16(a)
+    rows = _c(rows, np.int64)
+    experts = _c(experts, np.int32)
+    w_gate, w_up, w_down = _bf16(w_gate), _bf16(w_up), _bf16(w_down)
+    n = rows.shape[0]
+    d = a.shape[1]
+    F = w_gate.shape[-2]
+    h = np.zeros((n, F), np.uint16)
+    y = np.zeros((n, d), np.float64)
+    load().orc_expert_ffn_rows(_p(a), _p(rows), _p(experts), n, d, F, _p(w_gate), _p(w_up),
+                               _p(w_down), float(clamp_limit), int(clamp_mode), _p(h), _p(y))
+    return h, y
+
+
+def combine(y_perm, dest, w, ysh=None):
+    y_perm = _c(y_perm, np.float64)
+    dest = _c(dest, np.int32)
+    w = _c(w, np.float32)
+    T, k = w.shape
+    d = y_perm.shape[1]
+    ysh = _c(ysh, np.float64)
+    y = np.empty((T, d), np.float64)
+    load().orc_combine(_p(y_perm), _p(dest), _p(w), _p(ysh), T, d, k, _p(y))
+    return y
+
+
+def tokens_forward(x, tokens, ids, w, w_gate, w_up, w_down, s_gate, s_up, s_down,
+                   clamp_limit, clamp_mode=0):
+    """Layer output for the listed tokens from their routing (ids, w)."""
+    x = _bf16(x)
+    tokens = _c(tokens, np.int64)
+    ids = _c(ids, np.int32)
+    w = _c(w, np.float32)
+    w_gate, w_up, w_down = _bf16(w_gate), _bf16(w_up), _bf16(w_down)
+    s_gate, s_up, s_down = _bf16(s_gate), _bf16(s_up), _bf16(s_down)
+    n = tokens.shape[0]
+    d = x.shape[1]
+    k = ids.shape[1]
+    F = w_gate.shape[-2]
+    Fs = 0 if s_gate is None else s_gate.shape[0]
+    y = np.empty((n, d), np.float64)
+    load().orc_tokens_forward(_p(x), _p(tokens), n, d, F, k, _p(ids), _p(w), _p(w_gate),
+                              _p(w_up), _p(w_down), _p(s_gate), _p(s_up), _p(s_down), Fs,
+                              float(clamp_limit), int(clamp_mode), _p(y))
+    return y
+
+
+def forward(x, logits, k, scale, w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None,
+            clamp_limit=10.0, clamp_mode=0, bias=None, modality=None, input_ids=None,
+            tid2eid=None, mode=MODE_TOPK):
+    """Whole layer from given router logits, step by step.
+
+    Returns a dict with ids, w, counts, offsets, dest, src, x_perm, h, y_perm,
+    ysh, y (y and y_perm in fp64, h in bf16 bits) and the flag word.
+    """
+    x = _bf16(x)
+    E = np.asarray(logits).shape[1]
+    ids, w, f1 = route(logits, k, scale, bias, modality, input_ids, tid2eid, mode)
+    counts, offsets, dest, src, f2 = permute(ids, E)
+    x_perm = gather(x, src)
+    h, y_perm = expert_ffn(x_perm, offsets, w_gate, w_up, w_down, clamp_limit, clamp_mode)
+    ysh = None
+    if s_gate is not None:
+        T = x.shape[0]
+        _, ysh = expert_ffn(x, np.array([0, T], np.int32), _bf16(s_gate)[None],
+                            _bf16(s_up)[None], _bf16(s_down)[None], clamp_limit, clamp_mode)
+    y = combine(y_perm, dest, w, ysh)
+    return dict(ids=ids, w=w, counts=counts, offsets=offsets, dest=dest, src=src,
+                x_perm=x_perm, h=h, y_perm=y_perm, ysh=ysh, y=y, flags=f1 | f2)
