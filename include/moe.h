@@ -1,0 +1,228 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) fine-grained Mixture-of-Experts layer
+ * forward: router projection, sigmoid top-k / hash routing, token dispatch
+ * permutation, grouped expert FFN with clamped SwiGLU, shared expert and
+ * routing-weight combine.
+ *
+ * The operations follow these pages:
+ *   [HP]  "HyperParallel accelerates DeepSeek-V4.1 multimodal 1M long-sequence
+ *         training", section 2.3 (MegaKernel): MegaGate (score, bias ranking,
+ *         Top-K, score extraction, normalisation, scaling; text and vision
+ *         routing bias; projection matmul outside the gate) and MegaMoE (token
+ *         dispatch, two expert matmuls, SwiGLU with the V4.1 clamp, result
+ *         return, reused workspace).
+ *   [TW]  "Twinkle x Ascend ... DeepSeek-V4 training", section "FSDP2-4D
+ *         parallel engine adaptation": router output (logits, routing weights,
+ *         selected experts); HashRouter ids = tid2eid[input_ids] weighted from
+ *         the gate logits; one dispatch path for both routers; results merged
+ *         by routing weight.
+ *   [MS]  "MindSpore HyperParallel one-click DeepSeek-V4.1-Flash", section 01:
+ *         one shared expert plus 384 routed experts, 6 routed per token.
+ *
+ * Conventions (all entry points):
+ *   - Tensor arguments are DEVICE pointers owned by the caller, row-major and
+ *     contiguous.  bf16 tensors are passed as uint16_t bit patterns.  Pointers
+ *     to bf16 data and fp32 matrices must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued: no entry point synchronises the host, allocates or frees.
+ *   - Return 0 (MOE_OK) or a negative MOE_ERR_* code.  All argument checks run
+ *     on the host before the first launch, so an error leaves no partial work
+ *     queued.  Errors found in device data (ids out of range) do not abort:
+ *     the offending token/pair is dropped and a bit is OR-ed into `*d_flags`
+ *     (a device uint32, optional: NULL = not reported).  The caller clears it.
+ *   - Scratch memory comes from a caller workspace `ws` of at least the
+ *     size the matching *_workspace_size() returns (256-byte aligned).  Calls
+ *     that share a workspace must not overlap in time.
+ *   - Results are deterministic: the same inputs give the same bits.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_ERR_NULL (-1)        /* a required pointer is NULL */
+#define MOE_ERR_SHAPE (-2)       /* a size is out of range or inconsistent */
+#define MOE_ERR_UNSUPPORTED (-3) /* a mode or size outside the supported set */
+#define MOE_ERR_WORKSPACE (-4)   /* workspace missing, misaligned or too small */
+#define MOE_ERR_HIP (-5)         /* a HIP runtime call failed */
+#define MOE_ERR_ALIGN (-6)       /* a tensor pointer is not 16-byte aligned */
+
+#define MOE_MODE_TOPK 0 /* sigmoid score + bias-ranked top-k */
+#define MOE_MODE_HASH 1 /* ids from tid2eid[input_ids] */
+
+#define MOE_OUT_BF16 0
+#define MOE_OUT_F32 1
+
+#define MOE_CLAMP_SYMMETRIC 0  /* gate and up clamped to [-L, L] */
+#define MOE_CLAMP_GATE_UPPER 1 /* gate clamped to (-inf, L], up to [-L, L] */
+
+#define MOE_FLAG_BAD_INPUT_ID 1u  /* an input id outside [0, V) */
+#define MOE_FLAG_BAD_EXPERT_ID 2u /* an expert id outside [0, E) */
+
+/* Limits: 1 <= k <= 8, k <= E, 1 <= E <= 1024 (route/permute/forward);
+ * d, F multiples of 64 (expert FFN, forward); T * k < 2^31; G <= 4096. */
+#define MOE_MAX_K 8
+#define MOE_MAX_E 1024
+#define MOE_MAX_GROUPS 4096
+
+const char* moe_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * Router projection [HP 2.3 MegaGate: the projection matmul sits outside the
+ * gate; TW: router computes logits from hidden states].
+ *   logits[t,e] = fl32( sum_i x[t,i] * w_g[e,i]  (+ logit_offset[e]) )
+ * bf16 products, fp32 accumulation on MFMA.
+ *   x [T,d] bf16, w_g [E,d] bf16, logit_offset [E] fp32 or NULL,
+ *   logits [T,E] fp32 (written).  d multiple of 64; 1 <= E <= 4096.
+ */
+int moe_gate_logits(const uint16_t* x, const uint16_t* w_g, const float* logit_offset,
+                    int T, int d, int E, float* logits, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Routing [HP 2.3 MegaGate order: score -> bias ranking -> Top-K -> score
+ * extraction -> normalise -> scale; TW HashRouter].
+ *   s[e] = S(logits[t,e]), S = binary32 sigmoid evaluated as a fixed sequence
+ *          of IEEE operations (clamp to [-80,80]; n = rint(-x log2 e);
+ *          Cody-Waite reduction; degree-7 Taylor polynomial by fma; scale by
+ *          2^n; 1/(1+e) correctly rounded), so the scores are reproducible bit
+ *          for bit on any IEEE machine.
+ *   TOPK: r[e] = fl32(s[e] + score_bias[m(t), e]), m(t) = modality[t] ? 1 : 0
+ *         when n_bias == 2 and modality != NULL, else 0 (no bias if NULL);
+ *         topk_ids[t,:] = the k experts greatest under (r desc, index asc),
+ *         in that order.
+ *   HASH: topk_ids[t,j] = tid2eid[input_ids[t], j] (table order).  A token
+ *         with input_ids[t] outside [0,V) or a table id outside [0,E) gets
+ *         ids -1 and weights 0 and sets a flag bit.
+ *   both: g_j = s[topk_ids[t,j]] (unbiased); S_t = ((g_0 + g_1) + ...) in
+ *         fp32; topk_w[t,j] = fl32(fl32(g_j / S_t) * scale).
+ *   logits [T,E] fp32; score_bias [n_bias,E] fp32 or NULL (n_bias 0..2);
+ *   modality [T] u8 or NULL; input_ids [T] int32 and tid2eid [V,k] int32
+ *   (HASH only); topk_ids [T,k] int32 and topk_w [T,k] fp32 (written).
+ */
+int moe_route(const float* logits, const float* score_bias, const uint8_t* modality,
+              const int32_t* input_ids, const int32_t* tid2eid, int T, int E, int k,
+              int n_bias, int V, int mode, float scale, int32_t* topk_ids, float* topk_w,
+              uint32_t* d_flags, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Token dispatch [TW: ids from either router -> expert_mask -> one dispatch
+ * flow; HP 2.3 MegaMoE token dispatch].  On one device the expert-parallel
+ * all-to-all becomes a stable counting sort of the (t, j) pairs, t-major, by
+ * expert id, and a copy of each token row to its slots:
+ *   counts[e]    = #{(t,j): topk_ids[t,j] = e}
+ *   offsets[e]   = sum_{e' < e} counts[e'], offsets[E] = number of valid pairs
+ *   dest[t*k+j]  = offsets[e] + #{earlier pairs with the same expert}, or -1
+ *   src[row]     = t for filled rows, -1 for rows in [offsets[E], T*k)
+ *   x_perm[row]  = x[src[row]] (exact copy; rows past offsets[E] untouched)
+ * Pairs with an id outside [0,E) are dropped and set MOE_FLAG_BAD_EXPERT_ID.
+ *   topk_ids [T,k] int32, x [T,d] bf16 (d multiple of 8); counts [E],
+ *   offsets [E+1], dest [T*k], src [T*k] int32, x_perm [T*k,d] bf16.
+ *   ws: moe_permute_workspace_size(T, k, E) bytes.
+ */
+size_t moe_permute_workspace_size(int T, int k, int E);
+int moe_permute(const int32_t* topk_ids, const uint16_t* x, int T, int d, int E, int k,
+                int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
+                uint16_t* x_perm, uint32_t* d_flags, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Grouped expert FFN [HP 2.3 MegaMoE: two expert matmuls with SwiGLU and the
+ * V4.1 clamp between them].  For every group g and row r in
+ * [offsets[g], offsets[g+1]):
+ *   G_f = sum_i a[r,i] w_gate[g,f,i],  U_f = sum_i a[r,i] w_up[g,f,i]  (fp32)
+ *   clamp with limit L (L = +inf: none): SYMMETRIC G,U <- clamp(., -L, L);
+ *   GATE_UPPER G <- min(G, L), U <- clamp(U, -L, L)
+ *   h[r,f] = bf16( silu(G_f) * U_f ),  silu(z) = z / (1 + e^-z)
+ *   y[r,o] = sum_f h[r,f] w_down[g,o,f]  (fp32)
+ *   a [rows,d] bf16; offsets [G+1] int32 in DEVICE memory, non-decreasing
+ *   within [0, rows] (entries outside are clamped into range); w_gate, w_up
+ *   [G,F,d] bf16; w_down [G,d,F] bf16; h [rows,F] bf16 and y [rows,d] fp32
+ *   (written for rows inside a group only).  d, F multiples of 64.
+ *   The shared expert is the G = 1, offsets = {0, T} call on x.
+ */
+int moe_expert_ffn(const uint16_t* a, const int32_t* offsets, int G, int rows, int d, int F,
+                   const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                   float clamp_limit, int clamp_mode, uint16_t* h, float* y, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Result return merged by routing weight [TW], plus the always-on shared
+ * expert with weight 1 [MS]:
+ *   y[t,o] = y_shared[t,o] + sum_j topk_w[t,j] * y_perm[dest[t,j], o]
+ * in fp32 (pairs with dest < 0 skipped; y_shared may be NULL), written as
+ * bf16 (MOE_OUT_BF16, round to nearest even) or fp32 (MOE_OUT_F32).
+ *   y_perm [rows,d] fp32, dest [T*k] int32 (entries >= rows are skipped),
+ *   topk_w [T*k] fp32, y_shared [T,d] fp32 or NULL, y [T,d].  d multiple of 8.
+ */
+int moe_combine(const float* y_perm, const int32_t* dest, const float* topk_w,
+                const float* y_shared, int T, int d, int k, int rows, int out_dtype, void* y,
+                void* stream);
+
+/* ------------------------------------------------------------------------
+ * Whole layer forward: gate logits -> route -> permute -> grouped FFN (routed
+ * experts) and FFN (shared expert) -> combine.
+ */
+typedef struct moe_cfg {
+    int T;            /* tokens */
+    int d;            /* hidden size (multiple of 64) */
+    int E;            /* routed experts (<= 1024) */
+    int k;            /* routed experts per token (<= 8, <= E) */
+    int F;            /* routed expert FFN width (multiple of 64) */
+    int F_shared;     /* shared expert FFN width (multiple of 64), 0 = none */
+    int mode;         /* MOE_MODE_TOPK or MOE_MODE_HASH */
+    int n_bias;       /* routing bias rows: 0, 1 or 2 (text, vision) */
+    int V;            /* HASH: tid2eid rows (vocabulary) */
+    float scale;      /* routing weight scale */
+    float clamp_limit;/* SwiGLU clamp L (> 0; +inf = none) */
+    int clamp_mode;   /* MOE_CLAMP_* */
+    int out_dtype;    /* MOE_OUT_BF16 or MOE_OUT_F32 */
+} moe_cfg;
+
+typedef struct moe_weights {
+    const uint16_t* w_g;          /* [E,d] bf16 router projection */
+    const float* logit_offset;    /* [E] fp32 or NULL, added to the logits */
+    const float* score_bias;      /* [n_bias,E] fp32 or NULL (TOPK) */
+    const int32_t* tid2eid;       /* [V,k] int32 (HASH) */
+    const uint16_t* w_gate;       /* [E,F,d] bf16 */
+    const uint16_t* w_up;         /* [E,F,d] bf16 */
+    const uint16_t* w_down;       /* [E,d,F] bf16 */
+    const uint16_t* s_gate;       /* [F_shared,d] bf16 (shared expert) */
+    const uint16_t* s_up;         /* [F_shared,d] bf16 */
+    const uint16_t* s_down;       /* [d,F_shared] bf16 */
+} moe_weights;
+
+/* Workspace for moe_forward (all intermediates: logits, routing, permutation,
+ * x_perm, h, y_perm and the shared expert's h and y). */
+size_t moe_forward_workspace_size(const moe_cfg* cfg);
+
+/* x [T,d] bf16; input_ids [T] int32 (HASH) or NULL; modality [T] u8 or NULL;
+ * y [T,d] (bf16 or fp32 per out_dtype).  Optional outputs (NULL = kept in the
+ * workspace): logits_out [T,E] fp32, ids_out [T,k] int32, w_out [T,k] fp32. */
+int moe_forward(const moe_cfg* cfg, const moe_weights* w, const uint16_t* x,
+                const int32_t* input_ids, const uint8_t* modality, void* y,
+                float* logits_out, int32_t* ids_out, float* w_out, uint32_t* d_flags,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* moe_forward that also records caller-created hipEvent_t handles on the
+ * stream around its stages, for per-stage timing: events[0] before the first
+ * stage and events[i + 1] after stage i, i < MOE_FORWARD_STAGES, in the order
+ *   0 router projection, 1 routing, 2 dispatch permutation (+ row gather),
+ *   3 routed gate/up GEMM + clamped SwiGLU, 4 shared gate/up GEMM,
+ *   5 routed down GEMM, 6 shared down GEMM, 7 combine.
+ * Stages that do no work (no shared expert) still record their event.
+ * events may be NULL (= moe_forward). */
+#define MOE_FORWARD_STAGES 8
+int moe_forward_timed(const moe_cfg* cfg, const moe_weights* w, const uint16_t* x,
+                      const int32_t* input_ids, const uint8_t* modality, void* y,
+                      float* logits_out, int32_t* ids_out, float* w_out, uint32_t* d_flags,
+                      void* ws, size_t ws_bytes, void* stream, void* const* events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

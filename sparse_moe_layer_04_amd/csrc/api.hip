@@ -1,0 +1,386 @@
+// C ABI of the MoE layer library: argument validation (complete before any
+// launch), workspace layout and the launch sequence of the forward pass.
+#include <math.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+int device_cu_count() {
+    static int cached_dev = -1;
+    static int cached_cus = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev != cached_dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cached_cus = cus;
+        cached_dev = dev;
+    }
+    return cached_cus;
+}
+
+namespace {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+int route_checks(const float* logits, const float* bias, const int32_t* input_ids,
+                 const int32_t* tid2eid, int T, int E, int k, int n_bias, int V, int mode,
+                 float scale, const int32_t* ids, const float* w) {
+    if (T < 0 || E < 1 || k < 1) return MOE_ERR_SHAPE;
+    if (E > MOE_MAX_E || k > MOE_MAX_K || k > E) return MOE_ERR_UNSUPPORTED;
+    if (mode != MOE_MODE_TOPK && mode != MOE_MODE_HASH) return MOE_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!logits || !ids || !w) return MOE_ERR_NULL;
+    if (mode == MOE_MODE_TOPK) {
+        if (n_bias < 0 || n_bias > 2) return MOE_ERR_SHAPE;
+        if (n_bias > 0 && !bias) return MOE_ERR_NULL;
+    } else {
+        if (!input_ids || !tid2eid) return MOE_ERR_NULL;
+        if (V < 1) return MOE_ERR_SHAPE;
+    }
+    return MOE_OK;
+}
+
+int ffn_checks(int rows, int d, int F, float clamp_limit, int clamp_mode) {
+    if (rows < 0 || d < 64 || F < 64) return MOE_ERR_SHAPE;
+    if (d % 64 || F % 64) return MOE_ERR_UNSUPPORTED;
+    if (!(clamp_limit > 0.0f)) return MOE_ERR_SHAPE;  // also rejects NaN
+    if (clamp_mode != MOE_CLAMP_SYMMETRIC && clamp_mode != MOE_CLAMP_GATE_UPPER)
+        return MOE_ERR_UNSUPPORTED;
+    if ((long long)rows * d >= (1ll << 40) || (long long)rows * F >= (1ll << 40))
+        return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// moe_forward workspace layout
+struct FwdWs {
+    float* logits;
+    int32_t* ids;
+    float* w;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* dest;
+    int32_t* src;
+    uint16_t* x_perm;
+    uint16_t* h;
+    float* y_perm;
+    uint16_t* hs;
+    float* ys;
+    void* perm;
+    size_t total;
+};
+
+FwdWs forward_layout(const moe_cfg* c, char* base) {
+    const size_t T = (size_t)c->T, N = (size_t)c->T * c->k;
+    size_t off = 0;
+    FwdWs w;
+    auto take = [&](size_t bytes) {
+        char* p = base ? base + off : nullptr;
+        off += align256(bytes);
+        return (void*)p;
+    };
+    w.logits = (float*)take(T * c->E * 4);
+    w.ids = (int32_t*)take(N * 4);
+    w.w = (float*)take(N * 4);
+    w.counts = (int32_t*)take((size_t)c->E * 4);
+    w.offsets = (int32_t*)take((size_t)(c->E + 1) * 4);
+    w.dest = (int32_t*)take(N * 4);
+    w.src = (int32_t*)take(N * 4);
+    w.x_perm = (uint16_t*)take(N * c->d * 2);
+    w.h = (uint16_t*)take(N * c->F * 2);
+    w.y_perm = (float*)take(N * c->d * 4);
+    w.hs = (uint16_t*)take(T * (size_t)(c->F_shared > 0 ? c->F_shared : 0) * 2);
+    w.ys = (float*)take(c->F_shared > 0 ? T * c->d * 4 : 0);
+    w.perm = take(permute_workspace_bytes(c->T, c->k, c->E));
+    w.total = off;
+    return w;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case MOE_ERR_UNSUPPORTED: return "unsupported mode or size";
+        case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        case MOE_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+        default: return "unknown status";
+    }
+}
+
+int moe_gate_logits(const uint16_t* x, const uint16_t* w_g, const float* logit_offset, int T,
+                    int d, int E, float* logits, void* stream) {
+    if (T < 0 || E < 1 || d < 64) return MOE_ERR_SHAPE;
+    if (d % 64) return MOE_ERR_UNSUPPORTED;
+    if (E > MOE_MAX_GROUPS) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_g || !logits) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w_g)) return MOE_ERR_ALIGN;
+    GemmArgs g{};
+    g.a = x;
+    g.offsets = nullptr;
+    g.G = 1;
+    g.rows = T;
+    g.K = d;
+    g.N = E;
+    g.w1 = w_g;
+    g.w2 = nullptr;
+    g.offset = logit_offset;
+    g.out = logits;
+    return hip_status(launch_grouped_gemm(EPI_F32_OFFSET, g, as_stream(stream)));
+}
+
+int moe_route(const float* logits, const float* score_bias, const uint8_t* modality,
+              const int32_t* input_ids, const int32_t* tid2eid, int T, int E, int k, int n_bias,
+              int V, int mode, float scale, int32_t* topk_ids, float* topk_w, uint32_t* d_flags,
+              void* stream) {
+    int st = route_checks(logits, score_bias, input_ids, tid2eid, T, E, k, n_bias, V, mode, scale,
+                          topk_ids, topk_w);
+    if (st != MOE_OK || T == 0) return st;
+    return hip_status(launch_route(logits, n_bias > 0 ? score_bias : nullptr, modality, input_ids,
+                                   tid2eid, T, E, k, n_bias, V, mode, scale, topk_ids, topk_w,
+                                   d_flags, as_stream(stream)));
+}
+
+size_t moe_permute_workspace_size(int T, int k, int E) {
+    if (T < 0 || k < 1 || E < 1) return 0;
+    return permute_workspace_bytes(T, k, E);
+}
+
+int moe_permute(const int32_t* topk_ids, const uint16_t* x, int T, int d, int E, int k,
+                int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src, uint16_t* x_perm,
+                uint32_t* d_flags, void* ws, size_t ws_bytes, void* stream) {
+    if (T < 0 || d < 8 || E < 1 || k < 1) return MOE_ERR_SHAPE;
+    if (E > MOE_MAX_E || k > MOE_MAX_K || d % 8) return MOE_ERR_UNSUPPORTED;
+    if ((long long)T * k >= (1ll << 31)) return MOE_ERR_SHAPE;
+    if (!counts || !offsets || !ws) return MOE_ERR_NULL;
+    if (T > 0 && (!topk_ids || !x || !dest || !src || !x_perm)) return MOE_ERR_NULL;
+    if (((uintptr_t)ws & 255u) || ws_bytes < permute_workspace_bytes(T, k, E))
+        return MOE_ERR_WORKSPACE;
+    if (T > 0 && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_ALIGN;
+    return hip_status(launch_permute(topk_ids, x, T, d, E, k, counts, offsets, dest, src, x_perm,
+                                     d_flags, ws, as_stream(stream)));
+}
+
+int moe_expert_ffn(const uint16_t* a, const int32_t* offsets, int G, int rows, int d, int F,
+                   const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                   float clamp_limit, int clamp_mode, uint16_t* h, float* y, void* stream) {
+    if (G < 1) return MOE_ERR_SHAPE;
+    if (G > MOE_MAX_GROUPS) return MOE_ERR_UNSUPPORTED;
+    int st = ffn_checks(rows, d, F, clamp_limit, clamp_mode);
+    if (st != MOE_OK) return st;
+    if (rows == 0) return MOE_OK;
+    if (!a || !offsets || !w_gate || !w_up || !w_down || !h || !y) return MOE_ERR_NULL;
+    if (!aligned16(a) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+        !aligned16(h) || !aligned16(y))
+        return MOE_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    GemmArgs g1{};
+    g1.a = a;
+    g1.offsets = offsets;
+    g1.G = G;
+    g1.rows = rows;
+    g1.K = d;
+    g1.N = F;
+    g1.w1 = w_gate;
+    g1.w2 = w_up;
+    g1.clamp_limit = clamp_limit;
+    g1.clamp_mode = clamp_mode;
+    g1.out = h;
+    hipError_t e = launch_grouped_gemm(EPI_SWIGLU_BF16, g1, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    GemmArgs g2{};
+    g2.a = h;
+    g2.offsets = offsets;
+    g2.G = G;
+    g2.rows = rows;
+    g2.K = F;
+    g2.N = d;
+    g2.w1 = w_down;
+    g2.out = y;
+    return hip_status(launch_grouped_gemm(EPI_F32, g2, s));
+}
+
+int moe_combine(const float* y_perm, const int32_t* dest, const float* topk_w,
+                const float* y_shared, int T, int d, int k, int rows, int out_dtype, void* y,
+                void* stream) {
+    if (T < 0 || d < 8 || k < 1 || rows < 0) return MOE_ERR_SHAPE;
+    if (k > MOE_MAX_K || d % 8) return MOE_ERR_UNSUPPORTED;
+    if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!dest || !topk_w || !y || (rows > 0 && !y_perm)) return MOE_ERR_NULL;
+    if ((y_perm && !aligned16(y_perm)) || (y_shared && !aligned16(y_shared)) || !aligned16(y))
+        return MOE_ERR_ALIGN;
+    return hip_status(launch_combine(y_perm, dest, topk_w, y_shared, T, d, k, rows, out_dtype, y,
+                                     as_stream(stream)));
+}
+
+static int forward_checks(const moe_cfg* c, const moe_weights* w) {
+    if (!c || !w) return MOE_ERR_NULL;
+    if (c->T < 0 || c->E < 1 || c->k < 1 || c->F_shared < 0) return MOE_ERR_SHAPE;
+    if (c->E > MOE_MAX_E || c->k > MOE_MAX_K || c->k > c->E) return MOE_ERR_UNSUPPORTED;
+    int st = ffn_checks(c->T * c->k, c->d, c->F, c->clamp_limit, c->clamp_mode);
+    if (st != MOE_OK) return st;
+    if (c->F_shared % 64) return MOE_ERR_UNSUPPORTED;
+    if ((long long)c->T * c->k >= (1ll << 31)) return MOE_ERR_SHAPE;
+    if (c->mode != MOE_MODE_TOPK && c->mode != MOE_MODE_HASH) return MOE_ERR_UNSUPPORTED;
+    if (c->out_dtype != MOE_OUT_BF16 && c->out_dtype != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
+    if (!(c->scale == c->scale)) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+size_t moe_forward_workspace_size(const moe_cfg* cfg) {
+    if (!cfg || cfg->T < 0 || cfg->E < 1 || cfg->k < 1) return 0;
+    return forward_layout(cfg, nullptr).total;
+}
+
+int moe_forward(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
+                const int32_t* input_ids, const uint8_t* modality, void* y, float* logits_out,
+                int32_t* ids_out, float* w_out, uint32_t* d_flags, void* ws, size_t ws_bytes,
+                void* stream) {
+    return moe_forward_timed(c, w, x, input_ids, modality, y, logits_out, ids_out, w_out, d_flags,
+                             ws, ws_bytes, stream, nullptr);
+}
+
+int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
+                      const int32_t* input_ids, const uint8_t* modality, void* y,
+                      float* logits_out, int32_t* ids_out, float* w_out, uint32_t* d_flags,
+                      void* ws, size_t ws_bytes, void* stream, void* const* events) {
+    int st = forward_checks(c, w);
+    if (st != MOE_OK) return st;
+    if (c->T == 0) return MOE_OK;
+    if (!x || !y || !w->w_g || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL;
+    if (c->F_shared > 0 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_NULL;
+    if (c->mode == MOE_MODE_TOPK) {
+        if (c->n_bias < 0 || c->n_bias > 2) return MOE_ERR_SHAPE;
+        if (c->n_bias > 0 && !w->score_bias) return MOE_ERR_NULL;
+    } else {
+        if (!input_ids || !w->tid2eid) return MOE_ERR_NULL;
+        if (c->V < 1) return MOE_ERR_SHAPE;
+    }
+    if (!ws) return MOE_ERR_NULL;
+    FwdWs L = forward_layout(c, (char*)ws);
+    if (((uintptr_t)ws & 255u) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(w->w_g) || !aligned16(w->w_gate) ||
+        !aligned16(w->w_up) || !aligned16(w->w_down))
+        return MOE_ERR_ALIGN;
+    if (c->F_shared > 0 && (!aligned16(w->s_gate) || !aligned16(w->s_up) || !aligned16(w->s_down)))
+        return MOE_ERR_ALIGN;
+
+    hipStream_t s = as_stream(stream);
+    const int T = c->T, d = c->d, E = c->E, k = c->k, F = c->F, Fs = c->F_shared;
+    float* logits = logits_out ? logits_out : L.logits;
+    int32_t* ids = ids_out ? ids_out : L.ids;
+    float* wts = w_out ? w_out : L.w;
+    hipError_t e;
+    auto mark = [&](int i) -> bool {
+        return !events || hipEventRecord((hipEvent_t)events[i], s) == hipSuccess;
+    };
+    if (!mark(0)) return MOE_ERR_HIP;
+
+    // 1. router projection (+ logit offset)
+    GemmArgs gl{};
+    gl.a = x;
+    gl.G = 1;
+    gl.rows = T;
+    gl.K = d;
+    gl.N = E;
+    gl.w1 = w->w_g;
+    gl.offset = w->logit_offset;
+    gl.out = logits;
+    if ((e = launch_grouped_gemm(EPI_F32_OFFSET, gl, s)) != hipSuccess) return MOE_ERR_HIP;
+    if (!mark(1)) return MOE_ERR_HIP;
+    // 2. routing
+    if ((e = launch_route(logits, c->n_bias > 0 ? w->score_bias : nullptr, modality, input_ids,
+                          w->tid2eid, T, E, k, c->n_bias, c->V, c->mode, c->scale, ids, wts,
+                          d_flags, s)) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (!mark(2)) return MOE_ERR_HIP;
+    // 3. dispatch permutation + row gather
+    if ((e = launch_permute(ids, x, T, d, E, k, L.counts, L.offsets, L.dest, L.src, L.x_perm,
+                            d_flags, L.perm, s)) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (!mark(3)) return MOE_ERR_HIP;
+    const int rows = T * k;
+    // 4. routed experts: gate/up + clamped SwiGLU
+    GemmArgs g1{};
+    g1.a = L.x_perm;
+    g1.offsets = L.offsets;
+    g1.G = E;
+    g1.rows = rows;
+    g1.K = d;
+    g1.N = F;
+    g1.w1 = w->w_gate;
+    g1.w2 = w->w_up;
+    g1.clamp_limit = c->clamp_limit;
+    g1.clamp_mode = c->clamp_mode;
+    g1.out = L.h;
+    if ((e = launch_grouped_gemm(EPI_SWIGLU_BF16, g1, s)) != hipSuccess) return MOE_ERR_HIP;
+    if (!mark(4)) return MOE_ERR_HIP;
+    // 5. shared expert gate/up
+    if (Fs > 0) {
+        GemmArgs gs{};
+        gs.a = x;
+        gs.G = 1;
+        gs.rows = T;
+        gs.K = d;
+        gs.N = Fs;
+        gs.w1 = w->s_gate;
+        gs.w2 = w->s_up;
+        gs.clamp_limit = c->clamp_limit;
+        gs.clamp_mode = c->clamp_mode;
+        gs.out = L.hs;
+        if ((e = launch_grouped_gemm(EPI_SWIGLU_BF16, gs, s)) != hipSuccess) return MOE_ERR_HIP;
+    }
+    if (!mark(5)) return MOE_ERR_HIP;
+    // 6. routed experts: down projection
+    GemmArgs g2{};
+    g2.a = L.h;
+    g2.offsets = L.offsets;
+    g2.G = E;
+    g2.rows = rows;
+    g2.K = F;
+    g2.N = d;
+    g2.w1 = w->w_down;
+    g2.out = L.y_perm;
+    if ((e = launch_grouped_gemm(EPI_F32, g2, s)) != hipSuccess) return MOE_ERR_HIP;
+    if (!mark(6)) return MOE_ERR_HIP;
+    // 7. shared expert down
+    if (Fs > 0) {
+        GemmArgs gs{};
+        gs.a = L.hs;
+        gs.G = 1;
+        gs.rows = T;
+        gs.K = Fs;
+        gs.N = d;
+        gs.w1 = w->s_down;
+        gs.out = L.ys;
+        if ((e = launch_grouped_gemm(EPI_F32, gs, s)) != hipSuccess) return MOE_ERR_HIP;
+    }
+    if (!mark(7)) return MOE_ERR_HIP;
+    // 8. weighted combine + shared add
+    if ((e = launch_combine(L.y_perm, L.dest, wts, Fs > 0 ? L.ys : nullptr, T, d, k, rows,
+                            c->out_dtype, y, s)) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (!mark(8)) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+}  // extern "C"

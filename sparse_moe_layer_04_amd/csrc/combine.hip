@@ -1,0 +1,69 @@
+// Result return merged by routing weight ("Twinkle x Ascend ...", section
+// "FSDP2-4D parallel engine adaptation") plus the always-on shared expert
+// ("MindSpore HyperParallel one-click DeepSeek-V4.1-Flash", section 01):
+//   y[t, o] = y_shared[t, o] + sum_j w[t, j] * y_perm[dest[t, j], o]
+// One workgroup per token; each thread owns 4 consecutive columns per
+// 1024-column pass (16-byte loads of every source row, fully coalesced), the
+// k routed rows are accumulated in slot order in fp32.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+template <int OUT>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
+                                                      const int32_t* __restrict__ dest,
+                                                      const float* __restrict__ w,
+                                                      const float* __restrict__ y_shared, int T,
+                                                      int d, int k, int rows, void* __restrict__ y) {
+    const int t = blockIdx.x;
+    int rj[MOE_MAX_K];
+    float wj[MOE_MAX_K];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K; ++j) {
+        rj[j] = -1;
+        wj[j] = 0.0f;
+        if (j < k) {
+            const int r = dest[(size_t)t * k + j];
+            if (r >= 0 && r < rows) {
+                rj[j] = r;
+                wj[j] = w[(size_t)t * k + j];
+            }
+        }
+    }
+    for (int c = threadIdx.x * 4; c < d; c += 1024) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (y_shared) acc = *(const f32x4*)(y_shared + (size_t)t * d + c);
+#pragma unroll
+        for (int j = 0; j < MOE_MAX_K; ++j) {
+            if (rj[j] < 0) continue;
+            const f32x4 v = *(const f32x4*)(y_perm + (size_t)rj[j] * d + c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(wj[j], v[i], acc[i]);
+        }
+        if (OUT == MOE_OUT_F32) {
+            *(f32x4*)((float*)y + (size_t)t * d + c) = acc;
+        } else {
+            const uint32_t lo = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+            *(u32x2*)((uint16_t*)y + (size_t)t * d + c) = u32x2{lo, hi};
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* w,
+                          const float* y_shared, int T, int d, int k, int rows, int out_dtype,
+                          void* y, hipStream_t stream) {
+    if (T <= 0) return hipSuccess;
+    if (out_dtype == MOE_OUT_F32)
+        hipLaunchKernelGGL(combine_kernel<MOE_OUT_F32>, dim3(T), dim3(256), 0, stream, y_perm,
+                           dest, w, y_shared, T, d, k, rows, y);
+    else
+        hipLaunchKernelGGL(combine_kernel<MOE_OUT_BF16>, dim3(T), dim3(256), 0, stream, y_perm,
+                           dest, w, y_shared, T, d, k, rows, y);
+    return hipGetLastError();
+}
+
+}  // namespace moe

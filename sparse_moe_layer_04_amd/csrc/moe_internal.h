@@ -1,0 +1,73 @@
+// Internal declarations shared by the HIP translation units of the MoE
+// library: kernel launchers (host side) and small device helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- device ----
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits, round to nearest even (quiet NaN kept NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float((uint32_t)h << 16);
+}
+
+// ----------------------------------------------------------------- host -----
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// Grouped GEMM epilogues.
+enum GemmEpilogue : int {
+    EPI_SWIGLU_BF16 = 0,  // out = bf16(silu(clamp(A W1^T)) * clamp(A W2^T))
+    EPI_F32 = 1,          // out = fp32(A W1^T)
+    EPI_F32_OFFSET = 2,   // out = fp32(A W1^T + offset[n])
+};
+
+struct GemmArgs {
+    const uint16_t* a;        // [rows, K] bf16 activations
+    const int32_t* offsets;   // [G+1] device group row offsets, or NULL: one group [0, rows)
+    int G;
+    int rows;
+    int K;
+    int N;                    // weight rows per group (outputs per row)
+    const uint16_t* w1;       // [G, N, K] bf16
+    const uint16_t* w2;       // [G, N, K] bf16 (SWIGLU: up projection)
+    const float* offset;      // [N] (EPI_F32_OFFSET) or NULL
+    float clamp_limit;
+    int clamp_mode;
+    void* out;                // [rows, N] bf16 (SWIGLU) or fp32
+};
+
+hipError_t launch_grouped_gemm(int epilogue, const GemmArgs& g, hipStream_t stream);
+
+hipError_t launch_route(const float* logits, const float* bias, const uint8_t* modality,
+                        const int32_t* input_ids, const int32_t* tid2eid, int T, int E, int k,
+                        int n_bias, int V, int mode, float scale, int32_t* ids, float* w,
+                        uint32_t* flags, hipStream_t stream);
+
+size_t permute_workspace_bytes(int T, int k, int E);
+hipError_t launch_permute(const int32_t* ids, const uint16_t* x, int T, int d, int E, int k,
+                          int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
+                          uint16_t* x_perm, uint32_t* flags, void* ws, hipStream_t stream);
+
+hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* w,
+                          const float* y_shared, int T, int d, int k, int rows, int out_dtype,
+                          void* y, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,210 @@
+// Wavefront router: one 64-lane wave per token.
+//
+// MegaGate order ("HyperParallel accelerates DeepSeek-V4.1 ...", section 2.3):
+// score -> bias ranking -> Top-K -> score extraction -> normalise -> scale,
+// with separate text / vision bias rows; HashRouter variant ("Twinkle x
+// Ascend ...", section "FSDP2-4D parallel engine adaptation"): ids from
+// tid2eid[input_ids], weights still from the gate logits.
+//
+// Each lane owns experts e = lane + 64 i.  The ranking key of an expert packs
+// the order-preserving image of its biased score (high 32 bits) with ~e (low
+// 32 bits), so one unsigned 64-bit max picks (score desc, index asc).  Top-k
+// is k rounds of a wave-wide max (xor-shuffle butterfly) over the lanes'
+// current best keys.  This translation unit is built with FP contraction off:
+// the score function is a fixed sequence of IEEE binary32 operations.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxPerLane = MOE_MAX_E / 64;
+
+// Binary32 sigmoid as a fixed operation sequence (see moe.h): clamp to
+// [-80, 80] (NaN -> -80); z = -x; n = rint(z * log2 e); Cody-Waite
+// r = (z - n*C1) - n*C2 by two fmas with C1 = 0x1.62e4p-1 (exact n*C1) and
+// C2 = fl32(ln2 - C1); exp(r) by the degree-7 Taylor polynomial (Horner, fma)
+// with binary32 coefficients 1/j!; e = p * 2^n; S = 1 / (1 + e), correctly
+// rounded division.
+__device__ __forceinline__ float score_fn(float x) {
+    if (x != x) x = -80.0f;
+    if (x < -80.0f) x = -80.0f;
+    if (x > 80.0f) x = 80.0f;
+    const float log2e = 0x1.715476p+0f;
+    const float c1 = 0x1.62e4p-1f;
+    const float c2 = 0x1.7f7d1cp-20f;
+    float z = -x;
+    float t = z * log2e;
+    float n = __builtin_rintf(t);
+    float r = __builtin_fmaf(-n, c1, z);
+    r = __builtin_fmaf(-n, c2, r);
+    float p = 0x1.a01a02p-13f;              // 1/5040
+    p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);  // 1/720
+    p = __builtin_fmaf(p, r, 0x1.111112p-7f);   // 1/120
+    p = __builtin_fmaf(p, r, 0x1.555556p-5f);   // 1/24
+    p = __builtin_fmaf(p, r, 0x1.555556p-3f);   // 1/6
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    float e = __builtin_ldexpf(p, (int)n);
+    float den = 1.0f + e;
+    return 1.0f / den;
+}
+
+// Order-preserving unsigned image of a binary32 value (finite, no -0).
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
+        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+        uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+template <int NPL>
+__global__ __launch_bounds__(256) void route_topk_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias,
+    const uint8_t* __restrict__ modality, int T, int E, int k, int n_bias, float scale,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float* lt = logits + (size_t)t * E;
+    const float* b = nullptr;
+    if (bias) {
+        int row = (n_bias > 1 && modality && modality[t]) ? 1 : 0;
+        b = bias + (size_t)row * E;
+    }
+    uint64_t keys[NPL];
+    float sc[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        int e = lane + 64 * i;
+        if (e < E) {
+            float s = score_fn(lt[e]);
+            float r = b ? s + b[e] : s;
+            r = r + 0.0f;  // -0 -> +0
+            sc[i] = s;
+            keys[i] = ((uint64_t)ordered_bits(r) << 32) | (uint32_t)(~(uint32_t)e);
+        } else {
+            sc[i] = 0.0f;
+            keys[i] = 0;
+        }
+    }
+    float g_mine = 0.0f;  // lane j < k keeps g_j
+    int id_mine = -1;
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = 0;
+        float best_s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            if (keys[i] > best) {
+                best = keys[i];
+                best_s = sc[i];
+            }
+        }
+        uint64_t win = wave_max_u64(best);
+        int e = (int)(~(uint32_t)win);
+        float s = __shfl(best_s, e & 63, 64);
+        // owner retires the winner
+        if ((e & 63) == lane) {
+#pragma unroll
+            for (int i = 0; i < NPL; ++i)
+                if (lane + 64 * i == e) keys[i] = 0;
+        }
+        if (lane == j) {
+            g_mine = s;
+            id_mine = e;
+        }
+    }
+    // left-to-right fp32 sum of the k gathered (unbiased) scores
+    float sum = __shfl(g_mine, 0, 64);
+    for (int j = 1; j < k; ++j) sum = sum + __shfl(g_mine, j, 64);
+    if (lane < k) {
+        float q = g_mine / sum;
+        ids_out[(size_t)t * k + lane] = id_mine;
+        w_out[(size_t)t * k + lane] = q * scale;
+    }
+}
+
+__global__ __launch_bounds__(256) void route_hash_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ input_ids,
+    const int32_t* __restrict__ tid2eid, int T, int E, int k, int V, float scale,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, uint32_t* __restrict__ flags) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int tok = input_ids[t];
+    uint32_t bad = 0;
+    int id = -1;
+    if (tok < 0 || tok >= V) {
+        bad = MOE_FLAG_BAD_INPUT_ID;
+    } else {
+        if (lane < k) id = tid2eid[(size_t)tok * k + lane];
+        bool oob = lane < k && (id < 0 || id >= E);
+        if (__any(oob)) bad = MOE_FLAG_BAD_EXPERT_ID;
+    }
+    if (bad) {
+        if (lane == 0 && flags) atomicOr(flags, bad);
+        if (lane < k) {
+            ids_out[(size_t)t * k + lane] = -1;
+            w_out[(size_t)t * k + lane] = 0.0f;
+        }
+        return;
+    }
+    float g = 0.0f;
+    if (lane < k) g = score_fn(logits[(size_t)t * E + id]);
+    float sum = __shfl(g, 0, 64);
+    for (int j = 1; j < k; ++j) sum = sum + __shfl(g, j, 64);
+    if (lane < k) {
+        float q = g / sum;
+        ids_out[(size_t)t * k + lane] = id;
+        w_out[(size_t)t * k + lane] = q * scale;
+    }
+}
+
+template <int NPL>
+void launch_topk(dim3 grid, const float* logits, const float* bias, const uint8_t* modality,
+                 int T, int E, int k, int n_bias, float scale, int32_t* ids, float* w,
+                 hipStream_t stream) {
+    hipLaunchKernelGGL(route_topk_kernel<NPL>, grid, dim3(256), 0, stream, logits, bias,
+                       modality, T, E, k, n_bias, scale, ids, w);
+}
+
+}  // namespace
+
+hipError_t launch_route(const float* logits, const float* bias, const uint8_t* modality,
+                        const int32_t* input_ids, const int32_t* tid2eid, int T, int E, int k,
+                        int n_bias, int V, int mode, float scale, int32_t* ids, float* w,
+                        uint32_t* flags, hipStream_t stream) {
+    if (T <= 0) return hipSuccess;
+    dim3 grid((T + 3) / 4);
+    if (mode == MOE_MODE_HASH) {
+        hipLaunchKernelGGL(route_hash_kernel, grid, dim3(256), 0, stream, logits, input_ids,
+                           tid2eid, T, E, k, V, scale, ids, w, flags);
+        return hipGetLastError();
+    }
+    int npl = (E + 63) / 64;
+    if (npl <= 1)
+        launch_topk<1>(grid, logits, bias, modality, T, E, k, n_bias, scale, ids, w, stream);
+    else if (npl <= 2)
+        launch_topk<2>(grid, logits, bias, modality, T, E, k, n_bias, scale, ids, w, stream);
+    else if (npl <= 4)
+        launch_topk<4>(grid, logits, bias, modality, T, E, k, n_bias, scale, ids, w, stream);
+    else if (npl <= 6)
+        launch_topk<6>(grid, logits, bias, modality, T, E, k, n_bias, scale, ids, w, stream);
+    else if (npl <= 8)
+        launch_topk<8>(grid, logits, bias, modality, T, E, k, n_bias, scale, ids, w, stream);
+    else
+        launch_topk<kMaxPerLane>(grid, logits, bias, modality, T, E, k, n_bias, scale, ids, w,
+                                 stream);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,277 @@
+"""Python binding of the C-ABI MoE library (``libmoe_hip.so``).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch supplies device memory and the current HIP stream.  There is
+no fallback: if the library is missing or a call fails, an exception is
+raised.
+"""
+import ctypes
+import os
+import re
+
+import torch
+
+MODE_TOPK = 0
+MODE_HASH = 1
+OUT_BF16 = 0
+OUT_F32 = 1
+CLAMP_SYMMETRIC = 0
+CLAMP_GATE_UPPER = 1
+FLAG_BAD_INPUT_ID = 1
+FLAG_BAD_EXPERT_ID = 2
+FORWARD_STAGES = 8
+STAGE_NAMES = ("router_gemm", "route", "permute", "gate_up_routed", "gate_up_shared",
+               "down_routed", "down_shared", "combine")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_ROOT = os.path.dirname(_HERE)
+HEADER = os.path.join(_ROOT, "include", "moe.h")
+LIBRARY = os.path.join(_HERE, "libmoe_hip.so")
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+class MoeCfg(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int), ("d", ctypes.c_int), ("E", ctypes.c_int),
+                ("k", ctypes.c_int), ("F", ctypes.c_int), ("F_shared", ctypes.c_int),
+                ("mode", ctypes.c_int), ("n_bias", ctypes.c_int), ("V", ctypes.c_int),
+                ("scale", ctypes.c_float), ("clamp_limit", ctypes.c_float),
+                ("clamp_mode", ctypes.c_int), ("out_dtype", ctypes.c_int)]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w_g", "logit_offset", "score_bias", "tid2eid", "w_gate", "w_up", "w_down",
+                 "s_gate", "s_up", "s_down")]
+
+
+def declared_functions():
+    """Names of the functions include/moe.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise MoeError(f"{LIBRARY} is missing: build it with sparse_moe_layer_04_amd/build.py")
+    L = ctypes.CDLL(LIBRARY)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.moe_status_string.argtypes = [I]
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_gate_logits.argtypes = [P, P, P, I, I, I, P, P]
+    L.moe_route.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, P]
+    L.moe_permute_workspace_size.argtypes = [I, I, I]
+    L.moe_permute_workspace_size.restype = S
+    L.moe_permute.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, S, P]
+    L.moe_expert_ffn.argtypes = [P, P, I, I, I, I, P, P, P, F, I, P, P, P]
+    L.moe_combine.argtypes = [P, P, P, P, I, I, I, I, I, P, P]
+    L.moe_forward_workspace_size.argtypes = [ctypes.POINTER(MoeCfg)]
+    L.moe_forward_workspace_size.restype = S
+    L.moe_forward.argtypes = [ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeWeights), P, P, P, P,
+                              P, P, P, P, P, S, P]
+    L.moe_forward_timed.argtypes = L.moe_forward.argtypes + [P]
+    for name in ("moe_gate_logits", "moe_route", "moe_permute", "moe_expert_ffn",
+                 "moe_combine", "moe_forward", "moe_forward_timed"):
+        getattr(L, name).restype = I
+    _lib = L
+    return L
+
+
+def _check(status, what):
+    if status != 0:
+        msg = lib().moe_status_string(status).decode()
+        raise MoeError(f"{what} failed: {msg} ({status})")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t, dtype, name, dims=None):
+    if t is None:
+        raise MoeError(f"{name} is required")
+    if not t.is_cuda:
+        raise MoeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise MoeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise MoeError(f"{name} must be contiguous")
+    if dims is not None and t.dim() != dims:
+        raise MoeError(f"{name} must have {dims} dims")
+    return t
+
+
+def _opt(t, dtype, name):
+    return None if t is None else _need(t, dtype, name)
+
+
+def gate_logits(x, w_g, logit_offset=None, out=None):
+    """logits[T,E] fp32 = x[T,d] @ w_g[E,d]^T (+ logit_offset[E])."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(w_g, torch.bfloat16, "w_g", 2)
+    _opt(logit_offset, torch.float32, "logit_offset")
+    T, d = x.shape
+    E = w_g.shape[0]
+    if out is None:
+        out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check(lib().moe_gate_logits(_ptr(x), _ptr(w_g), _ptr(logit_offset), T, d, E, _ptr(out),
+                                 _stream()), "moe_gate_logits")
+    return out
+
+
+def route(logits, k, scale, score_bias=None, modality=None, input_ids=None, tid2eid=None,
+          mode=MODE_TOPK, flags=None, ids=None, w=None):
+    """Returns (topk_ids[T,k] int32, topk_w[T,k] fp32)."""
+    _need(logits, torch.float32, "logits", 2)
+    T, E = logits.shape
+    _opt(score_bias, torch.float32, "score_bias")
+    _opt(modality, torch.uint8, "modality")
+    _opt(input_ids, torch.int32, "input_ids")
+    _opt(tid2eid, torch.int32, "tid2eid")
+    n_bias = 0 if score_bias is None else score_bias.numel() // E
+    V = 0 if tid2eid is None else tid2eid.shape[0]
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(lib().moe_route(_ptr(logits), _ptr(score_bias), _ptr(modality), _ptr(input_ids),
+                           _ptr(tid2eid), T, E, k, n_bias, V, mode, float(scale), _ptr(ids),
+                           _ptr(w), _ptr(flags), _stream()), "moe_route")
+    return ids, w
+
+
+def permute_workspace_size(T, k, E):
+    return int(lib().moe_permute_workspace_size(T, k, E))
+
+
+def permute(topk_ids, x, E, flags=None, workspace=None):
+    """Returns dict(counts, offsets, dest, src, x_perm)."""
+    _need(topk_ids, torch.int32, "topk_ids", 2)
+    _need(x, torch.bfloat16, "x", 2)
+    T, k = topk_ids.shape
+    d = x.shape[1]
+    dev = x.device
+    ws_bytes = permute_workspace_size(T, k, E)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               dest=torch.empty(T * k, dtype=torch.int32, device=dev),
+               src=torch.empty(T * k, dtype=torch.int32, device=dev),
+               x_perm=torch.empty((T * k, d), dtype=torch.bfloat16, device=dev))
+    _check(lib().moe_permute(_ptr(topk_ids), _ptr(x), T, d, E, k, _ptr(out["counts"]),
+                             _ptr(out["offsets"]), _ptr(out["dest"]), _ptr(out["src"]),
+                             _ptr(out["x_perm"]), _ptr(flags), _ptr(workspace),
+                             workspace.numel(), _stream()), "moe_permute")
+    return out
+
+
+def expert_ffn(a, offsets, w_gate, w_up, w_down, clamp_limit=10.0, clamp_mode=CLAMP_SYMMETRIC,
+               h=None, y=None):
+    """Grouped FFN: returns (h[rows,F] bf16, y[rows,d] fp32)."""
+    _need(a, torch.bfloat16, "a", 2)
+    _need(offsets, torch.int32, "offsets", 1)
+    _need(w_gate, torch.bfloat16, "w_gate", 3)
+    _need(w_up, torch.bfloat16, "w_up", 3)
+    _need(w_down, torch.bfloat16, "w_down", 3)
+    rows, d = a.shape
+    G, F, _ = w_gate.shape
+    if offsets.numel() != G + 1:
+        raise MoeError("offsets must have G + 1 entries")
+    if h is None:
+        h = torch.empty((rows, F), dtype=torch.bfloat16, device=a.device)
+    if y is None:
+        y = torch.empty((rows, d), dtype=torch.float32, device=a.device)
+    _check(lib().moe_expert_ffn(_ptr(a), _ptr(offsets), G, rows, d, F, _ptr(w_gate), _ptr(w_up),
+                                _ptr(w_down), float(clamp_limit), int(clamp_mode), _ptr(h),
+                                _ptr(y), _stream()), "moe_expert_ffn")
+    return h, y
+
+
+def combine(y_perm, dest, topk_w, y_shared=None, out_dtype=OUT_BF16, y=None):
+    """y[T,d] = y_shared + sum_j topk_w[t,j] * y_perm[dest[t,j]]."""
+    _need(y_perm, torch.float32, "y_perm", 2)
+    _need(dest, torch.int32, "dest")
+    _need(topk_w, torch.float32, "topk_w", 2)
+    _opt(y_shared, torch.float32, "y_shared")
+    T, k = topk_w.shape
+    rows, d = y_perm.shape
+    if y is None:
+        dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+        y = torch.empty((T, d), dtype=dt, device=y_perm.device)
+    _check(lib().moe_combine(_ptr(y_perm), _ptr(dest), _ptr(topk_w), _ptr(y_shared), T, d, k,
+                             rows, int(out_dtype), _ptr(y), _stream()), "moe_combine")
+    return y
+
+
+class MoeLayer:
+    """One fine-grained MoE layer on the device: holds the weights, the config
+    and a preallocated workspace; ``forward`` is one C-ABI call."""
+
+    def __init__(self, T, d, E, k, F, F_shared, weights, mode=MODE_TOPK, n_bias=0, V=0,
+                 scale=1.0, clamp_limit=10.0, clamp_mode=CLAMP_SYMMETRIC, out_dtype=OUT_BF16):
+        self.cfg = MoeCfg(T=T, d=d, E=E, k=k, F=F, F_shared=F_shared, mode=mode, n_bias=n_bias,
+                          V=V, scale=float(scale), clamp_limit=float(clamp_limit),
+                          clamp_mode=int(clamp_mode), out_dtype=int(out_dtype))
+        self.weights = dict(weights)
+        _need(self.weights["w_g"], torch.bfloat16, "w_g", 2)
+        for key in ("w_gate", "w_up", "w_down"):
+            _need(self.weights[key], torch.bfloat16, key, 3)
+        if F_shared > 0:
+            for key in ("s_gate", "s_up", "s_down"):
+                _need(self.weights[key], torch.bfloat16, key, 2)
+        _opt(self.weights.get("logit_offset"), torch.float32, "logit_offset")
+        _opt(self.weights.get("score_bias"), torch.float32, "score_bias")
+        _opt(self.weights.get("tid2eid"), torch.int32, "tid2eid")
+        self.cw = MoeWeights(**{n: _ptr(self.weights.get(n)) for n, _ in MoeWeights._fields_})
+        self.device = self.weights["w_g"].device
+        self.ws_bytes = int(lib().moe_forward_workspace_size(ctypes.byref(self.cfg)))
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.flags = torch.zeros(1, dtype=torch.int32, device=self.device)
+
+    @classmethod
+    def from_workload(cls, w, inputs, out_dtype=OUT_BF16):
+        n_bias = 0 if inputs.get("score_bias") is None else inputs["score_bias"].shape[0]
+        return cls(w.T, w.d, w.E, w.k, w.F, w.Fs, inputs, mode=w.mode, n_bias=n_bias, V=w.V,
+                   scale=w.scale, clamp_limit=w.clamp_limit, clamp_mode=w.clamp_mode,
+                   out_dtype=out_dtype)
+
+    def forward(self, x, input_ids=None, modality=None, y=None, logits=None, ids=None, w=None,
+                events=None):
+        """One layer forward (one C-ABI call).  `events`: optional list of
+        FORWARD_STAGES + 1 recorded torch.cuda.Event objects, re-recorded
+        around the stages."""
+        c = self.cfg
+        _need(x, torch.bfloat16, "x", 2)
+        if tuple(x.shape) != (c.T, c.d):
+            raise MoeError(f"x must be [{c.T}, {c.d}]")
+        _opt(input_ids, torch.int32, "input_ids")
+        _opt(modality, torch.uint8, "modality")
+        if y is None:
+            dt = torch.float32 if c.out_dtype == OUT_F32 else torch.bfloat16
+            y = torch.empty((c.T, c.d), dtype=dt, device=x.device)
+        ev = None
+        if events is not None:
+            if len(events) != FORWARD_STAGES + 1:
+                raise MoeError(f"need {FORWARD_STAGES + 1} events")
+            ev = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        _check(lib().moe_forward_timed(ctypes.byref(c), ctypes.byref(self.cw), _ptr(x),
+                                       _ptr(input_ids), _ptr(modality), _ptr(y), _ptr(logits),
+                                       _ptr(ids), _ptr(w), _ptr(self.flags),
+                                       _ptr(self.workspace), self.ws_bytes, _stream(), ev),
+               "moe_forward")
+        return y

@@ -1,0 +1,142 @@
+"""The C-ABI library loads, exports every function include/moe.h declares, and
+rejects bad arguments on the host before any launch (no GPU needed: every
+case below returns before the first HIP call)."""
+import ctypes
+
+import pytest
+
+from sparse_moe_layer_04_amd import ops
+
+ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_ALIGN = -1, -2, -3, -4, -5, -6
+
+
+@pytest.fixture(scope="module")
+def L():
+    return ops.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = ops.declared_functions()
+    assert {"moe_gate_logits", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
+            "moe_forward"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in (0, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_ALIGN):
+        s = L.moe_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert L.moe_status_string(-99).decode() == "unknown status"
+
+
+FAKE = 0x10000  # an aligned non-NULL address; never dereferenced (checks fail first)
+
+
+def route(L, T=4, E=8, k=2, n_bias=0, V=0, mode=0, scale=1.0, logits=FAKE, bias=None, ids=FAKE,
+          w=FAKE, input_ids=None, tid2eid=None):
+    return L.moe_route(logits, bias, None, input_ids, tid2eid, T, E, k, n_bias, V, mode,
+                       ctypes.c_float(scale), ids, w, None, None)
+
+
+def test_route_validation(L):
+    assert route(L, k=0) == ERR_SHAPE
+    assert route(L, E=0) == ERR_SHAPE
+    assert route(L, T=-1) == ERR_SHAPE
+    assert route(L, k=9, E=16) == ERR_UNSUPPORTED
+    assert route(L, k=3, E=2) == ERR_UNSUPPORTED
+    assert route(L, E=2000) == ERR_UNSUPPORTED
+    assert route(L, mode=7) == ERR_UNSUPPORTED
+    assert route(L, scale=float("nan")) == ERR_SHAPE
+    assert route(L, logits=None) == ERR_NULL
+    assert route(L, ids=None) == ERR_NULL
+    assert route(L, n_bias=1, bias=None) == ERR_NULL
+    assert route(L, n_bias=3, bias=FAKE) == ERR_SHAPE
+    assert route(L, mode=1, input_ids=None, tid2eid=FAKE, V=10) == ERR_NULL
+    assert route(L, mode=1, input_ids=FAKE, tid2eid=FAKE, V=0) == ERR_SHAPE
+    assert route(L, T=0, logits=None, ids=None, w=None) == 0   # empty: nothing to do
+
+
+def test_gate_logits_validation(L):
+    assert L.moe_gate_logits(FAKE, FAKE, None, 4, 100, 8, FAKE, None) == ERR_UNSUPPORTED
+    assert L.moe_gate_logits(FAKE, FAKE, None, 4, 32, 8, FAKE, None) == ERR_SHAPE
+    assert L.moe_gate_logits(None, FAKE, None, 4, 128, 8, FAKE, None) == ERR_NULL
+    assert L.moe_gate_logits(FAKE + 8, FAKE, None, 4, 128, 8, FAKE, None) == ERR_ALIGN
+    assert L.moe_gate_logits(None, None, None, 0, 128, 8, None, None) == 0
+
+
+def test_permute_validation(L):
+    need = L.moe_permute_workspace_size(16, 2, 8)
+    assert need > 0
+    args = lambda **kw: [kw.get("ids", FAKE), kw.get("x", FAKE), kw.get("T", 16), kw.get("d", 64),
+                         kw.get("E", 8), kw.get("k", 2), FAKE, FAKE, FAKE, FAKE,
+                         kw.get("xp", FAKE), None, kw.get("ws", FAKE), kw.get("wsb", need), None]
+    assert L.moe_permute(*args(ws=None)) == ERR_NULL
+    assert L.moe_permute(*args(wsb=need - 1)) == ERR_WORKSPACE
+    assert L.moe_permute(*args(ws=FAKE + 16)) == ERR_WORKSPACE
+    assert L.moe_permute(*args(d=12)) == ERR_UNSUPPORTED
+    assert L.moe_permute(*args(k=9)) == ERR_UNSUPPORTED
+    assert L.moe_permute(*args(E=0)) == ERR_SHAPE
+    assert L.moe_permute(*args(x=FAKE + 2)) == ERR_ALIGN
+    assert L.moe_permute(*args(ids=None)) == ERR_NULL
+
+
+def test_expert_ffn_validation(L):
+    def ffn(G=2, rows=10, d=128, F=64, L_=10.0, mode=0, a=FAKE, h=FAKE, off=FAKE):
+        return L.moe_expert_ffn(a, off, G, rows, d, F, FAKE, FAKE, FAKE, ctypes.c_float(L_), mode,
+                                h, FAKE, None)
+    assert ffn(G=0) == ERR_SHAPE
+    assert ffn(G=5000) == ERR_UNSUPPORTED
+    assert ffn(d=96) == ERR_UNSUPPORTED
+    assert ffn(F=32) == ERR_SHAPE
+    assert ffn(L_=0.0) == ERR_SHAPE
+    assert ffn(L_=float("nan")) == ERR_SHAPE
+    assert ffn(mode=2) == ERR_UNSUPPORTED
+    assert ffn(a=None) == ERR_NULL
+    assert ffn(off=None) == ERR_NULL
+    assert ffn(h=FAKE + 4) == ERR_ALIGN
+    assert ffn(rows=0, a=None) == 0
+
+
+def test_combine_validation(L):
+    def comb(T=4, d=64, k=2, rows=8, out=0, yp=FAKE, y=FAKE):
+        return L.moe_combine(yp, FAKE, FAKE, None, T, d, k, rows, out, y, None)
+    assert comb(k=0) == ERR_SHAPE
+    assert comb(k=9) == ERR_UNSUPPORTED
+    assert comb(d=12) == ERR_UNSUPPORTED
+    assert comb(out=5) == ERR_UNSUPPORTED
+    assert comb(yp=None) == ERR_NULL
+    assert comb(y=FAKE + 4) == ERR_ALIGN
+    assert comb(T=0, yp=None, y=None) == 0
+
+
+def test_forward_validation(L):
+    cfg = ops.MoeCfg(T=8, d=128, E=8, k=2, F=64, F_shared=64, mode=0, n_bias=1, V=0, scale=1.0,
+                     clamp_limit=10.0, clamp_mode=0, out_dtype=0)
+    w = ops.MoeWeights(w_g=FAKE, logit_offset=None, score_bias=FAKE, tid2eid=None, w_gate=FAKE,
+                       w_up=FAKE, w_down=FAKE, s_gate=FAKE, s_up=FAKE, s_down=FAKE)
+    need = L.moe_forward_workspace_size(ctypes.byref(cfg))
+    assert need > 0
+
+    def fwd(c=cfg, wt=w, x=FAKE, ws=FAKE, wsb=need, ids=None):
+        return L.moe_forward(ctypes.byref(c), ctypes.byref(wt), x, ids, None, FAKE, None, None,
+                             None, None, ws, wsb, None)
+    assert L.moe_forward(None, ctypes.byref(w), FAKE, None, None, FAKE, None, None, None, None,
+                         FAKE, need, None) == ERR_NULL
+    assert fwd(x=None) == ERR_NULL
+    assert fwd(ws=None) == ERR_NULL
+    assert fwd(wsb=need - 1) == ERR_WORKSPACE
+    assert fwd(x=FAKE + 2) == ERR_ALIGN
+    for field, val, code in (("k", 9, ERR_UNSUPPORTED), ("k", 0, ERR_SHAPE),
+                             ("d", 100, ERR_UNSUPPORTED), ("F_shared", 32, ERR_UNSUPPORTED),
+                             ("mode", 3, ERR_UNSUPPORTED), ("out_dtype", 2, ERR_UNSUPPORTED),
+                             ("clamp_limit", -1.0, ERR_SHAPE), ("E", 4096, ERR_UNSUPPORTED)):
+        c = ops.MoeCfg.from_buffer_copy(cfg)
+        setattr(c, field, val)
+        assert fwd(c=c) == code, field
+    c = ops.MoeCfg.from_buffer_copy(cfg)
+    c.mode = 1
+    c.V = 100
+    assert fwd(c=c) == ERR_NULL                      # hash mode needs input_ids + tid2eid
+    c.T = 0
+    assert fwd(c=c, x=None, ws=None) == 0
