@@ -121,6 +121,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload index (0-4)")
     ap.add_argument("--out-dtype", choices=["bf16", "f32"], default="bf16")
+    ap.add_argument("--layout", choices=["packed", "plain"], default="packed",
+                    help="weight layout: packed once at load time (moe_pack_weights) or "
+                         "the plain [out, in] matrices")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle CPU work for the baseline (0: skip)")
     args = ap.parse_args()
@@ -138,7 +141,8 @@ def main():
     print(f"# generating workload {w.name}", file=sys.stderr, flush=True)
     inp = wl.make_inputs(w, dev)
     out_dtype = ops.OUT_F32 if args.out_dtype == "f32" else ops.OUT_BF16
-    layer = ops.MoeLayer.from_workload(w, inp, out_dtype=out_dtype)
+    layer = ops.MoeLayer.from_workload(w, inp, out_dtype=out_dtype,
+                                       packed=args.layout == "packed")
     y = torch.empty((w.T, w.d), dtype=torch.float32 if out_dtype == ops.OUT_F32 else torch.bfloat16,
                     device=dev)
     ids = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
@@ -213,7 +217,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": dict(w.describe(), out_dtype=args.out_dtype, non_empty_experts=n_nonempty,
+        "config": dict(w.describe(), out_dtype=args.out_dtype, weight_layout=args.layout,
+                       non_empty_experts=n_nonempty,
                        max_rows_per_expert=int(counts.max())),
         "grouped_gemm_tflops": gg_f / gg_t / 1e12,
         "grouped_gemm_mfma_frac": gg_f / gg_t / PEAK_BF16,

@@ -218,6 +218,19 @@ int moe_expert_ffn(const uint16_t* a, const int32_t* offsets, int G, int rows, i
     return hip_status(launch_grouped_gemm(EPI_F32, g2, s));
 }
 
+size_t moe_packed_weight_bytes(int G, int N, int K) {
+    if (G < 1 || N < 1 || K < 64 || K % 64) return 0;
+    return packed_weight_elems(G, N, K) * 2;
+}
+
+int moe_pack_weights(const uint16_t* src, int G, int N, int K, uint16_t* dst, void* stream) {
+    if (G < 1 || N < 1 || K < 64) return MOE_ERR_SHAPE;
+    if (K % 64) return MOE_ERR_UNSUPPORTED;
+    if (!src || !dst) return MOE_ERR_NULL;
+    if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_ALIGN;
+    return hip_status(launch_pack_weights(src, dst, G, N, K, as_stream(stream)));
+}
+
 int moe_combine(const float* y_perm, const int32_t* dest, const float* topk_w,
                 const float* y_shared, int T, int d, int k, int rows, int out_dtype, void* y,
                 void* stream) {
@@ -243,6 +256,7 @@ static int forward_checks(const moe_cfg* c, const moe_weights* w) {
     if (c->mode != MOE_MODE_TOPK && c->mode != MOE_MODE_HASH) return MOE_ERR_UNSUPPORTED;
     if (c->out_dtype != MOE_OUT_BF16 && c->out_dtype != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
     if (!(c->scale == c->scale)) return MOE_ERR_SHAPE;
+    if (w->packed != 0 && w->packed != 1) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -303,6 +317,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     gl.K = d;
     gl.N = E;
     gl.w1 = w->w_g;
+    gl.packed = w->packed;
     gl.offset = w->logit_offset;
     gl.out = logits;
     if ((e = launch_grouped_gemm(EPI_F32_OFFSET, gl, s)) != hipSuccess) return MOE_ERR_HIP;
@@ -329,6 +344,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g1.N = F;
     g1.w1 = w->w_gate;
     g1.w2 = w->w_up;
+    g1.packed = w->packed;
     g1.clamp_limit = c->clamp_limit;
     g1.clamp_mode = c->clamp_mode;
     g1.out = L.h;
@@ -344,6 +360,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
         gs.N = Fs;
         gs.w1 = w->s_gate;
         gs.w2 = w->s_up;
+        gs.packed = w->packed;
         gs.clamp_limit = c->clamp_limit;
         gs.clamp_mode = c->clamp_mode;
         gs.out = L.hs;
@@ -359,6 +376,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g2.K = F;
     g2.N = d;
     g2.w1 = w->w_down;
+    g2.packed = w->packed;
     g2.out = L.y_perm;
     if ((e = launch_grouped_gemm(EPI_F32, g2, s)) != hipSuccess) return MOE_ERR_HIP;
     if (!mark(6)) return MOE_ERR_HIP;
@@ -371,6 +389,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
         gs.K = Fs;
         gs.N = d;
         gs.w1 = w->s_down;
+        gs.packed = w->packed;
         gs.out = L.ys;
         if ((e = launch_grouped_gemm(EPI_F32, gs, s)) != hipSuccess) return MOE_ERR_HIP;
     }

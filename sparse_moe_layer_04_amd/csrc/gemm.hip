@@ -10,39 +10,47 @@
 //   - a tile is 128 activation rows x 256 weight rows (SwiGLU: 128 features
 //     x {gate, up}); each wave owns 64 weight rows (two 32-row MFMA blocks)
 //     against all 128 rows (four 32-row blocks): 8 accumulators of 32x32.
-//   - K advances in 128-wide stages.  The activation tile of a stage goes
-//     global -> registers -> LDS (double buffered, rows padded to 272 B);
-//     every weight element is used by exactly one wave, so weights go
-//     straight from global memory into the MFMA operand registers, double
-//     buffered one stage ahead (no LDS round trip for the streamed operand).
-//   - K order inside a stage: lane half h (lane / 32) holds k in
-//     [64 h, 64 h + 64); substep q uses k = 64 h + 8 q + [0, 8) from both
-//     operands, so each lane streams 128 contiguous weight bytes per stage.
+//   - K advances in 64-wide stages, 4 MFMA substeps of 16 each.  Substep q
+//     pairs k-chunk 2q (lanes 0-31) and 2q+1 (lanes 32-63) of both operands.
+//   - Weights: every weight element is used by exactly one wave, so they go
+//     straight from memory into the MFMA operand registers through a 4-deep
+//     register ring (stage j computes while stages j+1..j+3 are in flight:
+//     96 KB per CU).  Every load is issued unconditionally (tail stages and
+//     padding rows read clamped, valid addresses), so the in-order vmcnt
+//     accounting never collapses to a full drain.
+//   - Activations: each stage's 128 x 64 tile goes global -> registers -> LDS
+//     (3-deep LDS ring, rows padded to 144 B; loads issued two stages ahead),
+//     one barrier per stage.
+//   - Weight layouts: [out, in] row-major, or the packed layout written by
+//     moe_pack_weights, in which the 16-byte fragments one wave loads for one
+//     substep are 1 KB contiguous in lane order (fully coalesced loads).
 //   - MFMA operand A = weights (D rows = weight rows), operand B = the
 //     activation rows (D cols = activation rows): lane l holds activation row
 //     l % 32 and weight rows 8 (i / 4) + 4 (l / 32) + i % 4 of accumulator
 //     element i, so epilogue stores are 4 consecutive outputs per lane.
 // Scheduling: persistent grid; every workgroup builds the per-group m-tile
-// prefix in LDS from the device offsets (no host sync), work items are
+// prefix in LDS from the device offsets (no host sync); work items are
 // ordered (group, n-tile, m-tile) and split into 8 contiguous ranges, one
-// per XCD (workgroup id mod 8), so the m-tiles and n-tiles of one expert run
-// together on one XCD and share its L2 for the activation rows and weights.
+// per XCD (workgroup id mod 8), so the tiles of one expert run together on
+// one XCD and share its L2 for the activation rows and weights.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 constexpr int BM = 128;
-constexpr int BK = 128;
+constexpr int BK = 64;
 constexpr int kLdsRow = BK * 2 + 16;   // bytes per activation row in LDS
 constexpr int kLdsStage = BM * kLdsRow;
+constexpr int kLdsStages = 3;
+constexpr int kWRing = 4;
 
 __device__ __forceinline__ float clamp_sym(float v, float L) { return fminf(fmaxf(v, -L), L); }
 
-template <int EPI>
+template <int EPI, bool PACKED>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs args) {
     extern __shared__ __align__(16) unsigned char smem[];
-    int* tile_prefix = (int*)(smem + 2 * kLdsStage);
+    int* tile_prefix = (int*)(smem + kLdsStages * kLdsStage);
     __shared__ int scan_sh[4];
 
     const int tid = threadIdx.x;
@@ -98,8 +106,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs args) {
     const int per_xcd = gridDim.x >> 3;
     const long long q_lo = Q * xcd / 8, q_hi = Q * (xcd + 1) / 8;
 
-    const size_t KN = (size_t)K * N;
-    const int S = (K + BK - 1) / BK;
+    const int S = K / BK;                 // K is a multiple of 64
+    const int NB = (N + 31) >> 5;         // 32-row weight blocks per group
+    const size_t w_group = PACKED ? (size_t)NB * 32 * K : (size_t)N * K;
 
     for (long long q = q_lo + (blockIdx.x >> 3); q < q_hi; q += per_xcd) {
         // ---- decode (group, n-tile, m-tile) ----
@@ -124,32 +133,35 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs args) {
         }
         const int row0 = grp_lo + m_tile * BM;
 
-        // ---- operand pointers ----
-        // activation tile: thread loads 16 B chunks (row = tid/16 + 16 i, col16 = tid % 16)
-        const uint16_t* a_ptr[8];
+        // activation tile: thread loads 16 B chunks (row = tid/8 + 32 i, chunk = tid % 8)
+        const uint16_t* a_ptr[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = min(row0 + (tid >> 4) + 16 * i, grp_hi - 1);
-            a_ptr[i] = args.a + (size_t)r * K + (tid & 15) * 8;
+        for (int i = 0; i < 4; ++i) {
+            const int r = min(row0 + (tid >> 3) + 32 * i, grp_hi - 1);
+            a_ptr[i] = args.a + (size_t)r * K + (tid & 7) * 8;
         }
+        // weight rows of this wave: blocks nb0, nb1 (32 rows each)
         const int n_wave = (EPI == EPI_SWIGLU_BF16) ? n_tile * 128 + wave * 32
                                                     : n_tile * 256 + wave * 64;
         const bool active = n_wave < N;
         const uint16_t* w_ptr0;
         const uint16_t* w_ptr1;
         {
-            const uint16_t* wbase1 = args.w1 + (size_t)g * KN;
-            int r0, r1;
-            if (EPI == EPI_SWIGLU_BF16) {
-                r0 = min(n_wave + l32, N - 1);
-                r1 = r0;
-                w_ptr1 = args.w2 + (size_t)g * KN + (size_t)r1 * K + half * 64;
+            const uint16_t* base1 = args.w1 + (size_t)g * w_group;
+            const uint16_t* base2 = (EPI == EPI_SWIGLU_BF16 ? args.w2 : args.w1) +
+                                    (size_t)g * w_group;
+            int nb0 = min(n_wave >> 5, NB - 1);
+            int nb1 = (EPI == EPI_SWIGLU_BF16) ? nb0 : min((n_wave >> 5) + 1, NB - 1);
+            if (PACKED) {
+                // [nb][stage][substep][lane][8]
+                w_ptr0 = base1 + (size_t)nb0 * 32 * K + lane * 8;
+                w_ptr1 = base2 + (size_t)nb1 * 32 * K + lane * 8;
             } else {
-                r0 = min(n_wave + l32, N - 1);
-                r1 = min(n_wave + 32 + l32, N - 1);
-                w_ptr1 = wbase1 + (size_t)r1 * K + half * 64;
+                const int r0 = min(nb0 * 32 + l32, N - 1);
+                const int r1 = min(nb1 * 32 + l32, N - 1);
+                w_ptr0 = base1 + (size_t)r0 * K + half * 8;
+                w_ptr1 = base2 + (size_t)r1 * K + half * 8;
             }
-            w_ptr0 = wbase1 + (size_t)r0 * K + half * 64;
         }
 
         f32x16 acc[2][4];
@@ -160,84 +172,92 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs args) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[b][tb][i] = 0.0f;
 
-        u32x4 areg[8];
-        bf16x8 wa0[8], wa1[8], wb0[8], wb1[8];
+        u32x4 areg[2][4];
+        bf16x8 wr[kWRing][2][4];
 
-        auto load_a = [&](int s) {
-            const int k0 = s * BK;
-            const int kval = K - k0;
+        auto load_a = [&](int j, u32x4* dst) {
+            const int k0 = min(j, S - 1) * BK;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if ((tid & 15) * 8 < kval)
-                    areg[i] = *(const u32x4*)(a_ptr[i] + k0);
-                else
-                    areg[i] = u32x4{0, 0, 0, 0};
-            }
+            for (int i = 0; i < 4; ++i) dst[i] = *(const u32x4*)(a_ptr[i] + k0);
         };
-        auto store_a = [&](int buf) {
-            unsigned char* base = smem + buf * kLdsStage;
+        auto store_a = [&](int j, const u32x4* src) {
+            unsigned char* base = smem + (j % kLdsStages) * kLdsStage;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *(u32x4*)(base + ((tid >> 4) + 16 * i) * kLdsRow + (tid & 15) * 16) = areg[i];
+            for (int i = 0; i < 4; ++i)
+                *(u32x4*)(base + ((tid >> 3) + 32 * i) * kLdsRow + (tid & 7) * 16) = src[i];
         };
-        auto load_w = [&](int s, bf16x8* w0, bf16x8* w1) {
-            const int k0 = s * BK;
-            if (half * 64 < K - k0) {
+        auto load_w = [&](int j, bf16x8 (*dst)[4]) {
+            const int js = min(j, S - 1);
 #pragma unroll
-                for (int v = 0; v < 8; ++v) {
-                    w0[v] = *(const bf16x8*)(w_ptr0 + k0 + v * 8);
-                    w1[v] = *(const bf16x8*)(w_ptr1 + k0 + v * 8);
-                }
-            } else {
-#pragma unroll
-                for (int v = 0; v < 8; ++v) {
-                    w0[v] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-                    w1[v] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            for (int qq = 0; qq < 4; ++qq) {
+                if (PACKED) {
+                    const size_t off = (size_t)js * 2048 + qq * 512;
+                    dst[0][qq] = *(const bf16x8*)(w_ptr0 + off);
+                    dst[1][qq] = *(const bf16x8*)(w_ptr1 + off);
+                } else {
+                    const size_t off = (size_t)js * BK + qq * 16;
+                    dst[0][qq] = *(const bf16x8*)(w_ptr0 + off);
+                    dst[1][qq] = *(const bf16x8*)(w_ptr1 + off);
                 }
             }
         };
-        auto compute = [&](int buf, const bf16x8* w0, const bf16x8* w1) {
-            const unsigned char* base = smem + buf * kLdsStage + l32 * kLdsRow + half * 128;
+        auto compute = [&](int j, bf16x8 (*w)[4]) {
+            const unsigned char* base =
+                smem + (j % kLdsStages) * kLdsStage + l32 * kLdsRow + half * 16;
 #pragma unroll
-            for (int qq = 0; qq < 8; ++qq) {
+            for (int qq = 0; qq < 4; ++qq) {
                 bf16x8 bt[4];
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb)
-                    bt[tb] = *(const bf16x8*)(base + tb * 32 * kLdsRow + qq * 16);
+                    bt[tb] = *(const bf16x8*)(base + tb * 32 * kLdsRow + qq * 32);
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
-                    acc[0][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w0[qq], bt[tb],
+                    acc[0][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[0][qq], bt[tb],
                                                                           acc[0][tb], 0, 0, 0);
-                    acc[1][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w1[qq], bt[tb],
+                    acc[1][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[1][qq], bt[tb],
                                                                           acc[1][tb], 0, 0, 0);
                 }
             }
         };
 
-        // ---- K loop: two stages per iteration (static register buffers) ----
-        load_a(0);
-        if (active) {
-            load_w(0, wa0, wa1);
-            if (S > 1) load_w(1, wb0, wb1);
-        }
-        store_a(0);
+        // ---- prologue: LDS holds A(0); areg[1] = A(1); wr[0..2] = W(0..2) ----
+        // (issue order A(0) W(0) W(1) A(1) W(2) matches the steady state, in
+        // which A(j+1) is followed by W(j+2) and the next stage's A, W)
+        load_a(0, areg[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(0, wr[0]);
+        load_w(1, wr[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(1, areg[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(2, wr[2]);
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(0, areg[0]);
         __syncthreads();
-        for (int s = 0; s < S; s += 2) {
-            if (s + 1 < S) load_a(s + 1);
-            if (active) {
-                compute(0, wa0, wa1);
-                if (s + 2 < S) load_w(s + 2, wa0, wa1);
-            }
-            if (s + 1 < S) store_a(1);
-            __syncthreads();
-            if (s + 1 >= S) break;
-            if (s + 2 < S) load_a(s + 2);
-            if (active) {
-                compute(1, wb0, wb1);
-                if (s + 3 < S) load_w(s + 3, wb0, wb1);
-            }
-            if (s + 2 < S) store_a(0);
-            __syncthreads();
+
+        // ---- main loop: 4 stages per iteration (static register rings) ----
+        // stage j: issue A(j+2) -> areg[j%2], W(j+3) -> wr[(j+3)%4]; compute j;
+        // store A(j+1) (areg[(j+1)%2]) into LDS slot (j+1)%3; barrier.
+        for (int s = 0; s < S; s += 4) {
+// (scheduling barriers keep each stage's loads in issue order A then W, so
+// the in-order vmcnt waits for A(j+1) never cover W(j+2) or W(j+3))
+#define MOE_GEMM_STAGE(U)                                              \
+    {                                                                  \
+        const int j = s + (U);                                         \
+        load_a(j + 2, areg[(U) & 1]);                                  \
+        __builtin_amdgcn_sched_barrier(0);                             \
+        load_w(j + 3, wr[((U) + 3) & 3]);                              \
+        __builtin_amdgcn_sched_barrier(0);                             \
+        if (active && j < S) compute(j, wr[(U) & 3]);                  \
+        __builtin_amdgcn_sched_barrier(0);                             \
+        store_a(j + 1, areg[((U) + 1) & 1]);                           \
+        __syncthreads();                                               \
+    }
+            MOE_GEMM_STAGE(0)
+            MOE_GEMM_STAGE(1)
+            MOE_GEMM_STAGE(2)
+            MOE_GEMM_STAGE(3)
+#undef MOE_GEMM_STAGE
         }
 
         if (!active) continue;
@@ -302,38 +322,85 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs args) {
     }
 }
 
-template <int EPI>
+// Packed weight layout: [G][NB = ceil(N/32)][S = K/64][4][64 lanes][8 bf16];
+// fragment (nb, s, q, lane) = W[nb*32 + lane%32][s*64 + 16 q + 8 (lane/32) .. +8],
+// rows >= N zero-filled.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ src,
+                                                           uint16_t* __restrict__ dst, int N,
+                                                           int K, long long nfrag_group,
+                                                           long long nfrag) {
+    const long long f = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (f >= nfrag) return;
+    const long long g = f / nfrag_group;
+    long long r = f - g * nfrag_group;
+    const int lane = (int)(r & 63);
+    r >>= 6;
+    const int qq = (int)(r & 3);
+    r >>= 2;
+    const int S = K / BK;
+    const int s = (int)(r % S);
+    const int nb = (int)(r / S);
+    const int row = nb * 32 + (lane & 31);
+    const int col = s * BK + 16 * qq + 8 * (lane >> 5);
+    u32x4 v = {0, 0, 0, 0};
+    if (row < N) v = *(const u32x4*)(src + ((size_t)g * N + row) * K + col);
+    *(u32x4*)(dst + (size_t)f * 8) = v;
+}
+
+template <int EPI, bool PACKED>
 hipError_t launch_epi(const GemmArgs& g, hipStream_t stream) {
     static int configured_device = -1;
     static int grid = 0;
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
-    const size_t lds = 2 * kLdsStage + (size_t)(MOE_MAX_GROUPS + 1) * sizeof(int);
+    const size_t lds = kLdsStages * kLdsStage + (size_t)(MOE_MAX_GROUPS + 1) * sizeof(int);
     if (configured_device != dev) {
-        err = hipFuncSetAttribute((const void*)grouped_gemm_kernel<EPI>,
+        err = hipFuncSetAttribute((const void*)grouped_gemm_kernel<EPI, PACKED>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess) return err;
         int occ = 0;
-        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, grouped_gemm_kernel<EPI>, 256,
-                                                           lds);
+        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, grouped_gemm_kernel<EPI, PACKED>,
+                                                           256, lds);
         if (err != hipSuccess) return err;
         if (occ < 1) occ = 1;
         grid = device_cu_count() * occ;
         grid = (grid + 7) & ~7;
         configured_device = dev;
     }
-    hipLaunchKernelGGL(grouped_gemm_kernel<EPI>, dim3(grid), dim3(256), lds, stream, g);
+    hipLaunchKernelGGL((grouped_gemm_kernel<EPI, PACKED>), dim3(grid), dim3(256), lds, stream, g);
     return hipGetLastError();
 }
 
 }  // namespace
 
+size_t packed_weight_elems(int G, int N, int K) {
+    return (size_t)G * (size_t)((N + 31) / 32) * 32 * (size_t)K;
+}
+
+hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int G, int N, int K,
+                               hipStream_t stream) {
+    const long long nfrag_group = (long long)((N + 31) / 32) * (K / BK) * 4 * 64;
+    const long long nfrag = nfrag_group * G;
+    if (nfrag == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((nfrag + 255) / 256)), dim3(256), 0,
+                       stream, src, dst, N, K, nfrag_group, nfrag);
+    return hipGetLastError();
+}
+
 hipError_t launch_grouped_gemm(int epilogue, const GemmArgs& g, hipStream_t stream) {
+    if (g.packed) {
+        switch (epilogue) {
+            case EPI_SWIGLU_BF16: return launch_epi<EPI_SWIGLU_BF16, true>(g, stream);
+            case EPI_F32: return launch_epi<EPI_F32, true>(g, stream);
+            case EPI_F32_OFFSET: return launch_epi<EPI_F32_OFFSET, true>(g, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (epilogue) {
-        case EPI_SWIGLU_BF16: return launch_epi<EPI_SWIGLU_BF16>(g, stream);
-        case EPI_F32: return launch_epi<EPI_F32>(g, stream);
-        case EPI_F32_OFFSET: return launch_epi<EPI_F32_OFFSET>(g, stream);
+        case EPI_SWIGLU_BF16: return launch_epi<EPI_SWIGLU_BF16, false>(g, stream);
+        case EPI_F32: return launch_epi<EPI_F32, false>(g, stream);
+        case EPI_F32_OFFSET: return launch_epi<EPI_F32_OFFSET, false>(g, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -51,10 +51,14 @@ struct GemmArgs {
     const float* offset;      // [N] (EPI_F32_OFFSET) or NULL
     float clamp_limit;
     int clamp_mode;
+    int packed;               // weights in the moe_pack_weights layout
     void* out;                // [rows, N] bf16 (SWIGLU) or fp32
 };
 
 hipError_t launch_grouped_gemm(int epilogue, const GemmArgs& g, hipStream_t stream);
+size_t packed_weight_elems(int G, int N, int K);
+hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int G, int N, int K,
+                               hipStream_t stream);
 
 hipError_t launch_route(const float* logits, const float* bias, const uint8_t* modality,
                         const int32_t* input_ids, const int32_t* tid2eid, int T, int E, int k,

@@ -43,10 +43,13 @@ class MoeCfg(ctypes.Structure):
                 ("clamp_mode", ctypes.c_int), ("out_dtype", ctypes.c_int)]
 
 
+WEIGHT_NAMES = ("w_g", "logit_offset", "score_bias", "tid2eid", "w_gate", "w_up", "w_down",
+                "s_gate", "s_up", "s_down")
+MATRIX_NAMES = ("w_g", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")
+
+
 class MoeWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w_g", "logit_offset", "score_bias", "tid2eid", "w_gate", "w_up", "w_down",
-                 "s_gate", "s_up", "s_down")]
+    _fields_ = [("packed", ctypes.c_int)] + [(n, ctypes.c_void_p) for n in WEIGHT_NAMES]
 
 
 def declared_functions():
@@ -75,13 +78,16 @@ def lib():
     L.moe_permute.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, S, P]
     L.moe_expert_ffn.argtypes = [P, P, I, I, I, I, P, P, P, F, I, P, P, P]
     L.moe_combine.argtypes = [P, P, P, P, I, I, I, I, I, P, P]
+    L.moe_packed_weight_bytes.argtypes = [I, I, I]
+    L.moe_packed_weight_bytes.restype = S
+    L.moe_pack_weights.argtypes = [P, I, I, I, P, P]
     L.moe_forward_workspace_size.argtypes = [ctypes.POINTER(MoeCfg)]
     L.moe_forward_workspace_size.restype = S
     L.moe_forward.argtypes = [ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeWeights), P, P, P, P,
                               P, P, P, P, P, S, P]
     L.moe_forward_timed.argtypes = L.moe_forward.argtypes + [P]
     for name in ("moe_gate_logits", "moe_route", "moe_permute", "moe_expert_ffn",
-                 "moe_combine", "moe_forward", "moe_forward_timed"):
+                 "moe_combine", "moe_forward", "moe_forward_timed", "moe_pack_weights"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -218,12 +224,26 @@ def combine(y_perm, dest, topk_w, y_shared=None, out_dtype=OUT_BF16, y=None):
     return y
 
 
+def pack_weights(w):
+    """Packed copy (moe_pack_weights layout) of bf16 weights [G,N,K] or [N,K]."""
+    _need(w, torch.bfloat16, "w")
+    shape = tuple(w.shape)
+    G, N, K = (1,) + shape if w.dim() == 2 else shape
+    nbytes = int(lib().moe_packed_weight_bytes(G, N, K))
+    if nbytes == 0:
+        raise MoeError(f"cannot pack weights of shape {shape}")
+    out = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=w.device)
+    _check(lib().moe_pack_weights(_ptr(w), G, N, K, _ptr(out), _stream()), "moe_pack_weights")
+    return out
+
+
 class MoeLayer:
     """One fine-grained MoE layer on the device: holds the weights, the config
     and a preallocated workspace; ``forward`` is one C-ABI call."""
 
     def __init__(self, T, d, E, k, F, F_shared, weights, mode=MODE_TOPK, n_bias=0, V=0,
-                 scale=1.0, clamp_limit=10.0, clamp_mode=CLAMP_SYMMETRIC, out_dtype=OUT_BF16):
+                 scale=1.0, clamp_limit=10.0, clamp_mode=CLAMP_SYMMETRIC, out_dtype=OUT_BF16,
+                 packed=False):
         self.cfg = MoeCfg(T=T, d=d, E=E, k=k, F=F, F_shared=F_shared, mode=mode, n_bias=n_bias,
                           V=V, scale=float(scale), clamp_limit=float(clamp_limit),
                           clamp_mode=int(clamp_mode), out_dtype=int(out_dtype))
@@ -237,18 +257,25 @@ class MoeLayer:
         _opt(self.weights.get("logit_offset"), torch.float32, "logit_offset")
         _opt(self.weights.get("score_bias"), torch.float32, "score_bias")
         _opt(self.weights.get("tid2eid"), torch.int32, "tid2eid")
-        self.cw = MoeWeights(**{n: _ptr(self.weights.get(n)) for n, _ in MoeWeights._fields_})
+        if packed:
+            # one-time layout change at load time (moe_pack_weights)
+            for key in MATRIX_NAMES:
+                if self.weights.get(key) is not None:
+                    self.weights[key] = pack_weights(self.weights[key])
+        self.packed = bool(packed)
+        self.cw = MoeWeights(packed=int(self.packed),
+                             **{n: _ptr(self.weights.get(n)) for n in WEIGHT_NAMES})
         self.device = self.weights["w_g"].device
         self.ws_bytes = int(lib().moe_forward_workspace_size(ctypes.byref(self.cfg)))
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         self.flags = torch.zeros(1, dtype=torch.int32, device=self.device)
 
     @classmethod
-    def from_workload(cls, w, inputs, out_dtype=OUT_BF16):
+    def from_workload(cls, w, inputs, out_dtype=OUT_BF16, packed=False):
         n_bias = 0 if inputs.get("score_bias") is None else inputs["score_bias"].shape[0]
         return cls(w.T, w.d, w.E, w.k, w.F, w.Fs, inputs, mode=w.mode, n_bias=n_bias, V=w.V,
                    scale=w.scale, clamp_limit=w.clamp_limit, clamp_mode=w.clamp_mode,
-                   out_dtype=out_dtype)
+                   out_dtype=out_dtype, packed=packed)
 
     def forward(self, x, input_ids=None, modality=None, y=None, logits=None, ids=None, w=None,
                 events=None):

@@ -98,6 +98,15 @@ def test_expert_ffn_validation(L):
     assert ffn(rows=0, a=None) == 0
 
 
+def test_pack_validation(L):
+    assert L.moe_packed_weight_bytes(2, 40, 128) == 2 * 64 * 128 * 2   # rows padded to 32
+    assert L.moe_packed_weight_bytes(1, 8, 100) == 0
+    assert L.moe_pack_weights(FAKE, 1, 8, 100, FAKE, None) == ERR_UNSUPPORTED
+    assert L.moe_pack_weights(FAKE, 0, 8, 128, FAKE, None) == ERR_SHAPE
+    assert L.moe_pack_weights(None, 1, 8, 128, FAKE, None) == ERR_NULL
+    assert L.moe_pack_weights(FAKE, 1, 8, 128, FAKE + 2, None) == ERR_ALIGN
+
+
 def test_combine_validation(L):
     def comb(T=4, d=64, k=2, rows=8, out=0, yp=FAKE, y=FAKE):
         return L.moe_combine(yp, FAKE, FAKE, None, T, d, k, rows, out, y, None)
@@ -113,7 +122,7 @@ def test_combine_validation(L):
 def test_forward_validation(L):
     cfg = ops.MoeCfg(T=8, d=128, E=8, k=2, F=64, F_shared=64, mode=0, n_bias=1, V=0, scale=1.0,
                      clamp_limit=10.0, clamp_mode=0, out_dtype=0)
-    w = ops.MoeWeights(w_g=FAKE, logit_offset=None, score_bias=FAKE, tid2eid=None, w_gate=FAKE,
+    w = ops.MoeWeights(packed=0, w_g=FAKE, logit_offset=None, score_bias=FAKE, tid2eid=None, w_gate=FAKE,
                        w_up=FAKE, w_down=FAKE, s_gate=FAKE, s_up=FAKE, s_down=FAKE)
     need = L.moe_forward_workspace_size(ctypes.byref(cfg))
     assert need > 0
@@ -134,6 +143,9 @@ def test_forward_validation(L):
         c = ops.MoeCfg.from_buffer_copy(cfg)
         setattr(c, field, val)
         assert fwd(c=c) == code, field
+    wp = ops.MoeWeights.from_buffer_copy(w)
+    wp.packed = 2
+    assert fwd(wt=wp) == ERR_UNSUPPORTED
     c = ops.MoeCfg.from_buffer_copy(cfg)
     c.mode = 1
     c.V = 100

@@ -197,6 +197,47 @@ def test_expert_ffn_rows_outside_groups_untouched():
     assert torch.all(h[30:] == 7.0) and torch.all(y[30:] == 7.0)
 
 
+# ----------------------------------------------------------- weight pack ----
+def pack_ref(w):
+    """The documented packed layout, written out with numpy reshapes:
+    fragment (g, nb, s, q, lane) = W[g, nb*32 + lane%32, s*64 + 16q + 8(lane//32) + i]."""
+    G, N, K = w.shape
+    NB, S = (N + 31) // 32, K // 64
+    wp = np.zeros((G, NB * 32, K), np.uint16)
+    wp[:, :N] = w
+    x = wp.reshape(G, NB, 32, S, 4, 2, 8)
+    return x.transpose(0, 1, 3, 4, 5, 2, 6).reshape(-1)
+
+
+@pytest.mark.parametrize("G,N,K", [(1, 32, 64), (3, 40, 128), (2, 384, 192), (1, 8, 256)])
+def test_pack_weights_layout(G, N, K):
+    rng = np.random.default_rng(G * N + K)
+    w = _bf16(rng, (G, N, K), 1.0)
+    got = bits(ops.pack_weights(w))
+    assert np.array_equal(got, pack_ref(bits(w)))
+
+
+@pytest.mark.parametrize("E,d,T,offset", [(8, 128, 70, False), (384, 256, 300, True),
+                                          (5, 64, 33, True)])
+def test_gate_logits_packed_matches_plain(E, d, T, offset):
+    # the router projection through moe_forward with packed weights equals the
+    # plain-layout call (same kernel arithmetic, only the weight layout differs)
+    rng = np.random.default_rng(E + d)
+    w = wl.small(T=T, d=d, E=E, k=1, F=64, seed=E, F_shared=0)
+    inp = wl.make_inputs(w, DEV)
+    if offset:
+        inp["logit_offset"] = torch.from_numpy(rng.normal(0, 1, E).astype(np.float32)).to(DEV)
+    lg = {}
+    for packed in (False, True):
+        layer = ops.MoeLayer.from_workload(w, inp, out_dtype=ops.OUT_F32, packed=packed)
+        lg[packed] = torch.empty((T, E), dtype=torch.float32, device=DEV)
+        layer.forward(inp["x"], logits=lg[packed])
+    torch.cuda.synchronize()
+    assert torch.equal(lg[False], lg[True])
+    check_logits(bits(inp["x"]), bits(inp["w_g"]),
+                 None if inp["logit_offset"] is None else host(inp["logit_offset"]), host(lg[True]))
+
+
 # --------------------------------------------------------------- combine ----
 @pytest.mark.parametrize("T,d,k,shared", [(1, 8, 1, False), (100, 256, 6, True),
                                           (333, 1032, 8, True), (64, 4096, 2, False)])
@@ -234,9 +275,10 @@ FWD_CASES = [
 
 @pytest.mark.parametrize("w", FWD_CASES, ids=lambda w: w.name)
 @pytest.mark.parametrize("out_dtype", [ops.OUT_F32, ops.OUT_BF16])
-def test_forward(w, out_dtype):
+@pytest.mark.parametrize("packed", [False, True], ids=["plain", "packed"])
+def test_forward(w, out_dtype, packed):
     inp = wl.make_inputs(w, DEV)
-    layer = ops.MoeLayer.from_workload(w, inp, out_dtype=out_dtype)
+    layer = ops.MoeLayer.from_workload(w, inp, out_dtype=out_dtype, packed=packed)
     logits = torch.empty((w.T, w.E), dtype=torch.float32, device=DEV)
     ids = torch.empty((w.T, w.k), dtype=torch.int32, device=DEV)
     wts = torch.empty((w.T, w.k), dtype=torch.float32, device=DEV)
