@@ -153,14 +153,19 @@ int moe_expert_ffn(const uint16_t* a, const int32_t* offsets, int G, int rows, i
  * Weight packing (a one-time layout change at weight-load time, not part of
  * the per-step computation).  Rewrites G matrices W[g] of [N,K] bf16 ([out,
  * in], K multiple of 64) into the matrix-core fragment order the GEMM kernels
- * stream: [G][ceil(N/32)][K/64][4][64][8] with fragment (nb, s, q, lane) =
- * W[nb*32 + lane%32][s*64 + 16q + 8(lane/32) .. +8] and rows >= N zero.
- * One wave's weight fragments for one MFMA substep are then 1 KB contiguous.
- *   src [G,N,K] bf16, dst: moe_packed_weight_bytes(G,N,K) bytes, 16-byte
- *   aligned, must not overlap src.
+ * stream, in panels of P = panel_rows rows:
+ *   [G][ceil(N/P)][K/64][P/32][4][64][8],  fragment (panel, s, b, q, lane) =
+ *   W[panel*P + b*32 + lane%32][s*64 + 16q + 8(lane/32) .. +8], rows >= N zero.
+ * One wave's fragments for one MFMA substep are 1 KB contiguous and one
+ * workgroup's panel is contiguous per 64-wide K stage.  moe_forward expects
+ * P = 128 for w_gate, w_up, s_gate, s_up and P = 256 for w_down, s_down, w_g.
+ *   src [G,N,K] bf16; dst: moe_packed_weight_bytes(G,N,K,P) bytes, 16-byte
+ *   aligned, not overlapping src; panel_rows 128 or 256 (else 0 /
+ *   MOE_ERR_UNSUPPORTED).
  */
-size_t moe_packed_weight_bytes(int G, int N, int K);
-int moe_pack_weights(const uint16_t* src, int G, int N, int K, uint16_t* dst, void* stream);
+size_t moe_packed_weight_bytes(int G, int N, int K, int panel_rows);
+int moe_pack_weights(const uint16_t* src, int G, int N, int K, int panel_rows, uint16_t* dst,
+                     void* stream);
 
 /* ------------------------------------------------------------------------
  * Result return merged by routing weight [TW], plus the always-on shared
@@ -199,7 +204,9 @@ typedef struct moe_weights {
     int packed;                   /* 0: every bf16 matrix below is [out,in] as
                                      listed; 1: w_g, w_gate, w_up, w_down,
                                      s_gate, s_up, s_down hold the
-                                     moe_pack_weights layout of those matrices */
+                                     moe_pack_weights layout of those matrices
+                                     (panel_rows 128 for the gate / up
+                                     matrices, 256 for the others) */
     const uint16_t* w_g;          /* [E,d] bf16 router projection */
     const float* logit_offset;    /* [E] fp32 or NULL, added to the logits */
     const float* score_bias;      /* [n_bias,E] fp32 or NULL (TOPK) */

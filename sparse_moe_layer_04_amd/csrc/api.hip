@@ -218,17 +218,19 @@ int moe_expert_ffn(const uint16_t* a, const int32_t* offsets, int G, int rows, i
     return hip_status(launch_grouped_gemm(EPI_F32, g2, s));
 }
 
-size_t moe_packed_weight_bytes(int G, int N, int K) {
+size_t moe_packed_weight_bytes(int G, int N, int K, int panel_rows) {
     if (G < 1 || N < 1 || K < 64 || K % 64) return 0;
-    return packed_weight_elems(G, N, K) * 2;
+    if (panel_rows != 128 && panel_rows != 256) return 0;
+    return packed_weight_elems(G, N, K, panel_rows) * 2;
 }
 
-int moe_pack_weights(const uint16_t* src, int G, int N, int K, uint16_t* dst, void* stream) {
+int moe_pack_weights(const uint16_t* src, int G, int N, int K, int panel_rows, uint16_t* dst,
+                     void* stream) {
     if (G < 1 || N < 1 || K < 64) return MOE_ERR_SHAPE;
-    if (K % 64) return MOE_ERR_UNSUPPORTED;
+    if (K % 64 || (panel_rows != 128 && panel_rows != 256)) return MOE_ERR_UNSUPPORTED;
     if (!src || !dst) return MOE_ERR_NULL;
     if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_ALIGN;
-    return hip_status(launch_pack_weights(src, dst, G, N, K, as_stream(stream)));
+    return hip_status(launch_pack_weights(src, dst, G, N, K, panel_rows, as_stream(stream)));
 }
 
 int moe_combine(const float* y_perm, const int32_t* dest, const float* topk_w,

@@ -56,8 +56,8 @@ struct GemmArgs {
 };
 
 hipError_t launch_grouped_gemm(int epilogue, const GemmArgs& g, hipStream_t stream);
-size_t packed_weight_elems(int G, int N, int K);
-hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int G, int N, int K,
+size_t packed_weight_elems(int G, int N, int K, int P);
+hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int G, int N, int K, int P,
                                hipStream_t stream);
 
 hipError_t launch_route(const float* logits, const float* bias, const uint8_t* modality,

@@ -26,7 +26,8 @@ STAGE_NAMES = ("router_gemm", "route", "permute", "gate_up_routed", "gate_up_sha
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 HEADER = os.path.join(_ROOT, "include", "moe.h")
-LIBRARY = os.path.join(_HERE, "libmoe_hip.so")
+# the in-tree build; MOE_HIP_LIBRARY may point at another build of the same sources
+LIBRARY = os.environ.get("MOE_HIP_LIBRARY", os.path.join(_HERE, "libmoe_hip.so"))
 
 _lib = None
 
@@ -78,9 +79,9 @@ def lib():
     L.moe_permute.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, S, P]
     L.moe_expert_ffn.argtypes = [P, P, I, I, I, I, P, P, P, F, I, P, P, P]
     L.moe_combine.argtypes = [P, P, P, P, I, I, I, I, I, P, P]
-    L.moe_packed_weight_bytes.argtypes = [I, I, I]
+    L.moe_packed_weight_bytes.argtypes = [I, I, I, I]
     L.moe_packed_weight_bytes.restype = S
-    L.moe_pack_weights.argtypes = [P, I, I, I, P, P]
+    L.moe_pack_weights.argtypes = [P, I, I, I, I, P, P]
     L.moe_forward_workspace_size.argtypes = [ctypes.POINTER(MoeCfg)]
     L.moe_forward_workspace_size.restype = S
     L.moe_forward.argtypes = [ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeWeights), P, P, P, P,
@@ -224,16 +225,22 @@ def combine(y_perm, dest, topk_w, y_shared=None, out_dtype=OUT_BF16, y=None):
     return y
 
 
-def pack_weights(w):
-    """Packed copy (moe_pack_weights layout) of bf16 weights [G,N,K] or [N,K]."""
+# panel height each matrix is packed with for moe_forward
+PANEL_ROWS = dict(w_g=256, w_gate=128, w_up=128, w_down=256, s_gate=128, s_up=128, s_down=256)
+
+
+def pack_weights(w, panel_rows):
+    """Packed copy (moe_pack_weights layout, panels of `panel_rows` rows) of
+    bf16 weights [G,N,K] or [N,K]."""
     _need(w, torch.bfloat16, "w")
     shape = tuple(w.shape)
     G, N, K = (1,) + shape if w.dim() == 2 else shape
-    nbytes = int(lib().moe_packed_weight_bytes(G, N, K))
+    nbytes = int(lib().moe_packed_weight_bytes(G, N, K, panel_rows))
     if nbytes == 0:
-        raise MoeError(f"cannot pack weights of shape {shape}")
+        raise MoeError(f"cannot pack weights of shape {shape} in panels of {panel_rows}")
     out = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=w.device)
-    _check(lib().moe_pack_weights(_ptr(w), G, N, K, _ptr(out), _stream()), "moe_pack_weights")
+    _check(lib().moe_pack_weights(_ptr(w), G, N, K, panel_rows, _ptr(out), _stream()),
+           "moe_pack_weights")
     return out
 
 
@@ -261,7 +268,7 @@ class MoeLayer:
             # one-time layout change at load time (moe_pack_weights)
             for key in MATRIX_NAMES:
                 if self.weights.get(key) is not None:
-                    self.weights[key] = pack_weights(self.weights[key])
+                    self.weights[key] = pack_weights(self.weights[key], PANEL_ROWS[key])
         self.packed = bool(packed)
         self.cw = MoeWeights(packed=int(self.packed),
                              **{n: _ptr(self.weights.get(n)) for n in WEIGHT_NAMES})

@@ -99,12 +99,15 @@ def test_expert_ffn_validation(L):
 
 
 def test_pack_validation(L):
-    assert L.moe_packed_weight_bytes(2, 40, 128) == 2 * 64 * 128 * 2   # rows padded to 32
-    assert L.moe_packed_weight_bytes(1, 8, 100) == 0
-    assert L.moe_pack_weights(FAKE, 1, 8, 100, FAKE, None) == ERR_UNSUPPORTED
-    assert L.moe_pack_weights(FAKE, 0, 8, 128, FAKE, None) == ERR_SHAPE
-    assert L.moe_pack_weights(None, 1, 8, 128, FAKE, None) == ERR_NULL
-    assert L.moe_pack_weights(FAKE, 1, 8, 128, FAKE + 2, None) == ERR_ALIGN
+    assert L.moe_packed_weight_bytes(2, 40, 128, 128) == 2 * 128 * 128 * 2   # rows padded
+    assert L.moe_packed_weight_bytes(2, 300, 64, 256) == 2 * 512 * 64 * 2
+    assert L.moe_packed_weight_bytes(1, 8, 100, 128) == 0
+    assert L.moe_packed_weight_bytes(1, 8, 128, 64) == 0
+    assert L.moe_pack_weights(FAKE, 1, 8, 100, 128, FAKE, None) == ERR_UNSUPPORTED
+    assert L.moe_pack_weights(FAKE, 1, 8, 128, 32, FAKE, None) == ERR_UNSUPPORTED
+    assert L.moe_pack_weights(FAKE, 0, 8, 128, 128, FAKE, None) == ERR_SHAPE
+    assert L.moe_pack_weights(None, 1, 8, 128, 128, FAKE, None) == ERR_NULL
+    assert L.moe_pack_weights(FAKE, 1, 8, 128, 256, FAKE + 2, None) == ERR_ALIGN
 
 
 def test_combine_validation(L):

@@ -198,23 +198,24 @@ def test_expert_ffn_rows_outside_groups_untouched():
 
 
 # ----------------------------------------------------------- weight pack ----
-def pack_ref(w):
-    """The documented packed layout, written out with numpy reshapes:
-    fragment (g, nb, s, q, lane) = W[g, nb*32 + lane%32, s*64 + 16q + 8(lane//32) + i]."""
+def pack_ref(w, P):
+    """The documented packed layout, written out with numpy reshapes: fragment
+    (g, panel, s, b, q, lane) = W[g, panel*P + b*32 + lane%32, s*64 + 16q + 8(lane//32) + i]."""
     G, N, K = w.shape
-    NB, S = (N + 31) // 32, K // 64
-    wp = np.zeros((G, NB * 32, K), np.uint16)
+    NP, S = (N + P - 1) // P, K // 64
+    wp = np.zeros((G, NP * P, K), np.uint16)
     wp[:, :N] = w
-    x = wp.reshape(G, NB, 32, S, 4, 2, 8)
-    return x.transpose(0, 1, 3, 4, 5, 2, 6).reshape(-1)
+    x = wp.reshape(G, NP, P // 32, 32, S, 4, 2, 8)   # g, panel, b, r, s, q, h, i
+    return x.transpose(0, 1, 4, 2, 5, 6, 3, 7).reshape(-1)
 
 
-@pytest.mark.parametrize("G,N,K", [(1, 32, 64), (3, 40, 128), (2, 384, 192), (1, 8, 256)])
-def test_pack_weights_layout(G, N, K):
+@pytest.mark.parametrize("G,N,K,P", [(1, 32, 64, 128), (3, 40, 128, 128), (2, 384, 192, 256),
+                                     (1, 8, 256, 256), (2, 300, 64, 128)])
+def test_pack_weights_layout(G, N, K, P):
     rng = np.random.default_rng(G * N + K)
     w = _bf16(rng, (G, N, K), 1.0)
-    got = bits(ops.pack_weights(w))
-    assert np.array_equal(got, pack_ref(bits(w)))
+    got = bits(ops.pack_weights(w, P))
+    assert np.array_equal(got, pack_ref(bits(w), P))
 
 
 @pytest.mark.parametrize("E,d,T,offset", [(8, 128, 70, False), (384, 256, 300, True),
