@@ -61,6 +61,11 @@ int ffn_checks(int rows, int d, int F, float clamp_limit, int clamp_mode) {
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// expert GEMMs: packed weights take the LDS-staged 256 x 256 kernel
+inline hipError_t expert_gemm(int epi, const GemmArgs& g, hipStream_t s) {
+    return g.packed ? launch_grouped_gemm_lds(epi, g, s) : launch_grouped_gemm(epi, g, s);
+}
+
 // moe_forward workspace layout
 struct FwdWs {
     float* logits;
@@ -350,7 +355,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g1.clamp_limit = c->clamp_limit;
     g1.clamp_mode = c->clamp_mode;
     g1.out = L.h;
-    if ((e = launch_grouped_gemm(EPI_SWIGLU_BF16, g1, s)) != hipSuccess) return MOE_ERR_HIP;
+    if ((e = expert_gemm(EPI_SWIGLU_BF16, g1, s)) != hipSuccess) return MOE_ERR_HIP;
     if (!mark(4)) return MOE_ERR_HIP;
     // 5. shared expert gate/up
     if (Fs > 0) {
@@ -366,7 +371,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
         gs.clamp_limit = c->clamp_limit;
         gs.clamp_mode = c->clamp_mode;
         gs.out = L.hs;
-        if ((e = launch_grouped_gemm(EPI_SWIGLU_BF16, gs, s)) != hipSuccess) return MOE_ERR_HIP;
+        if ((e = expert_gemm(EPI_SWIGLU_BF16, gs, s)) != hipSuccess) return MOE_ERR_HIP;
     }
     if (!mark(5)) return MOE_ERR_HIP;
     // 6. routed experts: down projection
@@ -380,7 +385,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g2.w1 = w->w_down;
     g2.packed = w->packed;
     g2.out = L.y_perm;
-    if ((e = launch_grouped_gemm(EPI_F32, g2, s)) != hipSuccess) return MOE_ERR_HIP;
+    if ((e = expert_gemm(EPI_F32, g2, s)) != hipSuccess) return MOE_ERR_HIP;
     if (!mark(6)) return MOE_ERR_HIP;
     // 7. shared expert down
     if (Fs > 0) {
@@ -393,7 +398,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
         gs.w1 = w->s_down;
         gs.packed = w->packed;
         gs.out = L.ys;
-        if ((e = launch_grouped_gemm(EPI_F32, gs, s)) != hipSuccess) return MOE_ERR_HIP;
+        if ((e = expert_gemm(EPI_F32, gs, s)) != hipSuccess) return MOE_ERR_HIP;
     }
     if (!mark(7)) return MOE_ERR_HIP;
     // 8. weighted combine + shared add

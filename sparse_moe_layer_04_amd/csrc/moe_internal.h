@@ -56,6 +56,9 @@ struct GemmArgs {
 };
 
 hipError_t launch_grouped_gemm(int epilogue, const GemmArgs& g, hipStream_t stream);
+// Expert GEMMs on packed weights (EPI_SWIGLU_BF16 with 128-row panels,
+// EPI_F32 with 256-row panels): 256 x 256 tiles staged in LDS by DMA.
+hipError_t launch_grouped_gemm_lds(int epilogue, const GemmArgs& g, hipStream_t stream);
 size_t packed_weight_elems(int G, int N, int K, int P);
 hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int G, int N, int K, int P,
                                hipStream_t stream);
