@@ -61,9 +61,14 @@ int ffn_checks(int rows, int d, int F, float clamp_limit, int clamp_mode) {
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// expert GEMMs: packed weights take the LDS-staged 256 x 256 kernel
+// expert GEMMs: packed weights take the LDS-staged kernel when its LDS holds
+// the group table, else (and for plain weights) the register-direct kernel
+inline bool lds_gemm_ok(int packed, int G) {
+    return packed && G <= grouped_gemm_lds_max_groups();
+}
 inline hipError_t expert_gemm(int epi, const GemmArgs& g, hipStream_t s) {
-    return g.packed ? launch_grouped_gemm_lds(epi, g, s) : launch_grouped_gemm(epi, g, s);
+    return lds_gemm_ok(g.packed, g.G) ? launch_grouped_gemm_lds(epi, g, s)
+                                      : launch_grouped_gemm(epi, g, s);
 }
 
 // moe_forward workspace layout
@@ -100,8 +105,8 @@ FwdWs forward_layout(const moe_cfg* c, char* base) {
     w.offsets = (int32_t*)take((size_t)(c->E + 1) * 4);
     w.dest = (int32_t*)take(N * 4);
     w.src = (int32_t*)take(N * 4);
-    w.x_perm = (uint16_t*)take(N * c->d * 2);
-    w.h = (uint16_t*)take(N * c->F * 2);
+    w.x_perm = (uint16_t*)take(blocked_rows(N) * c->d * 2);
+    w.h = (uint16_t*)take(blocked_rows(N) * c->F * 2);
     w.y_perm = (float*)take(N * c->d * 4);
     w.hs = (uint16_t*)take(T * (size_t)(c->F_shared > 0 ? c->F_shared : 0) * 2);
     w.ys = (float*)take(c->F_shared > 0 ? T * c->d * 4 : 0);
@@ -336,8 +341,10 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
         return MOE_ERR_HIP;
     if (!mark(2)) return MOE_ERR_HIP;
     // 3. dispatch permutation + row gather
+    // the LDS-staged expert GEMM reads x_perm and h in the blocked layout
+    const bool blocked = lds_gemm_ok(w->packed, E);
     if ((e = launch_permute(ids, x, T, d, E, k, L.counts, L.offsets, L.dest, L.src, L.x_perm,
-                            d_flags, L.perm, s)) != hipSuccess)
+                            d_flags, L.perm, s, blocked)) != hipSuccess)
         return MOE_ERR_HIP;
     if (!mark(3)) return MOE_ERR_HIP;
     const int rows = T * k;
@@ -355,6 +362,10 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g1.clamp_limit = c->clamp_limit;
     g1.clamp_mode = c->clamp_mode;
     g1.out = L.h;
+    g1.a_blocked = blocked;
+    g1.out_blocked = blocked;
+    // experts averaging at most 128 rows take the 128 x 512 tile shape
+    g1.wide = (long long)rows <= 128ll * E;
     if ((e = expert_gemm(EPI_SWIGLU_BF16, g1, s)) != hipSuccess) return MOE_ERR_HIP;
     if (!mark(4)) return MOE_ERR_HIP;
     // 5. shared expert gate/up
@@ -385,6 +396,8 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g2.w1 = w->w_down;
     g2.packed = w->packed;
     g2.out = L.y_perm;
+    g2.a_blocked = blocked;
+    g2.wide = g1.wide;
     if ((e = expert_gemm(EPI_F32, g2, s)) != hipSuccess) return MOE_ERR_HIP;
     if (!mark(6)) return MOE_ERR_HIP;
     // 7. shared expert down

@@ -1,49 +1,96 @@
-// Grouped expert GEMM for packed weights: 256 x 256 tiles, both operands
-// staged in LDS by direct-to-LDS DMA loads ("HyperParallel accelerates
-// DeepSeek-V4.1 ...", section 2.3, MegaMoE: the two expert matmuls and the
-// clamped SwiGLU between them).
+// Grouped expert GEMM for packed weights, both operands staged in LDS by
+// direct-to-LDS DMA loads ("HyperParallel accelerates DeepSeek-V4.1 ...",
+// section 2.3, MegaMoE: the two expert matmuls and the clamped SwiGLU
+// between them).
 //
 // Problem: for each expert g and activation row r in [lo_g, hi_g),
 //   out[r, n] = sum_k A[r, k] * W[g, n, k]
 // with W in the moe_pack_weights panel layout (P = 128 rows for the gate and
-// up matrices, P = 256 for the down matrix).
+// up matrices, P = 256 for the down matrix) and A row-major or in the
+// blocked activation layout (16 x 32 blocks of 1 KB).
 //
-// One workgroup = 8 waves (two per SIMD); a tile is up to 256 activation rows
-// x 256 weight rows (SwiGLU: 128 features x {gate, up}).  Wave w = (wm, wn),
-// wm = w / 4 picks the 128-row half of the tile, wn = w % 4 the 64 weight
-// rows (two 32-row MFMA blocks: SwiGLU gate block wn and up block wn; down
-// blocks 2wn, 2wn+1).  An expert with up to 256 rows is one tile, so its
-// weights are read from memory once.  Per 32-wide K stage one LDS slot holds
-//   - the activation tile, 256 rows x 64 B, the 16-byte chunks of row r
-//     XOR-swizzled by ((r / 2) mod 4) so that MFMA operand reads spread
-//     over the banks;
-//   - the weight panel half-stage, 16 KB in matrix-core fragment order
-//     (copied from the packed layout in 1 KB runs; the operand reads are
-//     1 KB contiguous per wave).
-// A 4-slot LDS ring keeps three stages (96 KB) in flight per CU.  Each of
-// the 8 waves issues 2 activation and 2 weight DMA instructions of 1 KB per
-// stage (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16 l).  The
-// DMA is issued from inline assembly, so the compiler does not see LDS
-// writes it would otherwise guard with a full vmcnt drain before every LDS
-// read; explicit vmcnt waits + one barrier per stage are the complete
-// synchronisation.
+// Two tile shapes, one workgroup of 8 waves (two per SIMD) per tile; every
+// wave owns two 32-row weight blocks (SwiGLU: gate block and the up block of
+// the same 32 features; down: two adjacent output blocks) times up to four
+// 32-row activation blocks (acc: 2 x NTB MFMA 32x32 tiles):
+//   - square: up to TM = 256 activation rows x 256 weight rows (SwiGLU: 128
+//     features).  Wave w = (wm, wn): wm = w / 4 takes one half of the tile's
+//     valid rows (rounded to 32-row blocks), wn = w % 4 its weight blocks.
+//   - wide: up to 128 activation rows x 512 weight rows (SwiGLU: 256
+//     features); all 8 waves share the activation rows, wave w takes weight
+//     blocks of index w.  Each activation byte staged feeds twice the MFMA
+//     work, so experts with at most 128 rows move half the activation bytes
+//     per weight byte.
+// An expert with up to TM rows is one tile row, so its weights are read from
+// memory once.  Per 32-wide K stage one LDS slot holds
+//   - the activation tile, TM rows x 64 B, the 16-byte chunks of row r
+//     XOR-swizzled by sw(r) = ((r >> 1) ^ (r >> 3)) & 3, so that the 16
+//     lanes an LDS cycle serves (256 B over 64 banks: rows r, r+4, r+8,
+//     r+12 share banks) hit distinct banks in MFMA operand reads;
+//   - the weight half-stage in matrix-core fragment order (copied from the
+//     packed layout in 1 KB runs; operand reads are 1 KB contiguous per
+//     wave).
+// A ring of SLOTS LDS slots keeps SLOTS - 1 stages in flight per CU.  The
+// DMA (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16 l) moves
+// 1 KB per instruction: weight instructions and blocked-layout activation
+// instructions each read 1 KB of contiguous memory (8 full cache lines);
+// row-major activations cost 16 half-used lines per instruction.  Each wave
+// issues NW weight instructions and na activation instructions per stage
+// (only the 16-row groups that hold valid rows are copied); both are fixed
+// for a tile, so vmcnt counts stay exact.  The DMA is issued from inline
+// assembly, so the compiler does not see LDS writes it would otherwise guard
+// with a full vmcnt drain before every LDS read; explicit vmcnt waits + one
+// barrier per stage are the complete synchronisation.
 // Scheduling: persistent grid, per-expert tile prefix built in LDS from the
 // device offsets, items ordered (expert, n-tile, m-tile) and split into 8
 // contiguous ranges, one per XCD.
 #include "moe_internal.h"
 
+#ifndef MOE_LDS_TM
+#define MOE_LDS_TM 256
+#endif
+#ifndef MOE_LDS_SLOTS
+#define MOE_LDS_SLOTS 4
+#endif
+
 namespace moe {
 namespace {
 
-constexpr int TM = 256;                      // activation rows per tile
 constexpr int BK = 32;                       // K per pipeline stage
-constexpr int kSlotA = TM * 64;              // 16 KB activation tile per stage
-constexpr int kSlotW = 16 * 1024;            // 16 KB weight panel half-stage
-constexpr int kSlot = kSlotA + kSlotW;
-constexpr int kSlots = 4;                    // LDS ring: 3 stages in flight
 constexpr int kThreads = 512;
+constexpr int kLdsLimit = 160 * 1024;
+constexpr int kStaticLds = 8 * sizeof(int);  // scan_sh
+
+template <int EPI, bool WIDE>
+struct Shape {
+    static constexpr int TM = WIDE ? 128 : MOE_LDS_TM;      // activation rows per tile
+    static_assert(TM % 64 == 0 && TM >= 64 && TM <= 256, "TM: 64..256, multiple of 64");
+    static constexpr int MH = WIDE ? TM : TM / 2;           // max rows per wave
+    static constexpr int MAXNTB = MH / 32;                  // activation blocks per wave
+    static constexpr int WBLK = WIDE ? 16 : 8;              // 32-row weight blocks per tile
+    static constexpr int NW = WBLK / 4;                     // weight DMA instrs per wave per stage
+    static constexpr int WAVES_N = WIDE ? 8 : 4;            // waves along the weight rows
+    static constexpr int SLOTA = TM * 64;
+    static constexpr int SLOTW = WBLK * 2 * 1024;           // 2 substeps x 1 KB per block
+    static constexpr int SLOT = SLOTA + SLOTW;
+    static constexpr int SLOTS = WIDE ? 3 : MOE_LDS_SLOTS;
+    static constexpr int AHEAD = SLOTS - 1;                 // stages in flight
+    static_assert(SLOTS >= 2 && SLOTS <= 8, "ring depth");
+    static constexpr int AINSTR = TM / 16;                  // activation instrs per stage
+    static constexpr int APW = (AINSTR + 7) / 8;            // ... per wave (max)
+    static constexpr int PANEL = (EPI == EPI_SWIGLU_BF16) ? 128 : 256;
+    static constexpr int BPP = PANEL / 32;                  // blocks per panel
+    // weight rows (per matrix) and panels (per matrix) of one n-tile
+    static constexpr int TN = (EPI == EPI_SWIGLU_BF16) ? WBLK * 16 : WBLK * 32;
+    static constexpr int PPT = TN / PANEL;
+    static constexpr int RING = SLOTS * SLOT;
+    static_assert(RING + kStaticLds < kLdsLimit, "LDS ring");
+};
 
 __device__ __forceinline__ float clamp_sym(float v, float L) { return fminf(fmaxf(v, -L), L); }
+
+// position swizzle of the four 16-byte chunks of activation row r in LDS
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 // 1 KB direct-to-LDS copy: lane l's 16 bytes from gaddr go to LDS byte
 // lds_byte + 16 l.
@@ -62,95 +109,126 @@ __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int EPI>
+// wait for the oldest in-flight stage of a wave that issues na + NW
+// instructions per stage (AHEAD - 1 newer stages may stay outstanding)
+template <int NW, int AHEAD>
+__device__ __forceinline__ void wait_stage(int na) {
+    if (na == 2) wait_vm<(AHEAD - 1) * (NW + 2)>();
+    else if (na == 1) wait_vm<(AHEAD - 1) * (NW + 1)>();
+    else wait_vm<(AHEAD - 1) * NW>();
+}
+
 struct LdsTile {
     const GemmArgs* args;
     uint32_t lds0;         // LDS byte address of slot 0
     unsigned char* smem;
     int lane, wave, wm, wn, half, l32;
     int K, N, S;
-    int row0, grp_hi, valid;
+    int row0, valid;
+    int mh;                // activation rows per wave half (multiple of 32)
+    int na;                // activation DMA instructions of this wave per stage
     int n0;                // first weight row / feature of this wave's blocks
-    const uint16_t* wsrc0; // weight panel (gate panel for SwiGLU)
-    const uint16_t* wsrc1; // up panel (SwiGLU) or the same panel
+    const uint16_t* wsrc0; // first panel of this n-tile (gate matrix for SwiGLU)
+    const uint16_t* wsrc1; // up matrix panel (SwiGLU) or the same
+    int np_left;           // panels of this n-tile that exist (1..PPT)
+    size_t pstride;        // packed elements per panel
     size_t wstride;        // packed elements per 64-wide K stage of one panel
 };
 
-// DMA of pipeline stage j (32 k) into `slot`: 2 activation and 2 weight
-// instructions per wave, always issued (rows past the tile read the last
-// valid row), so every stage costs each wave exactly 4 vmcnt entries.
-//   activations: wave w copies rows [32 w, 32 w + 32), 16 rows x 64 B per
-//     instruction; chunk c of row r is stored at position c ^ ((r >> 1) & 3).
-//   weights: the 64-wide packed stage s = j / 2 holds, per 32-row block b,
+// DMA of pipeline stage j (32 k) into the LDS slot at byte offset `sbase`.
+//   activations: instruction n (rows [16 n, 16 n + 16) of the tile) belongs
+//     to wave n % 8 and is issued only if the group holds a valid row; rows
+//     past the tile read the last valid row.  Chunk c of row r is stored at
+//     position c ^ sw(r).
+//   weights: the 64-wide packed stage s = j / 2 holds, per 32-row block,
 //     4 substeps x 1 KB; this half-stage (h = j % 2) takes substeps 2h, 2h+1
-//     of all 8 blocks: instruction n = 2 w + i copies block n / 2, substep
-//     2h + n % 2 to LDS fragment slot n.
-template <int EPI>
-__device__ __forceinline__ void issue_stage(const LdsTile<EPI>& t, int j, int slot) {
-    const uint32_t base = t.lds0 + slot * kSlot;
+//     of all WBLK blocks: instruction n = NW w + i copies tile block n / 2,
+//     substep 2h + n % 2 to LDS fragment slot n.  SwiGLU tile blocks
+//     [0, WBLK/2) are gate rows, the rest up rows; a block of a panel past
+//     the matrix end re-reads the last panel (its outputs are never stored).
+template <int EPI, bool WIDE>
+__device__ __forceinline__ void issue_stage(const LdsTile& t, int j, uint32_t sbase) {
+    using C = Shape<EPI, WIDE>;
+    const uint32_t base = t.lds0 + sbase;
     const int kcol = j * BK;
+    const GemmArgs& args = *t.args;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r0 = 32 * t.wave + 16 * i;
-        const int r = r0 + (t.lane >> 2);
-        const int c = (t.lane & 3) ^ ((t.lane >> 3) & 3);
-        const int grow = t.row0 + min(r, t.valid - 1);
-        dma16(t.args->a + (size_t)grow * t.K + kcol + c * 8, base + r0 * 64);
+    for (int i = 0; i < C::APW; ++i) {
+        if (i < t.na) {
+            const int r0 = 16 * (t.wave + 8 * i);
+            const int r = r0 + (t.lane >> 2);
+            const int c = (t.lane & 3) ^ swz(r);
+            const size_t grow = (size_t)(t.row0 + min(r, t.valid - 1));
+            const uint16_t* src = args.a_blocked ? args.a + blocked_index(grow, kcol + c * 8, t.K)
+                                                 : args.a + grow * t.K + kcol + c * 8;
+            dma16(src, base + r0 * 64);
+        }
     }
     const int s64 = j >> 1, h2 = j & 1;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int n = 2 * t.wave + i;
+    for (int i = 0; i < C::NW; ++i) {
+        const int n = C::NW * t.wave + i;
         const int b = n >> 1;
         const int sub = 2 * h2 + (n & 1);
-        const uint16_t* src;
-        if (EPI == EPI_SWIGLU_BF16)
-            src = (b < 4 ? t.wsrc0 + (size_t)b * 2048 : t.wsrc1 + (size_t)(b - 4) * 2048);
-        else
-            src = t.wsrc0 + (size_t)b * 2048;
-        dma16(src + (size_t)s64 * t.wstride + sub * 512 + t.lane * 8, base + kSlotA + n * 1024);
+        const uint16_t* mat = t.wsrc0;
+        int bb = b;
+        if (EPI == EPI_SWIGLU_BF16 && b >= C::WBLK / 2) {
+            mat = t.wsrc1;
+            bb = b - C::WBLK / 2;
+        }
+        const int panel = min(bb / C::BPP, t.np_left - 1);
+        const uint16_t* src = mat + (size_t)panel * t.pstride + (size_t)s64 * t.wstride +
+                              (bb % C::BPP) * 2048 + sub * 512 + t.lane * 8;
+        dma16(src, base + C::SLOTA + n * 1024);
     }
 }
 
-template <int EPI, int NTB>
-__device__ __forceinline__ void compute_stage(const LdsTile<EPI>& t, int slot,
-                                              f32x16 (&acc)[2][4]) {
-    const unsigned char* base = t.smem + slot * kSlot;
+template <int EPI, bool WIDE, int NTB>
+__device__ __forceinline__ void compute_stage(const LdsTile& t, uint32_t sbase,
+                                              f32x16 (&acc)[2][Shape<EPI, WIDE>::MAXNTB]) {
+    using C = Shape<EPI, WIDE>;
+    const unsigned char* base = t.smem + sbase;
     // weight blocks of this wave (fragment slots 2 b + substep)
     const int b0 = (EPI == EPI_SWIGLU_BF16) ? t.wn : 2 * t.wn;
-    const int b1 = (EPI == EPI_SWIGLU_BF16) ? 4 + t.wn : 2 * t.wn + 1;
-    const unsigned char* wbase = base + kSlotA + t.lane * 16;
+    const int b1 = (EPI == EPI_SWIGLU_BF16) ? C::WBLK / 2 + t.wn : 2 * t.wn + 1;
+    const unsigned char* wbase = base + C::SLOTA + t.lane * 16;
+    // all operand reads of the stage first, in the order the MFMAs consume
+    // them, so each MFMA waits only for its own operands
+    bf16x8 w0[2], w1[2], at[2][NTB];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        const bf16x8 w0 = *(const bf16x8*)(wbase + (b0 * 2 + q) * 1024);
-        const bf16x8 w1 = *(const bf16x8*)(wbase + (b1 * 2 + q) * 1024);
-        bf16x8 at[NTB];
+        w0[q] = *(const bf16x8*)(wbase + (b0 * 2 + q) * 1024);
+        w1[q] = *(const bf16x8*)(wbase + (b1 * 2 + q) * 1024);
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
-            const int r = t.wm * 128 + tb * 32 + t.l32;
-            const int c = (2 * q + t.half) ^ ((r >> 1) & 3);
-            at[tb] = *(const bf16x8*)(base + r * 64 + c * 16);
-        }
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-            acc[0][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w0, at[tb], acc[0][tb], 0, 0, 0);
-            acc[1][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w1, at[tb], acc[1][tb], 0, 0, 0);
+            const int r = t.wm * t.mh + tb * 32 + t.l32;
+            const int c = (2 * q + t.half) ^ swz(r);
+            at[q][tb] = *(const bf16x8*)(base + r * 64 + c * 16);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            acc[0][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w0[q], at[q][tb], acc[0][tb], 0, 0, 0);
+            acc[1][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w1[q], at[q][tb], acc[1][tb], 0, 0, 0);
+        }
 }
 
-template <int EPI, int NTB>
-__device__ __forceinline__ void epilogue(const LdsTile<EPI>& t, const f32x16 (&acc)[2][4]) {
+template <int EPI, bool WIDE, int NTB>
+__device__ __forceinline__ void epilogue(const LdsTile& t,
+                                         const f32x16 (&acc)[2][Shape<EPI, WIDE>::MAXNTB]) {
     const GemmArgs& args = *t.args;
     const int N = t.N;
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
-        const int rl = t.wm * 128 + tb * 32 + t.l32;
+        const int rl = t.wm * t.mh + tb * 32 + t.l32;
         if (rl >= t.valid) continue;
-        const int r = t.row0 + rl;
+        const size_t r = (size_t)(t.row0 + rl);
         if (EPI == EPI_SWIGLU_BF16) {
             const float L = args.clamp_limit;
-            uint16_t* orow = (uint16_t*)args.out + (size_t)r * N;
+            uint16_t* out = (uint16_t*)args.out;
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
                 const int n = t.n0 + 8 * qq + 4 * t.half;
@@ -170,10 +248,11 @@ __device__ __forceinline__ void epilogue(const LdsTile<EPI>& t, const f32x16 (&a
                     }
                     packed[i >> 1] = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
                 }
-                *(u32x2*)(orow + n) = u32x2{packed[0], packed[1]};
+                uint16_t* dst = args.out_blocked ? out + blocked_index(r, n, N) : out + r * N + n;
+                *(u32x2*)dst = u32x2{packed[0], packed[1]};
             }
         } else {
-            float* orow = (float*)args.out + (size_t)r * N;
+            float* orow = (float*)args.out + r * N;
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -189,44 +268,61 @@ __device__ __forceinline__ void epilogue(const LdsTile<EPI>& t, const f32x16 (&a
 }
 
 // K loop of one tile for a wave computing NTB 32-row blocks (0: DMA only).
-// Stages j+1 and j+2 stay in flight while stage j computes: wait for stage j
-// (this wave's own DMA: at most 8 newer entries outstanding), barrier (all
-// waves' DMA of stage j landed, and all waves are done reading the slot the
-// next DMA overwrites), issue stage j+3, compute stage j.
-template <int EPI, int NTB>
-__device__ __forceinline__ void run_tile(const LdsTile<EPI>& t) {
-    f32x16 acc[2][4];
+// Stages j+1 .. j+AHEAD-1 stay in flight while stage j computes: wait for
+// stage j (this wave's own DMA), barrier (all waves' DMA of stage j landed,
+// and all waves are done reading the slot the next DMA overwrites), issue
+// stage j + AHEAD into the slot stage j - 1 used, compute stage j.  Stages
+// past the end re-issue the last stage, so every iteration issues the same
+// number of instructions.
+template <int EPI, bool WIDE, int NTB>
+__device__ __forceinline__ void run_tile(const LdsTile& t) {
+    using C = Shape<EPI, WIDE>;
+    f32x16 acc[2][C::MAXNTB];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < C::MAXNTB; ++tb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[b][tb][i] = 0.0f;
     const int S = t.S;
     wait_vm<0>();  // retire the previous tile's stores before counting DMA entries
-    issue_stage<EPI>(t, 0, 0);
-    issue_stage<EPI>(t, min(1, S - 1), 1);
-    issue_stage<EPI>(t, min(2, S - 1), 2);
+#pragma unroll
+    for (int p = 0; p < C::AHEAD; ++p) issue_stage<EPI, WIDE>(t, min(p, S - 1), p * C::SLOT);
+    uint32_t s_cmp = 0, s_iss = C::AHEAD * C::SLOT;
     for (int j = 0; j < S; ++j) {
-        wait_vm<8>();
+        wait_stage<C::NW, C::AHEAD>(t.na);
         __syncthreads();
-        issue_stage<EPI>(t, min(j + 3, S - 1), (j + 3) & 3);
-        if constexpr (NTB > 0) compute_stage<EPI, NTB>(t, j & 3, acc);
+        issue_stage<EPI, WIDE>(t, min(j + C::AHEAD, S - 1), s_iss);
+        s_iss = (s_iss + C::SLOT == C::RING) ? 0 : s_iss + C::SLOT;
+        if constexpr (NTB > 0) compute_stage<EPI, WIDE, NTB>(t, s_cmp, acc);
+        s_cmp = (s_cmp + C::SLOT == C::RING) ? 0 : s_cmp + C::SLOT;
     }
     wait_vm<0>();
     __syncthreads();
-    if constexpr (NTB > 0) epilogue<EPI, NTB>(t, acc);
+    if constexpr (NTB > 0) epilogue<EPI, WIDE, NTB>(t, acc);
 }
 
-template <int EPI>
+// run_tile for ntb in [0, NT] (ntb is wave-uniform)
+template <int EPI, bool WIDE, int NT>
+__device__ __forceinline__ void run_tile_ntb(const LdsTile& t, int ntb) {
+    if constexpr (NT == 0) {
+        run_tile<EPI, WIDE, 0>(t);
+    } else {
+        if (ntb >= NT) run_tile<EPI, WIDE, NT>(t);
+        else run_tile_ntb<EPI, WIDE, NT - 1>(t, ntb);
+    }
+}
+
+template <int EPI, bool WIDE>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs args) {
+    using C = Shape<EPI, WIDE>;
     extern __shared__ __align__(16) unsigned char smem[];
-    int* tile_prefix = (int*)(smem + kSlots * kSlot);
+    int* tile_prefix = (int*)(smem + C::RING);
     __shared__ int scan_sh[8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int G = args.G, rows = args.rows, K = args.K, N = args.N;
     const int* offs = args.offsets;
 
@@ -241,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs arg
                 lo = min(max(offs[g], 0), rows);
                 hi = max(lo, min(max(offs[g + 1], 0), rows));
             }
-            const int mt = (hi - lo + TM - 1) / TM;
+            const int mt = (hi - lo + C::TM - 1) / C::TM;
             tile_prefix[g] = mt;
             local += mt;
         }
@@ -268,27 +364,30 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs arg
         __syncthreads();
     }
 
-    constexpr int kPanel = (EPI == EPI_SWIGLU_BF16) ? 128 : 256;  // packed panel rows
-    const int NT = (N + kPanel - 1) / kPanel;
+    const int NP = (N + C::PANEL - 1) / C::PANEL;      // packed panels per expert
+    const int NT = (N + C::TN - 1) / C::TN;            // n-tiles per expert
     const long long Q = (long long)tile_prefix[G] * NT;
     const int xcd = blockIdx.x & 7;
     const int per_xcd = gridDim.x >> 3;
     const long long q_lo = Q * xcd / 8, q_hi = Q * (xcd + 1) / 8;
-    const size_t w_group = (size_t)NT * kPanel * K;   // packed elements per expert
+    const size_t pstride = (size_t)C::PANEL * K;
+    const size_t w_group = (size_t)NP * pstride;       // packed elements per expert
 
-    LdsTile<EPI> t;
+    LdsTile t;
     t.args = &args;
     t.smem = smem;
     t.lds0 = (uint32_t)(uintptr_t)smem;
     t.lane = lane;
     t.wave = wave;
-    t.wm = wave >> 2;
-    t.wn = wave & 3;
+    t.wm = WIDE ? 0 : wave >> 2;
+    t.wn = WIDE ? wave : wave & 3;
     t.half = lane >> 5;
     t.l32 = lane & 31;
     t.K = K;
     t.N = N;
     t.S = K / BK;
+    t.pstride = pstride;
+    t.wstride = (size_t)C::BPP * 2048;
 
     for (long long q = q_lo + (blockIdx.x >> 3); q < q_hi; q += per_xcd) {
         const int qm = (int)(q / NT);
@@ -310,54 +409,77 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs arg
             grp_lo = min(max(offs[g], 0), rows);
             grp_hi = max(grp_lo, min(max(offs[g + 1], 0), rows));
         }
-        t.row0 = grp_lo + m_tile * TM;
-        t.grp_hi = grp_hi;
-        t.valid = min(TM, grp_hi - t.row0);
-        // weight panel of this n-tile: stage chunks of kPanel/32 blocks x 4 KB
-        const size_t pbase = (size_t)g * w_group + (size_t)n_tile * kPanel * K;
+        t.row0 = grp_lo + m_tile * C::TM;
+        t.valid = min(C::TM, grp_hi - t.row0);
+        // activation instructions n = wave + 8 i with a valid row (16 n < valid)
+        t.na = 0;
+#pragma unroll
+        for (int i = 0; i < C::APW; ++i)
+            t.na += (wave + 8 * i < C::AINSTR && 16 * (wave + 8 * i) < t.valid) ? 1 : 0;
+        // weight panels of this n-tile
+        const int p0 = n_tile * C::PPT;
+        const size_t pbase = (size_t)g * w_group + (size_t)p0 * pstride;
         t.wsrc0 = args.w1 + pbase;
         t.wsrc1 = (EPI == EPI_SWIGLU_BF16 ? args.w2 : args.w1) + pbase;
-        t.wstride = (size_t)(kPanel / 32) * 2048;
-        t.n0 = (EPI == EPI_SWIGLU_BF16) ? n_tile * 128 + t.wn * 32 : n_tile * 256 + t.wn * 64;
-        // this wave computes the valid 32-row blocks of its 128-row half
-        const int wrows = min(max(t.valid - t.wm * 128, 0), 128);
-        const bool wact = t.n0 < N;
-        const int ntb = wact ? (wrows + 31) / 32 : 0;
-        switch (ntb) {
-            case 0: run_tile<EPI, 0>(t); break;
-            case 1: run_tile<EPI, 1>(t); break;
-            case 2: run_tile<EPI, 2>(t); break;
-            case 3: run_tile<EPI, 3>(t); break;
-            default: run_tile<EPI, 4>(t); break;
-        }
+        t.np_left = min(C::PPT, NP - p0);
+        t.n0 = (EPI == EPI_SWIGLU_BF16) ? n_tile * C::TN + t.wn * 32 : n_tile * C::TN + t.wn * 64;
+        // square tiles split the valid rows evenly (in 32-row blocks) between
+        // the two wave halves, so both waves of a SIMD compute
+        t.mh = WIDE ? C::MH : min(C::MH, (((t.valid + 1) >> 1) + 31) & ~31);
+        const int wrows = min(max(t.valid - t.wm * t.mh, 0), t.mh);
+        const int ntb = t.n0 < N ? (wrows + 31) / 32 : 0;
+        run_tile_ntb<EPI, WIDE, C::MAXNTB>(t, ntb);
     }
 }
 
-template <int EPI>
-hipError_t launch_lds_epi(const GemmArgs& g, hipStream_t stream) {
+template <int EPI, bool WIDE>
+hipError_t launch_lds(const GemmArgs& g, hipStream_t stream) {
+    using C = Shape<EPI, WIDE>;
     static int configured_device = -1;
     static int grid = 0;
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
-    const size_t lds = kSlots * kSlot + (size_t)(MOE_MAX_GROUPS + 1) * sizeof(int);
+    const size_t lds = C::RING + (size_t)(g.G + 1) * sizeof(int);
+    if (lds + kStaticLds > (size_t)kLdsLimit) return hipErrorInvalidValue;
     if (configured_device != dev) {
-        err = hipFuncSetAttribute((const void*)grouped_gemm_lds_kernel<EPI>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        err = hipFuncSetAttribute((const void*)grouped_gemm_lds_kernel<EPI, WIDE>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  kLdsLimit - kStaticLds);
         if (err != hipSuccess) return err;
         grid = (device_cu_count() + 7) & ~7;
         configured_device = dev;
     }
-    hipLaunchKernelGGL(grouped_gemm_lds_kernel<EPI>, dim3(grid), dim3(kThreads), lds, stream, g);
+    hipLaunchKernelGGL((grouped_gemm_lds_kernel<EPI, WIDE>), dim3(grid), dim3(kThreads), lds,
+                       stream, g);
     return hipGetLastError();
+}
+
+template <bool WIDE>
+int max_groups() {
+    constexpr int ring = Shape<EPI_SWIGLU_BF16, WIDE>::RING > Shape<EPI_F32, WIDE>::RING
+                             ? Shape<EPI_SWIGLU_BF16, WIDE>::RING
+                             : Shape<EPI_F32, WIDE>::RING;
+    return (kLdsLimit - kStaticLds - ring) / (int)sizeof(int) - 1;
 }
 
 }  // namespace
 
+int grouped_gemm_lds_max_groups() {
+    const int a = max_groups<false>(), b = max_groups<true>();
+    return a < b ? a : b;
+}
+
 hipError_t launch_grouped_gemm_lds(int epilogue, const GemmArgs& g, hipStream_t stream) {
+    if (g.K % BK != 0 || g.G < 1) return hipErrorInvalidValue;
+    const bool wide = g.wide != 0;
     switch (epilogue) {
-        case EPI_SWIGLU_BF16: return launch_lds_epi<EPI_SWIGLU_BF16>(g, stream);
-        case EPI_F32: return launch_lds_epi<EPI_F32>(g, stream);
+        case EPI_SWIGLU_BF16:
+            return wide ? launch_lds<EPI_SWIGLU_BF16, true>(g, stream)
+                        : launch_lds<EPI_SWIGLU_BF16, false>(g, stream);
+        case EPI_F32:
+            return wide ? launch_lds<EPI_F32, true>(g, stream)
+                        : launch_lds<EPI_F32, false>(g, stream);
         default: return hipErrorInvalidValue;
     }
 }

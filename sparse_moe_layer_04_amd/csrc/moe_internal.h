@@ -53,12 +53,30 @@ struct GemmArgs {
     int clamp_mode;
     int packed;               // weights in the moe_pack_weights layout
     void* out;                // [rows, N] bf16 (SWIGLU) or fp32
+    int a_blocked;            // a in the blocked activation layout (below)
+    int out_blocked;          // SWIGLU out in the blocked activation layout
+    int wide;                 // LDS kernel: 128-row x 512-weight-row tiles
 };
+
+// Blocked activation layout (internal to moe_forward): a [rows, K] bf16
+// matrix stored as 1 KB blocks of 16 rows x 32 columns, blocks ordered by row
+// block then column block, each block row-major:
+//   elem(r, c) at ((r / 16) * (K / 32) + c / 32) * 512 + (r % 16) * 32 + c % 32.
+// K must be a multiple of 32 and the buffer must hold ceil(rows / 16) * 16
+// rows.  Sixteen consecutive rows of a 32-wide K slice are then 1 KB of
+// contiguous memory, which is what the expert GEMM copies per DMA
+// instruction.
+__host__ __device__ __forceinline__ size_t blocked_index(size_t r, size_t c, size_t K) {
+    return ((r >> 4) * (K >> 5) + (c >> 5)) * 512 + (r & 15) * 32 + (c & 31);
+}
+inline size_t blocked_rows(size_t rows) { return (rows + 15) & ~size_t(15); }
 
 hipError_t launch_grouped_gemm(int epilogue, const GemmArgs& g, hipStream_t stream);
 // Expert GEMMs on packed weights (EPI_SWIGLU_BF16 with 128-row panels,
-// EPI_F32 with 256-row panels): 256 x 256 tiles staged in LDS by DMA.
+// EPI_F32 with 256-row panels): tiles staged in LDS by DMA.  Takes
+// G <= grouped_gemm_lds_max_groups().
 hipError_t launch_grouped_gemm_lds(int epilogue, const GemmArgs& g, hipStream_t stream);
+int grouped_gemm_lds_max_groups();
 size_t packed_weight_elems(int G, int N, int K, int P);
 hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int G, int N, int K, int P,
                                hipStream_t stream);
@@ -71,7 +89,8 @@ hipError_t launch_route(const float* logits, const float* bias, const uint8_t* m
 size_t permute_workspace_bytes(int T, int k, int E);
 hipError_t launch_permute(const int32_t* ids, const uint16_t* x, int T, int d, int E, int k,
                           int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
-                          uint16_t* x_perm, uint32_t* flags, void* ws, hipStream_t stream);
+                          uint16_t* x_perm, uint32_t* flags, void* ws, hipStream_t stream,
+                          bool blocked = false);
 
 hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* w,
                           const float* y_shared, int T, int d, int k, int rows, int out_dtype,
