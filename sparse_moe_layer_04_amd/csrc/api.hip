@@ -86,6 +86,7 @@ struct FwdWs {
     uint16_t* hs;
     float* ys;
     void* perm;
+    uint32_t* sched;  // 4 x kSchedWords expert GEMM counters
     size_t total;
 };
 
@@ -111,6 +112,7 @@ FwdWs forward_layout(const moe_cfg* c, char* base) {
     w.hs = (uint16_t*)take(T * (size_t)(c->F_shared > 0 ? c->F_shared : 0) * 2);
     w.ys = (float*)take(c->F_shared > 0 ? T * c->d * 4 : 0);
     w.perm = take(permute_workspace_bytes(c->T, c->k, c->E));
+    w.sched = (uint32_t*)take(4 * kSchedWords * sizeof(uint32_t));
     w.total = off;
     return w;
 }
@@ -343,8 +345,9 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     // 3. dispatch permutation + row gather
     // the LDS-staged expert GEMM reads x_perm and h in the blocked layout
     const bool blocked = lds_gemm_ok(w->packed, E);
+    // (its first kernel also clears the expert GEMMs' scheduling counters)
     if ((e = launch_permute(ids, x, T, d, E, k, L.counts, L.offsets, L.dest, L.src, L.x_perm,
-                            d_flags, L.perm, s, blocked)) != hipSuccess)
+                            d_flags, L.perm, s, blocked, L.sched, 4 * kSchedWords)) != hipSuccess)
         return MOE_ERR_HIP;
     if (!mark(3)) return MOE_ERR_HIP;
     const int rows = T * k;
@@ -364,8 +367,8 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g1.out = L.h;
     g1.a_blocked = blocked;
     g1.out_blocked = blocked;
-    // experts averaging at most 128 rows take the 128 x 512 tile shape
-    g1.wide = (long long)rows <= 128ll * E;
+    g1.wide = 1;
+    g1.sched = L.sched;
     if ((e = expert_gemm(EPI_SWIGLU_BF16, g1, s)) != hipSuccess) return MOE_ERR_HIP;
     if (!mark(4)) return MOE_ERR_HIP;
     // 5. shared expert gate/up
@@ -382,6 +385,8 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
         gs.clamp_limit = c->clamp_limit;
         gs.clamp_mode = c->clamp_mode;
         gs.out = L.hs;
+        gs.wide = 1;
+        gs.sched = L.sched + kSchedWords;
         if ((e = expert_gemm(EPI_SWIGLU_BF16, gs, s)) != hipSuccess) return MOE_ERR_HIP;
     }
     if (!mark(5)) return MOE_ERR_HIP;
@@ -397,7 +402,8 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g2.packed = w->packed;
     g2.out = L.y_perm;
     g2.a_blocked = blocked;
-    g2.wide = g1.wide;
+    g2.wide = 1;
+    g2.sched = L.sched + 2 * kSchedWords;
     if ((e = expert_gemm(EPI_F32, g2, s)) != hipSuccess) return MOE_ERR_HIP;
     if (!mark(6)) return MOE_ERR_HIP;
     // 7. shared expert down
@@ -411,6 +417,8 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
         gs.w1 = w->s_down;
         gs.packed = w->packed;
         gs.out = L.ys;
+        gs.wide = 1;
+        gs.sched = L.sched + 3 * kSchedWords;
         if ((e = expert_gemm(EPI_F32, gs, s)) != hipSuccess) return MOE_ERR_HIP;
     }
     if (!mark(7)) return MOE_ERR_HIP;

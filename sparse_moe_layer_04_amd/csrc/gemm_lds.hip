@@ -41,9 +41,9 @@
 // assembly, so the compiler does not see LDS writes it would otherwise guard
 // with a full vmcnt drain before every LDS read; explicit vmcnt waits + one
 // barrier per stage are the complete synchronisation.
-// Scheduling: persistent grid, per-expert tile prefix built in LDS from the
-// device offsets, items ordered (expert, n-tile, m-tile) and split into 8
-// contiguous ranges, one per XCD.
+// Scheduling: persistent grid; per-expert item and cost prefixes built in
+// LDS from the device offsets; cost-balanced contiguous item ranges per XCD,
+// claimed in order by the XCD's workgroups (see grouped_gemm_lds_kernel).
 #include "moe_internal.h"
 
 #ifndef MOE_LDS_TM
@@ -59,7 +59,7 @@ namespace {
 constexpr int BK = 32;                       // K per pipeline stage
 constexpr int kThreads = 512;
 constexpr int kLdsLimit = 160 * 1024;
-constexpr int kStaticLds = 8 * sizeof(int);  // scan_sh
+constexpr int kStaticLds = 256;              // reserve for static LDS (scan_sh, next_item)
 
 template <int EPI, bool WIDE>
 struct Shape {
@@ -133,6 +133,9 @@ struct LdsTile {
     int np_left;           // panels of this n-tile that exist (1..PPT)
     size_t pstride;        // packed elements per panel
     size_t wstride;        // packed elements per 64-wide K stage of one panel
+    unsigned* ctr;         // this XCD's item counter (dynamic scheduling) or NULL
+    int* next_item;        // LDS slot receiving the claimed next item
+    int item_lo;           // first item of this XCD's range
 };
 
 // DMA of pipeline stage j (32 k) into the LDS slot at byte offset `sbase`.
@@ -183,37 +186,39 @@ __device__ __forceinline__ void issue_stage(const LdsTile& t, int j, uint32_t sb
     }
 }
 
+// MFMA operands of one 16-wide K substep q of a stage: this wave's two weight
+// fragments and its NTB activation fragments.
+template <int NTB>
+struct Operands {
+    bf16x8 w0, w1, a[NTB];
+};
+
 template <int EPI, bool WIDE, int NTB>
-__device__ __forceinline__ void compute_stage(const LdsTile& t, uint32_t sbase,
-                                              f32x16 (&acc)[2][Shape<EPI, WIDE>::MAXNTB]) {
+__device__ __forceinline__ void read_operands(const LdsTile& t, uint32_t sbase, int q,
+                                              Operands<NTB>& o) {
     using C = Shape<EPI, WIDE>;
     const unsigned char* base = t.smem + sbase;
     // weight blocks of this wave (fragment slots 2 b + substep)
     const int b0 = (EPI == EPI_SWIGLU_BF16) ? t.wn : 2 * t.wn;
     const int b1 = (EPI == EPI_SWIGLU_BF16) ? C::WBLK / 2 + t.wn : 2 * t.wn + 1;
     const unsigned char* wbase = base + C::SLOTA + t.lane * 16;
-    // all operand reads of the stage first, in the order the MFMAs consume
-    // them, so each MFMA waits only for its own operands
-    bf16x8 w0[2], w1[2], at[2][NTB];
+    o.w0 = *(const bf16x8*)(wbase + (b0 * 2 + q) * 1024);
+    o.w1 = *(const bf16x8*)(wbase + (b1 * 2 + q) * 1024);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        w0[q] = *(const bf16x8*)(wbase + (b0 * 2 + q) * 1024);
-        w1[q] = *(const bf16x8*)(wbase + (b1 * 2 + q) * 1024);
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-            const int r = t.wm * t.mh + tb * 32 + t.l32;
-            const int c = (2 * q + t.half) ^ swz(r);
-            at[q][tb] = *(const bf16x8*)(base + r * 64 + c * 16);
-        }
+    for (int tb = 0; tb < NTB; ++tb) {
+        const int r = t.wm * t.mh + tb * 32 + t.l32;
+        const int c = (2 * q + t.half) ^ swz(r);
+        o.a[tb] = *(const bf16x8*)(base + r * 64 + c * 16);
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+}
+
+template <int NTB, int MAXNTB>
+__device__ __forceinline__ void mfma_substep(const Operands<NTB>& o, f32x16 (&acc)[2][MAXNTB]) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-            acc[0][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w0[q], at[q][tb], acc[0][tb], 0, 0, 0);
-            acc[1][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w1[q], at[q][tb], acc[1][tb], 0, 0, 0);
-        }
+    for (int tb = 0; tb < NTB; ++tb) {
+        acc[0][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.w0, o.a[tb], acc[0][tb], 0, 0, 0);
+        acc[1][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.w1, o.a[tb], acc[1][tb], 0, 0, 0);
+    }
 }
 
 template <int EPI, bool WIDE, int NTB>
@@ -289,15 +294,40 @@ __device__ __forceinline__ void run_tile(const LdsTile& t) {
 #pragma unroll
     for (int p = 0; p < C::AHEAD; ++p) issue_stage<EPI, WIDE>(t, min(p, S - 1), p * C::SLOT);
     uint32_t s_cmp = 0, s_iss = C::AHEAD * C::SLOT;
+    // Operand reads run one half-stage ahead of the MFMAs: after the barrier
+    // of stage j the wave reads substep 0 of stage j while it multiplies
+    // substep 1 of stage j - 1 (read before this barrier), then reads
+    // substep 1 of stage j while it multiplies substep 0.  Every LDS read
+    // latency hides behind MFMAs of the same wave; the reads of a slot
+    // complete before the next barrier, so the DMA that reuses the slot
+    // after that barrier never races them.
+    Operands<NTB> o0, o1;
     for (int j = 0; j < S; ++j) {
         wait_stage<C::NW, C::AHEAD>(t.na);
         __syncthreads();
         issue_stage<EPI, WIDE>(t, min(j + C::AHEAD, S - 1), s_iss);
         s_iss = (s_iss + C::SLOT == C::RING) ? 0 : s_iss + C::SLOT;
-        if constexpr (NTB > 0) compute_stage<EPI, WIDE, NTB>(t, s_cmp, acc);
+        if constexpr (NTB > 0) {
+            read_operands<EPI, WIDE, NTB>(t, s_cmp, 0, o0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (j > 0) mfma_substep<NTB, C::MAXNTB>(o1, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            read_operands<EPI, WIDE, NTB>(t, s_cmp, 1, o1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_substep<NTB, C::MAXNTB>(o0, acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         s_cmp = (s_cmp + C::SLOT == C::RING) ? 0 : s_cmp + C::SLOT;
     }
+    if constexpr (NTB > 0) mfma_substep<NTB, C::MAXNTB>(o1, acc);
+    // dynamic scheduling: thread 0 claims the workgroup's next item here,
+    // after the last stage wait, so no claim is in flight while the K loop
+    // counts DMA entries
+    const bool claim = t.ctr != nullptr && threadIdx.x == 0;
+    unsigned claimed = 0;
+    if (claim) claimed = atomicAdd(t.ctr, 1u);
     wait_vm<0>();
+    if (claim) *t.next_item = t.item_lo + (int)claimed;
     __syncthreads();
     if constexpr (NTB > 0) epilogue<EPI, WIDE, NTB>(t, acc);
 }
@@ -313,65 +343,163 @@ __device__ __forceinline__ void run_tile_ntb(const LdsTile& t, int ntb) {
     }
 }
 
+// Tile of item (group g, local item index) in the given shape: set up the
+// per-tile fields of t and run it.
 template <int EPI, bool WIDE>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs args) {
+__device__ __forceinline__ void do_tile(LdsTile& t, const GemmArgs& args, int g, int local,
+                                        int grp_lo, int grp_hi) {
     using C = Shape<EPI, WIDE>;
+    const int N = args.N;
+    int n_tile = local, m_tile = 0;
+    if (!WIDE) {
+        const int mt = (grp_hi - grp_lo + C::TM - 1) / C::TM;
+        n_tile = local / mt;
+        m_tile = local % mt;
+    }
+    t.row0 = grp_lo + m_tile * C::TM;
+    t.valid = min(C::TM, grp_hi - t.row0);
+    // activation instructions n = wave + 8 i with a valid row (16 n < valid)
+    t.na = 0;
+#pragma unroll
+    for (int i = 0; i < C::APW; ++i)
+        t.na += (t.wave + 8 * i < C::AINSTR && 16 * (t.wave + 8 * i) < t.valid) ? 1 : 0;
+    t.wm = WIDE ? 0 : t.wave >> 2;
+    t.wn = WIDE ? t.wave : t.wave & 3;
+    // weight panels of this n-tile
+    const int NP = (N + C::PANEL - 1) / C::PANEL;
+    const int p0 = n_tile * C::PPT;
+    t.pstride = (size_t)C::PANEL * t.K;
+    const size_t pbase = ((size_t)g * NP + p0) * t.pstride;
+    t.wsrc0 = args.w1 + pbase;
+    t.wsrc1 = (EPI == EPI_SWIGLU_BF16 ? args.w2 : args.w1) + pbase;
+    t.np_left = min(C::PPT, NP - p0);
+    t.wstride = (size_t)C::BPP * 2048;
+    t.n0 = (EPI == EPI_SWIGLU_BF16) ? n_tile * C::TN + t.wn * 32 : n_tile * C::TN + t.wn * 64;
+    // square tiles split the valid rows evenly (in 32-row blocks) between
+    // the two wave halves, so both waves of a SIMD compute
+    t.mh = WIDE ? C::MH : min(C::MH, (((t.valid + 1) >> 1) + 31) & ~31);
+    const int wrows = min(max(t.valid - t.wm * t.mh, 0), t.mh);
+    const int ntb = t.n0 < N ? (wrows + 31) / 32 : 0;
+    run_tile_ntb<EPI, WIDE, C::MAXNTB>(t, ntb);
+}
+
+template <int EPI>
+constexpr int ring_bytes() {
+    return Shape<EPI, false>::RING > Shape<EPI, true>::RING ? Shape<EPI, false>::RING
+                                                             : Shape<EPI, true>::RING;
+}
+
+// Work items: a group with at most 128 rows (when args.wide) is wide-tiled,
+// ceil(N / TN_wide) items; any other non-empty group is square-tiled,
+// ceil(N / TN_square) x ceil(rows / 256) items.  An item's cost is its
+// weight rows (wide 2, square 1 units of 256 rows x K), since every item
+// streams its weight panels through the CU.  Items are ordered (group,
+// n-tile, m-tile); the 8 XCDs take contiguous ranges of equal cost, and
+// inside an XCD the workgroups claim items in order from a per-XCD counter
+// (args.sched, zeroed before the launch) or, without counters, take every
+// 32nd item.  Workgroups of one XCD thus work on neighbouring items (the
+// n-tiles of the same experts) at the same time and share their
+// activations in L2.
+template <int EPI>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs args) {
+    using SQ = Shape<EPI, false>;
+    using WD = Shape<EPI, true>;
     extern __shared__ __align__(16) unsigned char smem[];
-    int* tile_prefix = (int*)(smem + C::RING);
-    __shared__ int scan_sh[8];
+    __shared__ int scan_sh[2][8];
+    __shared__ int next_item;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int G = args.G, rows = args.rows, K = args.K, N = args.N;
     const int* offs = args.offsets;
+    int* item_prefix = (int*)(smem + ring_bytes<EPI>());  // [G + 1]
+    int* cost_prefix = item_prefix + (G + 1);               // [G + 1]
+    const int NTs = (N + SQ::TN - 1) / SQ::TN;
+    const int NTw = (N + WD::TN - 1) / WD::TN;
 
-    // ---- per-group m-tile counts -> exclusive prefix in LDS ----
+    auto group_rows = [&](int g, int& lo, int& hi) {
+        lo = 0;
+        hi = rows;
+        if (offs) {
+            lo = min(max(offs[g], 0), rows);
+            hi = max(lo, min(max(offs[g + 1], 0), rows));
+        }
+    };
+    auto is_wide = [&](int n) { return args.wide && n <= WD::TM; };
+
+    // ---- per-group item counts and costs -> exclusive prefixes in LDS ----
     {
         const int per = (G + kThreads - 1) / kThreads;
         const int g0 = tid * per;
-        int local = 0;
+        int li = 0, lc = 0;
         for (int g = g0; g < g0 + per && g < G; ++g) {
-            int lo = 0, hi = rows;
-            if (offs) {
-                lo = min(max(offs[g], 0), rows);
-                hi = max(lo, min(max(offs[g + 1], 0), rows));
-            }
-            const int mt = (hi - lo + C::TM - 1) / C::TM;
-            tile_prefix[g] = mt;
-            local += mt;
+            int lo, hi;
+            group_rows(g, lo, hi);
+            const int n = hi - lo;
+            const int items = n == 0 ? 0 : is_wide(n) ? NTw : NTs * ((n + SQ::TM - 1) / SQ::TM);
+            item_prefix[g] = items;
+            cost_prefix[g] = items * (is_wide(n) ? 2 : 1);
+            li += items;
+            lc += cost_prefix[g];
         }
-        int x = local;
+        int xi = li, xc = lc;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            int y = __shfl_up(x, off, 64);
-            if (lane >= off) x += y;
+            const int yi = __shfl_up(xi, off, 64), yc = __shfl_up(xc, off, 64);
+            if (lane >= off) {
+                xi += yi;
+                xc += yc;
+            }
         }
-        if (lane == 63) scan_sh[wave] = x;
+        if (lane == 63) {
+            scan_sh[0][wave] = xi;
+            scan_sh[1][wave] = xc;
+        }
         __syncthreads();
-        int wbase = 0, total = 0;
+        int bi = 0, bc = 0, ti = 0, tc = 0;
         for (int w = 0; w < 8; ++w) {
-            if (w < wave) wbase += scan_sh[w];
-            total += scan_sh[w];
+            if (w < wave) {
+                bi += scan_sh[0][w];
+                bc += scan_sh[1][w];
+            }
+            ti += scan_sh[0][w];
+            tc += scan_sh[1][w];
         }
-        int run = wbase + x - local;
+        int ri = bi + xi - li, rc = bc + xc - lc;
         for (int g = g0; g < g0 + per && g < G; ++g) {
-            const int mt = tile_prefix[g];
-            tile_prefix[g] = run;
-            run += mt;
+            const int vi = item_prefix[g], vc = cost_prefix[g];
+            item_prefix[g] = ri;
+            cost_prefix[g] = rc;
+            ri += vi;
+            rc += vc;
         }
-        if (tid == 0) tile_prefix[G] = total;
+        if (tid == 0) {
+            item_prefix[G] = ti;
+            cost_prefix[G] = tc;
+        }
         __syncthreads();
     }
 
-    const int NP = (N + C::PANEL - 1) / C::PANEL;      // packed panels per expert
-    const int NT = (N + C::TN - 1) / C::TN;            // n-tiles per expert
-    const long long Q = (long long)tile_prefix[G] * NT;
+    // first item whose cost starts at or after `target`
+    auto boundary = [&](long long target) -> int {
+        int lo = 0, hi = G;  // largest g with cost_prefix[g] <= target
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cost_prefix[mid] <= target) lo = mid; else hi = mid - 1;
+        }
+        if (lo == G) return item_prefix[G];
+        const int items = item_prefix[lo + 1] - item_prefix[lo];
+        if (items == 0) return item_prefix[lo];
+        const int unit = (cost_prefix[lo + 1] - cost_prefix[lo]) / items;
+        const long long rem = target - cost_prefix[lo];
+        return item_prefix[lo] + (int)min((long long)items, (rem + unit - 1) / unit);
+    };
     const int xcd = blockIdx.x & 7;
     const int per_xcd = gridDim.x >> 3;
-    const long long q_lo = Q * xcd / 8, q_hi = Q * (xcd + 1) / 8;
-    const size_t pstride = (size_t)C::PANEL * K;
-    const size_t w_group = (size_t)NP * pstride;       // packed elements per expert
+    const long long total_cost = cost_prefix[G];
+    const int item_lo = boundary(total_cost * xcd / 8);
+    const int item_hi = boundary(total_cost * (xcd + 1) / 8);
 
     LdsTile t;
     t.args = &args;
@@ -379,107 +507,84 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs arg
     t.lds0 = (uint32_t)(uintptr_t)smem;
     t.lane = lane;
     t.wave = wave;
-    t.wm = WIDE ? 0 : wave >> 2;
-    t.wn = WIDE ? wave : wave & 3;
     t.half = lane >> 5;
     t.l32 = lane & 31;
     t.K = K;
     t.N = N;
     t.S = K / BK;
-    t.pstride = pstride;
-    t.wstride = (size_t)C::BPP * 2048;
+    t.ctr = args.sched ? args.sched + xcd * 32 : nullptr;
+    t.next_item = &next_item;
+    t.item_lo = item_lo;
 
-    for (long long q = q_lo + (blockIdx.x >> 3); q < q_hi; q += per_xcd) {
-        const int qm = (int)(q / NT);
+    int q;
+    if (t.ctr) {
+        if (tid == 0) next_item = item_lo + (int)atomicAdd(t.ctr, 1u);
+        __syncthreads();
+        q = next_item;
+    } else {
+        q = item_lo + (blockIdx.x >> 3);
+    }
+    while (q < item_hi) {
         int g = 0;
         {
             int lo = 0, hi = G;
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
-                if (tile_prefix[mid] <= qm) lo = mid; else hi = mid - 1;
+                if (item_prefix[mid] <= q) lo = mid; else hi = mid - 1;
             }
             g = lo;
         }
-        const int mt = tile_prefix[g + 1] - tile_prefix[g];
-        const int local = (int)(q - (long long)tile_prefix[g] * NT);
-        const int n_tile = local / mt;
-        const int m_tile = local % mt;
-        int grp_lo = 0, grp_hi = rows;
-        if (offs) {
-            grp_lo = min(max(offs[g], 0), rows);
-            grp_hi = max(grp_lo, min(max(offs[g + 1], 0), rows));
-        }
-        t.row0 = grp_lo + m_tile * C::TM;
-        t.valid = min(C::TM, grp_hi - t.row0);
-        // activation instructions n = wave + 8 i with a valid row (16 n < valid)
-        t.na = 0;
-#pragma unroll
-        for (int i = 0; i < C::APW; ++i)
-            t.na += (wave + 8 * i < C::AINSTR && 16 * (wave + 8 * i) < t.valid) ? 1 : 0;
-        // weight panels of this n-tile
-        const int p0 = n_tile * C::PPT;
-        const size_t pbase = (size_t)g * w_group + (size_t)p0 * pstride;
-        t.wsrc0 = args.w1 + pbase;
-        t.wsrc1 = (EPI == EPI_SWIGLU_BF16 ? args.w2 : args.w1) + pbase;
-        t.np_left = min(C::PPT, NP - p0);
-        t.n0 = (EPI == EPI_SWIGLU_BF16) ? n_tile * C::TN + t.wn * 32 : n_tile * C::TN + t.wn * 64;
-        // square tiles split the valid rows evenly (in 32-row blocks) between
-        // the two wave halves, so both waves of a SIMD compute
-        t.mh = WIDE ? C::MH : min(C::MH, (((t.valid + 1) >> 1) + 31) & ~31);
-        const int wrows = min(max(t.valid - t.wm * t.mh, 0), t.mh);
-        const int ntb = t.n0 < N ? (wrows + 31) / 32 : 0;
-        run_tile_ntb<EPI, WIDE, C::MAXNTB>(t, ntb);
+        const int local = q - item_prefix[g];
+        int grp_lo, grp_hi;
+        group_rows(g, grp_lo, grp_hi);
+        if (is_wide(grp_hi - grp_lo)) do_tile<EPI, true>(t, args, g, local, grp_lo, grp_hi);
+        else do_tile<EPI, false>(t, args, g, local, grp_lo, grp_hi);
+        q = t.ctr ? next_item : q + per_xcd;
     }
 }
 
-template <int EPI, bool WIDE>
+template <int EPI>
 hipError_t launch_lds(const GemmArgs& g, hipStream_t stream) {
-    using C = Shape<EPI, WIDE>;
     static int configured_device = -1;
     static int grid = 0;
+    static size_t static_lds = 0;
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
-    const size_t lds = C::RING + (size_t)(g.G + 1) * sizeof(int);
-    if (lds + kStaticLds > (size_t)kLdsLimit) return hipErrorInvalidValue;
     if (configured_device != dev) {
-        err = hipFuncSetAttribute((const void*)grouped_gemm_lds_kernel<EPI, WIDE>,
+        hipFuncAttributes fa;
+        err = hipFuncGetAttributes(&fa, (const void*)grouped_gemm_lds_kernel<EPI>);
+        if (err != hipSuccess) return err;
+        static_lds = fa.sharedSizeBytes;
+        if (static_lds > (size_t)kStaticLds) return hipErrorInvalidValue;
+        err = hipFuncSetAttribute((const void*)grouped_gemm_lds_kernel<EPI>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  kLdsLimit - kStaticLds);
+                                  kLdsLimit - (int)static_lds);
         if (err != hipSuccess) return err;
         grid = (device_cu_count() + 7) & ~7;
         configured_device = dev;
     }
-    hipLaunchKernelGGL((grouped_gemm_lds_kernel<EPI, WIDE>), dim3(grid), dim3(kThreads), lds,
-                       stream, g);
+    const size_t lds = ring_bytes<EPI>() + 2 * (size_t)(g.G + 1) * sizeof(int);
+    if (lds + static_lds > (size_t)kLdsLimit) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((grouped_gemm_lds_kernel<EPI>), dim3(grid), dim3(kThreads), lds, stream,
+                       g);
     return hipGetLastError();
-}
-
-template <bool WIDE>
-int max_groups() {
-    constexpr int ring = Shape<EPI_SWIGLU_BF16, WIDE>::RING > Shape<EPI_F32, WIDE>::RING
-                             ? Shape<EPI_SWIGLU_BF16, WIDE>::RING
-                             : Shape<EPI_F32, WIDE>::RING;
-    return (kLdsLimit - kStaticLds - ring) / (int)sizeof(int) - 1;
 }
 
 }  // namespace
 
 int grouped_gemm_lds_max_groups() {
-    const int a = max_groups<false>(), b = max_groups<true>();
-    return a < b ? a : b;
+    constexpr int ring = ring_bytes<EPI_SWIGLU_BF16>() > ring_bytes<EPI_F32>()
+                             ? ring_bytes<EPI_SWIGLU_BF16>()
+                             : ring_bytes<EPI_F32>();
+    return (kLdsLimit - kStaticLds - ring) / (2 * (int)sizeof(int)) - 1;
 }
 
 hipError_t launch_grouped_gemm_lds(int epilogue, const GemmArgs& g, hipStream_t stream) {
     if (g.K % BK != 0 || g.G < 1) return hipErrorInvalidValue;
-    const bool wide = g.wide != 0;
     switch (epilogue) {
-        case EPI_SWIGLU_BF16:
-            return wide ? launch_lds<EPI_SWIGLU_BF16, true>(g, stream)
-                        : launch_lds<EPI_SWIGLU_BF16, false>(g, stream);
-        case EPI_F32:
-            return wide ? launch_lds<EPI_F32, true>(g, stream)
-                        : launch_lds<EPI_F32, false>(g, stream);
+        case EPI_SWIGLU_BF16: return launch_lds<EPI_SWIGLU_BF16>(g, stream);
+        case EPI_F32: return launch_lds<EPI_F32>(g, stream);
         default: return hipErrorInvalidValue;
     }
 }

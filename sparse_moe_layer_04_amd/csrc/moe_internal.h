@@ -55,8 +55,12 @@ struct GemmArgs {
     void* out;                // [rows, N] bf16 (SWIGLU) or fp32
     int a_blocked;            // a in the blocked activation layout (below)
     int out_blocked;          // SWIGLU out in the blocked activation layout
-    int wide;                 // LDS kernel: 128-row x 512-weight-row tiles
+    int wide;                 // LDS kernel: groups of <= 128 rows take 128 x 512 tiles
+    uint32_t* sched;          // LDS kernel: 8 per-XCD item counters, 128 B apart,
+                              // zero at launch (NULL: static schedule)
 };
+// per-launch scheduling counters of the LDS-staged expert GEMM
+constexpr int kSchedWords = 8 * 32;
 
 // Blocked activation layout (internal to moe_forward): a [rows, K] bf16
 // matrix stored as 1 KB blocks of 16 rows x 32 columns, blocks ordered by row
@@ -90,7 +94,8 @@ size_t permute_workspace_bytes(int T, int k, int E);
 hipError_t launch_permute(const int32_t* ids, const uint16_t* x, int T, int d, int E, int k,
                           int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
                           uint16_t* x_perm, uint32_t* flags, void* ws, hipStream_t stream,
-                          bool blocked = false);
+                          bool blocked = false, uint32_t* zero = nullptr, int nzero = 0);
+// (the rank kernel also clears zero[0, nzero): the expert GEMMs' counters)
 
 hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* w,
                           const float* y_shared, int T, int d, int k, int rows, int out_dtype,

@@ -55,13 +55,17 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ rank,
                                                         int32_t* __restrict__ hist,
                                                         uint32_t* __restrict__ done,
-                                                        uint32_t* __restrict__ flags) {
+                                                        uint32_t* __restrict__ flags,
+                                                        uint32_t* __restrict__ zero, int nzero) {
     extern __shared__ int cnt_all[];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int c = blockIdx.x * 4 + wave;
     int* cnt = cnt_all + wave * E;
-    if (blockIdx.x == 0 && threadIdx.x == 0) *done = 0u;
+    if (blockIdx.x == 0) {
+        if (threadIdx.x == 0) *done = 0u;
+        for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0u;
+    }
     for (int e = lane; e < E; e += 64) cnt[e] = 0;
     __syncthreads();
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -226,19 +230,18 @@ size_t permute_workspace_bytes(int T, int k, int E) {
 hipError_t launch_permute(const int32_t* ids, const uint16_t* x, int T, int d, int E, int k,
                           int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
                           uint16_t* x_perm, uint32_t* flags, void* ws, hipStream_t stream,
-                          bool blocked) {
+                          bool blocked, uint32_t* zero, int nzero) {
     const int N = T * k;
     PermWs w = carve(ws, N, E);
     const int nchunks = (N + kChunk - 1) / kChunk;
     int id_bits = 0;
     while ((1 << id_bits) < E) ++id_bits;
-    if (N > 0) {
-        const int blocks = (nchunks + 3) / 4;
+    {
+        // (with N = 0 one block still runs: it only clears the counters)
+        const int blocks = N > 0 ? (nchunks + 3) / 4 : 1;
         hipLaunchKernelGGL(perm_rank_kernel, dim3(blocks), dim3(256), 4 * E * sizeof(int),
-                           stream, ids, N, E, nchunks, id_bits, w.rank, w.hist, w.done, flags);
-    } else {
-        hipError_t err = hipMemsetAsync(w.done, 0, sizeof(uint32_t), stream);
-        if (err != hipSuccess) return err;
+                           stream, ids, N, E, nchunks, id_bits, w.rank, w.hist, w.done, flags,
+                           zero, nzero);
     }
     hipLaunchKernelGGL(perm_scan_kernel, dim3(E), dim3(256), 0, stream, w.hist, nchunks, E, N,
                        w.base, counts, offsets, src, w.done);
