@@ -367,7 +367,6 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g1.out = L.h;
     g1.a_blocked = blocked;
     g1.out_blocked = blocked;
-    g1.wide = 1;
     g1.sched = L.sched;
     if ((e = expert_gemm(EPI_SWIGLU_BF16, g1, s)) != hipSuccess) return MOE_ERR_HIP;
     if (!mark(4)) return MOE_ERR_HIP;
@@ -385,7 +384,6 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
         gs.clamp_limit = c->clamp_limit;
         gs.clamp_mode = c->clamp_mode;
         gs.out = L.hs;
-        gs.wide = 1;
         gs.sched = L.sched + kSchedWords;
         if ((e = expert_gemm(EPI_SWIGLU_BF16, gs, s)) != hipSuccess) return MOE_ERR_HIP;
     }
@@ -402,7 +400,6 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g2.packed = w->packed;
     g2.out = L.y_perm;
     g2.a_blocked = blocked;
-    g2.wide = 1;
     g2.sched = L.sched + 2 * kSchedWords;
     if ((e = expert_gemm(EPI_F32, g2, s)) != hipSuccess) return MOE_ERR_HIP;
     if (!mark(6)) return MOE_ERR_HIP;
@@ -417,7 +414,6 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
         gs.w1 = w->s_down;
         gs.packed = w->packed;
         gs.out = L.ys;
-        gs.wide = 1;
         gs.sched = L.sched + 3 * kSchedWords;
         if ((e = expert_gemm(EPI_F32, gs, s)) != hipSuccess) return MOE_ERR_HIP;
     }

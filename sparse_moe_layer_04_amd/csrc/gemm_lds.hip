@@ -9,82 +9,67 @@
 // up matrices, P = 256 for the down matrix) and A row-major or in the
 // blocked activation layout (16 x 32 blocks of 1 KB).
 //
-// Two tile shapes, one workgroup of 8 waves (two per SIMD) per tile; every
-// wave owns two 32-row weight blocks (SwiGLU: gate block and the up block of
-// the same 32 features; down: two adjacent output blocks) times up to four
-// 32-row activation blocks (acc: 2 x NTB MFMA 32x32 tiles):
-//   - square: up to TM = 256 activation rows x 256 weight rows (SwiGLU: 128
-//     features).  Wave w = (wm, wn): wm = w / 4 takes one half of the tile's
-//     valid rows (rounded to 32-row blocks), wn = w % 4 its weight blocks.
-//   - wide: up to 128 activation rows x 512 weight rows (SwiGLU: 256
-//     features); all 8 waves share the activation rows, wave w takes weight
-//     blocks of index w.  Each activation byte staged feeds twice the MFMA
-//     work, so experts with at most 128 rows move half the activation bytes
-//     per weight byte.
-// An expert with up to TM rows is one tile row, so its weights are read from
-// memory once.  Per 32-wide K stage one LDS slot holds
-//   - the activation tile, TM rows x 64 B, the 16-byte chunks of row r
+// Tiles of up to 256 activation rows x 256 weight rows (SwiGLU: 128 features
+// x {gate, up}), one workgroup of 8 waves (two per SIMD) per tile.  Wave
+// w = (wm, wn): wn = w % 4 owns two 32-row weight blocks (SwiGLU: gate block
+// wn and the up block of the same 32 features; down: blocks 2 wn, 2 wn + 1),
+// wm = w / 4 one half of the tile's valid rows, split in 32-row blocks so
+// that both waves of a SIMD compute (acc: 2 x NTB MFMA 32x32 tiles,
+// NTB <= 4).  An expert with up to 256 rows is one tile row, so its weights
+// are streamed from memory once.  (Taller or wider tiles for mid-size or
+// very small experts stage more activation bytes per weight byte or hold
+// fewer stages in flight; measured on MI355X they were slower.)
+// Per 32-wide K stage one LDS slot holds
+//   - the activation tile, 256 rows x 64 B, the 16-byte chunks of row r
 //     XOR-swizzled by sw(r) = ((r >> 1) ^ (r >> 3)) & 3, so that the 16
 //     lanes an LDS cycle serves (256 B over 64 banks: rows r, r+4, r+8,
 //     r+12 share banks) hit distinct banks in MFMA operand reads;
-//   - the weight half-stage in matrix-core fragment order (copied from the
-//     packed layout in 1 KB runs; operand reads are 1 KB contiguous per
-//     wave).
-// A ring of SLOTS LDS slots keeps SLOTS - 1 stages in flight per CU.  The
-// DMA (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16 l) moves
-// 1 KB per instruction: weight instructions and blocked-layout activation
+//   - the weight half-stage, 16 KB in matrix-core fragment order (copied
+//     from the packed layout in 1 KB runs; operand reads are 1 KB
+//     contiguous per wave).
+// A ring of 4 slots keeps 3 stages (96 KB) in flight per CU.  The DMA
+// (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16 l) moves 1 KB
+// per instruction: weight instructions and blocked-layout activation
 // instructions each read 1 KB of contiguous memory (8 full cache lines);
 // row-major activations cost 16 half-used lines per instruction.  Each wave
-// issues NW weight instructions and na activation instructions per stage
-// (only the 16-row groups that hold valid rows are copied); both are fixed
-// for a tile, so vmcnt counts stay exact.  The DMA is issued from inline
-// assembly, so the compiler does not see LDS writes it would otherwise guard
-// with a full vmcnt drain before every LDS read; explicit vmcnt waits + one
-// barrier per stage are the complete synchronisation.
-// Scheduling: persistent grid; per-expert item and cost prefixes built in
-// LDS from the device offsets; cost-balanced contiguous item ranges per XCD,
-// claimed in order by the XCD's workgroups (see grouped_gemm_lds_kernel).
+// issues 2 weight instructions and na in {0, 1, 2} activation instructions
+// per stage (only the 16-row groups that hold valid rows are copied); na is
+// fixed for a tile, so vmcnt counts stay exact.  The DMA is issued from
+// inline assembly, so the compiler does not see LDS writes it would
+// otherwise guard with a full vmcnt drain before every LDS read; explicit
+// vmcnt waits + one barrier per stage are the complete synchronisation, and
+// the kernel keeps every other value in registers (a spill reload would make
+// the compiler drain vmcnt inside the pipeline).
+// Scheduling: see grouped_gemm_lds_kernel.
 #include "moe_internal.h"
-
-#ifndef MOE_LDS_TM
-#define MOE_LDS_TM 256
-#endif
-#ifndef MOE_LDS_SLOTS
-#define MOE_LDS_SLOTS 4
-#endif
 
 namespace moe {
 namespace {
 
+constexpr int TM = 256;                      // activation rows per tile
+constexpr int MH = TM / 2;                   // max rows per wave
+constexpr int MAXNTB = MH / 32;              // activation blocks per wave
+constexpr int WBLK = 8;                      // 32-row weight blocks per tile
 constexpr int BK = 32;                       // K per pipeline stage
+constexpr int kSlotA = TM * 64;              // activation tile per stage
+constexpr int kSlotW = WBLK * 2 * 1024;      // weight half-stage: 2 substeps x 1 KB per block
+constexpr int kSlot = kSlotA + kSlotW;
+constexpr int kSlots = 4;                    // LDS ring
+constexpr int kAhead = kSlots - 1;           // stages in flight
+constexpr int kRing = kSlots * kSlot;
+constexpr int kAInstr = TM / 16;             // activation DMA instructions per stage
+constexpr int kAPerWave = kAInstr / 8;
 constexpr int kThreads = 512;
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int kStaticLds = 256;              // reserve for static LDS (scan_sh, next_item)
 
-template <int EPI, bool WIDE>
-struct Shape {
-    static constexpr int TM = WIDE ? 128 : MOE_LDS_TM;      // activation rows per tile
-    static_assert(TM % 64 == 0 && TM >= 64 && TM <= 256, "TM: 64..256, multiple of 64");
-    static constexpr int MH = WIDE ? TM : TM / 2;           // max rows per wave
-    static constexpr int MAXNTB = MH / 32;                  // activation blocks per wave
-    static constexpr int WBLK = WIDE ? 16 : 8;              // 32-row weight blocks per tile
-    static constexpr int NW = WBLK / 4;                     // weight DMA instrs per wave per stage
-    static constexpr int WAVES_N = WIDE ? 8 : 4;            // waves along the weight rows
-    static constexpr int SLOTA = TM * 64;
-    static constexpr int SLOTW = WBLK * 2 * 1024;           // 2 substeps x 1 KB per block
-    static constexpr int SLOT = SLOTA + SLOTW;
-    static constexpr int SLOTS = WIDE ? 3 : MOE_LDS_SLOTS;
-    static constexpr int AHEAD = SLOTS - 1;                 // stages in flight
-    static_assert(SLOTS >= 2 && SLOTS <= 8, "ring depth");
-    static constexpr int AINSTR = TM / 16;                  // activation instrs per stage
-    static constexpr int APW = (AINSTR + 7) / 8;            // ... per wave (max)
-    static constexpr int PANEL = (EPI == EPI_SWIGLU_BF16) ? 128 : 256;
-    static constexpr int BPP = PANEL / 32;                  // blocks per panel
-    // weight rows (per matrix) and panels (per matrix) of one n-tile
-    static constexpr int TN = (EPI == EPI_SWIGLU_BF16) ? WBLK * 16 : WBLK * 32;
-    static constexpr int PPT = TN / PANEL;
-    static constexpr int RING = SLOTS * SLOT;
-    static_assert(RING + kStaticLds < kLdsLimit, "LDS ring");
+template <int EPI>
+struct Panel {
+    static constexpr int P = (EPI == EPI_SWIGLU_BF16) ? 128 : 256;  // packed panel rows
+    static constexpr int BPP = P / 32;                               // blocks per panel
+    // weight blocks per matrix in a tile (SwiGLU: 4 gate blocks, then 4 up)
+    static constexpr int BPM = (EPI == EPI_SWIGLU_BF16) ? WBLK / 2 : WBLK;
+    static constexpr int TN = BPM * 32;                              // rows of one matrix
 };
 
 __device__ __forceinline__ float clamp_sym(float v, float L) { return fminf(fmaxf(v, -L), L); }
@@ -109,13 +94,12 @@ __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// wait for the oldest in-flight stage of a wave that issues na + NW
-// instructions per stage (AHEAD - 1 newer stages may stay outstanding)
-template <int NW, int AHEAD>
+// wait for the oldest in-flight stage of a wave that issues na + 2
+// instructions per stage (kAhead - 1 newer stages may stay outstanding)
 __device__ __forceinline__ void wait_stage(int na) {
-    if (na == 2) wait_vm<(AHEAD - 1) * (NW + 2)>();
-    else if (na == 1) wait_vm<(AHEAD - 1) * (NW + 1)>();
-    else wait_vm<(AHEAD - 1) * NW>();
+    if (na == 2) wait_vm<(kAhead - 1) * 4>();
+    else if (na == 1) wait_vm<(kAhead - 1) * 3>();
+    else wait_vm<(kAhead - 1) * 2>();
 }
 
 struct LdsTile {
@@ -127,10 +111,13 @@ struct LdsTile {
     int row0, valid;
     int mh;                // activation rows per wave half (multiple of 32)
     int na;                // activation DMA instructions of this wave per stage
+    uint32_t a_off[kAPerWave];  // lane's stage-0 source of activation instruction i (16 B units)
+    uint32_t a_step;       // ... advance per stage (16 B units)
     int n0;                // first weight row / feature of this wave's blocks
-    const uint16_t* wsrc0; // first panel of this n-tile (gate matrix for SwiGLU)
-    const uint16_t* wsrc1; // up matrix panel (SwiGLU) or the same
-    int np_left;           // panels of this n-tile that exist (1..PPT)
+    const uint16_t* wsrc0; // this expert's packed matrix (gate matrix for SwiGLU)
+    const uint16_t* wsrc1; // up matrix (SwiGLU) or the same
+    int blk0;              // first 32-row block of this n-tile in each matrix
+    int np;                // packed panels per matrix
     size_t pstride;        // packed elements per panel
     size_t wstride;        // packed elements per 64-wide K stage of one panel
     unsigned* ctr;         // this XCD's item counter (dynamic scheduling) or NULL
@@ -140,49 +127,43 @@ struct LdsTile {
 
 // DMA of pipeline stage j (32 k) into the LDS slot at byte offset `sbase`.
 //   activations: instruction n (rows [16 n, 16 n + 16) of the tile) belongs
-//     to wave n % 8 and is issued only if the group holds a valid row; rows
-//     past the tile read the last valid row.  Chunk c of row r is stored at
-//     position c ^ sw(r).
+//     to wave n % 8 and is issued only if the group holds a valid row (the
+//     per-lane sources are set up per tile in t.a_off).
 //   weights: the 64-wide packed stage s = j / 2 holds, per 32-row block,
 //     4 substeps x 1 KB; this half-stage (h = j % 2) takes substeps 2h, 2h+1
-//     of all WBLK blocks: instruction n = NW w + i copies tile block n / 2,
-//     substep 2h + n % 2 to LDS fragment slot n.  SwiGLU tile blocks
-//     [0, WBLK/2) are gate rows, the rest up rows; a block of a panel past
-//     the matrix end re-reads the last panel (its outputs are never stored).
-template <int EPI, bool WIDE>
+//     of all 8 blocks: instruction n = 2 w + i copies tile block n / 2,
+//     substep 2h + n % 2 to LDS fragment slot n.  SwiGLU tile blocks [0, 4)
+//     are gate rows, [4, 8) up rows; a block of a panel past the matrix end
+//     re-reads the last panel (its outputs are never stored).
+template <int EPI>
 __device__ __forceinline__ void issue_stage(const LdsTile& t, int j, uint32_t sbase) {
-    using C = Shape<EPI, WIDE>;
+    using Pn = Panel<EPI>;
     const uint32_t base = t.lds0 + sbase;
-    const int kcol = j * BK;
     const GemmArgs& args = *t.args;
 #pragma unroll
-    for (int i = 0; i < C::APW; ++i) {
+    for (int i = 0; i < kAPerWave; ++i) {
         if (i < t.na) {
             const int r0 = 16 * (t.wave + 8 * i);
-            const int r = r0 + (t.lane >> 2);
-            const int c = (t.lane & 3) ^ swz(r);
-            const size_t grow = (size_t)(t.row0 + min(r, t.valid - 1));
-            const uint16_t* src = args.a_blocked ? args.a + blocked_index(grow, kcol + c * 8, t.K)
-                                                 : args.a + grow * t.K + kcol + c * 8;
-            dma16(src, base + r0 * 64);
+            const uint32_t off = t.a_off[i] + (uint32_t)j * t.a_step;
+            dma16((const u32x4*)args.a + off, base + r0 * 64);
         }
     }
     const int s64 = j >> 1, h2 = j & 1;
 #pragma unroll
-    for (int i = 0; i < C::NW; ++i) {
-        const int n = C::NW * t.wave + i;
+    for (int i = 0; i < 2; ++i) {
+        const int n = 2 * t.wave + i;
         const int b = n >> 1;
         const int sub = 2 * h2 + (n & 1);
         const uint16_t* mat = t.wsrc0;
-        int bb = b;
-        if (EPI == EPI_SWIGLU_BF16 && b >= C::WBLK / 2) {
+        int gb = t.blk0 + b;
+        if (EPI == EPI_SWIGLU_BF16 && b >= Pn::BPM) {
             mat = t.wsrc1;
-            bb = b - C::WBLK / 2;
+            gb -= Pn::BPM;
         }
-        const int panel = min(bb / C::BPP, t.np_left - 1);
+        const int panel = min(gb / Pn::BPP, t.np - 1);
         const uint16_t* src = mat + (size_t)panel * t.pstride + (size_t)s64 * t.wstride +
-                              (bb % C::BPP) * 2048 + sub * 512 + t.lane * 8;
-        dma16(src, base + C::SLOTA + n * 1024);
+                              (gb % Pn::BPP) * 2048 + sub * 512 + t.lane * 8;
+        dma16(src, base + kSlotA + n * 1024);
     }
 }
 
@@ -193,15 +174,14 @@ struct Operands {
     bf16x8 w0, w1, a[NTB];
 };
 
-template <int EPI, bool WIDE, int NTB>
+template <int EPI, int NTB>
 __device__ __forceinline__ void read_operands(const LdsTile& t, uint32_t sbase, int q,
                                               Operands<NTB>& o) {
-    using C = Shape<EPI, WIDE>;
     const unsigned char* base = t.smem + sbase;
     // weight blocks of this wave (fragment slots 2 b + substep)
     const int b0 = (EPI == EPI_SWIGLU_BF16) ? t.wn : 2 * t.wn;
-    const int b1 = (EPI == EPI_SWIGLU_BF16) ? C::WBLK / 2 + t.wn : 2 * t.wn + 1;
-    const unsigned char* wbase = base + C::SLOTA + t.lane * 16;
+    const int b1 = (EPI == EPI_SWIGLU_BF16) ? Panel<EPI>::BPM + t.wn : 2 * t.wn + 1;
+    const unsigned char* wbase = base + kSlotA + t.lane * 16;
     o.w0 = *(const bf16x8*)(wbase + (b0 * 2 + q) * 1024);
     o.w1 = *(const bf16x8*)(wbase + (b1 * 2 + q) * 1024);
 #pragma unroll
@@ -212,7 +192,7 @@ __device__ __forceinline__ void read_operands(const LdsTile& t, uint32_t sbase, 
     }
 }
 
-template <int NTB, int MAXNTB>
+template <int NTB>
 __device__ __forceinline__ void mfma_substep(const Operands<NTB>& o, f32x16 (&acc)[2][MAXNTB]) {
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
@@ -221,9 +201,8 @@ __device__ __forceinline__ void mfma_substep(const Operands<NTB>& o, f32x16 (&ac
     }
 }
 
-template <int EPI, bool WIDE, int NTB>
-__device__ __forceinline__ void epilogue(const LdsTile& t,
-                                         const f32x16 (&acc)[2][Shape<EPI, WIDE>::MAXNTB]) {
+template <int EPI, bool BLK, int NTB>
+__device__ __forceinline__ void epilogue(const LdsTile& t, const f32x16 (&acc)[2][MAXNTB]) {
     const GemmArgs& args = *t.args;
     const int N = t.N;
 #pragma unroll
@@ -253,7 +232,7 @@ __device__ __forceinline__ void epilogue(const LdsTile& t,
                     }
                     packed[i >> 1] = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
                 }
-                uint16_t* dst = args.out_blocked ? out + blocked_index(r, n, N) : out + r * N + n;
+                uint16_t* dst = BLK ? out + blocked_index(r, n, N) : out + r * N + n;
                 *(u32x2*)dst = u32x2{packed[0], packed[1]};
             }
         } else {
@@ -273,27 +252,26 @@ __device__ __forceinline__ void epilogue(const LdsTile& t,
 }
 
 // K loop of one tile for a wave computing NTB 32-row blocks (0: DMA only).
-// Stages j+1 .. j+AHEAD-1 stay in flight while stage j computes: wait for
+// Stages j+1 .. j+kAhead-1 stay in flight while stage j computes: wait for
 // stage j (this wave's own DMA), barrier (all waves' DMA of stage j landed,
 // and all waves are done reading the slot the next DMA overwrites), issue
-// stage j + AHEAD into the slot stage j - 1 used, compute stage j.  Stages
+// stage j + kAhead into the slot stage j - 1 used, compute stage j.  Stages
 // past the end re-issue the last stage, so every iteration issues the same
 // number of instructions.
-template <int EPI, bool WIDE, int NTB>
+template <int EPI, bool BLK, int NTB>
 __device__ __forceinline__ void run_tile(const LdsTile& t) {
-    using C = Shape<EPI, WIDE>;
-    f32x16 acc[2][C::MAXNTB];
+    f32x16 acc[2][MAXNTB];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int tb = 0; tb < C::MAXNTB; ++tb)
+        for (int tb = 0; tb < MAXNTB; ++tb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[b][tb][i] = 0.0f;
     const int S = t.S;
     wait_vm<0>();  // retire the previous tile's stores before counting DMA entries
 #pragma unroll
-    for (int p = 0; p < C::AHEAD; ++p) issue_stage<EPI, WIDE>(t, min(p, S - 1), p * C::SLOT);
-    uint32_t s_cmp = 0, s_iss = C::AHEAD * C::SLOT;
+    for (int p = 0; p < kAhead; ++p) issue_stage<EPI>(t, min(p, S - 1), p * kSlot);
+    uint32_t s_cmp = 0, s_iss = kAhead * kSlot;
     // Operand reads run one half-stage ahead of the MFMAs: after the barrier
     // of stage j the wave reads substep 0 of stage j while it multiplies
     // substep 1 of stage j - 1 (read before this barrier), then reads
@@ -303,23 +281,23 @@ __device__ __forceinline__ void run_tile(const LdsTile& t) {
     // after that barrier never races them.
     Operands<NTB> o0, o1;
     for (int j = 0; j < S; ++j) {
-        wait_stage<C::NW, C::AHEAD>(t.na);
+        wait_stage(t.na);
         __syncthreads();
-        issue_stage<EPI, WIDE>(t, min(j + C::AHEAD, S - 1), s_iss);
-        s_iss = (s_iss + C::SLOT == C::RING) ? 0 : s_iss + C::SLOT;
+        issue_stage<EPI>(t, min(j + kAhead, S - 1), s_iss);
+        s_iss = (s_iss + kSlot == kRing) ? 0 : s_iss + kSlot;
         if constexpr (NTB > 0) {
-            read_operands<EPI, WIDE, NTB>(t, s_cmp, 0, o0);
+            read_operands<EPI, NTB>(t, s_cmp, 0, o0);
             __builtin_amdgcn_sched_barrier(0);
-            if (j > 0) mfma_substep<NTB, C::MAXNTB>(o1, acc);
+            if (j > 0) mfma_substep<NTB>(o1, acc);
             __builtin_amdgcn_sched_barrier(0);
-            read_operands<EPI, WIDE, NTB>(t, s_cmp, 1, o1);
+            read_operands<EPI, NTB>(t, s_cmp, 1, o1);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_substep<NTB, C::MAXNTB>(o0, acc);
+            mfma_substep<NTB>(o0, acc);
             __builtin_amdgcn_sched_barrier(0);
         }
-        s_cmp = (s_cmp + C::SLOT == C::RING) ? 0 : s_cmp + C::SLOT;
+        s_cmp = (s_cmp + kSlot == kRing) ? 0 : s_cmp + kSlot;
     }
-    if constexpr (NTB > 0) mfma_substep<NTB, C::MAXNTB>(o1, acc);
+    if constexpr (NTB > 0) mfma_substep<NTB>(o1, acc);
     // dynamic scheduling: thread 0 claims the workgroup's next item here,
     // after the last stage wait, so no claim is in flight while the K loop
     // counts DMA entries
@@ -329,83 +307,75 @@ __device__ __forceinline__ void run_tile(const LdsTile& t) {
     wait_vm<0>();
     if (claim) *t.next_item = t.item_lo + (int)claimed;
     __syncthreads();
-    if constexpr (NTB > 0) epilogue<EPI, WIDE, NTB>(t, acc);
+    if constexpr (NTB > 0) epilogue<EPI, BLK, NTB>(t, acc);
 }
 
 // run_tile for ntb in [0, NT] (ntb is wave-uniform)
-template <int EPI, bool WIDE, int NT>
+template <int EPI, bool BLK, int NT>
 __device__ __forceinline__ void run_tile_ntb(const LdsTile& t, int ntb) {
     if constexpr (NT == 0) {
-        run_tile<EPI, WIDE, 0>(t);
+        run_tile<EPI, BLK, 0>(t);
     } else {
-        if (ntb >= NT) run_tile<EPI, WIDE, NT>(t);
-        else run_tile_ntb<EPI, WIDE, NT - 1>(t, ntb);
+        if (ntb >= NT) run_tile<EPI, BLK, NT>(t);
+        else run_tile_ntb<EPI, BLK, NT - 1>(t, ntb);
     }
 }
 
-// Tile of item (group g, local item index) in the given shape: set up the
-// per-tile fields of t and run it.
-template <int EPI, bool WIDE>
+// Tile of item (group g, local item index): set up the per-tile fields of t
+// and run it.
+template <int EPI, bool BLK>
 __device__ __forceinline__ void do_tile(LdsTile& t, const GemmArgs& args, int g, int local,
                                         int grp_lo, int grp_hi) {
-    using C = Shape<EPI, WIDE>;
+    using Pn = Panel<EPI>;
     const int N = args.N;
-    int n_tile = local, m_tile = 0;
-    if (!WIDE) {
-        const int mt = (grp_hi - grp_lo + C::TM - 1) / C::TM;
-        n_tile = local / mt;
-        m_tile = local % mt;
-    }
-    t.row0 = grp_lo + m_tile * C::TM;
-    t.valid = min(C::TM, grp_hi - t.row0);
-    // activation instructions n = wave + 8 i with a valid row (16 n < valid)
+    const int mt = (grp_hi - grp_lo + TM - 1) / TM;
+    const int n_tile = local / mt, m_tile = local % mt;
+    t.row0 = grp_lo + m_tile * TM;
+    t.valid = min(TM, grp_hi - t.row0);
+    // activation instructions n = wave + 8 i with a valid row (16 n < valid);
+    // lane l copies 16 bytes of row r = 16 n + l / 4: chunk c = (l % 4) ^ sw(r)
+    // of the stage's 32 columns (rows past the tile read the last valid row)
     t.na = 0;
 #pragma unroll
-    for (int i = 0; i < C::APW; ++i)
-        t.na += (t.wave + 8 * i < C::AINSTR && 16 * (t.wave + 8 * i) < t.valid) ? 1 : 0;
-    t.wm = WIDE ? 0 : t.wave >> 2;
-    t.wn = WIDE ? t.wave : t.wave & 3;
-    // weight panels of this n-tile
-    const int NP = (N + C::PANEL - 1) / C::PANEL;
-    const int p0 = n_tile * C::PPT;
-    t.pstride = (size_t)C::PANEL * t.K;
-    const size_t pbase = ((size_t)g * NP + p0) * t.pstride;
-    t.wsrc0 = args.w1 + pbase;
-    t.wsrc1 = (EPI == EPI_SWIGLU_BF16 ? args.w2 : args.w1) + pbase;
-    t.np_left = min(C::PPT, NP - p0);
-    t.wstride = (size_t)C::BPP * 2048;
-    t.n0 = (EPI == EPI_SWIGLU_BF16) ? n_tile * C::TN + t.wn * 32 : n_tile * C::TN + t.wn * 64;
-    // square tiles split the valid rows evenly (in 32-row blocks) between
-    // the two wave halves, so both waves of a SIMD compute
-    t.mh = WIDE ? C::MH : min(C::MH, (((t.valid + 1) >> 1) + 31) & ~31);
+    for (int i = 0; i < kAPerWave; ++i) {
+        t.na += (16 * (t.wave + 8 * i) < t.valid) ? 1 : 0;
+        const int r = 16 * (t.wave + 8 * i) + (t.lane >> 2);
+        const int c = (t.lane & 3) ^ swz(r);
+        const size_t grow = (size_t)(t.row0 + min(r, t.valid - 1));
+        const size_t e = BLK ? blocked_index(grow, c * 8, t.K) : grow * t.K + c * 8;
+        t.a_off[i] = (uint32_t)(e >> 3);
+    }
+    t.a_step = BLK ? 512 / 8 : BK / 8;
+    // this expert's packed matrices and the n-tile's first block
+    t.np = (N + Pn::P - 1) / Pn::P;
+    t.pstride = (size_t)Pn::P * t.K;
+    const size_t ebase = (size_t)g * t.np * t.pstride;
+    t.wsrc0 = args.w1 + ebase;
+    t.wsrc1 = (EPI == EPI_SWIGLU_BF16 ? args.w2 : args.w1) + ebase;
+    t.blk0 = n_tile * Pn::BPM;
+    t.wstride = (size_t)Pn::BPP * 2048;
+    t.n0 = n_tile * Pn::TN + t.wn * ((EPI == EPI_SWIGLU_BF16) ? 32 : 64);
+    // the valid rows split evenly (in 32-row blocks) over the two wave halves
+    t.mh = min(MH, (((t.valid + 1) >> 1) + 31) & ~31);
     const int wrows = min(max(t.valid - t.wm * t.mh, 0), t.mh);
     const int ntb = t.n0 < N ? (wrows + 31) / 32 : 0;
-    run_tile_ntb<EPI, WIDE, C::MAXNTB>(t, ntb);
+    run_tile_ntb<EPI, BLK, MAXNTB>(t, ntb);
 }
 
-template <int EPI>
-constexpr int ring_bytes() {
-    return Shape<EPI, false>::RING > Shape<EPI, true>::RING ? Shape<EPI, false>::RING
-                                                             : Shape<EPI, true>::RING;
-}
-
-// Work items: a group with at most 128 rows (when args.wide) is wide-tiled,
-// ceil(N / TN_wide) items; any other non-empty group is square-tiled,
-// ceil(N / TN_square) x ceil(rows / 256) items.  An item's cost is its
-// weight rows (wide 2, square 1 units of 256 rows x K), since every item
-// streams its weight panels through the CU.  Items are ordered (group,
-// n-tile, m-tile); the 8 XCDs take contiguous ranges of equal cost, and
-// inside an XCD the workgroups claim items in order from a per-XCD counter
-// (args.sched, zeroed before the launch) or, without counters, take every
-// 32nd item.  Workgroups of one XCD thus work on neighbouring items (the
-// n-tiles of the same experts) at the same time and share their
-// activations in L2.
-template <int EPI>
+// Work items: a group of n > 0 rows has ceil(N / TN) x ceil(n / 256) items
+// (n-tile major); every item streams the same weight bytes (one tile's
+// panels).  Items are ordered (group, n-tile, m-tile) and the 8 XCDs take
+// contiguous ranges of equal item count; inside an XCD the workgroups claim
+// items in order from a per-XCD counter (args.sched, zeroed before the
+// launch) or, without counters, take every 32nd item.  Workgroups of one XCD
+// thus work on neighbouring items (the n-tiles of the same experts) at the
+// same time and share their activations in L2, and a workgroup that drew
+// cheap tiles (few valid rows) takes more of them.
+template <int EPI, bool BLK>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs args) {
-    using SQ = Shape<EPI, false>;
-    using WD = Shape<EPI, true>;
+    using Pn = Panel<EPI>;
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ int scan_sh[2][8];
+    __shared__ int scan_sh[8];
     __shared__ int next_item;
 
     const int tid = threadIdx.x;
@@ -413,10 +383,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs arg
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int G = args.G, rows = args.rows, K = args.K, N = args.N;
     const int* offs = args.offsets;
-    int* item_prefix = (int*)(smem + ring_bytes<EPI>());  // [G + 1]
-    int* cost_prefix = item_prefix + (G + 1);               // [G + 1]
-    const int NTs = (N + SQ::TN - 1) / SQ::TN;
-    const int NTw = (N + WD::TN - 1) / WD::TN;
+    int* item_prefix = (int*)(smem + kRing);  // [G + 1]
+    const int NT = (N + Pn::TN - 1) / Pn::TN;
 
     auto group_rows = [&](int g, int& lo, int& hi) {
         lo = 0;
@@ -426,80 +394,46 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs arg
             hi = max(lo, min(max(offs[g + 1], 0), rows));
         }
     };
-    auto is_wide = [&](int n) { return args.wide && n <= WD::TM; };
 
-    // ---- per-group item counts and costs -> exclusive prefixes in LDS ----
+    // ---- per-group item counts -> exclusive prefix in LDS ----
     {
         const int per = (G + kThreads - 1) / kThreads;
         const int g0 = tid * per;
-        int li = 0, lc = 0;
+        int local = 0;
         for (int g = g0; g < g0 + per && g < G; ++g) {
             int lo, hi;
             group_rows(g, lo, hi);
-            const int n = hi - lo;
-            const int items = n == 0 ? 0 : is_wide(n) ? NTw : NTs * ((n + SQ::TM - 1) / SQ::TM);
+            const int items = NT * ((hi - lo + TM - 1) / TM);
             item_prefix[g] = items;
-            cost_prefix[g] = items * (is_wide(n) ? 2 : 1);
-            li += items;
-            lc += cost_prefix[g];
+            local += items;
         }
-        int xi = li, xc = lc;
+        int x = local;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            const int yi = __shfl_up(xi, off, 64), yc = __shfl_up(xc, off, 64);
-            if (lane >= off) {
-                xi += yi;
-                xc += yc;
-            }
+            const int y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
         }
-        if (lane == 63) {
-            scan_sh[0][wave] = xi;
-            scan_sh[1][wave] = xc;
-        }
+        if (lane == 63) scan_sh[wave] = x;
         __syncthreads();
-        int bi = 0, bc = 0, ti = 0, tc = 0;
+        int wbase = 0, total = 0;
         for (int w = 0; w < 8; ++w) {
-            if (w < wave) {
-                bi += scan_sh[0][w];
-                bc += scan_sh[1][w];
-            }
-            ti += scan_sh[0][w];
-            tc += scan_sh[1][w];
+            if (w < wave) wbase += scan_sh[w];
+            total += scan_sh[w];
         }
-        int ri = bi + xi - li, rc = bc + xc - lc;
+        int run = wbase + x - local;
         for (int g = g0; g < g0 + per && g < G; ++g) {
-            const int vi = item_prefix[g], vc = cost_prefix[g];
-            item_prefix[g] = ri;
-            cost_prefix[g] = rc;
-            ri += vi;
-            rc += vc;
+            const int v = item_prefix[g];
+            item_prefix[g] = run;
+            run += v;
         }
-        if (tid == 0) {
-            item_prefix[G] = ti;
-            cost_prefix[G] = tc;
-        }
+        if (tid == 0) item_prefix[G] = total;
         __syncthreads();
     }
 
-    // first item whose cost starts at or after `target`
-    auto boundary = [&](long long target) -> int {
-        int lo = 0, hi = G;  // largest g with cost_prefix[g] <= target
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (cost_prefix[mid] <= target) lo = mid; else hi = mid - 1;
-        }
-        if (lo == G) return item_prefix[G];
-        const int items = item_prefix[lo + 1] - item_prefix[lo];
-        if (items == 0) return item_prefix[lo];
-        const int unit = (cost_prefix[lo + 1] - cost_prefix[lo]) / items;
-        const long long rem = target - cost_prefix[lo];
-        return item_prefix[lo] + (int)min((long long)items, (rem + unit - 1) / unit);
-    };
     const int xcd = blockIdx.x & 7;
     const int per_xcd = gridDim.x >> 3;
-    const long long total_cost = cost_prefix[G];
-    const int item_lo = boundary(total_cost * xcd / 8);
-    const int item_hi = boundary(total_cost * (xcd + 1) / 8);
+    const long long Q = item_prefix[G];
+    const int item_lo = (int)(Q * xcd / 8), item_hi = (int)(Q * (xcd + 1) / 8);
 
     LdsTile t;
     t.args = &args;
@@ -507,6 +441,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs arg
     t.lds0 = (uint32_t)(uintptr_t)smem;
     t.lane = lane;
     t.wave = wave;
+    t.wm = wave >> 2;
+    t.wn = wave & 3;
     t.half = lane >> 5;
     t.l32 = lane & 31;
     t.K = K;
@@ -534,16 +470,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs arg
             }
             g = lo;
         }
-        const int local = q - item_prefix[g];
         int grp_lo, grp_hi;
         group_rows(g, grp_lo, grp_hi);
-        if (is_wide(grp_hi - grp_lo)) do_tile<EPI, true>(t, args, g, local, grp_lo, grp_hi);
-        else do_tile<EPI, false>(t, args, g, local, grp_lo, grp_hi);
+        do_tile<EPI, BLK>(t, args, g, q - item_prefix[g], grp_lo, grp_hi);
         q = t.ctr ? next_item : q + per_xcd;
     }
 }
 
-template <int EPI>
+template <int EPI, bool BLK>
 hipError_t launch_lds(const GemmArgs& g, hipStream_t stream) {
     static int configured_device = -1;
     static int grid = 0;
@@ -553,38 +487,44 @@ hipError_t launch_lds(const GemmArgs& g, hipStream_t stream) {
     if (err != hipSuccess) return err;
     if (configured_device != dev) {
         hipFuncAttributes fa;
-        err = hipFuncGetAttributes(&fa, (const void*)grouped_gemm_lds_kernel<EPI>);
+        err = hipFuncGetAttributes(&fa, (const void*)grouped_gemm_lds_kernel<EPI, BLK>);
         if (err != hipSuccess) return err;
         static_lds = fa.sharedSizeBytes;
         if (static_lds > (size_t)kStaticLds) return hipErrorInvalidValue;
-        err = hipFuncSetAttribute((const void*)grouped_gemm_lds_kernel<EPI>,
+        err = hipFuncSetAttribute((const void*)grouped_gemm_lds_kernel<EPI, BLK>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize,
                                   kLdsLimit - (int)static_lds);
         if (err != hipSuccess) return err;
         grid = (device_cu_count() + 7) & ~7;
         configured_device = dev;
     }
-    const size_t lds = ring_bytes<EPI>() + 2 * (size_t)(g.G + 1) * sizeof(int);
+    const size_t lds = kRing + (size_t)(g.G + 1) * sizeof(int);
     if (lds + static_lds > (size_t)kLdsLimit) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((grouped_gemm_lds_kernel<EPI>), dim3(grid), dim3(kThreads), lds, stream,
-                       g);
+    hipLaunchKernelGGL((grouped_gemm_lds_kernel<EPI, BLK>), dim3(grid), dim3(kThreads), lds,
+                       stream, g);
     return hipGetLastError();
 }
 
 }  // namespace
 
 int grouped_gemm_lds_max_groups() {
-    constexpr int ring = ring_bytes<EPI_SWIGLU_BF16>() > ring_bytes<EPI_F32>()
-                             ? ring_bytes<EPI_SWIGLU_BF16>()
-                             : ring_bytes<EPI_F32>();
-    return (kLdsLimit - kStaticLds - ring) / (2 * (int)sizeof(int)) - 1;
+    return (kLdsLimit - kStaticLds - kRing) / (int)sizeof(int) - 1;
 }
 
 hipError_t launch_grouped_gemm_lds(int epilogue, const GemmArgs& g, hipStream_t stream) {
     if (g.K % BK != 0 || g.G < 1) return hipErrorInvalidValue;
+    // activation sources are 32-bit offsets in 16-byte units
+    if ((size_t)g.rows * g.K / 8 + 2 * (size_t)g.K >= (1ull << 32)) return hipErrorInvalidValue;
     switch (epilogue) {
-        case EPI_SWIGLU_BF16: return launch_lds<EPI_SWIGLU_BF16>(g, stream);
-        case EPI_F32: return launch_lds<EPI_F32>(g, stream);
+        case EPI_SWIGLU_BF16:
+            // the blocked layout is all or nothing for the SwiGLU GEMM (h feeds
+            // the down GEMM in the same layout as x_perm)
+            if (g.out_blocked != g.a_blocked) return hipErrorInvalidValue;
+            return g.a_blocked ? launch_lds<EPI_SWIGLU_BF16, true>(g, stream)
+                               : launch_lds<EPI_SWIGLU_BF16, false>(g, stream);
+        case EPI_F32:
+            return g.a_blocked ? launch_lds<EPI_F32, true>(g, stream)
+                               : launch_lds<EPI_F32, false>(g, stream);
         default: return hipErrorInvalidValue;
     }
 }

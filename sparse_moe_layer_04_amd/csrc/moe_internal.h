@@ -55,7 +55,6 @@ struct GemmArgs {
     void* out;                // [rows, N] bf16 (SWIGLU) or fp32
     int a_blocked;            // a in the blocked activation layout (below)
     int out_blocked;          // SWIGLU out in the blocked activation layout
-    int wide;                 // LDS kernel: groups of <= 128 rows take 128 x 512 tiles
     uint32_t* sched;          // LDS kernel: 8 per-XCD item counters, 128 B apart,
                               // zero at launch (NULL: static schedule)
 };
