@@ -343,17 +343,22 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
         return MOE_ERR_HIP;
     if (!mark(2)) return MOE_ERR_HIP;
     // 3. dispatch permutation + row gather
-    // the LDS-staged expert GEMM reads x_perm and h in the blocked layout
-    const bool blocked = lds_gemm_ok(w->packed, E);
-    // (its first kernel also clears the expert GEMMs' scheduling counters)
-    if ((e = launch_permute(ids, x, T, d, E, k, L.counts, L.offsets, L.dest, L.src, L.x_perm,
-                            d_flags, L.perm, s, blocked, L.sched, 4 * kSchedWords)) != hipSuccess)
+    // The LDS-staged expert GEMM gathers the token rows through src (no
+    // x_perm copy) and passes h in the blocked layout; the register-direct
+    // kernel (plain weights) reads a row-major x_perm.  The permutation's
+    // first kernel also clears the expert GEMMs' scheduling counters.
+    const bool lds = lds_gemm_ok(w->packed, E);
+    if ((e = launch_permute(ids, x, T, d, E, k, L.counts, L.offsets, L.dest, L.src,
+                            lds ? nullptr : L.x_perm, d_flags, L.perm, s, L.sched,
+                            4 * kSchedWords)) != hipSuccess)
         return MOE_ERR_HIP;
     if (!mark(3)) return MOE_ERR_HIP;
     const int rows = T * k;
     // 4. routed experts: gate/up + clamped SwiGLU
     GemmArgs g1{};
-    g1.a = L.x_perm;
+    g1.a = lds ? x : L.x_perm;
+    g1.gather = lds ? L.src : nullptr;
+    g1.a_rows = T;
     g1.offsets = L.offsets;
     g1.G = E;
     g1.rows = rows;
@@ -365,8 +370,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g1.clamp_limit = c->clamp_limit;
     g1.clamp_mode = c->clamp_mode;
     g1.out = L.h;
-    g1.a_blocked = blocked;
-    g1.out_blocked = blocked;
+    g1.out_blocked = lds;
     g1.sched = L.sched;
     if ((e = expert_gemm(EPI_SWIGLU_BF16, g1, s)) != hipSuccess) return MOE_ERR_HIP;
     if (!mark(4)) return MOE_ERR_HIP;
@@ -399,7 +403,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g2.w1 = w->w_down;
     g2.packed = w->packed;
     g2.out = L.y_perm;
-    g2.a_blocked = blocked;
+    g2.a_blocked = lds;
     g2.sched = L.sched + 2 * kSchedWords;
     if ((e = expert_gemm(EPI_F32, g2, s)) != hipSuccess) return MOE_ERR_HIP;
     if (!mark(6)) return MOE_ERR_HIP;

@@ -6,8 +6,10 @@
 // Problem: for each expert g and activation row r in [lo_g, hi_g),
 //   out[r, n] = sum_k A[r, k] * W[g, n, k]
 // with W in the moe_pack_weights panel layout (P = 128 rows for the gate and
-// up matrices, P = 256 for the down matrix) and A row-major or in the
-// blocked activation layout (16 x 32 blocks of 1 KB).
+// up matrices, P = 256 for the down matrix) and A row-major, in the blocked
+// activation layout (16 x 32 blocks of 1 KB), or gathered: row r of A is row
+// gather[r] of a row-major matrix (the dispatch permutation applied while
+// loading, so the permuted copy of the tokens is never written).
 //
 // Tiles of up to 256 activation rows x 256 weight rows (SwiGLU: 128 features
 // x {gate, up}), one workgroup of 8 waves (two per SIMD) per tile.  Wave
@@ -62,6 +64,12 @@ constexpr int kAPerWave = kAInstr / 8;
 constexpr int kThreads = 512;
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int kStaticLds = 256;              // reserve for static LDS (scan_sh, next_item)
+
+// activation addressing: row-major a, the blocked layout, or row-major a
+// with row r of the problem taken from row gather[r] (the dispatch
+// permutation applied while loading).  The SwiGLU output is written in the
+// blocked layout unless the activations are plain row-major.
+enum AMode : int { A_ROW = 0, A_BLK = 1, A_GATHER = 2 };
 
 template <int EPI>
 struct Panel {
@@ -201,7 +209,7 @@ __device__ __forceinline__ void mfma_substep(const Operands<NTB>& o, f32x16 (&ac
     }
 }
 
-template <int EPI, bool BLK, int NTB>
+template <int EPI, int AM, int NTB>
 __device__ __forceinline__ void epilogue(const LdsTile& t, const f32x16 (&acc)[2][MAXNTB]) {
     const GemmArgs& args = *t.args;
     const int N = t.N;
@@ -232,7 +240,7 @@ __device__ __forceinline__ void epilogue(const LdsTile& t, const f32x16 (&acc)[2
                     }
                     packed[i >> 1] = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
                 }
-                uint16_t* dst = BLK ? out + blocked_index(r, n, N) : out + r * N + n;
+                uint16_t* dst = AM != A_ROW ? out + blocked_index(r, n, N) : out + r * N + n;
                 *(u32x2*)dst = u32x2{packed[0], packed[1]};
             }
         } else {
@@ -258,7 +266,7 @@ __device__ __forceinline__ void epilogue(const LdsTile& t, const f32x16 (&acc)[2
 // stage j + kAhead into the slot stage j - 1 used, compute stage j.  Stages
 // past the end re-issue the last stage, so every iteration issues the same
 // number of instructions.
-template <int EPI, bool BLK, int NTB>
+template <int EPI, int AM, int NTB>
 __device__ __forceinline__ void run_tile(const LdsTile& t) {
     f32x16 acc[2][MAXNTB];
 #pragma unroll
@@ -307,23 +315,23 @@ __device__ __forceinline__ void run_tile(const LdsTile& t) {
     wait_vm<0>();
     if (claim) *t.next_item = t.item_lo + (int)claimed;
     __syncthreads();
-    if constexpr (NTB > 0) epilogue<EPI, BLK, NTB>(t, acc);
+    if constexpr (NTB > 0) epilogue<EPI, AM, NTB>(t, acc);
 }
 
 // run_tile for ntb in [0, NT] (ntb is wave-uniform)
-template <int EPI, bool BLK, int NT>
+template <int EPI, int AM, int NT>
 __device__ __forceinline__ void run_tile_ntb(const LdsTile& t, int ntb) {
     if constexpr (NT == 0) {
-        run_tile<EPI, BLK, 0>(t);
+        run_tile<EPI, AM, 0>(t);
     } else {
-        if (ntb >= NT) run_tile<EPI, BLK, NT>(t);
-        else run_tile_ntb<EPI, BLK, NT - 1>(t, ntb);
+        if (ntb >= NT) run_tile<EPI, AM, NT>(t);
+        else run_tile_ntb<EPI, AM, NT - 1>(t, ntb);
     }
 }
 
 // Tile of item (group g, local item index): set up the per-tile fields of t
 // and run it.
-template <int EPI, bool BLK>
+template <int EPI, int AM>
 __device__ __forceinline__ void do_tile(LdsTile& t, const GemmArgs& args, int g, int local,
                                         int grp_lo, int grp_hi) {
     using Pn = Panel<EPI>;
@@ -342,10 +350,13 @@ __device__ __forceinline__ void do_tile(LdsTile& t, const GemmArgs& args, int g,
         const int r = 16 * (t.wave + 8 * i) + (t.lane >> 2);
         const int c = (t.lane & 3) ^ swz(r);
         const size_t grow = (size_t)(t.row0 + min(r, t.valid - 1));
-        const size_t e = BLK ? blocked_index(grow, c * 8, t.K) : grow * t.K + c * 8;
+        size_t e;
+        if (AM == A_BLK) e = blocked_index(grow, c * 8, t.K);
+        else if (AM == A_GATHER) e = (size_t)args.gather[grow] * t.K + c * 8;
+        else e = grow * t.K + c * 8;
         t.a_off[i] = (uint32_t)(e >> 3);
     }
-    t.a_step = BLK ? 512 / 8 : BK / 8;
+    t.a_step = AM == A_BLK ? 512 / 8 : BK / 8;
     // this expert's packed matrices and the n-tile's first block
     t.np = (N + Pn::P - 1) / Pn::P;
     t.pstride = (size_t)Pn::P * t.K;
@@ -359,7 +370,7 @@ __device__ __forceinline__ void do_tile(LdsTile& t, const GemmArgs& args, int g,
     t.mh = min(MH, (((t.valid + 1) >> 1) + 31) & ~31);
     const int wrows = min(max(t.valid - t.wm * t.mh, 0), t.mh);
     const int ntb = t.n0 < N ? (wrows + 31) / 32 : 0;
-    run_tile_ntb<EPI, BLK, MAXNTB>(t, ntb);
+    run_tile_ntb<EPI, AM, MAXNTB>(t, ntb);
 }
 
 // Work items: a group of n > 0 rows has ceil(N / TN) x ceil(n / 256) items
@@ -371,7 +382,7 @@ __device__ __forceinline__ void do_tile(LdsTile& t, const GemmArgs& args, int g,
 // thus work on neighbouring items (the n-tiles of the same experts) at the
 // same time and share their activations in L2, and a workgroup that drew
 // cheap tiles (few valid rows) takes more of them.
-template <int EPI, bool BLK>
+template <int EPI, int AM>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs args) {
     using Pn = Panel<EPI>;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -472,12 +483,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs arg
         }
         int grp_lo, grp_hi;
         group_rows(g, grp_lo, grp_hi);
-        do_tile<EPI, BLK>(t, args, g, q - item_prefix[g], grp_lo, grp_hi);
+        do_tile<EPI, AM>(t, args, g, q - item_prefix[g], grp_lo, grp_hi);
         q = t.ctr ? next_item : q + per_xcd;
     }
 }
 
-template <int EPI, bool BLK>
+template <int EPI, int AM>
 hipError_t launch_lds(const GemmArgs& g, hipStream_t stream) {
     static int configured_device = -1;
     static int grid = 0;
@@ -487,11 +498,11 @@ hipError_t launch_lds(const GemmArgs& g, hipStream_t stream) {
     if (err != hipSuccess) return err;
     if (configured_device != dev) {
         hipFuncAttributes fa;
-        err = hipFuncGetAttributes(&fa, (const void*)grouped_gemm_lds_kernel<EPI, BLK>);
+        err = hipFuncGetAttributes(&fa, (const void*)grouped_gemm_lds_kernel<EPI, AM>);
         if (err != hipSuccess) return err;
         static_lds = fa.sharedSizeBytes;
         if (static_lds > (size_t)kStaticLds) return hipErrorInvalidValue;
-        err = hipFuncSetAttribute((const void*)grouped_gemm_lds_kernel<EPI, BLK>,
+        err = hipFuncSetAttribute((const void*)grouped_gemm_lds_kernel<EPI, AM>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize,
                                   kLdsLimit - (int)static_lds);
         if (err != hipSuccess) return err;
@@ -500,7 +511,7 @@ hipError_t launch_lds(const GemmArgs& g, hipStream_t stream) {
     }
     const size_t lds = kRing + (size_t)(g.G + 1) * sizeof(int);
     if (lds + static_lds > (size_t)kLdsLimit) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((grouped_gemm_lds_kernel<EPI, BLK>), dim3(grid), dim3(kThreads), lds,
+    hipLaunchKernelGGL((grouped_gemm_lds_kernel<EPI, AM>), dim3(grid), dim3(kThreads), lds,
                        stream, g);
     return hipGetLastError();
 }
@@ -513,18 +524,23 @@ int grouped_gemm_lds_max_groups() {
 
 hipError_t launch_grouped_gemm_lds(int epilogue, const GemmArgs& g, hipStream_t stream) {
     if (g.K % BK != 0 || g.G < 1) return hipErrorInvalidValue;
-    // activation sources are 32-bit offsets in 16-byte units
-    if ((size_t)g.rows * g.K / 8 + 2 * (size_t)g.K >= (1ull << 32)) return hipErrorInvalidValue;
+    // activation sources are 32-bit offsets in 16-byte units (a gathered a
+    // has at most g.a_rows rows)
+    const size_t a_rows = g.gather ? (size_t)g.a_rows : (size_t)g.rows;
+    if (a_rows * g.K / 8 + 2 * (size_t)g.K >= (1ull << 32)) return hipErrorInvalidValue;
+    if (g.gather && g.a_blocked) return hipErrorInvalidValue;
+    const int am = g.gather ? A_GATHER : g.a_blocked ? A_BLK : A_ROW;
     switch (epilogue) {
         case EPI_SWIGLU_BF16:
-            // the blocked layout is all or nothing for the SwiGLU GEMM (h feeds
-            // the down GEMM in the same layout as x_perm)
-            if (g.out_blocked != g.a_blocked) return hipErrorInvalidValue;
-            return g.a_blocked ? launch_lds<EPI_SWIGLU_BF16, true>(g, stream)
-                               : launch_lds<EPI_SWIGLU_BF16, false>(g, stream);
+            // h is blocked exactly when the activations are not plain row-major
+            if (g.out_blocked != (am != A_ROW)) return hipErrorInvalidValue;
+            if (am == A_GATHER) return launch_lds<EPI_SWIGLU_BF16, A_GATHER>(g, stream);
+            if (am == A_BLK) return launch_lds<EPI_SWIGLU_BF16, A_BLK>(g, stream);
+            return launch_lds<EPI_SWIGLU_BF16, A_ROW>(g, stream);
         case EPI_F32:
-            return g.a_blocked ? launch_lds<EPI_F32, true>(g, stream)
-                               : launch_lds<EPI_F32, false>(g, stream);
+            if (am == A_GATHER) return launch_lds<EPI_F32, A_GATHER>(g, stream);
+            if (am == A_BLK) return launch_lds<EPI_F32, A_BLK>(g, stream);
+            return launch_lds<EPI_F32, A_ROW>(g, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -54,6 +54,8 @@ struct GemmArgs {
     int packed;               // weights in the moe_pack_weights layout
     void* out;                // [rows, N] bf16 (SWIGLU) or fp32
     int a_blocked;            // a in the blocked activation layout (below)
+    const int32_t* gather;    // LDS kernel: row r of A is row gather[r] of a (or NULL)
+    int a_rows;               // rows of a when gathered
     int out_blocked;          // SWIGLU out in the blocked activation layout
     uint32_t* sched;          // LDS kernel: 8 per-XCD item counters, 128 B apart,
                               // zero at launch (NULL: static schedule)
@@ -93,8 +95,9 @@ size_t permute_workspace_bytes(int T, int k, int E);
 hipError_t launch_permute(const int32_t* ids, const uint16_t* x, int T, int d, int E, int k,
                           int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
                           uint16_t* x_perm, uint32_t* flags, void* ws, hipStream_t stream,
-                          bool blocked = false, uint32_t* zero = nullptr, int nzero = 0);
-// (the rank kernel also clears zero[0, nzero): the expert GEMMs' counters)
+                          uint32_t* zero = nullptr, int nzero = 0);
+// (x_perm may be NULL: dest/src only; the rank kernel also clears
+// zero[0, nzero): the expert GEMMs' counters)
 
 hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* w,
                           const float* y_shared, int T, int d, int k, int rows, int out_dtype,

@@ -17,8 +17,9 @@
 //               the unused tail of src.
 //   K3 scatter: one wave per token: dest/src for its k pairs and k copies of
 //               its row of x into x_perm (16-byte vector loads and stores;
-//               the row is read once), row-major or, inside moe_forward, in
-//               the blocked activation layout the expert GEMM reads.
+//               the row is read once).  Without x_perm (moe_forward with
+//               packed weights: the expert GEMM gathers rows through src)
+//               only dest and src are written.
 #include "moe_internal.h"
 
 namespace moe {
@@ -164,7 +165,6 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t* __restric
     for (int r = run + threadIdx.x; r < N; r += 256) src[r] = -1;
 }
 
-template <bool BLOCKED>
 __global__ __launch_bounds__(256) void perm_scatter_kernel(
     const int32_t* __restrict__ ids, const uint16_t* __restrict__ x, int T, int d, int E, int k,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ base,
@@ -184,6 +184,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
         }
         dest[i] = row;
     }
+    if (x_perm == nullptr) return;
     int rows[MOE_MAX_K];
 #pragma unroll
     for (int j = 0; j < MOE_MAX_K; ++j) rows[j] = __shfl(row, j, 64);
@@ -200,20 +201,11 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
 #pragma unroll
         for (int j = 0; j < MOE_MAX_K; ++j) {
             if (j >= k || rows[j] < 0) continue;
-            if (BLOCKED) {
+            u32x4* xd = (u32x4*)(x_perm + (size_t)rows[j] * d);
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int v = v0 + u * 64 + lane;
-                    if (v < nvec)
-                        *(u32x4*)(x_perm + blocked_index(rows[j], (size_t)v * 8, d)) = buf[u];
-                }
-            } else {
-                u32x4* xd = (u32x4*)(x_perm + (size_t)rows[j] * d);
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int v = v0 + u * 64 + lane;
-                    if (v < nvec) xd[v] = buf[u];
-                }
+            for (int u = 0; u < 8; ++u) {
+                const int v = v0 + u * 64 + lane;
+                if (v < nvec) xd[v] = buf[u];
             }
         }
     }
@@ -230,7 +222,7 @@ size_t permute_workspace_bytes(int T, int k, int E) {
 hipError_t launch_permute(const int32_t* ids, const uint16_t* x, int T, int d, int E, int k,
                           int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
                           uint16_t* x_perm, uint32_t* flags, void* ws, hipStream_t stream,
-                          bool blocked, uint32_t* zero, int nzero) {
+                          uint32_t* zero, int nzero) {
     const int N = T * k;
     PermWs w = carve(ws, N, E);
     const int nchunks = (N + kChunk - 1) / kChunk;
@@ -246,9 +238,8 @@ hipError_t launch_permute(const int32_t* ids, const uint16_t* x, int T, int d, i
     hipLaunchKernelGGL(perm_scan_kernel, dim3(E), dim3(256), 0, stream, w.hist, nchunks, E, N,
                        w.base, counts, offsets, src, w.done);
     if (T > 0) {
-        auto kern = blocked ? perm_scatter_kernel<true> : perm_scatter_kernel<false>;
-        hipLaunchKernelGGL(kern, dim3((T + 3) / 4), dim3(256), 0, stream, ids, x, T, d, E, k,
-                           w.rank, w.base, offsets, dest, src, x_perm);
+        hipLaunchKernelGGL(perm_scatter_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, ids, x, T,
+                           d, E, k, w.rank, w.base, offsets, dest, src, x_perm);
     }
     return hipGetLastError();
 }
