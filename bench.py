@@ -37,7 +37,11 @@ def stage_work(w, n_nonempty, out_bytes=2):
     st["router_gemm"] = (T * d * 2 + E * d * 2 + T * E * 4, 2.0 * T * d * E)
     route_bytes = T * E * 4 + T * k * 8 + (T * 4 + T * k * 4 if hash_mode else 0)
     st["route"] = (route_bytes, 0.0)
-    st["permute"] = (N * 4 + T * d * 2 + N * d * 2 + 2 * N * 4, 0.0)
+    # the forward's permutation writes dest/src only (the routed gate/up GEMM
+    # gathers the token rows through src)
+    st["permute"] = (N * 4 + 2 * N * 4, 0.0)
+    # routed gate/up: weights of the non-empty experts once, every routed row
+    # of x once (gathered), h written once
     st["gate_up_routed"] = (n_nonempty * 2 * F * d * 2 + N * d * 2 + N * F * 2,
                             2.0 * N * d * 2 * F)
     st["gate_up_shared"] = (2 * Fs * d * 2 + T * d * 2 + T * Fs * 2, 2.0 * T * d * 2 * Fs)
