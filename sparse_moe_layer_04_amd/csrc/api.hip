@@ -106,7 +106,7 @@ FwdWs forward_layout(const moe_cfg* c, char* base) {
     w.offsets = (int32_t*)take((size_t)(c->E + 1) * 4);
     w.dest = (int32_t*)take(N * 4);
     w.src = (int32_t*)take(N * 4);
-    w.x_perm = (uint16_t*)take(blocked_rows(N) * c->d * 2);
+    w.x_perm = (uint16_t*)take(N * c->d * 2);  // plain-weight path only
     w.h = (uint16_t*)take(blocked_rows(N) * c->F * 2);
     w.y_perm = (float*)take(N * c->d * 4);
     w.hs = (uint16_t*)take(T * (size_t)(c->F_shared > 0 ? c->F_shared : 0) * 2);

@@ -40,7 +40,7 @@ enum GemmEpilogue : int {
 };
 
 struct GemmArgs {
-    const uint16_t* a;        // [rows, K] bf16 activations
+    const uint16_t* a;        // [rows, K] bf16 activations ([a_rows, K] when gathered)
     const int32_t* offsets;   // [G+1] device group row offsets, or NULL: one group [0, rows)
     int G;
     int rows;
