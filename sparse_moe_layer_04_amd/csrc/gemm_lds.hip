@@ -21,27 +21,29 @@
 // are streamed from memory once.  (Taller or wider tiles for mid-size or
 // very small experts stage more activation bytes per weight byte or hold
 // fewer stages in flight; measured on MI355X they were slower.)
-// Per 32-wide K stage one LDS slot holds
-//   - the activation tile, 256 rows x 64 B, the 16-byte chunks of row r
-//     XOR-swizzled by sw(r) = ((r >> 1) ^ (r >> 3)) & 3, so that the 16
-//     lanes an LDS cycle serves (256 B over 64 banks: rows r, r+4, r+8,
-//     r+12 share banks) hit distinct banks in MFMA operand reads;
-//   - the weight half-stage, 16 KB in matrix-core fragment order (copied
-//     from the packed layout in 1 KB runs; operand reads are 1 KB
-//     contiguous per wave).
-// A ring of 4 slots keeps 3 stages (96 KB) in flight per CU.  The DMA
-// (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16 l) moves 1 KB
-// per instruction: weight instructions and blocked-layout activation
-// instructions each read 1 KB of contiguous memory (8 full cache lines);
-// row-major activations cost 16 half-used lines per instruction.  Each wave
-// issues 2 weight instructions and na in {0, 1, 2} activation instructions
-// per stage (only the 16-row groups that hold valid rows are copied); na is
-// fixed for a tile, so vmcnt counts stay exact.  The DMA is issued from
-// inline assembly, so the compiler does not see LDS writes it would
-// otherwise guard with a full vmcnt drain before every LDS read; explicit
-// vmcnt waits + one barrier per stage are the complete synchronisation, and
-// the kernel keeps every other value in registers (a spill reload would make
-// the compiler drain vmcnt inside the pipeline).
+// The K loop runs in stages; the LDS ring (128 KB) holds either 4 slots of
+// 32-wide stages (3 in flight, for tiles of at most 192 valid rows: few MFMAs
+// per weight byte, so the deeper lookahead hides more memory latency) or 2
+// slots of 64-wide stages (1 in flight while one computes, for fuller tiles:
+// half the barriers and waits per K).  Measured on MI355X, the split beats
+// either width alone on every workload tried.  Per stage one slot holds
+//   - the activation tile, 256 rows x KB columns, the 16-byte chunks of row
+//     r XOR-swizzled (swz), so that the 16 lanes an LDS cycle serves (256 B
+//     over 64 banks) hit distinct banks in MFMA operand reads;
+//   - the weight stage, KB / 16 substeps x 1 KB per 32-row block in
+//     matrix-core fragment order (copied from the packed layout in 1 KB runs;
+//     operand reads are 1 KB contiguous per wave).
+// The DMA (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16 l)
+// moves 1 KB per instruction: weight instructions and blocked-layout
+// activation instructions read whole cache lines; row-major activations read
+// 64 of 128 bytes per line at KB = 32, whole lines at KB = 64.  Each wave issues KB / 16 weight instructions and na
+// activation instructions per stage (only the row groups that hold valid
+// rows are copied); na is fixed for a tile, so vmcnt counts stay exact.  The
+// DMA is issued from inline assembly, so the compiler does not see LDS writes
+// it would otherwise guard with a full vmcnt drain before every LDS read;
+// explicit vmcnt waits + one barrier per stage are the complete
+// synchronisation, and the kernel keeps every other value in registers (a
+// spill reload would make the compiler drain vmcnt inside the pipeline).
 // Scheduling: see grouped_gemm_lds_kernel.
 #include "moe_internal.h"
 
@@ -52,18 +54,35 @@ constexpr int TM = 256;                      // activation rows per tile
 constexpr int MH = TM / 2;                   // max rows per wave
 constexpr int MAXNTB = MH / 32;              // activation blocks per wave
 constexpr int WBLK = 8;                      // 32-row weight blocks per tile
-constexpr int BK = 32;                       // K per pipeline stage
-constexpr int kSlotA = TM * 64;              // activation tile per stage
-constexpr int kSlotW = WBLK * 2 * 1024;      // weight half-stage: 2 substeps x 1 KB per block
-constexpr int kSlot = kSlotA + kSlotW;
-constexpr int kSlots = 4;                    // LDS ring
-constexpr int kAhead = kSlots - 1;           // stages in flight
-constexpr int kRing = kSlots * kSlot;
-constexpr int kAInstr = TM / 16;             // activation DMA instructions per stage
-constexpr int kAPerWave = kAInstr / 8;
+constexpr int kRing = 128 * 1024;            // LDS operand ring (either stage width)
 constexpr int kThreads = 512;
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int kStaticLds = 256;              // reserve for static LDS (scan_sh, next_item)
+// tiles with more valid rows than this take the 64-wide stages (MFMA-heavy),
+// the others the 32-wide ones (memory-bound: deeper lookahead)
+constexpr int kWideStageRows = 192;
+
+// Pipeline of one stage width KB (32 or 64 columns of K per stage).
+//   KB = 32: 4 slots of 32 KB (16 KB activations + 16 KB weights), 3 stages
+//            in flight; per stage 2 activation + 2 weight DMA instructions
+//            per wave; the waits count the instructions of later stages.
+//   KB = 64: 2 slots of 64 KB, 1 stage in flight while one computes; per
+//            stage 4 + 4 instructions per wave; every wait is vmcnt(0).
+template <int KB>
+struct Stage {
+    static_assert(KB == 32 || KB == 64, "stage width");
+    static constexpr int ROWB = KB * 2;                    // LDS bytes per activation row
+    static constexpr int LPR = ROWB / 16;                  // lanes per row in one DMA
+    static constexpr int RPI = 64 / LPR;                   // rows per DMA instruction
+    static constexpr int APW = TM / RPI / 8;               // activation instrs per wave (max)
+    static constexpr int Q = KB / 16;                      // MFMA substeps per stage
+    static constexpr int SLOTA = TM * ROWB;
+    static constexpr int SLOTW = WBLK * Q * 1024;
+    static constexpr int SLOT = SLOTA + SLOTW;
+    static constexpr int SLOTS = kRing / SLOT;
+    static constexpr int AHEAD = SLOTS - 1;                // stages in flight
+    static_assert(SLOTS * SLOT == kRing, "ring");
+};
 
 // activation addressing: row-major a, the blocked layout, or row-major a
 // with row r of the problem taken from row gather[r] (the dispatch
@@ -82,8 +101,14 @@ struct Panel {
 
 __device__ __forceinline__ float clamp_sym(float v, float L) { return fminf(fmaxf(v, -L), L); }
 
-// position swizzle of the four 16-byte chunks of activation row r in LDS
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// position swizzle of the 16-byte chunks of activation row r in LDS: the 16
+// lanes an LDS cycle serves (256 B over 64 banks) read 16 rows of one chunk
+// index and must hit distinct banks.  64-byte rows (KB = 32): rows r, r+4,
+// r+8, r+12 share banks; 128-byte rows (KB = 64): rows of equal parity do.
+template <int KB>
+__device__ __forceinline__ int swz(int r) {
+    return KB == 32 ? ((r >> 1) ^ (r >> 3)) & 3 : (r >> 1) & 7;
+}
 
 // 1 KB direct-to-LDS copy: lane l's 16 bytes from gaddr go to LDS byte
 // lds_byte + 16 l.
@@ -102,12 +127,18 @@ __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// wait for the oldest in-flight stage of a wave that issues na + 2
-// instructions per stage (kAhead - 1 newer stages may stay outstanding)
+// wait for the oldest in-flight stage (AHEAD - 1 later stages of na + NW
+// instructions each may stay outstanding)
+template <int KB>
 __device__ __forceinline__ void wait_stage(int na) {
-    if (na == 2) wait_vm<(kAhead - 1) * 4>();
-    else if (na == 1) wait_vm<(kAhead - 1) * 3>();
-    else wait_vm<(kAhead - 1) * 2>();
+    constexpr int A1 = Stage<KB>::AHEAD - 1, NW = Stage<KB>::Q;
+    if constexpr (A1 == 0) {
+        wait_vm<0>();
+    } else {
+        if (na == 2) wait_vm<A1 * (NW + 2)>();
+        else if (na == 1) wait_vm<A1 * (NW + 1)>();
+        else wait_vm<A1 * NW>();
+    }
 }
 
 struct LdsTile {
@@ -115,11 +146,11 @@ struct LdsTile {
     uint32_t lds0;         // LDS byte address of slot 0
     unsigned char* smem;
     int lane, wave, wm, wn, half, l32;
-    int K, N, S;
+    int K, N;
     int row0, valid;
     int mh;                // activation rows per wave half (multiple of 32)
     int na;                // activation DMA instructions of this wave per stage
-    uint32_t a_off[kAPerWave];  // lane's stage-0 source of activation instruction i (16 B units)
+    uint32_t a_off[4];     // lane's stage-0 source of activation instruction i (16 B units)
     uint32_t a_step;       // ... advance per stage (16 B units)
     int n0;                // first weight row / feature of this wave's blocks
     const uint16_t* wsrc0; // this expert's packed matrix (gate matrix for SwiGLU)
@@ -133,35 +164,37 @@ struct LdsTile {
     int item_lo;           // first item of this XCD's range
 };
 
-// DMA of pipeline stage j (32 k) into the LDS slot at byte offset `sbase`.
-//   activations: instruction n (rows [16 n, 16 n + 16) of the tile) belongs
-//     to wave n % 8 and is issued only if the group holds a valid row (the
-//     per-lane sources are set up per tile in t.a_off).
-//   weights: the 64-wide packed stage s = j / 2 holds, per 32-row block,
-//     4 substeps x 1 KB; this half-stage (h = j % 2) takes substeps 2h, 2h+1
-//     of all 8 blocks: instruction n = 2 w + i copies tile block n / 2,
-//     substep 2h + n % 2 to LDS fragment slot n.  SwiGLU tile blocks [0, 4)
-//     are gate rows, [4, 8) up rows; a block of a panel past the matrix end
-//     re-reads the last panel (its outputs are never stored).
-template <int EPI>
+// DMA of pipeline stage j (KB columns of K) into the LDS slot at byte offset
+// `sbase`.
+//   activations: instruction n (rows [RPI n, RPI n + RPI) of the tile)
+//     belongs to wave n % 8 and is issued only if the group holds a valid
+//     row (the per-lane sources are set up per tile in t.a_off).
+//   weights: the 64-wide packed stage holds, per 32-row block, 4 substeps x
+//     1 KB; the stage takes Q of them from all 8 blocks: instruction
+//     n = Q w + i copies tile block n / Q, substep n % Q (KB = 32: the half
+//     j % 2 of the packed stage j / 2) to LDS fragment slot n.  SwiGLU tile
+//     blocks [0, 4) are gate rows, [4, 8) up rows; a block of a panel past
+//     the matrix end re-reads the last panel (its outputs are never stored).
+template <int EPI, int KB>
 __device__ __forceinline__ void issue_stage(const LdsTile& t, int j, uint32_t sbase) {
     using Pn = Panel<EPI>;
+    using St = Stage<KB>;
     const uint32_t base = t.lds0 + sbase;
     const GemmArgs& args = *t.args;
 #pragma unroll
-    for (int i = 0; i < kAPerWave; ++i) {
+    for (int i = 0; i < St::APW; ++i) {
         if (i < t.na) {
-            const int r0 = 16 * (t.wave + 8 * i);
+            const int r0 = St::RPI * (t.wave + 8 * i);
             const uint32_t off = t.a_off[i] + (uint32_t)j * t.a_step;
-            dma16((const u32x4*)args.a + off, base + r0 * 64);
+            dma16((const u32x4*)args.a + off, base + r0 * St::ROWB);
         }
     }
-    const int s64 = j >> 1, h2 = j & 1;
+    const int s64 = (j * KB) >> 6, sub0 = ((j * KB) & 63) >> 4;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int n = 2 * t.wave + i;
-        const int b = n >> 1;
-        const int sub = 2 * h2 + (n & 1);
+    for (int i = 0; i < St::Q; ++i) {
+        const int n = St::Q * t.wave + i;
+        const int b = n / St::Q;
+        const int sub = sub0 + n % St::Q;
         const uint16_t* mat = t.wsrc0;
         int gb = t.blk0 + b;
         if (EPI == EPI_SWIGLU_BF16 && b >= Pn::BPM) {
@@ -171,7 +204,7 @@ __device__ __forceinline__ void issue_stage(const LdsTile& t, int j, uint32_t sb
         const int panel = min(gb / Pn::BPP, t.np - 1);
         const uint16_t* src = mat + (size_t)panel * t.pstride + (size_t)s64 * t.wstride +
                               (gb % Pn::BPP) * 2048 + sub * 512 + t.lane * 8;
-        dma16(src, base + kSlotA + n * 1024);
+        dma16(src, base + St::SLOTA + n * 1024);
     }
 }
 
@@ -182,21 +215,22 @@ struct Operands {
     bf16x8 w0, w1, a[NTB];
 };
 
-template <int EPI, int NTB>
+template <int EPI, int KB, int NTB>
 __device__ __forceinline__ void read_operands(const LdsTile& t, uint32_t sbase, int q,
                                               Operands<NTB>& o) {
+    using St = Stage<KB>;
     const unsigned char* base = t.smem + sbase;
-    // weight blocks of this wave (fragment slots 2 b + substep)
+    // weight blocks of this wave (fragment slots Q b + substep)
     const int b0 = (EPI == EPI_SWIGLU_BF16) ? t.wn : 2 * t.wn;
     const int b1 = (EPI == EPI_SWIGLU_BF16) ? Panel<EPI>::BPM + t.wn : 2 * t.wn + 1;
-    const unsigned char* wbase = base + kSlotA + t.lane * 16;
-    o.w0 = *(const bf16x8*)(wbase + (b0 * 2 + q) * 1024);
-    o.w1 = *(const bf16x8*)(wbase + (b1 * 2 + q) * 1024);
+    const unsigned char* wbase = base + St::SLOTA + t.lane * 16;
+    o.w0 = *(const bf16x8*)(wbase + (b0 * St::Q + q) * 1024);
+    o.w1 = *(const bf16x8*)(wbase + (b1 * St::Q + q) * 1024);
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
         const int r = t.wm * t.mh + tb * 32 + t.l32;
-        const int c = (2 * q + t.half) ^ swz(r);
-        o.a[tb] = *(const bf16x8*)(base + r * 64 + c * 16);
+        const int c = (2 * q + t.half) ^ swz<KB>(r);
+        o.a[tb] = *(const bf16x8*)(base + r * St::ROWB + c * 16);
     }
 }
 
@@ -259,15 +293,23 @@ __device__ __forceinline__ void epilogue(const LdsTile& t, const f32x16 (&acc)[2
     }
 }
 
-// K loop of one tile for a wave computing NTB 32-row blocks (0: DMA only).
-// Stages j+1 .. j+kAhead-1 stay in flight while stage j computes: wait for
-// stage j (this wave's own DMA), barrier (all waves' DMA of stage j landed,
-// and all waves are done reading the slot the next DMA overwrites), issue
-// stage j + kAhead into the slot stage j - 1 used, compute stage j.  Stages
-// past the end re-issue the last stage, so every iteration issues the same
-// number of instructions.
-template <int EPI, int AM, int NTB>
+// K loop of one tile for a wave computing NTB 32-row blocks (0: DMA only),
+// in stages of KB columns.  Stages j+1 .. j+AHEAD-1 stay in flight while
+// stage j computes: wait for stage j (this wave's own DMA), barrier (all
+// waves' DMA of stage j landed, and all waves are done reading the slot the
+// next DMA overwrites), issue stage j + AHEAD into the slot stage j - 1 used,
+// compute stage j.  With more than one stage in flight, stages past the end
+// re-issue the last stage, so every iteration issues the same number of
+// instructions and the vmcnt counts of wait_stage stay exact.
+// Operand reads run one substep ahead of the MFMAs: after the barrier of
+// stage j the wave reads substep 0 of stage j while it multiplies the last
+// substep of stage j - 1 (read before this barrier), and so on.  Every LDS
+// read latency hides behind MFMAs of the same wave; the reads of a slot
+// complete before the next barrier, so the DMA that reuses the slot after
+// that barrier never races them.
+template <int EPI, int AM, int KB, int NTB>
 __device__ __forceinline__ void run_tile(const LdsTile& t) {
+    using St = Stage<KB>;
     f32x16 acc[2][MAXNTB];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -275,37 +317,30 @@ __device__ __forceinline__ void run_tile(const LdsTile& t) {
         for (int tb = 0; tb < MAXNTB; ++tb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[b][tb][i] = 0.0f;
-    const int S = t.S;
+    const int S = t.K / KB;
     wait_vm<0>();  // retire the previous tile's stores before counting DMA entries
 #pragma unroll
-    for (int p = 0; p < kAhead; ++p) issue_stage<EPI>(t, min(p, S - 1), p * kSlot);
-    uint32_t s_cmp = 0, s_iss = kAhead * kSlot;
-    // Operand reads run one half-stage ahead of the MFMAs: after the barrier
-    // of stage j the wave reads substep 0 of stage j while it multiplies
-    // substep 1 of stage j - 1 (read before this barrier), then reads
-    // substep 1 of stage j while it multiplies substep 0.  Every LDS read
-    // latency hides behind MFMAs of the same wave; the reads of a slot
-    // complete before the next barrier, so the DMA that reuses the slot
-    // after that barrier never races them.
-    Operands<NTB> o0, o1;
+    for (int p = 0; p < St::AHEAD; ++p) issue_stage<EPI, KB>(t, min(p, S - 1), p * St::SLOT);
+    uint32_t s_cmp = 0, s_iss = St::AHEAD * St::SLOT;
+    Operands<NTB> o[2];
     for (int j = 0; j < S; ++j) {
-        wait_stage(t.na);
+        wait_stage<KB>(t.na);
         __syncthreads();
-        issue_stage<EPI>(t, min(j + kAhead, S - 1), s_iss);
-        s_iss = (s_iss + kSlot == kRing) ? 0 : s_iss + kSlot;
+        // (one stage in flight: every wait is vmcnt(0), nothing to re-issue)
+        if (St::AHEAD > 1 || j + 1 < S) issue_stage<EPI, KB>(t, min(j + St::AHEAD, S - 1), s_iss);
+        s_iss = (s_iss + St::SLOT == kRing) ? 0 : s_iss + St::SLOT;
         if constexpr (NTB > 0) {
-            read_operands<EPI, NTB>(t, s_cmp, 0, o0);
-            __builtin_amdgcn_sched_barrier(0);
-            if (j > 0) mfma_substep<NTB>(o1, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            read_operands<EPI, NTB>(t, s_cmp, 1, o1);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_substep<NTB>(o0, acc);
-            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < St::Q; ++q) {
+                read_operands<EPI, KB, NTB>(t, s_cmp, q, o[q & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (q > 0 || j > 0) mfma_substep<NTB>(o[(q + 1) & 1], acc);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        s_cmp = (s_cmp + kSlot == kRing) ? 0 : s_cmp + kSlot;
+        s_cmp = (s_cmp + St::SLOT == kRing) ? 0 : s_cmp + St::SLOT;
     }
-    if constexpr (NTB > 0) mfma_substep<NTB>(o1, acc);
+    if constexpr (NTB > 0) mfma_substep<NTB>(o[(St::Q - 1) & 1], acc);
     // dynamic scheduling: thread 0 claims the workgroup's next item here,
     // after the last stage wait, so no claim is in flight while the K loop
     // counts DMA entries
@@ -319,14 +354,38 @@ __device__ __forceinline__ void run_tile(const LdsTile& t) {
 }
 
 // run_tile for ntb in [0, NT] (ntb is wave-uniform)
-template <int EPI, int AM, int NT>
+template <int EPI, int AM, int KB, int NT>
 __device__ __forceinline__ void run_tile_ntb(const LdsTile& t, int ntb) {
     if constexpr (NT == 0) {
-        run_tile<EPI, AM, 0>(t);
+        run_tile<EPI, AM, KB, 0>(t);
     } else {
-        if (ntb >= NT) run_tile<EPI, AM, NT>(t);
-        else run_tile_ntb<EPI, AM, NT - 1>(t, ntb);
+        if (ntb >= NT) run_tile<EPI, AM, KB, NT>(t);
+        else run_tile_ntb<EPI, AM, KB, NT - 1>(t, ntb);
     }
+}
+
+// activation sources of a tile for stage width KB: instruction n = wave + 8 i
+// (rows [RPI n, RPI n + RPI)) is issued if it holds a valid row; lane l
+// copies 16 bytes of row r = RPI n + l / LPR: chunk c = (l % LPR) ^ swz(r) of
+// the stage's KB columns (rows past the tile read the last valid row)
+template <int AM, int KB>
+__device__ __forceinline__ void setup_a(LdsTile& t, const GemmArgs& args) {
+    using St = Stage<KB>;
+    t.na = 0;
+#pragma unroll
+    for (int i = 0; i < St::APW; ++i) {
+        t.na += (St::RPI * (t.wave + 8 * i) < t.valid) ? 1 : 0;
+        const int r = St::RPI * (t.wave + 8 * i) + t.lane / St::LPR;
+        const int c = (t.lane % St::LPR) ^ swz<KB>(r);
+        const size_t grow = (size_t)(t.row0 + min(r, t.valid - 1));
+        size_t e;
+        if (AM == A_BLK) e = blocked_index(grow, c * 8, t.K);
+        else if (AM == A_GATHER) e = (size_t)args.gather[grow] * t.K + c * 8;
+        else e = grow * t.K + c * 8;
+        t.a_off[i] = (uint32_t)(e >> 3);
+    }
+    // per stage: KB / 32 blocks of 512 elements (blocked) or KB elements
+    t.a_step = AM == A_BLK ? KB * 2 : KB / 8;
 }
 
 // Tile of item (group g, local item index): set up the per-tile fields of t
@@ -340,23 +399,6 @@ __device__ __forceinline__ void do_tile(LdsTile& t, const GemmArgs& args, int g,
     const int n_tile = local / mt, m_tile = local % mt;
     t.row0 = grp_lo + m_tile * TM;
     t.valid = min(TM, grp_hi - t.row0);
-    // activation instructions n = wave + 8 i with a valid row (16 n < valid);
-    // lane l copies 16 bytes of row r = 16 n + l / 4: chunk c = (l % 4) ^ sw(r)
-    // of the stage's 32 columns (rows past the tile read the last valid row)
-    t.na = 0;
-#pragma unroll
-    for (int i = 0; i < kAPerWave; ++i) {
-        t.na += (16 * (t.wave + 8 * i) < t.valid) ? 1 : 0;
-        const int r = 16 * (t.wave + 8 * i) + (t.lane >> 2);
-        const int c = (t.lane & 3) ^ swz(r);
-        const size_t grow = (size_t)(t.row0 + min(r, t.valid - 1));
-        size_t e;
-        if (AM == A_BLK) e = blocked_index(grow, c * 8, t.K);
-        else if (AM == A_GATHER) e = (size_t)args.gather[grow] * t.K + c * 8;
-        else e = grow * t.K + c * 8;
-        t.a_off[i] = (uint32_t)(e >> 3);
-    }
-    t.a_step = AM == A_BLK ? 512 / 8 : BK / 8;
     // this expert's packed matrices and the n-tile's first block
     t.np = (N + Pn::P - 1) / Pn::P;
     t.pstride = (size_t)Pn::P * t.K;
@@ -370,7 +412,13 @@ __device__ __forceinline__ void do_tile(LdsTile& t, const GemmArgs& args, int g,
     t.mh = min(MH, (((t.valid + 1) >> 1) + 31) & ~31);
     const int wrows = min(max(t.valid - t.wm * t.mh, 0), t.mh);
     const int ntb = t.n0 < N ? (wrows + 31) / 32 : 0;
-    run_tile_ntb<EPI, AM, MAXNTB>(t, ntb);
+    if (t.valid > kWideStageRows) {
+        setup_a<AM, 64>(t, args);
+        run_tile_ntb<EPI, AM, 64, MAXNTB>(t, ntb);
+    } else {
+        setup_a<AM, 32>(t, args);
+        run_tile_ntb<EPI, AM, 32, MAXNTB>(t, ntb);
+    }
 }
 
 // Work items: a group of n > 0 rows has ceil(N / TN) x ceil(n / 256) items
@@ -458,7 +506,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs arg
     t.l32 = lane & 31;
     t.K = K;
     t.N = N;
-    t.S = K / BK;
     t.ctr = args.sched ? args.sched + xcd * 32 : nullptr;
     t.next_item = &next_item;
     t.item_lo = item_lo;
@@ -523,7 +570,7 @@ int grouped_gemm_lds_max_groups() {
 }
 
 hipError_t launch_grouped_gemm_lds(int epilogue, const GemmArgs& g, hipStream_t stream) {
-    if (g.K % BK != 0 || g.G < 1) return hipErrorInvalidValue;
+    if (g.K % 64 != 0 || g.G < 1) return hipErrorInvalidValue;
     // activation sources are 32-bit offsets in 16-byte units (a gathered a
     // has at most g.a_rows rows)
     const size_t a_rows = g.gather ? (size_t)g.a_rows : (size_t)g.rows;
