@@ -274,11 +274,9 @@ FWD_CASES = [
 ]
 
 
-@pytest.mark.parametrize("w", FWD_CASES, ids=lambda w: w.name)
-@pytest.mark.parametrize("out_dtype", [ops.OUT_F32, ops.OUT_BF16])
-@pytest.mark.parametrize("packed", [False, True], ids=["plain", "packed"])
-def test_forward(w, out_dtype, packed):
-    inp = wl.make_inputs(w, DEV)
+def _check_forward(w, inp, out_dtype, packed):
+    """One moe_forward call against the oracle fed the GPU's logits: routes
+    and weights bit-exact, y within the tolerance.  Returns the routes."""
     layer = ops.MoeLayer.from_workload(w, inp, out_dtype=out_dtype, packed=packed)
     logits = torch.empty((w.T, w.E), dtype=torch.float32, device=DEV)
     ids = torch.empty((w.T, w.k), dtype=torch.int32, device=DEV)
@@ -304,3 +302,40 @@ def test_forward(w, out_dtype, packed):
         rms = np.sqrt(np.mean(yr ** 2))
         err = np.abs(bf16_f64(bits(y)) - yr)
         assert np.all(err <= 2.0 ** -8 * np.abs(yr) + 1e-2 * rms)
+    return host(ids)
+
+
+@pytest.mark.parametrize("w", FWD_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("out_dtype", [ops.OUT_F32, ops.OUT_BF16])
+@pytest.mark.parametrize("packed", [False, True], ids=["plain", "packed"])
+def test_forward(w, out_dtype, packed):
+    _check_forward(w, wl.make_inputs(w, DEV), out_dtype, packed)
+
+
+# Expert row counts at every tile-shape boundary of the packed expert GEMM:
+# empty, single rows, 16-row DMA groups, one tile of 128, 192 and 256 rows
+# and one row past each, two- and three-tile experts.
+EXACT_COUNTS = [0, 1, 16, 17, 127, 128, 129, 191, 192, 193, 255, 256, 257, 384, 385, 512, 513,
+                700]
+
+
+def _hash_routes(counts, k):
+    """input_ids and a tid2eid table that route exactly counts[e] (token, slot)
+    pairs to expert e: the sorted list of expert slots, token t taking slots
+    t, t + T, ..., t + (k-1) T (distinct experts while no count exceeds T)."""
+    slots = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    T = len(slots) // k
+    assert len(slots) == T * k and max(counts) <= T
+    return np.arange(T, dtype=np.int32), np.ascontiguousarray(slots.reshape(k, T).T)
+
+
+@pytest.mark.parametrize("d,F,k", [(128, 64, 2), (256, 192, 4)])
+def test_forward_exact_group_sizes(d, F, k):
+    input_ids, table = _hash_routes(EXACT_COUNTS, k)
+    T, E = len(input_ids), len(EXACT_COUNTS)
+    w = wl.small(T=T, d=d, E=E, k=k, F=F, seed=20 + k, scale=2.5, mode=wl.MODE_HASH, V=T)
+    inp = wl.make_inputs(w, DEV)
+    inp["input_ids"] = torch.from_numpy(input_ids).to(DEV)
+    inp["tid2eid"] = torch.from_numpy(table).to(DEV)
+    ids = _check_forward(w, inp, ops.OUT_F32, packed=True)
+    assert np.array_equal(np.bincount(ids.ravel(), minlength=E), EXACT_COUNTS)
