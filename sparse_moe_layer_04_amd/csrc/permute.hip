@@ -25,7 +25,9 @@
 namespace moe {
 namespace {
 
-constexpr int kChunkSteps = 16;              // 64-entry steps per chunk
+// short chunks: the rank kernel is a serial ballot chain per wave, so it
+// needs many waves (49,152 entries: 384 chunks) more than long walks
+constexpr int kChunkSteps = 2;               // 64-entry steps per chunk
 constexpr int kChunk = 64 * kChunkSteps;     // entries per chunk (one wave)
 
 struct PermWs {
@@ -85,14 +87,14 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restric
         }
         const int r = __popcll(m & lt_mask);
         const int tot = __popcll(m);
+        // cnt is this wave's own: its LDS reads and writes execute in program
+        // order, so no barrier is needed between the steps
         int base = 0;
         if (valid) base = cnt[id];
-        __syncthreads();
         if (valid) {
             rank[i] = base + r;
             if (r == 0) cnt[id] = base + tot;
         }
-        __syncthreads();
     }
     if (__any(bad) && lane == 0 && flags) atomicOr(flags, MOE_FLAG_BAD_EXPERT_ID);
     if (c < nchunks)
