@@ -230,6 +230,49 @@ int moe_expert_ffn(const uint16_t* a, const int32_t* offsets, int G, int rows, i
     return hip_status(launch_grouped_gemm(EPI_F32, g2, s));
 }
 
+int moe_expert_ffn_packed(const uint16_t* a, const int32_t* offsets, int G, int rows, int d,
+                          int F, const uint16_t* w_gate, const uint16_t* w_up,
+                          const uint16_t* w_down, float clamp_limit, int clamp_mode, uint16_t* h,
+                          float* y, void* stream) {
+    if (G < 1) return MOE_ERR_SHAPE;
+    if (G > MOE_MAX_GROUPS || G > grouped_gemm_lds_max_groups()) return MOE_ERR_UNSUPPORTED;
+    int st = ffn_checks(rows, d, F, clamp_limit, clamp_mode);
+    if (st != MOE_OK) return st;
+    if (rows == 0) return MOE_OK;
+    if (!a || !offsets || !w_gate || !w_up || !w_down || !h || !y) return MOE_ERR_NULL;
+    if (!aligned16(a) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+        !aligned16(h) || !aligned16(y))
+        return MOE_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    // no workspace: both GEMMs take the static schedule (sched = NULL)
+    GemmArgs g1{};
+    g1.a = a;
+    g1.offsets = offsets;
+    g1.G = G;
+    g1.rows = rows;
+    g1.K = d;
+    g1.N = F;
+    g1.w1 = w_gate;
+    g1.w2 = w_up;
+    g1.packed = 1;
+    g1.clamp_limit = clamp_limit;
+    g1.clamp_mode = clamp_mode;
+    g1.out = h;
+    hipError_t e = launch_grouped_gemm_lds(EPI_SWIGLU_BF16, g1, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    GemmArgs g2{};
+    g2.a = h;
+    g2.offsets = offsets;
+    g2.G = G;
+    g2.rows = rows;
+    g2.K = F;
+    g2.N = d;
+    g2.w1 = w_down;
+    g2.packed = 1;
+    g2.out = y;
+    return hip_status(launch_grouped_gemm_lds(EPI_F32, g2, s));
+}
+
 size_t moe_packed_weight_bytes(int G, int N, int K, int panel_rows) {
     if (G < 1 || N < 1 || K < 64 || K % 64) return 0;
     if (panel_rows != 128 && panel_rows != 256) return 0;

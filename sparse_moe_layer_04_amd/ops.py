@@ -78,6 +78,7 @@ def lib():
     L.moe_permute_workspace_size.restype = S
     L.moe_permute.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, S, P]
     L.moe_expert_ffn.argtypes = [P, P, I, I, I, I, P, P, P, F, I, P, P, P]
+    L.moe_expert_ffn_packed.argtypes = L.moe_expert_ffn.argtypes
     L.moe_combine.argtypes = [P, P, P, P, I, I, I, I, I, P, P]
     L.moe_packed_weight_bytes.argtypes = [I, I, I, I]
     L.moe_packed_weight_bytes.restype = S
@@ -88,6 +89,7 @@ def lib():
                               P, P, P, P, P, S, P]
     L.moe_forward_timed.argtypes = L.moe_forward.argtypes + [P]
     for name in ("moe_gate_logits", "moe_route", "moe_permute", "moe_expert_ffn",
+                 "moe_expert_ffn_packed",
                  "moe_combine", "moe_forward", "moe_forward_timed", "moe_pack_weights"):
         getattr(L, name).restype = I
     _lib = L
@@ -206,6 +208,31 @@ def expert_ffn(a, offsets, w_gate, w_up, w_down, clamp_limit=10.0, clamp_mode=CL
     _check(lib().moe_expert_ffn(_ptr(a), _ptr(offsets), G, rows, d, F, _ptr(w_gate), _ptr(w_up),
                                 _ptr(w_down), float(clamp_limit), int(clamp_mode), _ptr(h),
                                 _ptr(y), _stream()), "moe_expert_ffn")
+    return h, y
+
+
+def expert_ffn_packed(a, offsets, w_gate_p, w_up_p, w_down_p, G, F, clamp_limit=10.0,
+                      clamp_mode=CLAMP_SYMMETRIC, h=None, y=None):
+    """Grouped FFN on packed weights (pack_weights with PANEL_ROWS): returns
+    (h[rows,F] bf16, y[rows,d] fp32)."""
+    _need(a, torch.bfloat16, "a", 2)
+    _need(offsets, torch.int32, "offsets", 1)
+    rows, d = a.shape
+    for name, t, n, k, p in (("w_gate", w_gate_p, F, d, 128), ("w_up", w_up_p, F, d, 128),
+                             ("w_down", w_down_p, d, F, 256)):
+        _need(t, torch.bfloat16, name, 1)
+        if t.numel() * 2 != lib().moe_packed_weight_bytes(G, n, k, p):
+            raise MoeError(f"{name} is not a packed [{G},{n},{k}] matrix (panel_rows {p})")
+    if offsets.numel() != G + 1:
+        raise MoeError("offsets must have G + 1 entries")
+    if h is None:
+        h = torch.empty((rows, F), dtype=torch.bfloat16, device=a.device)
+    if y is None:
+        y = torch.empty((rows, d), dtype=torch.float32, device=a.device)
+    _check(lib().moe_expert_ffn_packed(_ptr(a), _ptr(offsets), G, rows, d, F, _ptr(w_gate_p),
+                                       _ptr(w_up_p), _ptr(w_down_p), float(clamp_limit),
+                                       int(clamp_mode), _ptr(h), _ptr(y), _stream()),
+           "moe_expert_ffn_packed")
     return h, y
 
 

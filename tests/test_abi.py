@@ -81,10 +81,11 @@ def test_permute_validation(L):
     assert L.moe_permute(*args(ids=None)) == ERR_NULL
 
 
-def test_expert_ffn_validation(L):
+@pytest.mark.parametrize("entry", ["moe_expert_ffn", "moe_expert_ffn_packed"])
+def test_expert_ffn_validation(L, entry):
     def ffn(G=2, rows=10, d=128, F=64, L_=10.0, mode=0, a=FAKE, h=FAKE, off=FAKE):
-        return L.moe_expert_ffn(a, off, G, rows, d, F, FAKE, FAKE, FAKE, ctypes.c_float(L_), mode,
-                                h, FAKE, None)
+        return getattr(L, entry)(a, off, G, rows, d, F, FAKE, FAKE, FAKE, ctypes.c_float(L_),
+                                 mode, h, FAKE, None)
     assert ffn(G=0) == ERR_SHAPE
     assert ffn(G=5000) == ERR_UNSUPPORTED
     assert ffn(d=96) == ERR_UNSUPPORTED

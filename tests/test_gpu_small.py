@@ -339,3 +339,24 @@ def test_forward_exact_group_sizes(d, F, k):
     inp["tid2eid"] = torch.from_numpy(table).to(DEV)
     ids = _check_forward(w, inp, ops.OUT_F32, packed=True)
     assert np.array_equal(np.bincount(ids.ravel(), minlength=E), EXACT_COUNTS)
+
+
+# ------------------------------------------------------ packed expert FFN ----
+@pytest.mark.parametrize("G,d,F,counts", [
+    (1, 64, 64, [1]), (3, 128, 192, [0, 130, 5]), (5, 256, 128, [257, 0, 1, 128, 300]),
+    (len(EXACT_COUNTS), 128, 64, EXACT_COUNTS), (2, 512, 256, [1000, 23]),
+    (4, 64, 1088, [40, 40, 40, 40])])
+def test_expert_ffn_packed(G, d, F, counts):
+    a, wgt, wup, wdn, offs = _ffn_case(G * 37 + d + F, G, d, F, counts)
+    offs_d = torch.from_numpy(offs).to(DEV)
+    h, y = ops.expert_ffn_packed(a, offs_d, ops.pack_weights(wgt, 128),
+                                 ops.pack_weights(wup, 128), ops.pack_weights(wdn, 256), G, F,
+                                 10.0)
+    hr, yr = oracle.expert_ffn(bits(a), offs, bits(wgt), bits(wup), bits(wdn), 10.0)
+    check_h(bits(h), hr, ffn_h_bound(bits(a), offs, bits(wgt), bits(wup), 10.0, 0))
+    check_rms(host(y), yr)
+    # the plain-weight kernel runs the same MFMA chain per output element
+    # (16-wide K substeps in ascending order, the same epilogue): same bits
+    h2, y2 = ops.expert_ffn(a, offs_d, wgt, wup, wdn, 10.0)
+    assert np.array_equal(bits(h), bits(h2))
+    assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
