@@ -123,7 +123,8 @@ int moe_route(const float* logits, const float* score_bias, const uint8_t* modal
  * Pairs with an id outside [0,E) are dropped and set MOE_FLAG_BAD_EXPERT_ID.
  *   topk_ids [T,k] int32, x [T,d] bf16 (d multiple of 8); counts [E],
  *   offsets [E+1], dest [T*k], src [T*k] int32, x_perm [T*k,d] bf16.
- *   ws: moe_permute_workspace_size(T, k, E) bytes.
+ *   ws: moe_permute_workspace_size(T, k, E) bytes, 256-byte aligned (may be
+ *   NULL when that size is 0, i.e. T = 0).
  */
 size_t moe_permute_workspace_size(int T, int k, int E);
 int moe_permute(const int32_t* topk_ids, const uint16_t* x, int T, int d, int E, int k,

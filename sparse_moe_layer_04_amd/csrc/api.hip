@@ -182,7 +182,8 @@ int moe_permute(const int32_t* topk_ids, const uint16_t* x, int T, int d, int E,
     if (T < 0 || d < 8 || E < 1 || k < 1) return MOE_ERR_SHAPE;
     if (E > MOE_MAX_E || k > MOE_MAX_K || d % 8) return MOE_ERR_UNSUPPORTED;
     if ((long long)T * k >= (1ll << 31)) return MOE_ERR_SHAPE;
-    if (!counts || !offsets || !ws) return MOE_ERR_NULL;
+    if (!counts || !offsets) return MOE_ERR_NULL;
+    if (!ws && permute_workspace_bytes(T, k, E) > 0) return MOE_ERR_NULL;
     if (T > 0 && (!topk_ids || !x || !dest || !src || !x_perm)) return MOE_ERR_NULL;
     if (((uintptr_t)ws & 255u) || ws_bytes < permute_workspace_bytes(T, k, E))
         return MOE_ERR_WORKSPACE;

@@ -9,9 +9,10 @@
 // Each lane owns experts e = lane + 64 i.  The ranking key of an expert packs
 // the order-preserving image of its biased score (high 32 bits) with ~e (low
 // 32 bits), so one unsigned 64-bit max picks (score desc, index asc).  Top-k
-// is k rounds of a wave-wide max (xor-shuffle butterfly) over the lanes'
-// current best keys.  This translation unit is built with FP contraction off:
-// the score function is a fixed sequence of IEEE binary32 operations.
+// is k rounds of a wave-wide max (DPP row operations, then a lane read) over
+// the lanes' current best keys.  This translation unit is built with FP
+// contraction off: the score function is a fixed sequence of IEEE binary32
+// operations.
 #include "moe_internal.h"
 
 namespace moe {
@@ -56,15 +57,42 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// One DPP move of a 64-bit value (both halves through the same lane
+// pattern); lanes the pattern leaves unwritten keep v.
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const uint32_t l2 = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROWMASK, 0xf, false);
+    const uint32_t h2 = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROWMASK, 0xf, false);
+    return ((uint64_t)h2 << 32) | l2;
+}
+
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+    const uint64_t o = dpp_u64<CTRL, ROWMASK>(v);
+    return o > v ? o : v;
+}
+
+// Wave-wide maximum of a 64-bit key, returned in every lane (wave-uniform).
+// DPP row operations only (no LDS crossbar): quad xor 1 and xor 2, half-row
+// and row mirrors leave every lane with its 16-lane row maximum; row
+// broadcasts of lanes 15 and 31 carry the row maxima up, so lane 63 ends
+// with the wave maximum, which a lane read makes uniform.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
+    v = dpp_max_step<0xB1>(v);         // quad_perm [1,0,3,2]
+    v = dpp_max_step<0x4E>(v);         // quad_perm [2,3,0,1]
+    v = dpp_max_step<0x141>(v);        // row_half_mirror
+    v = dpp_max_step<0x140>(v);        // row_mirror
+    v = dpp_max_step<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+    v = dpp_max_step<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// value of lane `src` (wave-uniform) in every lane
+__device__ __forceinline__ float lane_read(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
 }
 
 template <int NPL>
@@ -111,7 +139,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
         }
         uint64_t win = wave_max_u64(best);
         int e = (int)(~(uint32_t)win);
-        float s = __shfl(best_s, e & 63, 64);
+        const float s = lane_read(best_s, e & 63);
         // owner retires the winner
         if ((e & 63) == lane) {
 #pragma unroll
@@ -124,8 +152,8 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
         }
     }
     // left-to-right fp32 sum of the k gathered (unbiased) scores
-    float sum = __shfl(g_mine, 0, 64);
-    for (int j = 1; j < k; ++j) sum = sum + __shfl(g_mine, j, 64);
+    float sum = lane_read(g_mine, 0);
+    for (int j = 1; j < k; ++j) sum = sum + lane_read(g_mine, j);
     if (lane < k) {
         float q = g_mine / sum;
         ids_out[(size_t)t * k + lane] = id_mine;
@@ -160,8 +188,8 @@ __global__ __launch_bounds__(256) void route_hash_kernel(
     }
     float g = 0.0f;
     if (lane < k) g = score_fn(logits[(size_t)t * E + id]);
-    float sum = __shfl(g, 0, 64);
-    for (int j = 1; j < k; ++j) sum = sum + __shfl(g, j, 64);
+    float sum = lane_read(g, 0);
+    for (int j = 1; j < k; ++j) sum = sum + lane_read(g, j);
     if (lane < k) {
         float q = g / sum;
         ids_out[(size_t)t * k + lane] = id;
