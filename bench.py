@@ -51,10 +51,24 @@ def stage_work(w, n_nonempty, out_bytes=2):
     return st
 
 
-def kernel_source_digest():
+# source files that define each stage's kernels: a recorded counter value
+# stays valid only while these are unchanged
+STAGE_SOURCES = {
+    "router_gemm": ("gemm.hip", "moe_internal.h"),
+    "route": ("route.hip", "moe_internal.h"),
+    "permute": ("permute.hip", "moe_internal.h"),
+    "gate_up_routed": ("gemm_lds.hip", "moe_internal.h"),
+    "gate_up_shared": ("gemm_lds.hip", "moe_internal.h"),
+    "down_routed": ("gemm_lds.hip", "moe_internal.h"),
+    "down_shared": ("gemm_lds.hip", "moe_internal.h"),
+    "combine": ("combine.hip", "moe_internal.h"),
+}
+
+
+def kernel_source_digest(stage):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_moe_layer_04_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in STAGE_SOURCES[stage]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -62,17 +76,16 @@ def kernel_source_digest():
 
 
 def load_traffic(stage, workload_name):
-    """Counter-derived HBM traffic of a stage's kernel, if recorded for the
-    current kernel sources (profiles/traffic.json), else None."""
+    """Counter-derived HBM traffic of a stage's kernels per launch, if it was
+    recorded (profiles/traffic.json) for the current sources of those
+    kernels, else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_digest") != kernel_source_digest():
-        return None
     ent = rec.get("kernels", {}).get(f"{workload_name}:{stage}")
-    if not ent:
+    if not ent or ent.get("source_digest") != kernel_source_digest(stage):
         return None
     return ent.get("bytes_per_launch")
 

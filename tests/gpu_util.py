@@ -106,6 +106,27 @@ def near_ties(logits, bias_rows, k, gap=1e-6):
     return int((part[:, 0] - part[:, 1] < gap).sum())
 
 
+def route_flips(xb, wg, off, lg_gpu, bias, modality, ids_gpu, k):
+    """TopK route flips between the oracle's fp64-accumulated logits and the
+    GPU's fp32 logits: [(token, gap, bound)] for every token whose expert set
+    differs.  gap = k-th minus (k+1)-th biased score under the GPU logits;
+    bound = 0.5 x max |logit difference| of the row + 1e-6 (sigmoid slope is
+    at most 1/4, and the two scores of the swapped pair can both move)."""
+    lg_ref = oracle.gate_logits(xb, wg, off)
+    ids_ref, _, _ = oracle.route(lg_ref, k, 1.0, bias=bias, modality=modality)
+    rows = 0.0
+    if bias is not None:
+        b = np.asarray(bias, np.float64).reshape(-1, lg_gpu.shape[1])
+        rows = b[modality.astype(np.int64)] if (modality is not None and b.shape[0] > 1) else b[:1]
+    r_gpu = oracle.score(lg_gpu).astype(np.float64) + rows
+    diff = np.abs(lg_ref.astype(np.float64) - lg_gpu.astype(np.float64)).max(axis=1)
+    out = []
+    for t in np.nonzero(np.any(np.sort(ids_ref, axis=1) != np.sort(ids_gpu, axis=1), axis=1))[0]:
+        part = -np.sort(-r_gpu[t])[k - 1:k + 1]
+        out.append((int(t), float(part[0] - part[1]), float(0.5 * diff[t] + 1e-6)))
+    return out
+
+
 def free_cuda():
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

@@ -15,13 +15,20 @@ weights, one moe_forward call):
     of that bound.
 Near-ties (k-th vs (k+1)-th biased score gap below 1e-6) are counted and
 printed (they are bit-exact here because both sides use the same logits).
+Route flips are counted and printed too: the tokens whose expert set under
+the oracle's own fp64-accumulated logits differs from the set under the
+GPU's fp32-accumulated logits.  A flip may only happen at a near-tie: the
+k-th vs (k+1)-th biased-score gap of a flipped token must be within what the
+logit difference can move two scores (sigmoid slope <= 1/4, so at most
+0.5 x max |logit difference| of the row, plus a few score ulps).
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_util import bits, host, bf16_f64, check_logits, check_rms, near_ties, free_cuda
+from gpu_util import (bits, host, bf16_f64, check_logits, check_rms, near_ties, route_flips,
+                      free_cuda)
 from sparse_moe_layer_04_amd import ops, workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -61,6 +68,12 @@ def test_full_size(cfg):
         rows = bias[mod.astype(np.int64)] if (bias is not None and mod is not None and
                                              bias.shape[0] > 1) else bias
         print(f"[{w.name}] near-tie tokens (gap < 1e-6): {near_ties(lg, rows, w.k)}", flush=True)
+        flips = route_flips(bits(inp["x"]), bits(inp["w_g"]), _opt(inp, "logit_offset"), lg,
+                            bias, mod, rid, w.k)
+        print(f"[{w.name}] route flips vs fp64 logits: {len(flips)} tokens"
+              + "".join(f"; t={t} gap={g:.2e} (bound {b:.2e})" for t, g, b in flips[:8]),
+              flush=True)
+        assert all(g <= b for _, g, b in flips)
 
     # permutation: bit-exact, gathered rows byte-equal
     perm = ops.permute(ids, inp["x"], w.E)
