@@ -9,6 +9,8 @@ The arithmetic lives in ``moe_oracle.c`` (plain C, fp64, built by
 Parity unpinned: the clamp form (symmetric vs gate-above-only), the shared
 expert's form and the init-std reading are readings of what the pages leave
 open; they are configurable, and every other step is pinned by the tests.
+The fp8 weight encoding (E4M3 with one power-of-two scale per output row) is
+likewise a reading: the pages name FP8 weights but no format.
 """
 from .oracle import (  # noqa: F401
     MODE_TOPK,
@@ -28,4 +30,8 @@ from .oracle import (  # noqa: F401
     combine,
     tokens_forward,
     forward,
+    e4m3_decode,
+    e4m3_encode,
+    quant_fp8_rows,
+    dequant_fp8_rows,
 )

@@ -479,3 +479,100 @@ void orc_tokens_forward(const uint16_t* x, const int64_t* tokens, int n, int d, 
         free(ye);
     }
 }
+
+/* ------------------------------------------------------ fp8 expert weights -- */
+/*
+ * 8-bit expert weights.  The pages name FP8 (MXFP8 / MXFP4) weights as the
+ * low-precision direction ("Twinkle x Ascend ... DeepSeek-V4 training",
+ * functional-expansion section; the V4-Flash checkpoints ship in FP4/FP8,
+ * quick-start section) but fix no encoding or scale granularity.  Reading
+ * used here: OCP 8-bit floating point E4M3 ("E4M3FN": 1 sign bit, 4
+ * exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities,
+ * S.1111.111 is NaN, largest finite 448), one power-of-two scale 2^e per
+ * output row of each weight matrix:
+ *   e    = the smallest integer with max_k |w[k]| <= 448 * 2^e
+ *          (e = 0 for an all-zero row), clamped to [-110, 110];
+ *   q[k] = E4M3 of w[k] / 2^e, rounded to nearest, ties to even, values
+ *          beyond 448 saturated to +-448;
+ *   dequantised weight = E4M3 value of q[k] * 2^e.
+ * The dequantised weight has at most 4 significant bits and a binary
+ * exponent inside bfloat16's range, so it is exactly a bf16 value: the FFN
+ * of the fp8 mode is the bf16 FFN on the dequantised weights.
+ */
+
+/* value of an E4M3 code (NaN for S.1111.111) */
+double orc_e4m3_decode(uint8_t c)
+{
+    const double s = (c & 0x80) ? -1.0 : 1.0;
+    const int E = (c >> 3) & 15, M = c & 7;
+    if ((c & 0x7f) == 0x7f)
+        return NAN;
+    if (E == 0)
+        return s * ldexp((double)M, -9);          /* subnormal: M/8 * 2^-6 */
+    return s * ldexp(1.0 + M / 8.0, E - 7);
+}
+
+/* E4M3 code of v: round to nearest, ties to even; |v| > 448 saturates */
+uint8_t orc_e4m3_encode(double v)
+{
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs(v);
+    if (a >= 448.0)
+        return sign | 0x7e;
+    if (a < ldexp(1.0, -6)) {                     /* subnormal range, spacing 2^-9 */
+        const double m = nearbyint(ldexp(a, 9)); /* 0 .. 8 (8 = smallest normal) */
+        return sign | (uint8_t)m;                 /* m = 8 encodes as E = 1, M = 0 */
+    }
+    int x;
+    frexp(a, &x);                                 /* a = f * 2^x, f in [0.5, 1) */
+    int E = x - 1;                                /* 2^E <= a < 2^(E+1), E >= -6 */
+    double m = nearbyint((ldexp(a, -E) - 1.0) * 8.0);   /* 0 .. 8 */
+    if (m == 8.0) {
+        m = 0.0;
+        E += 1;
+    }
+    if (E > 8 || (E == 8 && m > 6.0))             /* above 448 after rounding */
+        return sign | 0x7e;
+    return sign | (uint8_t)(((E + 7) << 3) | (int)m);
+}
+
+/* per-row quantisation of bf16 weights [R, K] -> codes [R, K], exponents [R] */
+void orc_quant_fp8_rows(const uint16_t* w, int64_t R, int K, uint8_t* q, int32_t* e)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        const uint16_t* row = w + r * K;
+        double amax = 0.0;
+        for (int k = 0; k < K; ++k) {
+            const double a = fabs(bf16_value(row[k]));
+            if (a > amax)
+                amax = a;
+        }
+        int ex = 0;
+        if (amax > 0.0) {
+            int x;
+            frexp(amax, &x);                      /* 2^(x-1) <= amax < 2^x */
+            ex = x - 9;                           /* 448 * 2^ex >= 2^(x-1) * 1.75 ... */
+            while (amax > 448.0 * ldexp(1.0, ex))
+                ++ex;
+            while (amax <= 448.0 * ldexp(1.0, ex - 1))
+                --ex;
+            if (ex < -110)
+                ex = -110;
+            if (ex > 110)
+                ex = 110;
+        }
+        e[r] = ex;
+        for (int k = 0; k < K; ++k)
+            q[r * K + k] = orc_e4m3_encode(ldexp(bf16_value(row[k]), -ex));
+    }
+}
+
+/* dequantised weights as bf16 bit patterns (exact; see above) */
+void orc_dequant_fp8_rows(const uint8_t* q, const int32_t* e, int64_t R, int K, uint16_t* w)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r)
+        for (int k = 0; k < K; ++k)
+            w[r * K + k] = orc_f64_to_bf16(ldexp(orc_e4m3_decode(q[r * K + k]), e[r]));
+}

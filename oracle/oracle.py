@@ -57,6 +57,14 @@ def load():
     lib.orc_expert_ffn.restype = None
     lib.orc_expert_ffn_rows.argtypes = [P, P, P, I, I, I, P, P, P, D, I, P, P]
     lib.orc_expert_ffn_rows.restype = None
+    lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3_decode.restype = D
+    lib.orc_e4m3_encode.argtypes = [D]
+    lib.orc_e4m3_encode.restype = ctypes.c_uint8
+    lib.orc_quant_fp8_rows.argtypes = [P, I64, I, P, P]
+    lib.orc_quant_fp8_rows.restype = None
+    lib.orc_dequant_fp8_rows.argtypes = [P, P, I64, I, P]
+    lib.orc_dequant_fp8_rows.restype = None
     lib.orc_combine.argtypes = [P, P, P, P, I, I, I, P]
     lib.orc_combine.restype = None
     lib.orc_tokens_forward.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, P, I, D, I, P]
@@ -238,3 +246,34 @@ def forward(x, logits, k, scale, w_gate, w_up, w_down, s_gate=None, s_up=None, s
     y = combine(y_perm, dest, w, ysh)
     return dict(ids=ids, w=w, counts=counts, offsets=offsets, dest=dest, src=src,
                 x_perm=x_perm, h=h, y_perm=y_perm, ysh=ysh, y=y, flags=f1 | f2)
+
+
+def e4m3_decode(code):
+    """Value of an E4M3 code (float; NaN for S.1111.111)."""
+    return float(load().orc_e4m3_decode(int(code)))
+
+
+def e4m3_encode(v):
+    """E4M3 code of v (round to nearest even, saturating)."""
+    return int(load().orc_e4m3_encode(float(v)))
+
+
+def quant_fp8_rows(w):
+    """bf16 bits [..., K] -> (codes uint8 [..., K], row exponents int32 [...])."""
+    w = _c(w, np.uint16)
+    K = w.shape[-1]
+    R = w.size // K
+    q = np.empty(w.shape, np.uint8)
+    e = np.empty(w.shape[:-1], np.int32)
+    load().orc_quant_fp8_rows(_p(w), R, K, _p(q), _p(e))
+    return q, e
+
+
+def dequant_fp8_rows(q, e):
+    """(codes [..., K], row exponents [...]) -> dequantised weights as bf16 bits."""
+    q = _c(q, np.uint8)
+    e = _c(e, np.int32)
+    K = q.shape[-1]
+    w = np.empty(q.shape, np.uint16)
+    load().orc_dequant_fp8_rows(_p(q), _p(e), q.size // K, K, _p(w))
+    return w
