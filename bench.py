@@ -28,8 +28,9 @@ PEAK_BF16 = 2.5e15         # FLOP/s, MI355X dense bf16 MFMA
 RIDGE = PEAK_BF16 / PEAK_HBM
 
 
-def stage_work(w, n_nonempty, out_bytes=2):
-    """Algorithmic (minimum) HBM bytes and FLOPs per stage."""
+def stage_work(w, n_nonempty, out_bytes=2, wbytes=2):
+    """Algorithmic (minimum) HBM bytes and FLOPs per stage (wbytes: bytes per
+    routed expert weight; fp8 weights also read one fp32 scale per row)."""
     T, d, E, k, F, Fs = w.T, w.d, w.E, w.k, w.F, w.Fs
     N = T * k
     hash_mode = w.mode == 1
@@ -42,10 +43,11 @@ def stage_work(w, n_nonempty, out_bytes=2):
     st["permute"] = (N * 4 + 2 * N * 4, 0.0)
     # routed gate/up: weights of the non-empty experts once, every routed row
     # of x once (gathered), h written once
-    st["gate_up_routed"] = (n_nonempty * 2 * F * d * 2 + N * d * 2 + N * F * 2,
-                            2.0 * N * d * 2 * F)
+    st["gate_up_routed"] = (n_nonempty * 2 * F * (d * wbytes + (4 if wbytes == 1 else 0)) +
+                            N * d * 2 + N * F * 2, 2.0 * N * d * 2 * F)
     st["gate_up_shared"] = (2 * Fs * d * 2 + T * d * 2 + T * Fs * 2, 2.0 * T * d * 2 * Fs)
-    st["down_routed"] = (n_nonempty * d * F * 2 + N * F * 2 + N * d * 4, 2.0 * N * F * d)
+    st["down_routed"] = (n_nonempty * d * (F * wbytes + (4 if wbytes == 1 else 0)) +
+                         N * F * 2 + N * d * 4, 2.0 * N * F * d)
     st["down_shared"] = (d * Fs * 2 + T * Fs * 2 + T * d * 4, 2.0 * T * Fs * d)
     st["combine"] = (N * d * 4 + (T * d * 4 if Fs else 0) + N * 8 + T * d * out_bytes, 0.0)
     return st
@@ -141,6 +143,9 @@ def main():
     ap.add_argument("--layout", choices=["packed", "plain"], default="packed",
                     help="weight layout: packed once at load time (moe_pack_weights) or "
                          "the plain [out, in] matrices")
+    ap.add_argument("--weights", choices=["bf16", "fp8"], default="bf16",
+                    help="routed expert weights: bf16, or E4M3 codes with one power-of-two "
+                         "scale per row (moe_pack_weights_fp8; packed layout only)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle CPU work for the baseline (0: skip)")
     args = ap.parse_args()
@@ -158,8 +163,11 @@ def main():
     print(f"# generating workload {w.name}", file=sys.stderr, flush=True)
     inp = wl.make_inputs(w, dev)
     out_dtype = ops.OUT_F32 if args.out_dtype == "f32" else ops.OUT_BF16
+    if args.weights == "fp8" and args.layout != "packed":
+        ap.error("--weights fp8 needs --layout packed")
     layer = ops.MoeLayer.from_workload(w, inp, out_dtype=out_dtype,
-                                       packed=args.layout == "packed")
+                                       packed="fp8" if args.weights == "fp8" else
+                                       args.layout == "packed")
     y = torch.empty((w.T, w.d), dtype=torch.float32 if out_dtype == ops.OUT_F32 else torch.bfloat16,
                     device=dev)
     ids = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
@@ -193,7 +201,8 @@ def main():
 
     counts = torch.bincount(ids.flatten().long(), minlength=w.E).cpu().numpy()
     n_nonempty = int((counts > 0).sum())
-    work = stage_work(w, n_nonempty, 4 if out_dtype == ops.OUT_F32 else 2)
+    work = stage_work(w, n_nonempty, 4 if out_dtype == ops.OUT_F32 else 2,
+                      wbytes=1 if args.weights == "fp8" else 2)
     stages = {}
     for s, name in enumerate(ops.STAGE_NAMES):
         b, f = work[name]
@@ -211,7 +220,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": b / t / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = load_traffic(dname, w.name)
+    roof["traffic"] = load_traffic(dname, w.name) if args.weights == "bf16" else None
     roof["kernel"] = dname
     roof["algorithmic_bytes"] = b
     roof["flops"] = f
@@ -232,10 +241,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if args.weights == "bf16" else "bf16 activations, fp8 (E4M3) routed weights",
         "data": "synthetic",
         "config": dict(w.describe(), out_dtype=args.out_dtype, weight_layout=args.layout,
-                       non_empty_experts=n_nonempty,
+                       routed_weights=args.weights, non_empty_experts=n_nonempty,
                        max_rows_per_expert=int(counts.max())),
         "grouped_gemm_tflops": gg_f / gg_t / 1e12,
         "grouped_gemm_mfma_frac": gg_f / gg_t / PEAK_BF16,

@@ -181,6 +181,31 @@ int moe_pack_weights(const uint16_t* src, int G, int N, int K, int panel_rows, u
                      void* stream);
 
 /* ------------------------------------------------------------------------
+ * 8-bit routed-expert weights (a one-time conversion at weight-load time).
+ * The pages name FP8 expert weights ("Twinkle x Ascend", MXFP8 / MXFP4 in
+ * the functional-expansion section; FP4/FP8 checkpoints in the quick start)
+ * without an encoding; the one used here is OCP E4M3 (bias 7, subnormals, no
+ * infinities, largest finite 448) with one power-of-two scale per output
+ * row:
+ *   e[g,n]   = smallest integer with max_k |W[g,n,k]| <= 448 * 2^e (0 for
+ *              a zero row), clamped to [-110, 110];
+ *   q[g,n,k] = E4M3(W[g,n,k] / 2^e), round to nearest even, saturating;
+ *   scales[g*N + n] = 2^e (fp32).
+ * The dequantised weight E4M3(q) * 2^e is exactly a bf16 value; the fp8
+ * GEMMs compute with it exactly (codes decoded to bf16 for the matrix
+ * cores, 2^e applied to the fp32 accumulator).  Code layout, panels of P
+ * rows: [G][ceil(N/P)][K/64][P/32][2][64][16 B]; chunk c of block b, lane l
+ * holds row panel*P + b*32 + l%32, columns 64 s + 32 c + 8 (l/32) + {0..7}
+ * in bytes 0-7 and the same + 16 in bytes 8-15; rows >= N are zero codes.
+ *   src [G,N,K] bf16 (finite); dst moe_packed_fp8_weight_bytes(G,N,K,P)
+ *   bytes, 16-byte aligned; scales [G*N] fp32.  K multiple of 64; P 128 (gate,
+ *   up) or 256 (down), else 0 / MOE_ERR_UNSUPPORTED.
+ */
+size_t moe_packed_fp8_weight_bytes(int G, int N, int K, int panel_rows);
+int moe_pack_weights_fp8(const uint16_t* src, int G, int N, int K, int panel_rows, uint8_t* dst,
+                         float* scales, void* stream);
+
+/* ------------------------------------------------------------------------
  * Result return merged by routing weight [TW], plus the always-on shared
  * expert with weight 1 [MS]:
  *   y[t,o] = y_shared[t,o] + sum_j topk_w[t,j] * y_perm[dest[t,j], o]
@@ -219,7 +244,10 @@ typedef struct moe_weights {
                                      s_gate, s_up, s_down hold the
                                      moe_pack_weights layout of those matrices
                                      (panel_rows 128 for the gate / up
-                                     matrices, 256 for the others) */
+                                     matrices, 256 for the others);
+                                     MOE_WEIGHTS_FP8: as 1, except that w_gate,
+                                     w_up, w_down hold moe_pack_weights_fp8
+                                     codes (uint8) with the row scales below */
     const uint16_t* w_g;          /* [E,d] bf16 router projection */
     const float* logit_offset;    /* [E] fp32 or NULL, added to the logits */
     const float* score_bias;      /* [n_bias,E] fp32 or NULL (TOPK) */
@@ -230,7 +258,11 @@ typedef struct moe_weights {
     const uint16_t* s_gate;       /* [F_shared,d] bf16 (shared expert) */
     const uint16_t* s_up;         /* [F_shared,d] bf16 */
     const uint16_t* s_down;       /* [d,F_shared] bf16 */
+    const float* w_gate_scale;    /* MOE_WEIGHTS_FP8: [E*F] fp32 row scales */
+    const float* w_up_scale;      /* MOE_WEIGHTS_FP8: [E*F] */
+    const float* w_down_scale;    /* MOE_WEIGHTS_FP8: [E*d] */
 } moe_weights;
+#define MOE_WEIGHTS_FP8 2
 
 /* Workspace for moe_forward (all intermediates: logits, routing, permutation,
  * x_perm, h, y_perm and the shared expert's h and y). */

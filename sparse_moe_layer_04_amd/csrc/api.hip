@@ -289,6 +289,22 @@ int moe_pack_weights(const uint16_t* src, int G, int N, int K, int panel_rows, u
     return hip_status(launch_pack_weights(src, dst, G, N, K, panel_rows, as_stream(stream)));
 }
 
+size_t moe_packed_fp8_weight_bytes(int G, int N, int K, int panel_rows) {
+    if (G < 1 || N < 1 || K < 64 || K % 64) return 0;
+    if (panel_rows != 128 && panel_rows != 256) return 0;
+    return packed_fp8_weight_bytes(G, N, K, panel_rows);
+}
+
+int moe_pack_weights_fp8(const uint16_t* src, int G, int N, int K, int panel_rows, uint8_t* dst,
+                         float* scales, void* stream) {
+    if (G < 1 || N < 1 || K < 64) return MOE_ERR_SHAPE;
+    if (K % 64 || (panel_rows != 128 && panel_rows != 256)) return MOE_ERR_UNSUPPORTED;
+    if (!src || !dst || !scales) return MOE_ERR_NULL;
+    if (!aligned16(src) || !aligned16(dst) || ((uintptr_t)scales & 3u)) return MOE_ERR_ALIGN;
+    return hip_status(
+        launch_pack_weights_fp8(src, dst, scales, G, N, K, panel_rows, as_stream(stream)));
+}
+
 int moe_combine(const float* y_perm, const int32_t* dest, const float* topk_w,
                 const float* y_shared, int T, int d, int k, int rows, int out_dtype, void* y,
                 void* stream) {
@@ -314,7 +330,10 @@ static int forward_checks(const moe_cfg* c, const moe_weights* w) {
     if (c->mode != MOE_MODE_TOPK && c->mode != MOE_MODE_HASH) return MOE_ERR_UNSUPPORTED;
     if (c->out_dtype != MOE_OUT_BF16 && c->out_dtype != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
     if (!(c->scale == c->scale)) return MOE_ERR_SHAPE;
-    if (w->packed != 0 && w->packed != 1) return MOE_ERR_UNSUPPORTED;
+    if (w->packed != 0 && w->packed != 1 && w->packed != MOE_WEIGHTS_FP8)
+        return MOE_ERR_UNSUPPORTED;
+    // fp8 routed weights run on the LDS-staged expert GEMM only
+    if (w->packed == MOE_WEIGHTS_FP8 && !lds_gemm_ok(1, c->E)) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -340,6 +359,13 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     if (c->T == 0) return MOE_OK;
     if (!x || !y || !w->w_g || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL;
     if (c->F_shared > 0 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_NULL;
+    const bool fp8 = w->packed == MOE_WEIGHTS_FP8;
+    if (fp8 && (!w->w_gate_scale || !w->w_up_scale || !w->w_down_scale)) return MOE_ERR_NULL;
+    if (fp8 && (!aligned16(w->w_gate_scale) || !aligned16(w->w_up_scale) ||
+                !aligned16(w->w_down_scale)))
+        return MOE_ERR_ALIGN;
+    // layout of the bf16 matrices (router, shared expert; routed unless fp8)
+    const int wpk = fp8 ? 1 : w->packed;
     if (c->mode == MOE_MODE_TOPK) {
         if (c->n_bias < 0 || c->n_bias > 2) return MOE_ERR_SHAPE;
         if (c->n_bias > 0 && !w->score_bias) return MOE_ERR_NULL;
@@ -375,7 +401,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     gl.K = d;
     gl.N = E;
     gl.w1 = w->w_g;
-    gl.packed = w->packed;
+    gl.packed = wpk;
     gl.offset = w->logit_offset;
     gl.out = logits;
     if ((e = launch_grouped_gemm(EPI_F32_OFFSET, gl, s)) != hipSuccess) return MOE_ERR_HIP;
@@ -391,7 +417,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     // x_perm copy) and passes h in the blocked layout; the register-direct
     // kernel (plain weights) reads a row-major x_perm.  The permutation's
     // first kernel also clears the expert GEMMs' scheduling counters.
-    const bool lds = lds_gemm_ok(w->packed, E);
+    const bool lds = lds_gemm_ok(wpk, E);
     if ((e = launch_permute(ids, x, T, d, E, k, L.counts, L.offsets, L.dest, L.src,
                             lds ? nullptr : L.x_perm, d_flags, L.perm, s, L.sched,
                             4 * kSchedWords)) != hipSuccess)
@@ -410,7 +436,10 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g1.N = F;
     g1.w1 = w->w_gate;
     g1.w2 = w->w_up;
-    g1.packed = w->packed;
+    g1.packed = wpk;
+    g1.wfp8 = fp8;
+    g1.s1 = w->w_gate_scale;
+    g1.s2 = w->w_up_scale;
     g1.clamp_limit = c->clamp_limit;
     g1.clamp_mode = c->clamp_mode;
     g1.out = L.h;
@@ -428,7 +457,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
         gs.N = Fs;
         gs.w1 = w->s_gate;
         gs.w2 = w->s_up;
-        gs.packed = w->packed;
+        gs.packed = wpk;
         gs.clamp_limit = c->clamp_limit;
         gs.clamp_mode = c->clamp_mode;
         gs.out = L.hs;
@@ -445,7 +474,9 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g2.K = F;
     g2.N = d;
     g2.w1 = w->w_down;
-    g2.packed = w->packed;
+    g2.packed = wpk;
+    g2.wfp8 = fp8;
+    g2.s1 = w->w_down_scale;
     g2.out = L.y_perm;
     g2.a_blocked = lds;
     g2.sched = L.sched + 2 * kSchedWords;
@@ -460,7 +491,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
         gs.K = Fs;
         gs.N = d;
         gs.w1 = w->s_down;
-        gs.packed = w->packed;
+        gs.packed = wpk;
         gs.out = L.ys;
         gs.sched = L.sched + 3 * kSchedWords;
         if ((e = expert_gemm(EPI_F32, gs, s)) != hipSuccess) return MOE_ERR_HIP;

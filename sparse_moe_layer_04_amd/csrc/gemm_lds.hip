@@ -62,13 +62,17 @@ constexpr int kStaticLds = 256;              // reserve for static LDS (scan_sh,
 // the others the 32-wide ones (memory-bound: deeper lookahead)
 constexpr int kWideStageRows = 192;
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 // Pipeline of one stage width KB (32 or 64 columns of K per stage).
 //   KB = 32: 4 slots of 32 KB (16 KB activations + 16 KB weights), 3 stages
 //            in flight; per stage 2 activation + 2 weight DMA instructions
 //            per wave; the waits count the instructions of later stages.
 //   KB = 64: 2 slots of 64 KB, 1 stage in flight while one computes; per
 //            stage 4 + 4 instructions per wave; every wait is vmcnt(0).
-template <int KB>
+//   WF = 1 (fp8 weights): the weight stage is half as many bytes (one 1 KB
+//            chunk per 32-row block per 32 columns of K), same slot count.
+template <int KB, int WF = 0>
 struct Stage {
     static_assert(KB == 32 || KB == 64, "stage width");
     static constexpr int ROWB = KB * 2;                    // LDS bytes per activation row
@@ -76,12 +80,13 @@ struct Stage {
     static constexpr int RPI = 64 / LPR;                   // rows per DMA instruction
     static constexpr int APW = TM / RPI / 8;               // activation instrs per wave (max)
     static constexpr int Q = KB / 16;                      // MFMA substeps per stage
+    static constexpr int WI = WF ? KB / 32 : Q;            // weight instrs per wave (1 KB each)
     static constexpr int SLOTA = TM * ROWB;
-    static constexpr int SLOTW = WBLK * Q * 1024;
+    static constexpr int SLOTW = WBLK * WI * 1024;
     static constexpr int SLOT = SLOTA + SLOTW;
-    static constexpr int SLOTS = kRing / SLOT;
+    static constexpr int SLOTS = KB == 32 ? 4 : 2;
     static constexpr int AHEAD = SLOTS - 1;                // stages in flight
-    static_assert(SLOTS * SLOT == kRing, "ring");
+    static_assert(SLOTS * SLOT <= kRing, "ring");
 };
 
 // activation addressing: row-major a, the blocked layout, or row-major a
@@ -129,9 +134,9 @@ __device__ __forceinline__ void wait_vm() {
 
 // wait for the oldest in-flight stage (AHEAD - 1 later stages of na + NW
 // instructions each may stay outstanding)
-template <int KB>
+template <int KB, int WF>
 __device__ __forceinline__ void wait_stage(int na) {
-    constexpr int A1 = Stage<KB>::AHEAD - 1, NW = Stage<KB>::Q;
+    constexpr int A1 = Stage<KB, WF>::AHEAD - 1, NW = Stage<KB, WF>::WI;
     if constexpr (A1 == 0) {
         wait_vm<0>();
     } else {
@@ -155,6 +160,12 @@ struct LdsTile {
     int n0;                // first weight row / feature of this wave's blocks
     const uint16_t* wsrc0; // this expert's packed matrix (gate matrix for SwiGLU)
     const uint16_t* wsrc1; // up matrix (SwiGLU) or the same
+    const uint8_t* bsrc0;  // fp8 weights: this expert's code matrices (gate / the one)
+    const uint8_t* bsrc1;  // fp8 weights: up matrix (SwiGLU) or the same
+    size_t pstride_b;      // fp8 weights: bytes per panel
+    size_t wstride_b;      // fp8 weights: bytes per 64-wide K stage of one panel
+    const float* sc0;      // fp8 weights: row scales of this expert (gate / the one)
+    const float* sc1;      // fp8 weights: row scales of the up matrix (SwiGLU)
     int blk0;              // first 32-row block of this n-tile in each matrix
     int np;                // packed panels per matrix
     size_t pstride;        // packed elements per panel
@@ -175,10 +186,10 @@ struct LdsTile {
 //     j % 2 of the packed stage j / 2) to LDS fragment slot n.  SwiGLU tile
 //     blocks [0, 4) are gate rows, [4, 8) up rows; a block of a panel past
 //     the matrix end re-reads the last panel (its outputs are never stored).
-template <int EPI, int KB>
+template <int EPI, int KB, int WF>
 __device__ __forceinline__ void issue_stage(const LdsTile& t, int j, uint32_t sbase) {
     using Pn = Panel<EPI>;
-    using St = Stage<KB>;
+    using St = Stage<KB, WF>;
     const uint32_t base = t.lds0 + sbase;
     const GemmArgs& args = *t.args;
 #pragma unroll
@@ -190,6 +201,27 @@ __device__ __forceinline__ void issue_stage(const LdsTile& t, int j, uint32_t sb
         }
     }
     const int s64 = (j * KB) >> 6, sub0 = ((j * KB) & 63) >> 4;
+    if constexpr (WF) {
+        // fp8 codes: wave w copies block w, chunks c0 .. c0 + WI - 1 (each the
+        // 32 columns of one 32-wide K slice, both substeps) to fragment slot
+        // WI w + i
+        const int b = t.wave;
+        const uint8_t* mat = t.bsrc0;
+        int gb = t.blk0 + b;
+        if (EPI == EPI_SWIGLU_BF16 && b >= Pn::BPM) {
+            mat = t.bsrc1;
+            gb -= Pn::BPM;
+        }
+        const int panel = min(gb / Pn::BPP, t.np - 1);
+        const int c0 = ((j * KB) & 63) >> 5;
+#pragma unroll
+        for (int i = 0; i < St::WI; ++i) {
+            const uint8_t* src = mat + (size_t)panel * t.pstride_b + (size_t)s64 * t.wstride_b +
+                                 (gb % Pn::BPP) * 2048 + (c0 + i) * 1024 + t.lane * 16;
+            dma16(src, base + St::SLOTA + (b * St::WI + i) * 1024);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < St::Q; ++i) {
         const int n = St::Q * t.wave + i;
@@ -215,17 +247,40 @@ struct Operands {
     bf16x8 w0, w1, a[NTB];
 };
 
-template <int EPI, int KB, int NTB>
+// eight E4M3 codes (bytes of v, in order) -> bf16x8: the hardware
+// conversion gives the exact fp32 values, whose upper halves are the exact
+// bf16 values (at most 4 significant bits)
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 v) {
+    const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[0], false);
+    const f32x2 f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[0], true);
+    const f32x2 f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[1], false);
+    const f32x2 f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[1], true);
+    u32x4 r;
+    r[0] = __builtin_amdgcn_perm(__float_as_uint(f0.y), __float_as_uint(f0.x), 0x07060302u);
+    r[1] = __builtin_amdgcn_perm(__float_as_uint(f1.y), __float_as_uint(f1.x), 0x07060302u);
+    r[2] = __builtin_amdgcn_perm(__float_as_uint(f2.y), __float_as_uint(f2.x), 0x07060302u);
+    r[3] = __builtin_amdgcn_perm(__float_as_uint(f3.y), __float_as_uint(f3.x), 0x07060302u);
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+template <int EPI, int KB, int NTB, int WF>
 __device__ __forceinline__ void read_operands(const LdsTile& t, uint32_t sbase, int q,
                                               Operands<NTB>& o) {
-    using St = Stage<KB>;
+    using St = Stage<KB, WF>;
     const unsigned char* base = t.smem + sbase;
-    // weight blocks of this wave (fragment slots Q b + substep)
+    // weight blocks of this wave (bf16: fragment slots Q b + substep; fp8:
+    // chunk slots WI b + substep / 2, substep parity selects the 8-byte half)
     const int b0 = (EPI == EPI_SWIGLU_BF16) ? t.wn : 2 * t.wn;
     const int b1 = (EPI == EPI_SWIGLU_BF16) ? Panel<EPI>::BPM + t.wn : 2 * t.wn + 1;
-    const unsigned char* wbase = base + St::SLOTA + t.lane * 16;
-    o.w0 = *(const bf16x8*)(wbase + (b0 * St::Q + q) * 1024);
-    o.w1 = *(const bf16x8*)(wbase + (b1 * St::Q + q) * 1024);
+    if constexpr (WF) {
+        const unsigned char* wbase = base + St::SLOTA + t.lane * 16 + (q & 1) * 8;
+        o.w0 = fp8x8_to_bf16x8(*(const u32x2*)(wbase + (b0 * St::WI + (q >> 1)) * 1024));
+        o.w1 = fp8x8_to_bf16x8(*(const u32x2*)(wbase + (b1 * St::WI + (q >> 1)) * 1024));
+    } else {
+        const unsigned char* wbase = base + St::SLOTA + t.lane * 16;
+        o.w0 = *(const bf16x8*)(wbase + (b0 * St::Q + q) * 1024);
+        o.w1 = *(const bf16x8*)(wbase + (b1 * St::Q + q) * 1024);
+    }
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
         const int r = t.wm * t.mh + tb * 32 + t.l32;
@@ -243,7 +298,7 @@ __device__ __forceinline__ void mfma_substep(const Operands<NTB>& o, f32x16 (&ac
     }
 }
 
-template <int EPI, int AM, int NTB>
+template <int EPI, int AM, int NTB, int WF>
 __device__ __forceinline__ void epilogue(const LdsTile& t, const f32x16 (&acc)[2][MAXNTB]) {
     const GemmArgs& args = *t.args;
     const int N = t.N;
@@ -258,6 +313,12 @@ __device__ __forceinline__ void epilogue(const LdsTile& t, const f32x16 (&acc)[2
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
                 const int n = t.n0 + 8 * qq + 4 * t.half;
+                // fp8 weights: row scales 2^e of features n .. n+3 (exact products)
+                f32x4 sg = {1.0f, 1.0f, 1.0f, 1.0f}, su = sg;
+                if constexpr (WF) {
+                    sg = *(const f32x4*)(t.sc0 + n);
+                    su = *(const f32x4*)(t.sc1 + n);
+                }
                 uint32_t packed[2];
 #pragma unroll
                 for (int i = 0; i < 4; i += 2) {
@@ -266,6 +327,10 @@ __device__ __forceinline__ void epilogue(const LdsTile& t, const f32x16 (&acc)[2
                     for (int u = 0; u < 2; ++u) {
                         float gv = acc[0][tb][4 * qq + i + u];
                         float uv = acc[1][tb][4 * qq + i + u];
+                        if constexpr (WF) {
+                            gv = gv * sg[i + u];
+                            uv = uv * su[i + u];
+                        }
                         gv = args.clamp_mode == MOE_CLAMP_SYMMETRIC ? clamp_sym(gv, L)
                                                                     : fminf(gv, L);
                         uv = clamp_sym(uv, L);
@@ -287,6 +352,11 @@ __device__ __forceinline__ void epilogue(const LdsTile& t, const f32x16 (&acc)[2
                     f32x4 v;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[i] = acc[b][tb][4 * qq + i];
+                    if constexpr (WF) {
+                        const f32x4 sc = *(const f32x4*)(t.sc0 + n);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) v[i] = v[i] * sc[i];
+                    }
                     *(f32x4*)(orow + n) = v;
                 }
         }
@@ -307,9 +377,9 @@ __device__ __forceinline__ void epilogue(const LdsTile& t, const f32x16 (&acc)[2
 // read latency hides behind MFMAs of the same wave; the reads of a slot
 // complete before the next barrier, so the DMA that reuses the slot after
 // that barrier never races them.
-template <int EPI, int AM, int KB, int NTB>
+template <int EPI, int AM, int KB, int NTB, int WF>
 __device__ __forceinline__ void run_tile(const LdsTile& t) {
-    using St = Stage<KB>;
+    using St = Stage<KB, WF>;
     f32x16 acc[2][MAXNTB];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -320,25 +390,26 @@ __device__ __forceinline__ void run_tile(const LdsTile& t) {
     const int S = t.K / KB;
     wait_vm<0>();  // retire the previous tile's stores before counting DMA entries
 #pragma unroll
-    for (int p = 0; p < St::AHEAD; ++p) issue_stage<EPI, KB>(t, min(p, S - 1), p * St::SLOT);
+    for (int p = 0; p < St::AHEAD; ++p) issue_stage<EPI, KB, WF>(t, min(p, S - 1), p * St::SLOT);
     uint32_t s_cmp = 0, s_iss = St::AHEAD * St::SLOT;
     Operands<NTB> o[2];
     for (int j = 0; j < S; ++j) {
-        wait_stage<KB>(t.na);
+        wait_stage<KB, WF>(t.na);
         __syncthreads();
         // (one stage in flight: every wait is vmcnt(0), nothing to re-issue)
-        if (St::AHEAD > 1 || j + 1 < S) issue_stage<EPI, KB>(t, min(j + St::AHEAD, S - 1), s_iss);
-        s_iss = (s_iss + St::SLOT == kRing) ? 0 : s_iss + St::SLOT;
+        if (St::AHEAD > 1 || j + 1 < S)
+            issue_stage<EPI, KB, WF>(t, min(j + St::AHEAD, S - 1), s_iss);
+        s_iss = (s_iss + St::SLOT == St::SLOTS * St::SLOT) ? 0 : s_iss + St::SLOT;
         if constexpr (NTB > 0) {
 #pragma unroll
             for (int q = 0; q < St::Q; ++q) {
-                read_operands<EPI, KB, NTB>(t, s_cmp, q, o[q & 1]);
+                read_operands<EPI, KB, NTB, WF>(t, s_cmp, q, o[q & 1]);
                 __builtin_amdgcn_sched_barrier(0);
                 if (q > 0 || j > 0) mfma_substep<NTB>(o[(q + 1) & 1], acc);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        s_cmp = (s_cmp + St::SLOT == kRing) ? 0 : s_cmp + St::SLOT;
+        s_cmp = (s_cmp + St::SLOT == St::SLOTS * St::SLOT) ? 0 : s_cmp + St::SLOT;
     }
     if constexpr (NTB > 0) mfma_substep<NTB>(o[(St::Q - 1) & 1], acc);
     // dynamic scheduling: thread 0 claims the workgroup's next item here,
@@ -350,17 +421,17 @@ __device__ __forceinline__ void run_tile(const LdsTile& t) {
     wait_vm<0>();
     if (claim) *t.next_item = t.item_lo + (int)claimed;
     __syncthreads();
-    if constexpr (NTB > 0) epilogue<EPI, AM, NTB>(t, acc);
+    if constexpr (NTB > 0) epilogue<EPI, AM, NTB, WF>(t, acc);
 }
 
 // run_tile for ntb in [0, NT] (ntb is wave-uniform)
-template <int EPI, int AM, int KB, int NT>
+template <int EPI, int AM, int KB, int NT, int WF>
 __device__ __forceinline__ void run_tile_ntb(const LdsTile& t, int ntb) {
     if constexpr (NT == 0) {
-        run_tile<EPI, AM, KB, 0>(t);
+        run_tile<EPI, AM, KB, 0, WF>(t);
     } else {
-        if (ntb >= NT) run_tile<EPI, AM, KB, NT>(t);
-        else run_tile_ntb<EPI, AM, KB, NT - 1>(t, ntb);
+        if (ntb >= NT) run_tile<EPI, AM, KB, NT, WF>(t);
+        else run_tile_ntb<EPI, AM, KB, NT - 1, WF>(t, ntb);
     }
 }
 
@@ -390,7 +461,7 @@ __device__ __forceinline__ void setup_a(LdsTile& t, const GemmArgs& args) {
 
 // Tile of item (group g, local item index): set up the per-tile fields of t
 // and run it.
-template <int EPI, int AM>
+template <int EPI, int AM, int WF>
 __device__ __forceinline__ void do_tile(LdsTile& t, const GemmArgs& args, int g, int local,
                                         int grp_lo, int grp_hi) {
     using Pn = Panel<EPI>;
@@ -407,6 +478,16 @@ __device__ __forceinline__ void do_tile(LdsTile& t, const GemmArgs& args, int g,
     t.wsrc1 = (EPI == EPI_SWIGLU_BF16 ? args.w2 : args.w1) + ebase;
     t.blk0 = n_tile * Pn::BPM;
     t.wstride = (size_t)Pn::BPP * 2048;
+    if constexpr (WF) {
+        // fp8 codes: one byte per weight, panels of P rows x K bytes
+        const size_t ebase_b = (size_t)g * t.np * (size_t)Pn::P * t.K;
+        t.bsrc0 = (const uint8_t*)args.w1 + ebase_b;
+        t.bsrc1 = (const uint8_t*)(EPI == EPI_SWIGLU_BF16 ? args.w2 : args.w1) + ebase_b;
+        t.pstride_b = (size_t)Pn::P * t.K;
+        t.wstride_b = (size_t)Pn::BPP * 2048;
+        t.sc0 = args.s1 + (size_t)g * N;
+        t.sc1 = (EPI == EPI_SWIGLU_BF16 ? args.s2 : args.s1) + (size_t)g * N;
+    }
     t.n0 = n_tile * Pn::TN + t.wn * ((EPI == EPI_SWIGLU_BF16) ? 32 : 64);
     // the valid rows split evenly (in 32-row blocks) over the two wave halves
     t.mh = min(MH, (((t.valid + 1) >> 1) + 31) & ~31);
@@ -414,10 +495,10 @@ __device__ __forceinline__ void do_tile(LdsTile& t, const GemmArgs& args, int g,
     const int ntb = t.n0 < N ? (wrows + 31) / 32 : 0;
     if (t.valid > kWideStageRows) {
         setup_a<AM, 64>(t, args);
-        run_tile_ntb<EPI, AM, 64, MAXNTB>(t, ntb);
+        run_tile_ntb<EPI, AM, 64, MAXNTB, WF>(t, ntb);
     } else {
         setup_a<AM, 32>(t, args);
-        run_tile_ntb<EPI, AM, 32, MAXNTB>(t, ntb);
+        run_tile_ntb<EPI, AM, 32, MAXNTB, WF>(t, ntb);
     }
 }
 
@@ -430,7 +511,7 @@ __device__ __forceinline__ void do_tile(LdsTile& t, const GemmArgs& args, int g,
 // thus work on neighbouring items (the n-tiles of the same experts) at the
 // same time and share their activations in L2, and a workgroup that drew
 // cheap tiles (few valid rows) takes more of them.
-template <int EPI, int AM>
+template <int EPI, int AM, int WF>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs args) {
     using Pn = Panel<EPI>;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -530,12 +611,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs arg
         }
         int grp_lo, grp_hi;
         group_rows(g, grp_lo, grp_hi);
-        do_tile<EPI, AM>(t, args, g, q - item_prefix[g], grp_lo, grp_hi);
+        do_tile<EPI, AM, WF>(t, args, g, q - item_prefix[g], grp_lo, grp_hi);
         q = t.ctr ? next_item : q + per_xcd;
     }
 }
 
-template <int EPI, int AM>
+template <int EPI, int AM, int WF = 0>
 hipError_t launch_lds(const GemmArgs& g, hipStream_t stream) {
     static int configured_device = -1;
     static int grid = 0;
@@ -545,11 +626,11 @@ hipError_t launch_lds(const GemmArgs& g, hipStream_t stream) {
     if (err != hipSuccess) return err;
     if (configured_device != dev) {
         hipFuncAttributes fa;
-        err = hipFuncGetAttributes(&fa, (const void*)grouped_gemm_lds_kernel<EPI, AM>);
+        err = hipFuncGetAttributes(&fa, (const void*)grouped_gemm_lds_kernel<EPI, AM, WF>);
         if (err != hipSuccess) return err;
         static_lds = fa.sharedSizeBytes;
         if (static_lds > (size_t)kStaticLds) return hipErrorInvalidValue;
-        err = hipFuncSetAttribute((const void*)grouped_gemm_lds_kernel<EPI, AM>,
+        err = hipFuncSetAttribute((const void*)grouped_gemm_lds_kernel<EPI, AM, WF>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize,
                                   kLdsLimit - (int)static_lds);
         if (err != hipSuccess) return err;
@@ -558,7 +639,7 @@ hipError_t launch_lds(const GemmArgs& g, hipStream_t stream) {
     }
     const size_t lds = kRing + (size_t)(g.G + 1) * sizeof(int);
     if (lds + static_lds > (size_t)kLdsLimit) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((grouped_gemm_lds_kernel<EPI, AM>), dim3(grid), dim3(kThreads), lds,
+    hipLaunchKernelGGL((grouped_gemm_lds_kernel<EPI, AM, WF>), dim3(grid), dim3(kThreads), lds,
                        stream, g);
     return hipGetLastError();
 }
@@ -577,6 +658,15 @@ hipError_t launch_grouped_gemm_lds(int epilogue, const GemmArgs& g, hipStream_t 
     if (a_rows * g.K / 8 + 2 * (size_t)g.K >= (1ull << 32)) return hipErrorInvalidValue;
     if (g.gather && g.a_blocked) return hipErrorInvalidValue;
     const int am = g.gather ? A_GATHER : g.a_blocked ? A_BLK : A_ROW;
+    if (g.wfp8) {
+        // fp8 weights: the two routed expert GEMMs of moe_forward (gate/up
+        // on gathered token rows, down on the blocked h)
+        if (!g.s1 || (epilogue == EPI_SWIGLU_BF16 && !g.s2)) return hipErrorInvalidValue;
+        if (epilogue == EPI_SWIGLU_BF16 && am == A_GATHER && g.out_blocked)
+            return launch_lds<EPI_SWIGLU_BF16, A_GATHER, 1>(g, stream);
+        if (epilogue == EPI_F32 && am == A_BLK) return launch_lds<EPI_F32, A_BLK, 1>(g, stream);
+        return hipErrorInvalidValue;
+    }
     switch (epilogue) {
         case EPI_SWIGLU_BF16:
             // h is blocked exactly when the activations are not plain row-major

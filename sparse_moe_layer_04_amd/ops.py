@@ -45,7 +45,9 @@ class MoeCfg(ctypes.Structure):
 
 
 WEIGHT_NAMES = ("w_g", "logit_offset", "score_bias", "tid2eid", "w_gate", "w_up", "w_down",
-                "s_gate", "s_up", "s_down")
+                "s_gate", "s_up", "s_down", "w_gate_scale", "w_up_scale", "w_down_scale")
+# moe_weights.packed value of fp8 routed-expert weights (MOE_WEIGHTS_FP8)
+WEIGHTS_FP8 = 2
 MATRIX_NAMES = ("w_g", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")
 
 
@@ -83,6 +85,9 @@ def lib():
     L.moe_packed_weight_bytes.argtypes = [I, I, I, I]
     L.moe_packed_weight_bytes.restype = S
     L.moe_pack_weights.argtypes = [P, I, I, I, I, P, P]
+    L.moe_packed_fp8_weight_bytes.argtypes = [I, I, I, I]
+    L.moe_packed_fp8_weight_bytes.restype = S
+    L.moe_pack_weights_fp8.argtypes = [P, I, I, I, I, P, P, P]
     L.moe_forward_workspace_size.argtypes = [ctypes.POINTER(MoeCfg)]
     L.moe_forward_workspace_size.restype = S
     L.moe_forward.argtypes = [ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeWeights), P, P, P, P,
@@ -90,7 +95,8 @@ def lib():
     L.moe_forward_timed.argtypes = L.moe_forward.argtypes + [P]
     for name in ("moe_gate_logits", "moe_route", "moe_permute", "moe_expert_ffn",
                  "moe_expert_ffn_packed",
-                 "moe_combine", "moe_forward", "moe_forward_timed", "moe_pack_weights"):
+                 "moe_combine", "moe_forward", "moe_forward_timed", "moe_pack_weights",
+                 "moe_pack_weights_fp8"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -271,6 +277,23 @@ def pack_weights(w, panel_rows):
     return out
 
 
+def pack_weights_fp8(w, panel_rows):
+    """fp8 copy (moe_pack_weights_fp8: E4M3 codes in the packed layout, one
+    power-of-two scale per row) of bf16 weights [G,N,K] or [N,K]; returns
+    (codes uint8 tensor, scales fp32 tensor [G*N])."""
+    _need(w, torch.bfloat16, "w")
+    shape = tuple(w.shape)
+    G, N, K = (1,) + shape if w.dim() == 2 else shape
+    nbytes = int(lib().moe_packed_fp8_weight_bytes(G, N, K, panel_rows))
+    if nbytes == 0:
+        raise MoeError(f"cannot pack weights of shape {shape} in panels of {panel_rows}")
+    codes = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(G * N, dtype=torch.float32, device=w.device)
+    _check(lib().moe_pack_weights_fp8(_ptr(w), G, N, K, panel_rows, _ptr(codes), _ptr(scales),
+                                      _stream()), "moe_pack_weights_fp8")
+    return codes, scales
+
+
 class MoeLayer:
     """One fine-grained MoE layer on the device: holds the weights, the config
     and a preallocated workspace; ``forward`` is one C-ABI call."""
@@ -291,13 +314,21 @@ class MoeLayer:
         _opt(self.weights.get("logit_offset"), torch.float32, "logit_offset")
         _opt(self.weights.get("score_bias"), torch.float32, "score_bias")
         _opt(self.weights.get("tid2eid"), torch.int32, "tid2eid")
+        fp8 = packed == "fp8"
         if packed:
-            # one-time layout change at load time (moe_pack_weights)
+            # one-time layout change at load time (moe_pack_weights; with
+            # packed="fp8" the routed expert matrices are quantised to E4M3
+            # by moe_pack_weights_fp8 instead)
             for key in MATRIX_NAMES:
-                if self.weights.get(key) is not None:
+                if self.weights.get(key) is None:
+                    continue
+                if fp8 and key in ("w_gate", "w_up", "w_down"):
+                    self.weights[key], self.weights[key + "_scale"] = pack_weights_fp8(
+                        self.weights[key], PANEL_ROWS[key])
+                else:
                     self.weights[key] = pack_weights(self.weights[key], PANEL_ROWS[key])
-        self.packed = bool(packed)
-        self.cw = MoeWeights(packed=int(self.packed),
+        self.packed = WEIGHTS_FP8 if fp8 else int(bool(packed))
+        self.cw = MoeWeights(packed=self.packed,
                              **{n: _ptr(self.weights.get(n)) for n in WEIGHT_NAMES})
         self.device = self.weights["w_g"].device
         self.ws_bytes = int(lib().moe_forward_workspace_size(ctypes.byref(self.cfg)))

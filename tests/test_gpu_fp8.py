@@ -1,0 +1,116 @@
+"""GPU parity of the fp8 routed-expert weight mode (E4M3 codes, one
+power-of-two scale per output row; moe_pack_weights_fp8 + moe_forward with
+packed = MOE_WEIGHTS_FP8) against the oracle:
+
+  - quantisation: codes and scales bit-exact against the oracle's row
+    quantiser, on random rows plus zero, huge, tiny and tie rows, every code
+    at its place in the packed layout and padding rows zero;
+  - forward: routes bit-exact and y within 1e-2 x RMS of the oracle run on
+    the dequantised weights (exact bf16 values);
+  - the fp8 forward is bit-equal to the bf16 packed forward on the
+    dequantised weights (the row scale is a power of two, so scaling the
+    fp32 accumulator commutes with every rounding of the sum).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import bits, host, bf16_f64, check_rms
+from sparse_moe_layer_04_amd import ops, workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda")
+
+
+def unpack_codes(codes, G, N, K, P):
+    """[G][ceil(N/P)][K/64][P/32][2][64][16] -> [G, ceil(N/P)*P, K] codes."""
+    npan = (N + P - 1) // P
+    a = codes.reshape(G, npan, K // 64, P // 32, 2, 2, 32, 2, 8)
+    # axes: g, panel, s, b, c, lane_hi, lane_lo, h, i ->
+    #       g, panel, b, lane_lo | s, c, h, lane_hi, i
+    a = a.transpose(0, 1, 3, 6, 2, 4, 7, 5, 8)
+    return a.reshape(G, npan * P, K)
+
+
+def weights_with_special_rows(G, N, K, seed):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((G, N, K)) / np.sqrt(K)).astype(np.float32)
+    w[0, 0] = 0.0                                     # zero row
+    w[0, 1] *= 2.0 ** 40                              # huge row
+    w[0, 2] *= 2.0 ** -60                             # tiny row (subnormal codes)
+    # ties: consecutive E4M3 values and their midpoints, scaled by 2^-5,
+    # with the row maximum exactly 448 * 2^-5
+    vals = sorted({oracle.e4m3_decode(c) for c in range(0x7F)})
+    mids = [(a + b) / 2 for a, b in zip(vals[:-1], vals[1:])]
+    row = np.resize(np.array(vals + mids, np.float64), K) * 2.0 ** -5
+    row[0] = 448.0 * 2.0 ** -5
+    row[1::2] *= -1
+    w[G - 1, N - 1] = row.astype(np.float32)
+    b = (w.view(np.uint32) >> 16).astype(np.uint16)   # bf16 (truncation; exact for the ties)
+    return b
+
+
+@pytest.mark.parametrize("G,N,K,P", [(1, 64, 64, 128), (3, 200, 192, 128), (2, 256, 128, 256),
+                                     (5, 96, 320, 256)])
+def test_pack_weights_fp8(G, N, K, P):
+    wb = weights_with_special_rows(G, N, K, seed=G * 1000 + N)
+    w = torch.from_numpy(wb.view(np.int16)).to(DEV).view(torch.bfloat16)
+    codes, scales = ops.pack_weights_fp8(w, P)
+    torch.cuda.synchronize()
+    q_ref, e_ref = oracle.quant_fp8_rows(wb.reshape(G * N, K))
+    got = unpack_codes(host(codes), G, N, K, P)
+    assert np.array_equal(got[:, :N].reshape(G * N, K), q_ref)
+    assert not got[:, N:].any()
+    assert np.array_equal(host(scales), np.ldexp(np.float32(1.0), e_ref))
+
+
+FP8_CASES = [
+    wl.WORKLOADS[0],
+    wl.small(T=300, d=256, E=16, k=4, F=192, seed=11, scale=2.5, F_shared=128),
+    wl.small(T=515, d=128, E=64, k=6, F=64, seed=12, n_bias=2, vision_spans=2, span_len=100,
+             zipf_expert_s=1.2),
+    wl.small(T=400, d=192, E=32, k=6, F=128, seed=13, scale=2.5, mode=wl.MODE_HASH, V=500,
+             zipf_token_s=1.1),
+    wl.small(T=600, d=128, E=8, k=2, F=128, seed=15, scale=1.0),   # 2-3 m-tiles per expert
+]
+
+
+def _dequantised(inp):
+    """inputs with the routed matrices replaced by their dequantised fp8
+    weights (exact bf16 values, from the oracle's quantiser)."""
+    out = dict(inp)
+    for key in ("w_gate", "w_up", "w_down"):
+        wb = bits(inp[key])
+        q, e = oracle.quant_fp8_rows(wb.reshape(-1, wb.shape[-1]))
+        deq = oracle.dequant_fp8_rows(q, e).reshape(wb.shape)
+        out[key] = torch.from_numpy(deq.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return out
+
+
+@pytest.mark.parametrize("w", FP8_CASES, ids=lambda w: w.name)
+def test_forward_fp8(w):
+    inp = wl.make_inputs(w, DEV)
+    deq = _dequantised(inp)
+    layer = ops.MoeLayer.from_workload(w, inp, out_dtype=ops.OUT_F32, packed="fp8")
+    logits = torch.empty((w.T, w.E), dtype=torch.float32, device=DEV)
+    ids = torch.empty((w.T, w.k), dtype=torch.int32, device=DEV)
+    wts = torch.empty((w.T, w.k), dtype=torch.float32, device=DEV)
+    y = layer.forward(inp["x"], input_ids=inp["input_ids"], modality=inp["modality"],
+                      logits=logits, ids=ids, w=wts)
+    # the bf16 packed forward on the dequantised weights: bit-equal
+    ref_layer = ops.MoeLayer.from_workload(w, deq, out_dtype=ops.OUT_F32, packed=True)
+    y_deq = ref_layer.forward(inp["x"], input_ids=inp["input_ids"], modality=inp["modality"])
+    torch.cuda.synchronize()
+    assert int(layer.flags.item()) == 0
+    assert torch.equal(y.view(torch.int32), y_deq.view(torch.int32))
+    # oracle on the dequantised weights, fed the GPU's logits
+    opt = lambda key: None if inp[key] is None else host(inp[key])
+    shared = [bits(inp[k]) if inp[k] is not None else None for k in ("s_gate", "s_up", "s_down")]
+    ref = oracle.forward(bits(inp["x"]), host(logits), w.k, w.scale, bits(deq["w_gate"]),
+                         bits(deq["w_up"]), bits(deq["w_down"]), *shared, w.clamp_limit,
+                         w.clamp_mode, bias=opt("score_bias"), modality=opt("modality"),
+                         input_ids=opt("input_ids"), tid2eid=opt("tid2eid"), mode=w.mode)
+    assert np.array_equal(host(ids), ref["ids"])
+    assert np.array_equal(host(wts).view(np.uint32), ref["w"].view(np.uint32))
+    check_rms(host(y), ref["y"])
