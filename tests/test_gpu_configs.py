@@ -110,3 +110,41 @@ def test_full_size(cfg):
           flush=True)
     del layer, inp, y, y16, logits, ids, wts
     free_cuda()
+
+
+def test_full_size_fp8():
+    """The fp8 routed-weight mode at the 384-expert workload's full size, in
+    the benchmark's launch configuration (--weights fp8): routes bit-exact,
+    and sampled tokens within 1e-2 x RMS of the oracle run on the oracle's
+    own dequantisation of the fp8 weights of the experts those tokens use."""
+    w = wl.WORKLOADS[2]
+    print(f"\n[{w.name}, fp8 weights] generating inputs", flush=True)
+    inp = wl.make_inputs(w, DEV)
+    layer = ops.MoeLayer.from_workload(w, inp, out_dtype=ops.OUT_F32, packed="fp8")
+    logits = torch.empty((w.T, w.E), dtype=torch.float32, device=DEV)
+    ids = torch.empty((w.T, w.k), dtype=torch.int32, device=DEV)
+    wts = torch.empty((w.T, w.k), dtype=torch.float32, device=DEV)
+    y = layer.forward(inp["x"], logits=logits, ids=ids, w=wts)
+    torch.cuda.synchronize()
+    assert int(layer.flags.item()) == 0
+    rid, rw, _ = oracle.route(host(logits), w.k, w.scale, bias=_opt(inp, "score_bias"))
+    assert np.array_equal(host(ids), rid)
+    assert np.array_equal(host(wts).view(np.uint32), rw.view(np.uint32))
+    rng = np.random.default_rng(77)
+    toks = np.sort(rng.choice(w.T, size=8, replace=False))
+    experts = np.unique(rid[toks])
+    mats = {}
+    for key in ("w_gate", "w_up", "w_down"):
+        m = bits(inp[key])
+        for e in experts:
+            q, ex = oracle.quant_fp8_rows(m[e])
+            m[e] = oracle.dequant_fp8_rows(q, ex)
+        mats[key] = m
+    shared = [bits(inp[k]) for k in ("s_gate", "s_up", "s_down")]
+    yref = oracle.tokens_forward(bits(inp["x"]), toks, rid, rw, mats["w_gate"], mats["w_up"],
+                                 mats["w_down"], *shared, w.clamp_limit, w.clamp_mode)
+    rel = check_rms(host(y)[toks], yref)
+    print(f"[{w.name}, fp8 weights] {len(toks)} sampled tokens ({len(experts)} experts): "
+          f"max|y - y_oracle| / rms = {rel:.2e}", flush=True)
+    del layer, inp, y, logits, ids, wts, mats
+    free_cuda()
