@@ -181,29 +181,33 @@ int moe_pack_weights(const uint16_t* src, int G, int N, int K, int panel_rows, u
                      void* stream);
 
 /* ------------------------------------------------------------------------
- * 8-bit routed-expert weights (a one-time conversion at weight-load time).
- * The pages name FP8 expert weights ("Twinkle x Ascend", MXFP8 / MXFP4 in
- * the functional-expansion section; FP4/FP8 checkpoints in the quick start)
- * without an encoding; the one used here is OCP E4M3 (bias 7, subnormals, no
- * infinities, largest finite 448) with one power-of-two scale per output
- * row:
- *   e[g,n]   = smallest integer with max_k |W[g,n,k]| <= 448 * 2^e (0 for
- *              a zero row), clamped to [-110, 110];
- *   q[g,n,k] = E4M3(W[g,n,k] / 2^e), round to nearest even, saturating;
- *   scales[g*N + n] = 2^e (fp32).
- * The dequantised weight E4M3(q) * 2^e is exactly a bf16 value; the fp8
- * GEMMs compute with it exactly (codes decoded to bf16 for the matrix
- * cores, 2^e applied to the fp32 accumulator).  Code layout, panels of P
- * rows: [G][ceil(N/P)][K/64][P/32][2][64][16 B]; chunk c of block b, lane l
- * holds row panel*P + b*32 + l%32, columns 64 s + 32 c + 8 (l/32) + {0..7}
- * in bytes 0-7 and the same + 16 in bytes 8-15; rows >= N are zero codes.
+ * MXFP8 routed-expert weights (a one-time conversion at weight-load time).
+ * The pages name MXFP8 / MXFP4 expert weights ("Twinkle x Ascend",
+ * functional-expansion section; FP4/FP8 checkpoints in the quick start);
+ * MXFP8 is the OCP Microscaling format: blocks of 32 values along K (the
+ * input dimension) share one power-of-two scale, each value an OCP E4M3
+ * float (bias 7, subnormals, no infinities, largest finite 448).  Per block,
+ * with the OCP specification's scale rule:
+ *   X = floor(log2(max |W| over the block)) - 8, clamped to [-110, 110]
+ *       (0 for an all-zero block);
+ *   q = E4M3(W / 2^X), round to nearest even, saturating at +-448.
+ * The dequantised weight E4M3(q) * 2^X is exactly a bf16 value; moe_forward
+ * computes with it exactly (codes and scale decoded together to bf16 for the
+ * matrix cores).
+ *   Codes, panels of P rows: [G][ceil(N/P)][K/64][P/32][2][64][16 B]; chunk
+ *   c of block b, lane l holds row panel*P + b*32 + l%32, columns
+ *   64 s + 32 c + 8 (l/32) + {0..7} in bytes 0-7 and the same + 16 in bytes
+ *   8-15; rows >= N are zero codes.
+ *   Scales: one byte X + 127 per (row, block), [G][ceil(N/P)][K/32][P/32][32].
  *   src [G,N,K] bf16 (finite); dst moe_packed_fp8_weight_bytes(G,N,K,P)
- *   bytes, 16-byte aligned; scales [G*N] fp32.  K multiple of 64; P 128 (gate,
- *   up) or 256 (down), else 0 / MOE_ERR_UNSUPPORTED.
+ *   bytes; scales moe_packed_fp8_scale_bytes(G,N,K,P) bytes; both 16-byte
+ *   aligned.  K multiple of 64; P 128 (gate, up) or 256 (down), else 0 /
+ *   MOE_ERR_UNSUPPORTED.
  */
 size_t moe_packed_fp8_weight_bytes(int G, int N, int K, int panel_rows);
+size_t moe_packed_fp8_scale_bytes(int G, int N, int K, int panel_rows);
 int moe_pack_weights_fp8(const uint16_t* src, int G, int N, int K, int panel_rows, uint8_t* dst,
-                         float* scales, void* stream);
+                         uint8_t* scales, void* stream);
 
 /* ------------------------------------------------------------------------
  * Result return merged by routing weight [TW], plus the always-on shared
@@ -247,7 +251,8 @@ typedef struct moe_weights {
                                      matrices, 256 for the others);
                                      MOE_WEIGHTS_FP8: as 1, except that w_gate,
                                      w_up, w_down hold moe_pack_weights_fp8
-                                     codes (uint8) with the row scales below */
+                                     MXFP8 codes (uint8) with the block
+                                     scales below */
     const uint16_t* w_g;          /* [E,d] bf16 router projection */
     const float* logit_offset;    /* [E] fp32 or NULL, added to the logits */
     const float* score_bias;      /* [n_bias,E] fp32 or NULL (TOPK) */
@@ -258,9 +263,9 @@ typedef struct moe_weights {
     const uint16_t* s_gate;       /* [F_shared,d] bf16 (shared expert) */
     const uint16_t* s_up;         /* [F_shared,d] bf16 */
     const uint16_t* s_down;       /* [d,F_shared] bf16 */
-    const float* w_gate_scale;    /* MOE_WEIGHTS_FP8: [E*F] fp32 row scales */
-    const float* w_up_scale;      /* MOE_WEIGHTS_FP8: [E*F] */
-    const float* w_down_scale;    /* MOE_WEIGHTS_FP8: [E*d] */
+    const uint8_t* w_gate_scale;  /* MOE_WEIGHTS_FP8: moe_pack_weights_fp8 scales */
+    const uint8_t* w_up_scale;    /* MOE_WEIGHTS_FP8 */
+    const uint8_t* w_down_scale;  /* MOE_WEIGHTS_FP8 */
 } moe_weights;
 #define MOE_WEIGHTS_FP8 2
 

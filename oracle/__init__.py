@@ -9,8 +9,9 @@ The arithmetic lives in ``moe_oracle.c`` (plain C, fp64, built by
 Parity unpinned: the clamp form (symmetric vs gate-above-only), the shared
 expert's form and the init-std reading are readings of what the pages leave
 open; they are configurable, and every other step is pinned by the tests.
-The fp8 weight encoding (E4M3 with one power-of-two scale per output row) is
-likewise a reading: the pages name FP8 weights but no format.
+The fp8 weight encoding (OCP MXFP8: E4M3 values, one power-of-two scale per
+32 values along K) follows the OCP specification the pages' "MxFP8" names;
+its exponent clamp to [-110, 110] is this build's reading.
 """
 from .oracle import (  # noqa: F401
     MODE_TOPK,
@@ -32,6 +33,6 @@ from .oracle import (  # noqa: F401
     forward,
     e4m3_decode,
     e4m3_encode,
-    quant_fp8_rows,
-    dequant_fp8_rows,
+    quant_mxfp8,
+    dequant_mxfp8,
 )

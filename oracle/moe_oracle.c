@@ -482,22 +482,25 @@ void orc_tokens_forward(const uint16_t* x, const int64_t* tokens, int n, int d, 
 
 /* ------------------------------------------------------ fp8 expert weights -- */
 /*
- * 8-bit expert weights.  The pages name FP8 (MXFP8 / MXFP4) weights as the
- * low-precision direction ("Twinkle x Ascend ... DeepSeek-V4 training",
- * functional-expansion section; the V4-Flash checkpoints ship in FP4/FP8,
- * quick-start section) but fix no encoding or scale granularity.  Reading
- * used here: OCP 8-bit floating point E4M3 ("E4M3FN": 1 sign bit, 4
+ * 8-bit expert weights.  The pages name MXFP8 / MXFP4 as the low-precision
+ * direction ("Twinkle x Ascend ... DeepSeek-V4 training", functional-
+ * expansion section; the V4-Flash checkpoints ship in FP4/FP8, quick-start
+ * section) without restating the format.  MXFP8 is the OCP Microscaling
+ * format: blocks of 32 consecutive values along K share one power-of-two
+ * scale (E8M0), each value an OCP 8-bit float E4M3 ("E4M3FN": 1 sign bit, 4
  * exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities,
- * S.1111.111 is NaN, largest finite 448), one power-of-two scale 2^e per
- * output row of each weight matrix:
- *   e    = the smallest integer with max_k |w[k]| <= 448 * 2^e
- *          (e = 0 for an all-zero row), clamped to [-110, 110];
- *   q[k] = E4M3 of w[k] / 2^e, rounded to nearest, ties to even, values
- *          beyond 448 saturated to +-448;
- *   dequantised weight = E4M3 value of q[k] * 2^e.
- * The dequantised weight has at most 4 significant bits and a binary
- * exponent inside bfloat16's range, so it is exactly a bf16 value: the FFN
- * of the fp8 mode is the bf16 FFN on the dequantised weights.
+ * S.1111.111 is NaN, largest finite 448).  Conversion, per the OCP MX
+ * specification's rule:
+ *   X    = floor(log2(max |v| over the block)) - 8   (8 = E4M3's largest
+ *          exponent), clamped here to [-110, 110] (X = 0 for an all-zero
+ *          block);
+ *   q[i] = E4M3(v[i] / 2^X), round to nearest, ties to even, values beyond
+ *          448 saturated to +-448;
+ *   dequantised value = E4M3 value of q[i] * 2^X.
+ * With X in [-110, 110] the dequantised value has at most 4 significant bits
+ * and a binary exponent inside bfloat16's normal range, so it is exactly a
+ * bf16 value: the FFN of the fp8 mode is the bf16 FFN on the dequantised
+ * weights.
  */
 
 /* value of an E4M3 code (NaN for S.1111.111) */
@@ -536,43 +539,43 @@ uint8_t orc_e4m3_encode(double v)
     return sign | (uint8_t)(((E + 7) << 3) | (int)m);
 }
 
-/* per-row quantisation of bf16 weights [R, K] -> codes [R, K], exponents [R] */
-void orc_quant_fp8_rows(const uint16_t* w, int64_t R, int K, uint8_t* q, int32_t* e)
+/* MXFP8 quantisation of bf16 weights [R, K] (K multiple of 32): codes
+ * [R, K], block exponents X [R, K/32] */
+void orc_quant_mxfp8(const uint16_t* w, int64_t R, int K, uint8_t* q, int32_t* x)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < R; ++r) {
-        const uint16_t* row = w + r * K;
-        double amax = 0.0;
-        for (int k = 0; k < K; ++k) {
-            const double a = fabs(bf16_value(row[k]));
-            if (a > amax)
-                amax = a;
+        for (int b = 0; b < K / 32; ++b) {
+            const uint16_t* v = w + r * K + 32 * b;
+            double amax = 0.0;
+            for (int i = 0; i < 32; ++i) {
+                const double a = fabs(bf16_value(v[i]));
+                if (a > amax)
+                    amax = a;
+            }
+            int X = 0;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);                 /* 2^(ex-1) <= amax < 2^ex */
+                X = (ex - 1) - 8;
+                if (X < -110)
+                    X = -110;
+                if (X > 110)
+                    X = 110;
+            }
+            x[r * (K / 32) + b] = X;
+            for (int i = 0; i < 32; ++i)
+                q[r * K + 32 * b + i] = orc_e4m3_encode(ldexp(bf16_value(v[i]), -X));
         }
-        int ex = 0;
-        if (amax > 0.0) {
-            int x;
-            frexp(amax, &x);                      /* 2^(x-1) <= amax < 2^x */
-            ex = x - 9;                           /* 448 * 2^ex >= 2^(x-1) * 1.75 ... */
-            while (amax > 448.0 * ldexp(1.0, ex))
-                ++ex;
-            while (amax <= 448.0 * ldexp(1.0, ex - 1))
-                --ex;
-            if (ex < -110)
-                ex = -110;
-            if (ex > 110)
-                ex = 110;
-        }
-        e[r] = ex;
-        for (int k = 0; k < K; ++k)
-            q[r * K + k] = orc_e4m3_encode(ldexp(bf16_value(row[k]), -ex));
     }
 }
 
-/* dequantised weights as bf16 bit patterns (exact; see above) */
-void orc_dequant_fp8_rows(const uint8_t* q, const int32_t* e, int64_t R, int K, uint16_t* w)
+/* dequantised MXFP8 weights as bf16 bit patterns (exact; see above) */
+void orc_dequant_mxfp8(const uint8_t* q, const int32_t* x, int64_t R, int K, uint16_t* w)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < R; ++r)
         for (int k = 0; k < K; ++k)
-            w[r * K + k] = orc_f64_to_bf16(ldexp(orc_e4m3_decode(q[r * K + k]), e[r]));
+            w[r * K + k] = orc_f64_to_bf16(
+                ldexp(orc_e4m3_decode(q[r * K + k]), x[r * (K / 32) + k / 32]));
 }

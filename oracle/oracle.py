@@ -61,10 +61,10 @@ def load():
     lib.orc_e4m3_decode.restype = D
     lib.orc_e4m3_encode.argtypes = [D]
     lib.orc_e4m3_encode.restype = ctypes.c_uint8
-    lib.orc_quant_fp8_rows.argtypes = [P, I64, I, P, P]
-    lib.orc_quant_fp8_rows.restype = None
-    lib.orc_dequant_fp8_rows.argtypes = [P, P, I64, I, P]
-    lib.orc_dequant_fp8_rows.restype = None
+    lib.orc_quant_mxfp8.argtypes = [P, I64, I, P, P]
+    lib.orc_quant_mxfp8.restype = None
+    lib.orc_dequant_mxfp8.argtypes = [P, P, I64, I, P]
+    lib.orc_dequant_mxfp8.restype = None
     lib.orc_combine.argtypes = [P, P, P, P, I, I, I, P]
     lib.orc_combine.restype = None
     lib.orc_tokens_forward.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, P, I, D, I, P]
@@ -258,22 +258,22 @@ def e4m3_encode(v):
     return int(load().orc_e4m3_encode(float(v)))
 
 
-def quant_fp8_rows(w):
-    """bf16 bits [..., K] -> (codes uint8 [..., K], row exponents int32 [...])."""
+def quant_mxfp8(w):
+    """bf16 bits [..., K] -> (codes uint8 [..., K], block exponents int32 [..., K/32])."""
     w = _c(w, np.uint16)
     K = w.shape[-1]
     R = w.size // K
     q = np.empty(w.shape, np.uint8)
-    e = np.empty(w.shape[:-1], np.int32)
-    load().orc_quant_fp8_rows(_p(w), R, K, _p(q), _p(e))
-    return q, e
+    x = np.empty(w.shape[:-1] + (K // 32,), np.int32)
+    load().orc_quant_mxfp8(_p(w), R, K, _p(q), _p(x))
+    return q, x
 
 
-def dequant_fp8_rows(q, e):
-    """(codes [..., K], row exponents [...]) -> dequantised weights as bf16 bits."""
+def dequant_mxfp8(q, x):
+    """(codes [..., K], block exponents [..., K/32]) -> dequantised weights as bf16 bits."""
     q = _c(q, np.uint8)
-    e = _c(e, np.int32)
+    x = _c(x, np.int32)
     K = q.shape[-1]
     w = np.empty(q.shape, np.uint16)
-    load().orc_dequant_fp8_rows(_p(q), _p(e), q.size // K, K, _p(w))
+    load().orc_dequant_mxfp8(_p(q), _p(x), q.size // K, K, _p(w))
     return w

@@ -295,12 +295,18 @@ size_t moe_packed_fp8_weight_bytes(int G, int N, int K, int panel_rows) {
     return packed_fp8_weight_bytes(G, N, K, panel_rows);
 }
 
+size_t moe_packed_fp8_scale_bytes(int G, int N, int K, int panel_rows) {
+    if (G < 1 || N < 1 || K < 64 || K % 64) return 0;
+    if (panel_rows != 128 && panel_rows != 256) return 0;
+    return packed_fp8_scale_bytes(G, N, K, panel_rows);
+}
+
 int moe_pack_weights_fp8(const uint16_t* src, int G, int N, int K, int panel_rows, uint8_t* dst,
-                         float* scales, void* stream) {
+                         uint8_t* scales, void* stream) {
     if (G < 1 || N < 1 || K < 64) return MOE_ERR_SHAPE;
     if (K % 64 || (panel_rows != 128 && panel_rows != 256)) return MOE_ERR_UNSUPPORTED;
     if (!src || !dst || !scales) return MOE_ERR_NULL;
-    if (!aligned16(src) || !aligned16(dst) || ((uintptr_t)scales & 3u)) return MOE_ERR_ALIGN;
+    if (!aligned16(src) || !aligned16(dst) || !aligned16(scales)) return MOE_ERR_ALIGN;
     return hip_status(
         launch_pack_weights_fp8(src, dst, scales, G, N, K, panel_rows, as_stream(stream)));
 }

@@ -70,8 +70,10 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 //            per wave; the waits count the instructions of later stages.
 //   KB = 64: 2 slots of 64 KB, 1 stage in flight while one computes; per
 //            stage 4 + 4 instructions per wave; every wait is vmcnt(0).
-//   WF = 1 (fp8 weights): the weight stage is half as many bytes (one 1 KB
-//            chunk per 32-row block per 32 columns of K), same slot count.
+//   WF = 1 (MXFP8 weights): the weight stage is half as many bytes (one 1 KB
+//            chunk per 32-row block per 32 columns of K) plus the 8 blocks'
+//            scale bytes (256 per 32 columns: one more DMA instruction for
+//            waves 0 .. KB/32 - 1), same slot count.
 template <int KB, int WF = 0>
 struct Stage {
     static_assert(KB == 32 || KB == 64, "stage width");
@@ -81,9 +83,11 @@ struct Stage {
     static constexpr int APW = TM / RPI / 8;               // activation instrs per wave (max)
     static constexpr int Q = KB / 16;                      // MFMA substeps per stage
     static constexpr int WI = WF ? KB / 32 : Q;            // weight instrs per wave (1 KB each)
+    // (waves w < WI also issue one scale instruction per stage)
     static constexpr int SLOTA = TM * ROWB;
     static constexpr int SLOTW = WBLK * WI * 1024;
-    static constexpr int SLOT = SLOTA + SLOTW;
+    static constexpr int SLOTS_B = WF ? WBLK * (KB / 32) * 32 : 0;   // MXFP8 scale bytes
+    static constexpr int SLOT = SLOTA + SLOTW + SLOTS_B;
     static constexpr int SLOTS = KB == 32 ? 4 : 2;
     static constexpr int AHEAD = SLOTS - 1;                // stages in flight
     static_assert(SLOTS * SLOT <= kRing, "ring");
@@ -126,6 +130,16 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_byte) {
                  : "memory", "m0");
 }
 
+// 4-byte direct-to-LDS copy: lane l's 4 bytes from gaddr go to LDS byte
+// lds_byte + 4 l (only the active lanes copy)
+__device__ __forceinline__ void dma4(const void* gaddr, uint32_t lds_byte) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_byte);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :
+                 : "s"(m0v), "v"(gaddr)
+                 : "memory", "m0");
+}
+
 // wait until at most N of this wave's memory operations are outstanding
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -134,11 +148,18 @@ __device__ __forceinline__ void wait_vm() {
 
 // wait for the oldest in-flight stage (AHEAD - 1 later stages of na + NW
 // instructions each may stay outstanding)
+// instructions per stage: na activation + NW weight (+ sc scale)
 template <int KB, int WF>
-__device__ __forceinline__ void wait_stage(int na) {
+__device__ __forceinline__ void wait_stage(int na, int sc) {
     constexpr int A1 = Stage<KB, WF>::AHEAD - 1, NW = Stage<KB, WF>::WI;
     if constexpr (A1 == 0) {
         wait_vm<0>();
+    } else if constexpr (WF) {
+        const int n = na + sc;
+        if (n == 3) wait_vm<A1 * (NW + 3)>();
+        else if (n == 2) wait_vm<A1 * (NW + 2)>();
+        else if (n == 1) wait_vm<A1 * (NW + 1)>();
+        else wait_vm<A1 * NW>();
     } else {
         if (na == 2) wait_vm<A1 * (NW + 2)>();
         else if (na == 1) wait_vm<A1 * (NW + 1)>();
@@ -164,8 +185,9 @@ struct LdsTile {
     const uint8_t* bsrc1;  // fp8 weights: up matrix (SwiGLU) or the same
     size_t pstride_b;      // fp8 weights: bytes per panel
     size_t wstride_b;      // fp8 weights: bytes per 64-wide K stage of one panel
-    const float* sc0;      // fp8 weights: row scales of this expert (gate / the one)
-    const float* sc1;      // fp8 weights: row scales of the up matrix (SwiGLU)
+    const uint8_t* ssrc0;  // fp8 weights: MX block scale bytes of this expert (gate / the one)
+    const uint8_t* ssrc1;  // fp8 weights: MX block scale bytes of the up matrix (SwiGLU)
+    size_t sstride;        // fp8 weights: scale bytes per panel
     int blk0;              // first 32-row block of this n-tile in each matrix
     int np;                // packed panels per matrix
     size_t pstride;        // packed elements per panel
@@ -220,6 +242,22 @@ __device__ __forceinline__ void issue_stage(const LdsTile& t, int j, uint32_t sb
                                  (gb % Pn::BPP) * 2048 + (c0 + i) * 1024 + t.lane * 16;
             dma16(src, base + St::SLOTA + (b * St::WI + i) * 1024);
         }
+        // scale bytes of MX block kb = j KB / 32 + w for all 8 weight blocks
+        // (wave w < WI): lanes 8 b' .. 8 b' + 7 copy the 32 rows of block b'
+        if (t.wave < St::WI) {
+            const int bs = t.lane >> 3;
+            const uint8_t* smat2 = t.ssrc0;
+            int gs = t.blk0 + bs;
+            if (EPI == EPI_SWIGLU_BF16 && bs >= Pn::BPM) {
+                smat2 = t.ssrc1;
+                gs -= Pn::BPM;
+            }
+            const int pans = min(gs / Pn::BPP, t.np - 1);
+            const int kb = (j * KB) / 32 + t.wave;
+            const uint8_t* ssrc = smat2 + (size_t)pans * t.sstride + (size_t)kb * Pn::P +
+                                  (gs % Pn::BPP) * 32 + (t.lane & 7) * 4;
+            dma4(ssrc, base + St::SLOTA + St::SLOTW + t.wave * 256);
+        }
         return;
     }
 #pragma unroll
@@ -247,14 +285,15 @@ struct Operands {
     bf16x8 w0, w1, a[NTB];
 };
 
-// eight E4M3 codes (bytes of v, in order) -> bf16x8: the hardware
-// conversion gives the exact fp32 values, whose upper halves are the exact
-// bf16 values (at most 4 significant bits)
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 v) {
-    const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[0], false);
-    const f32x2 f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[0], true);
-    const f32x2 f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[1], false);
-    const f32x2 f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[1], true);
+// eight E4M3 codes (bytes of v, in order) times the MX block scale sc (a
+// power of two in [2^-110, 2^110]) -> bf16x8: the hardware conversion gives
+// the exact fp32 products, whose upper halves are the exact bf16 values (at
+// most 4 significant bits, normal range)
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 v, float sc) {
+    const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[0], sc, false);
+    const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[0], sc, true);
+    const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[1], sc, false);
+    const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[1], sc, true);
     u32x4 r;
     r[0] = __builtin_amdgcn_perm(__float_as_uint(f0.y), __float_as_uint(f0.x), 0x07060302u);
     r[1] = __builtin_amdgcn_perm(__float_as_uint(f1.y), __float_as_uint(f1.x), 0x07060302u);
@@ -263,9 +302,11 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 v) {
     return __builtin_bit_cast(bf16x8, r);
 }
 
+// (msc: the MX block scales 2^X of this lane's two weight rows, read at even
+// substeps and reused at the odd one of the same 32-column MX block)
 template <int EPI, int KB, int NTB, int WF>
 __device__ __forceinline__ void read_operands(const LdsTile& t, uint32_t sbase, int q,
-                                              Operands<NTB>& o) {
+                                              Operands<NTB>& o, float (&msc)[2]) {
     using St = Stage<KB, WF>;
     const unsigned char* base = t.smem + sbase;
     // weight blocks of this wave (bf16: fragment slots Q b + substep; fp8:
@@ -274,8 +315,16 @@ __device__ __forceinline__ void read_operands(const LdsTile& t, uint32_t sbase, 
     const int b1 = (EPI == EPI_SWIGLU_BF16) ? Panel<EPI>::BPM + t.wn : 2 * t.wn + 1;
     if constexpr (WF) {
         const unsigned char* wbase = base + St::SLOTA + t.lane * 16 + (q & 1) * 8;
-        o.w0 = fp8x8_to_bf16x8(*(const u32x2*)(wbase + (b0 * St::WI + (q >> 1)) * 1024));
-        o.w1 = fp8x8_to_bf16x8(*(const u32x2*)(wbase + (b1 * St::WI + (q >> 1)) * 1024));
+        // scale byte X + 127 of this lane's row and MX block -> 2^X
+        // (scale region: [MX block of the stage][8 weight blocks][32 rows])
+        if ((q & 1) == 0) {
+            const unsigned char* sbase =
+                base + St::SLOTA + St::SLOTW + (q >> 1) * 256 + (t.lane & 31);
+            msc[0] = __uint_as_float((uint32_t)sbase[b0 * 32] << 23);
+            msc[1] = __uint_as_float((uint32_t)sbase[b1 * 32] << 23);
+        }
+        o.w0 = fp8x8_to_bf16x8(*(const u32x2*)(wbase + (b0 * St::WI + (q >> 1)) * 1024), msc[0]);
+        o.w1 = fp8x8_to_bf16x8(*(const u32x2*)(wbase + (b1 * St::WI + (q >> 1)) * 1024), msc[1]);
     } else {
         const unsigned char* wbase = base + St::SLOTA + t.lane * 16;
         o.w0 = *(const bf16x8*)(wbase + (b0 * St::Q + q) * 1024);
@@ -313,12 +362,6 @@ __device__ __forceinline__ void epilogue(const LdsTile& t, const f32x16 (&acc)[2
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
                 const int n = t.n0 + 8 * qq + 4 * t.half;
-                // fp8 weights: row scales 2^e of features n .. n+3 (exact products)
-                f32x4 sg = {1.0f, 1.0f, 1.0f, 1.0f}, su = sg;
-                if constexpr (WF) {
-                    sg = *(const f32x4*)(t.sc0 + n);
-                    su = *(const f32x4*)(t.sc1 + n);
-                }
                 uint32_t packed[2];
 #pragma unroll
                 for (int i = 0; i < 4; i += 2) {
@@ -327,10 +370,6 @@ __device__ __forceinline__ void epilogue(const LdsTile& t, const f32x16 (&acc)[2
                     for (int u = 0; u < 2; ++u) {
                         float gv = acc[0][tb][4 * qq + i + u];
                         float uv = acc[1][tb][4 * qq + i + u];
-                        if constexpr (WF) {
-                            gv = gv * sg[i + u];
-                            uv = uv * su[i + u];
-                        }
                         gv = args.clamp_mode == MOE_CLAMP_SYMMETRIC ? clamp_sym(gv, L)
                                                                     : fminf(gv, L);
                         uv = clamp_sym(uv, L);
@@ -352,11 +391,6 @@ __device__ __forceinline__ void epilogue(const LdsTile& t, const f32x16 (&acc)[2
                     f32x4 v;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[i] = acc[b][tb][4 * qq + i];
-                    if constexpr (WF) {
-                        const f32x4 sc = *(const f32x4*)(t.sc0 + n);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) v[i] = v[i] * sc[i];
-                    }
                     *(f32x4*)(orow + n) = v;
                 }
         }
@@ -393,8 +427,9 @@ __device__ __forceinline__ void run_tile(const LdsTile& t) {
     for (int p = 0; p < St::AHEAD; ++p) issue_stage<EPI, KB, WF>(t, min(p, S - 1), p * St::SLOT);
     uint32_t s_cmp = 0, s_iss = St::AHEAD * St::SLOT;
     Operands<NTB> o[2];
+    float msc[2] = {1.0f, 1.0f};
     for (int j = 0; j < S; ++j) {
-        wait_stage<KB, WF>(t.na);
+        wait_stage<KB, WF>(t.na, WF && t.wave < St::WI ? 1 : 0);
         __syncthreads();
         // (one stage in flight: every wait is vmcnt(0), nothing to re-issue)
         if (St::AHEAD > 1 || j + 1 < S)
@@ -403,7 +438,7 @@ __device__ __forceinline__ void run_tile(const LdsTile& t) {
         if constexpr (NTB > 0) {
 #pragma unroll
             for (int q = 0; q < St::Q; ++q) {
-                read_operands<EPI, KB, NTB, WF>(t, s_cmp, q, o[q & 1]);
+                read_operands<EPI, KB, NTB, WF>(t, s_cmp, q, o[q & 1], msc);
                 __builtin_amdgcn_sched_barrier(0);
                 if (q > 0 || j > 0) mfma_substep<NTB>(o[(q + 1) & 1], acc);
                 __builtin_amdgcn_sched_barrier(0);
@@ -485,8 +520,9 @@ __device__ __forceinline__ void do_tile(LdsTile& t, const GemmArgs& args, int g,
         t.bsrc1 = (const uint8_t*)(EPI == EPI_SWIGLU_BF16 ? args.w2 : args.w1) + ebase_b;
         t.pstride_b = (size_t)Pn::P * t.K;
         t.wstride_b = (size_t)Pn::BPP * 2048;
-        t.sc0 = args.s1 + (size_t)g * N;
-        t.sc1 = (EPI == EPI_SWIGLU_BF16 ? args.s2 : args.s1) + (size_t)g * N;
+        t.sstride = (size_t)(t.K / 32) * Pn::P;
+        t.ssrc0 = args.s1 + (size_t)g * t.np * t.sstride;
+        t.ssrc1 = (EPI == EPI_SWIGLU_BF16 ? args.s2 : args.s1) + (size_t)g * t.np * t.sstride;
     }
     t.n0 = n_tile * Pn::TN + t.wn * ((EPI == EPI_SWIGLU_BF16) ? 32 : 64);
     // the valid rows split evenly (in 32-row blocks) over the two wave halves

@@ -59,10 +59,10 @@ struct GemmArgs {
     int out_blocked;          // SWIGLU out in the blocked activation layout
     uint32_t* sched;          // LDS kernel: 8 per-XCD item counters, 128 B apart,
                               // zero at launch (NULL: static schedule)
-    int wfp8;                 // LDS kernel: w1 / w2 hold E4M3 codes in the fp8 packed
-                              // layout (moe_pack_weights_fp8), scaled per row by s1 / s2
-    const float* s1;          // [G, N] fp32 row scales of w1 (fp8 weights)
-    const float* s2;          // [G, N] fp32 row scales of w2 (fp8 weights, SWIGLU)
+    int wfp8;                 // LDS kernel: w1 / w2 hold MXFP8 codes in the fp8 packed
+                              // layout (moe_pack_weights_fp8), block scales in s1 / s2
+    const uint8_t* s1;        // MXFP8 block scale bytes of w1
+    const uint8_t* s2;        // MXFP8 block scale bytes of w2 (SWIGLU)
 };
 // per-launch scheduling counters of the LDS-staged expert GEMM
 constexpr int kSchedWords = 8 * 32;
@@ -90,10 +90,11 @@ size_t packed_weight_elems(int G, int N, int K, int P);
 hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int G, int N, int K, int P,
                                hipStream_t stream);
 
-// fp8 expert weights (E4M3 codes, one power-of-two scale per row)
+// MXFP8 expert weights (E4M3 codes, one power-of-two scale per 32 values of K)
 size_t packed_fp8_weight_bytes(int G, int N, int K, int P);
-hipError_t launch_pack_weights_fp8(const uint16_t* src, uint8_t* dst, float* scales, int G, int N,
-                                   int K, int P, hipStream_t stream);
+size_t packed_fp8_scale_bytes(int G, int N, int K, int P);
+hipError_t launch_pack_weights_fp8(const uint16_t* src, uint8_t* dst, uint8_t* scales, int G,
+                                   int N, int K, int P, hipStream_t stream);
 
 hipError_t launch_route(const float* logits, const float* bias, const uint8_t* modality,
                         const int32_t* input_ids, const int32_t* tid2eid, int T, int E, int k,

@@ -1,23 +1,26 @@
-// One-time quantisation of bf16 expert weights to 8-bit floats for the fp8
-// weight mode of the expert GEMMs.
+// One-time quantisation of bf16 expert weights to MXFP8 for the fp8 weight
+// mode of the expert GEMMs.
 //
-// The pages name FP8 expert weights as the low-precision direction
-// ("Twinkle x Ascend ... DeepSeek-V4 training": MXFP8 / MXFP4 in the
-// functional-expansion section, FP4/FP8 checkpoints in the quick start) but
-// fix no encoding.  Encoding used: OCP E4M3 (bias 7, subnormals, no
-// infinities, largest finite 448) with one power-of-two scale per output
-// row: e = the smallest integer with max_k |W[n,k]| <= 448 * 2^e (0 for a
-// zero row, clamped to [-110, 110]); q = E4M3(W / 2^e), round to nearest
-// even, saturating at +-448.  The dequantised weight E4M3(q) * 2^e is
-// exactly a bf16 value, so the GEMM multiplies the bf16 activations by the
-// decoded codes and applies 2^e to the fp32 accumulator (exact).
+// The pages name MXFP8 / MXFP4 weights as the low-precision direction
+// ("Twinkle x Ascend ... DeepSeek-V4 training": functional-expansion
+// section; FP4/FP8 checkpoints in the quick start).  MXFP8 (OCP
+// Microscaling): blocks of 32 values along K share one power-of-two scale,
+// each value an OCP E4M3 float (bias 7, subnormals, no infinities, largest
+// finite 448).  Scale rule of the OCP specification: X = floor(log2(block
+// max |v|)) - 8, clamped here to [-110, 110] (0 for an all-zero block);
+// q = E4M3(v / 2^X), round to nearest even, saturating at +-448.  The
+// dequantised value E4M3(q) * 2^X is exactly a bf16 value; the GEMM decodes
+// codes and scale together (v_cvt_scalef32_pk_f32_fp8, exact for these
+// scales) into the bf16 operands of the matrix cores.
 //
 // Layout of the codes (per matrix, panels of P rows, K multiple of 64):
 //   [G][ceil(N/P)][K/64][P/32][2][64 lanes][16 bytes]; chunk c of 32-row
 //   block b, lane l holds row panel*P + b*32 + l%32, columns
 //   64 s + 32 c + 8 (l/32) + {0..7} (bytes 0-7) and the same + 16 (bytes
 //   8-15): the operand fragments of the two 16-wide MFMA substeps of that
-//   32-wide K slice.  Rows >= N are zero codes.  Scales: fp32 2^e, [G, N].
+//   32-wide K slice, which is one MX block.  Rows >= N are zero codes.
+// Scales: one byte X + 127 per (row, block), [G][ceil(N/P)][K/32][P/32][32]:
+//   the 32 rows of one 32-row weight block for one K block are contiguous.
 #include "moe_internal.h"
 
 namespace moe {
@@ -47,44 +50,13 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
     return sign | ((uint32_t)(E + 7) << 3) | r;
 }
 
-// one wave per row: amax -> e -> scales[row] = 2^e
-__global__ __launch_bounds__(256) void fp8_row_scale_kernel(const uint16_t* __restrict__ src,
-                                                            long long rows, int K,
-                                                            float* __restrict__ scales) {
-    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (row >= rows) return;
-    const u32x4* p = (const u32x4*)(src + row * K);
-    float amax = 0.0f;
-    for (int v = lane; v < K / 8; v += 64) {
-        const u32x4 w = p[v];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
-            amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xffff0000u)));
-        }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-    if (lane != 0) return;
-    int e = 0;
-    if (amax > 0.0f) {
-        // 2^(x-1) <= amax < 2^x, then the smallest e with amax <= 448 * 2^e
-        int x = (int)((__float_as_uint(amax) >> 23) & 0xff) - 126;
-        if ((__float_as_uint(amax) >> 23) == 0) x = -125;   // (bf16 subnormal amax)
-        e = x - 9;
-        while (e < kMaxExp && amax > __builtin_ldexpf(kE4M3Max, e)) ++e;
-        while (e > -kMaxExp && amax <= __builtin_ldexpf(kE4M3Max, e - 1)) --e;
-        e = min(max(e, -kMaxExp), kMaxExp);
-    }
-    scales[row] = __builtin_ldexpf(1.0f, e);
-}
-
-// one thread per 16-byte chunk of the packed codes
-__global__ __launch_bounds__(256) void fp8_pack_kernel(const uint16_t* __restrict__ src,
-                                                       const float* __restrict__ scales,
-                                                       uint8_t* __restrict__ dst, int N, int K,
-                                                       int P, long long nchunks) {
+// One thread per 16-byte chunk of codes (16 values of one MX block of one
+// row): block exponent from all 32 values of the block, then its 16 codes;
+// the lane holding columns 0-7 of the block also writes the scale byte.
+__global__ __launch_bounds__(256) void mxfp8_pack_kernel(const uint16_t* __restrict__ src,
+                                                         uint8_t* __restrict__ dst,
+                                                         uint8_t* __restrict__ scales, int N,
+                                                         int K, int P, long long nchunks) {
     const long long f = (long long)blockIdx.x * 256 + threadIdx.x;
     if (f >= nchunks) return;
     const int lane = (int)(f & 63);
@@ -100,12 +72,29 @@ __global__ __launch_bounds__(256) void fp8_pack_kernel(const uint16_t* __restric
     const int panel = (int)(r % np);
     const long long g = r / np;
     const int row = panel * P + b * 32 + (lane & 31);
+    const int kb = 2 * s + c;                             // MX block (32 columns)
     u32x4 out = {0u, 0u, 0u, 0u};
+    int X = 0;
     if (row < N) {
-        const long long grow = g * N + row;
-        const float inv = 1.0f / scales[grow];            // exact: a power of two
-        const int col = s * 64 + 32 * c + 8 * (lane >> 5);
-        const uint16_t* rp = src + grow * K + col;
+        const uint16_t* bp = src + (g * N + row) * (long long)K + 32 * kb;
+        float amax = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const u32x4 w = *(const u32x4*)(bp + 8 * v);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
+                amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xffff0000u)));
+            }
+        }
+        if (amax > 0.0f) {
+            // floor(log2(amax)) from the exponent field (subnormal amax is
+            // below 2^-126 and clamps to -110 anyway)
+            const int e = (int)((__float_as_uint(amax) >> 23) & 0xff) - 127;
+            X = min(max(e - 8, -kMaxExp), kMaxExp);
+        }
+        const float inv = __builtin_ldexpf(1.0f, -X);   // exact power of two
+        const uint16_t* rp = bp + 8 * (lane >> 5);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const u32x4 w = *(const u32x4*)(rp + 16 * h);
@@ -113,13 +102,15 @@ __global__ __launch_bounds__(256) void fp8_pack_kernel(const uint16_t* __restric
             for (int i = 0; i < 4; ++i) {
                 const uint32_t lo = e4m3_rne(__uint_as_float(w[i] << 16) * inv);
                 const uint32_t hi = e4m3_rne(__uint_as_float(w[i] & 0xffff0000u) * inv);
-                const uint32_t pair = lo | (hi << 8);
-                const int byte = 8 * h + 2 * i;           // element 2i, 2i+1 of half h
-                out[byte >> 2] |= pair << (8 * (byte & 3));
+                const int byte = 8 * h + 2 * i;           // elements 2i, 2i+1 of half h
+                out[byte >> 2] |= (lo | (hi << 8)) << (8 * (byte & 3));
             }
         }
     }
     *(u32x4*)(dst + f * 16) = out;
+    if (lane < 32)
+        scales[((g * np + panel) * (K / 32) + kb) * (long long)P + b * 32 + lane] =
+            (uint8_t)(X + 127);
 }
 
 }  // namespace
@@ -128,15 +119,16 @@ size_t packed_fp8_weight_bytes(int G, int N, int K, int P) {
     return (size_t)G * (size_t)((N + P - 1) / P) * P * (size_t)K;
 }
 
-hipError_t launch_pack_weights_fp8(const uint16_t* src, uint8_t* dst, float* scales, int G, int N,
-                                   int K, int P, hipStream_t stream) {
-    const long long rows = (long long)G * N;
-    if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(fp8_row_scale_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
-                       src, rows, K, scales);
+size_t packed_fp8_scale_bytes(int G, int N, int K, int P) {
+    return packed_fp8_weight_bytes(G, N, K, P) / 32;
+}
+
+hipError_t launch_pack_weights_fp8(const uint16_t* src, uint8_t* dst, uint8_t* scales, int G,
+                                   int N, int K, int P, hipStream_t stream) {
     const long long nchunks = (long long)packed_fp8_weight_bytes(G, N, K, P) / 16;
-    hipLaunchKernelGGL(fp8_pack_kernel, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0,
-                       stream, src, scales, dst, N, K, P, nchunks);
+    if (nchunks == 0) return hipSuccess;
+    hipLaunchKernelGGL(mxfp8_pack_kernel, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0,
+                       stream, src, dst, scales, N, K, P, nchunks);
     return hipGetLastError();
 }
 

@@ -87,6 +87,8 @@ def lib():
     L.moe_pack_weights.argtypes = [P, I, I, I, I, P, P]
     L.moe_packed_fp8_weight_bytes.argtypes = [I, I, I, I]
     L.moe_packed_fp8_weight_bytes.restype = S
+    L.moe_packed_fp8_scale_bytes.argtypes = [I, I, I, I]
+    L.moe_packed_fp8_scale_bytes.restype = S
     L.moe_pack_weights_fp8.argtypes = [P, I, I, I, I, P, P, P]
     L.moe_forward_workspace_size.argtypes = [ctypes.POINTER(MoeCfg)]
     L.moe_forward_workspace_size.restype = S
@@ -278,9 +280,9 @@ def pack_weights(w, panel_rows):
 
 
 def pack_weights_fp8(w, panel_rows):
-    """fp8 copy (moe_pack_weights_fp8: E4M3 codes in the packed layout, one
-    power-of-two scale per row) of bf16 weights [G,N,K] or [N,K]; returns
-    (codes uint8 tensor, scales fp32 tensor [G*N])."""
+    """MXFP8 copy (moe_pack_weights_fp8: E4M3 codes in the packed layout, one
+    power-of-two scale per 32 values of K) of bf16 weights [G,N,K] or [N,K];
+    returns (codes uint8 tensor, scale bytes uint8 tensor)."""
     _need(w, torch.bfloat16, "w")
     shape = tuple(w.shape)
     G, N, K = (1,) + shape if w.dim() == 2 else shape
@@ -288,7 +290,8 @@ def pack_weights_fp8(w, panel_rows):
     if nbytes == 0:
         raise MoeError(f"cannot pack weights of shape {shape} in panels of {panel_rows}")
     codes = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
-    scales = torch.empty(G * N, dtype=torch.float32, device=w.device)
+    scales = torch.empty(int(lib().moe_packed_fp8_scale_bytes(G, N, K, panel_rows)),
+                         dtype=torch.uint8, device=w.device)
     _check(lib().moe_pack_weights_fp8(_ptr(w), G, N, K, panel_rows, _ptr(codes), _ptr(scales),
                                       _stream()), "moe_pack_weights_fp8")
     return codes, scales
@@ -317,7 +320,7 @@ class MoeLayer:
         fp8 = packed == "fp8"
         if packed:
             # one-time layout change at load time (moe_pack_weights; with
-            # packed="fp8" the routed expert matrices are quantised to E4M3
+            # packed="fp8" the routed expert matrices are quantised to MXFP8
             # by moe_pack_weights_fp8 instead)
             for key in MATRIX_NAMES:
                 if self.weights.get(key) is None:

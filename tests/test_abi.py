@@ -111,6 +111,7 @@ def test_pack_validation(L):
     assert L.moe_pack_weights(FAKE, 1, 8, 128, 256, FAKE + 2, None) == ERR_ALIGN
     assert L.moe_packed_fp8_weight_bytes(2, 100, 128, 128) == 2 * 128 * 128
     assert L.moe_packed_fp8_weight_bytes(1, 8, 100, 128) == 0
+    assert L.moe_packed_fp8_scale_bytes(2, 100, 128, 128) == 2 * 128 * 128 // 32
     assert L.moe_pack_weights_fp8(FAKE, 1, 8, 100, 128, FAKE, FAKE, None) == ERR_UNSUPPORTED
     assert L.moe_pack_weights_fp8(FAKE, 0, 8, 128, 128, FAKE, FAKE, None) == ERR_SHAPE
     assert L.moe_pack_weights_fp8(FAKE, 1, 8, 128, 128, FAKE, None, None) == ERR_NULL

@@ -113,7 +113,7 @@ def test_full_size(cfg):
 
 
 def test_full_size_fp8():
-    """The fp8 routed-weight mode at the 384-expert workload's full size, in
+    """The MXFP8 routed-weight mode at the 384-expert workload's full size, in
     the benchmark's launch configuration (--weights fp8): routes bit-exact,
     and sampled tokens within 1e-2 x RMS of the oracle run on the oracle's
     own dequantisation of the fp8 weights of the experts those tokens use."""
@@ -137,8 +137,8 @@ def test_full_size_fp8():
     for key in ("w_gate", "w_up", "w_down"):
         m = bits(inp[key])
         for e in experts:
-            q, ex = oracle.quant_fp8_rows(m[e])
-            m[e] = oracle.dequant_fp8_rows(q, ex)
+            q, ex = oracle.quant_mxfp8(m[e])
+            m[e] = oracle.dequant_mxfp8(q, ex)
         mats[key] = m
     shared = [bits(inp[k]) for k in ("s_gate", "s_up", "s_down")]
     yref = oracle.tokens_forward(bits(inp["x"]), toks, rid, rw, mats["w_gate"], mats["w_up"],

@@ -1,15 +1,16 @@
-"""GPU parity of the fp8 routed-expert weight mode (E4M3 codes, one
-power-of-two scale per output row; moe_pack_weights_fp8 + moe_forward with
-packed = MOE_WEIGHTS_FP8) against the oracle:
+"""GPU parity of the MXFP8 routed-expert weight mode (E4M3 codes, one
+power-of-two scale per 32 values of K; moe_pack_weights_fp8 + moe_forward
+with packed = MOE_WEIGHTS_FP8) against the oracle:
 
-  - quantisation: codes and scales bit-exact against the oracle's row
-    quantiser, on random rows plus zero, huge, tiny and tie rows, every code
-    at its place in the packed layout and padding rows zero;
+  - quantisation: codes and block scales bit-exact against the oracle's MX
+    quantiser, on random rows plus zero, huge, tiny, saturating and tie
+    blocks, every code and scale at its place in the packed layout and
+    padding rows zero;
   - forward: routes bit-exact and y within 1e-2 x RMS of the oracle run on
     the dequantised weights (exact bf16 values);
   - the fp8 forward is bit-equal to the bf16 packed forward on the
-    dequantised weights (the row scale is a power of two, so scaling the
-    fp32 accumulator commutes with every rounding of the sum).
+    dequantised weights (codes and scale decode exactly to those bf16
+    values, and the MFMA chain is the same).
 """
 import numpy as np
 import pytest
@@ -33,12 +34,23 @@ def unpack_codes(codes, G, N, K, P):
     return a.reshape(G, npan * P, K)
 
 
+def unpack_scales(scales, G, N, K, P):
+    """[G][ceil(N/P)][K/32][P/32][32] scale bytes -> block exponents X
+    [G, ceil(N/P)*P, K/32]."""
+    npan = (N + P - 1) // P
+    a = scales.reshape(G, npan, K // 32, P // 32, 32).transpose(0, 1, 3, 4, 2)
+    return a.reshape(G, npan * P, K // 32).astype(np.int32) - 127
+
+
 def weights_with_special_rows(G, N, K, seed):
     rng = np.random.default_rng(seed)
     w = (rng.standard_normal((G, N, K)) / np.sqrt(K)).astype(np.float32)
     w[0, 0] = 0.0                                     # zero row
     w[0, 1] *= 2.0 ** 40                              # huge row
     w[0, 2] *= 2.0 ** -60                             # tiny row (subnormal codes)
+    w[0, 3] *= 2.0 ** -115                            # exponent clamped at -110
+    w[0, 4, :32] = 500.0                              # saturating block
+    w[0, 4, 5] = 1.0
     # ties: consecutive E4M3 values and their midpoints, scaled by 2^-5,
     # with the row maximum exactly 448 * 2^-5
     vals = sorted({oracle.e4m3_decode(c) for c in range(0x7F)})
@@ -58,11 +70,12 @@ def test_pack_weights_fp8(G, N, K, P):
     w = torch.from_numpy(wb.view(np.int16)).to(DEV).view(torch.bfloat16)
     codes, scales = ops.pack_weights_fp8(w, P)
     torch.cuda.synchronize()
-    q_ref, e_ref = oracle.quant_fp8_rows(wb.reshape(G * N, K))
+    q_ref, x_ref = oracle.quant_mxfp8(wb.reshape(G * N, K))
     got = unpack_codes(host(codes), G, N, K, P)
     assert np.array_equal(got[:, :N].reshape(G * N, K), q_ref)
     assert not got[:, N:].any()
-    assert np.array_equal(host(scales), np.ldexp(np.float32(1.0), e_ref))
+    xs = unpack_scales(host(scales), G, N, K, P)
+    assert np.array_equal(xs[:, :N].reshape(G * N, K // 32), x_ref)
 
 
 FP8_CASES = [
@@ -82,8 +95,8 @@ def _dequantised(inp):
     out = dict(inp)
     for key in ("w_gate", "w_up", "w_down"):
         wb = bits(inp[key])
-        q, e = oracle.quant_fp8_rows(wb.reshape(-1, wb.shape[-1]))
-        deq = oracle.dequant_fp8_rows(q, e).reshape(wb.shape)
+        q, x = oracle.quant_mxfp8(wb.reshape(-1, wb.shape[-1]))
+        deq = oracle.dequant_mxfp8(q, x).reshape(wb.shape)
         out[key] = torch.from_numpy(deq.view(np.int16)).to(DEV).view(torch.bfloat16)
     return out
 

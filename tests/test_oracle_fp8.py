@@ -1,11 +1,13 @@
-"""Pins of the oracle's fp8 expert-weight encoding (OCP 8-bit floating point,
-E4M3 with bias 7, subnormals, no infinities, largest finite 448; one
-power-of-two scale per output row - the reading of the pages' FP8 weights).
+"""Pins of the oracle's fp8 expert-weight encoding: OCP MXFP8 (blocks of 32
+values along K sharing one power-of-two scale X = floor(log2 amax) - 8,
+elements OCP 8-bit floats E4M3: bias 7, subnormals, no infinities, largest
+finite 448, saturating), the format the pages' "MxFP8" names.
 
 External anchors: torch's float8_e4m3fn dtype, an independent library
-implementation of the same OCP format (decode of every code, and the
-round-to-nearest-even cast of values inside the finite range), plus the
-format's fixed points (1.0, 448, the smallest normal and subnormal values).
+implementation of the same OCP element format (decode of every code, and the
+round-to-nearest-even cast of values inside the finite range), numpy's frexp
+for the block exponent, plus the format's fixed points (1.0, 448, the
+smallest normal and subnormal values).
 """
 import math
 
@@ -76,28 +78,37 @@ def test_encode_matches_library_cast():
 
 
 @pytest.mark.parametrize("K", [64, 2048])
-def test_row_quantisation(K):
+def test_mx_block_quantisation(K):
     rng = np.random.default_rng(K)
-    w = (rng.standard_normal((40, K)) / np.sqrt(K)).astype(np.float32)
-    w[3] = 0.0                                        # all-zero row
+    R = 40
+    w = (rng.standard_normal((R, K)) / np.sqrt(K)).astype(np.float32)
+    w[3, :32] = 0.0                                   # all-zero block
     w[5] *= 2.0 ** 20                                 # large row
-    w[6, :] = w[6, :] * 2.0 ** -30                    # tiny row (subnormal codes)
+    w[6] *= 2.0 ** -110                               # tiny row: exponent clamped at -110
+    w[7, :32] = 500.0 * 2.0 ** -4                     # saturating block: amax / 2^X = 500 > 448
+    w[7, 1] = 1.0 * 2.0 ** -4
     wb = (w.view(np.uint32) >> 16).astype(np.uint16)  # bf16 (truncated) bits
     wf = (wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    q, e = oracle.quant_fp8_rows(wb)
-    amax = np.abs(wf).max(axis=1)
-    for r in range(w.shape[0]):
-        if amax[r] == 0:
-            assert e[r] == 0 and not q[r].any()
-            continue
-        # the smallest e with amax <= 448 * 2^e
-        assert amax[r] <= 448 * 2.0 ** e[r] < 2 * amax[r]
-        # codes are the library's RNE cast of w / 2^e
-        assert np.array_equal(q[r], torch_encode(wf[r] / 2.0 ** e[r]))
-    deq = oracle.dequant_fp8_rows(q, e)
+    q, x = oracle.quant_mxfp8(wb)
+    assert x.shape == (R, K // 32)
+    blocks = wf.reshape(R, K // 32, 32)
+    amax = np.abs(blocks).max(axis=2)
+    _, ex = np.frexp(amax)                            # amax = f * 2^ex, f in [0.5, 1)
+    want_x = np.where(amax > 0, np.clip(ex - 1 - 8, -110, 110), 0)
+    assert np.array_equal(x, want_x)
+    assert x[6].max() == -110 and x[3, 0] == 0
+    # codes: the library's RNE cast of v / 2^X after saturation to +-448
+    scaled = np.clip(blocks / 2.0 ** x[:, :, None], -448, 448).reshape(R, K)
+    assert np.array_equal(q, torch_encode(scaled).reshape(R, K))
+    assert q[7, 0] == 0x7E                            # saturated to 448
+    deq = oracle.dequant_mxfp8(q, x)
     dv = (deq.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    # dequantised weights are exactly decode(q) * 2^e (bf16-exact)
-    assert np.array_equal(dv, torch_decode(q.ravel()).reshape(q.shape) * 2.0 ** e[:, None])
-    # error: half an E4M3 ulp (relative 2^-4 in the normal range, 2^-10 * 2^e below)
-    bound = np.maximum(np.abs(wf) * 2.0 ** -4, 2.0 ** (e[:, None] - 10.0))
-    assert np.all(np.abs(dv - wf) <= bound)
+    scale = np.repeat(2.0 ** x, 32, axis=1)
+    # dequantised weights are exactly decode(q) * 2^X (bf16-exact)
+    assert np.array_equal(dv, torch_decode(q.ravel()).reshape(R, K) * scale)
+    # error: half an E4M3 ulp (relative 2^-4 normal, 2^-10 * 2^X subnormal)
+    # unless saturated (|v| / 2^X in (448, 512))
+    sat = np.abs(wf) / scale > 448
+    bound = np.maximum(np.abs(wf) * 2.0 ** -4, scale * 2.0 ** -10)
+    assert np.all((np.abs(dv - wf) <= bound) | sat)
+    assert np.all(np.abs(dv[sat]) == 448 * scale[sat])
