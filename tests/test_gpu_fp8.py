@@ -127,3 +127,40 @@ def test_forward_fp8(w):
     assert np.array_equal(host(ids), ref["ids"])
     assert np.array_equal(host(wts).view(np.uint32), ref["w"].view(np.uint32))
     check_rms(host(y), ref["y"])
+
+
+# expert row counts at every tile-shape boundary of the expert GEMM (empty,
+# single rows, 16-row DMA groups, 128 / 192 / 256-row tiles and one row past
+# each: both stage widths, multi-tile experts)
+EXACT_COUNTS = [0, 1, 16, 17, 127, 128, 129, 191, 192, 193, 255, 256, 257, 384, 385, 512, 513,
+                700]
+
+
+@pytest.mark.parametrize("d,F,k", [(128, 64, 2), (256, 192, 4)])
+def test_forward_fp8_exact_group_sizes(d, F, k):
+    slots = np.repeat(np.arange(len(EXACT_COUNTS), dtype=np.int32), EXACT_COUNTS)
+    T = len(slots) // k
+    table = np.ascontiguousarray(slots.reshape(k, T).T)
+    w = wl.small(T=T, d=d, E=len(EXACT_COUNTS), k=k, F=F, seed=30 + k, scale=2.5,
+                 mode=wl.MODE_HASH, V=T)
+    inp = wl.make_inputs(w, DEV)
+    inp["input_ids"] = torch.arange(T, dtype=torch.int32, device=DEV)
+    inp["tid2eid"] = torch.from_numpy(table).to(DEV)
+    deq = _dequantised(inp)
+    layer = ops.MoeLayer.from_workload(w, inp, out_dtype=ops.OUT_F32, packed="fp8")
+    ids = torch.empty((w.T, w.k), dtype=torch.int32, device=DEV)
+    logits = torch.empty((w.T, w.E), dtype=torch.float32, device=DEV)
+    wts = torch.empty((w.T, w.k), dtype=torch.float32, device=DEV)
+    y = layer.forward(inp["x"], input_ids=inp["input_ids"], logits=logits, ids=ids, w=wts)
+    ref_layer = ops.MoeLayer.from_workload(w, deq, out_dtype=ops.OUT_F32, packed=True)
+    y_deq = ref_layer.forward(inp["x"], input_ids=inp["input_ids"])
+    torch.cuda.synchronize()
+    assert np.array_equal(np.bincount(host(ids).ravel(), minlength=w.E), EXACT_COUNTS)
+    assert torch.equal(y.view(torch.int32), y_deq.view(torch.int32))
+    shared = [bits(inp[k]) for k in ("s_gate", "s_up", "s_down")]
+    ref = oracle.forward(bits(inp["x"]), host(logits), w.k, w.scale, bits(deq["w_gate"]),
+                         bits(deq["w_up"]), bits(deq["w_down"]), *shared, w.clamp_limit,
+                         w.clamp_mode, input_ids=host(inp["input_ids"]), tid2eid=table,
+                         mode=w.mode)
+    assert np.array_equal(host(ids), ref["ids"])
+    check_rms(host(y), ref["y"])
