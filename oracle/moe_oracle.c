@@ -37,7 +37,9 @@
  * sigmoid ratio; the permutation against a library stable argsort and its
  * invariants; the FFN against a numpy fp64 dense FFN and the clamp's closed
  * form; the combine against the dense reductions (single forced expert,
- * identical experts, scale 0).
+ * identical experts, scale 0); the MXFP8 encoding against torch's
+ * float8_e4m3fn (every code, RNE casts, saturated block codes) and numpy's
+ * frexp for the block exponent.
  */
 #include <math.h>
 #include <stdint.h>
