@@ -81,6 +81,10 @@ __host__ __device__ __forceinline__ size_t blocked_index(size_t r, size_t c, siz
 inline size_t blocked_rows(size_t rows) { return (rows + 15) & ~size_t(15); }
 
 hipError_t launch_grouped_gemm(int epilogue, const GemmArgs& g, hipStream_t stream);
+// Router projection on packed router weights (panel_rows 256): logits[T,E] =
+// x W_g^T (+ offset), every output accumulated like the grouped GEMM's.
+hipError_t launch_router_packed(const uint16_t* x, const uint16_t* wg_packed, const float* offset,
+                                int T, int K, int E, float* logits, hipStream_t stream);
 // Expert GEMMs on packed weights (EPI_SWIGLU_BF16 with 128-row panels,
 // EPI_F32 with 256-row panels): tiles staged in LDS by DMA.  Takes
 // G <= grouped_gemm_lds_max_groups().
