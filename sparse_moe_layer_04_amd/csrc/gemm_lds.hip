@@ -62,7 +62,7 @@ constexpr int kStaticLds = 256;              // reserve for static LDS (scan_sh,
 // the others the 32-wide ones (memory-bound: deeper lookahead)
 constexpr int kWideStageRows = 192;
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Pipeline of one stage width KB (32 or 64 columns of K per stage).
 //   KB = 32: 4 slots of 32 KB (16 KB activations + 16 KB weights), 3 stages
@@ -286,24 +286,23 @@ struct Operands {
 };
 
 // eight E4M3 codes (bytes of v, in order) times the MX block scale sc (a
-// power of two in [2^-110, 2^110]) -> bf16x8: the hardware conversion gives
-// the exact fp32 products, whose upper halves are the exact bf16 values (at
-// most 4 significant bits, normal range)
+// power of two in [2^-110, 2^110]) -> bf16x8.  The products have at most 4
+// significant bits and a normal exponent, so the conversion is exact (on
+// MI355X it gives the upper halves of the exact fp32 products, checked for
+// every code and scales 2^-110 .. 2^110).
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 v, float sc) {
-    const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[0], sc, false);
-    const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[0], sc, true);
-    const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[1], sc, false);
-    const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[1], sc, true);
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], sc, false);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], sc, true);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], sc, false);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], sc, true);
     u32x4 r;
-    r[0] = __builtin_amdgcn_perm(__float_as_uint(f0.y), __float_as_uint(f0.x), 0x07060302u);
-    r[1] = __builtin_amdgcn_perm(__float_as_uint(f1.y), __float_as_uint(f1.x), 0x07060302u);
-    r[2] = __builtin_amdgcn_perm(__float_as_uint(f2.y), __float_as_uint(f2.x), 0x07060302u);
-    r[3] = __builtin_amdgcn_perm(__float_as_uint(f3.y), __float_as_uint(f3.x), 0x07060302u);
+    r[0] = __builtin_bit_cast(uint32_t, p0);
+    r[1] = __builtin_bit_cast(uint32_t, p1);
+    r[2] = __builtin_bit_cast(uint32_t, p2);
+    r[3] = __builtin_bit_cast(uint32_t, p3);
     return __builtin_bit_cast(bf16x8, r);
 }
 
-// (msc: the MX block scales 2^X of this lane's two weight rows, read at even
-// substeps and reused at the odd one of the same 32-column MX block)
 template <int EPI, int KB, int NTB, int WF>
 __device__ __forceinline__ void read_operands(const LdsTile& t, uint32_t sbase, int q,
                                               Operands<NTB>& o, float (&msc)[2]) {
