@@ -219,7 +219,8 @@ def test_pack_weights_layout(G, N, K, P):
 
 
 @pytest.mark.parametrize("E,d,T,offset", [(8, 128, 70, False), (384, 256, 300, True),
-                                          (5, 64, 33, True)])
+                                          (5, 64, 33, True), (1000, 128, 200, True),
+                                          (1024, 64, 129, False), (97, 192, 1, True)])
 def test_gate_logits_packed_matches_plain(E, d, T, offset):
     # the router projection through moe_forward with packed weights equals the
     # plain-layout call (same kernel arithmetic, only the weight layout differs)
