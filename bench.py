@@ -56,7 +56,7 @@ def stage_work(w, n_nonempty, out_bytes=2, wbytes=2):
 # source files that define each stage's kernels: a recorded counter value
 # stays valid only while these are unchanged
 STAGE_SOURCES = {
-    "router_gemm": ("gemm.hip", "moe_internal.h"),
+    "router_gemm": ("router.hip", "moe_internal.h"),
     "route": ("route.hip", "moe_internal.h"),
     "permute": ("permute.hip", "moe_internal.h"),
     "gate_up_routed": ("gemm_lds.hip", "moe_internal.h"),
