@@ -410,7 +410,8 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     gl.packed = wpk;
     gl.offset = w->logit_offset;
     gl.out = logits;
-    if (wpk) e = launch_router_packed(x, w->w_g, w->logit_offset, T, d, E, logits, s);
+    if (wpk && router_packed_preferred(T, E))
+        e = launch_router_packed(x, w->w_g, w->logit_offset, T, d, E, logits, s);
     else e = launch_grouped_gemm(EPI_F32_OFFSET, gl, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (!mark(1)) return MOE_ERR_HIP;

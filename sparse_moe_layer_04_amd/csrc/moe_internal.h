@@ -85,6 +85,8 @@ hipError_t launch_grouped_gemm(int epilogue, const GemmArgs& g, hipStream_t stre
 // x W_g^T (+ offset), every output accumulated like the grouped GEMM's.
 hipError_t launch_router_packed(const uint16_t* x, const uint16_t* wg_packed, const float* offset,
                                 int T, int K, int E, float* logits, hipStream_t stream);
+// whether launch_router_packed is the faster router for T tokens, E experts
+bool router_packed_preferred(int T, int E);
 // Expert GEMMs on packed weights (EPI_SWIGLU_BF16 with 128-row panels,
 // EPI_F32 with 256-row panels): tiles staged in LDS by DMA.  Takes
 // G <= grouped_gemm_lds_max_groups().

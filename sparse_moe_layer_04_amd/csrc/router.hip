@@ -11,7 +11,8 @@
 // smallest for a square-ish tile.  Tile: 128 tokens x 96 experts (three
 // 32-row weight blocks), T / 128 x ceil(E / 96) workgroups (256 at the
 // 384-expert layer): ~0.47 GB of operand reads instead of ~1 GB for
-// 32 tokens x all experts; the kernel is bound by that traffic.
+// 32 tokens x all experts.  The workgroups of one token tile run together
+// on one XCD (see the order below), so x comes from memory once.
 //   - workgroup: 4 waves (one per SIMD); wave w owns tokens 32 w .. 32 w + 31
 //     of the tile and all of its (up to) three weight blocks;
 //   - per 16-wide K substep: one activation fragment (16 bytes per lane,
@@ -39,10 +40,17 @@ __global__ __launch_bounds__(256, 1) void router_kernel(const uint16_t* __restri
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31, half = lane >> 5;
-    const int t0 = blockIdx.x * kTokens + wave * 32;
-    if (t0 >= T) return;                          // (wave-uniform; no barrier below)
+    // XCD-aware order: workgroup id mod 8 is its XCD; on each XCD the
+    // consecutive workgroups take the expert groups of one token tile, so
+    // the tile's rows of x are read from memory once and then hit that
+    // XCD's L2 (and every XCD keeps all of W_g in its L2)
     const int NB = (E + 31) / 32;                 // 32-row weight blocks
-    const int eb0 = blockIdx.y * kBlocks;         // this workgroup's first block
+    const int groups = (NB + kBlocks - 1) / kBlocks;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int tile = (slot / groups) * 8 + xcd, group = slot % groups;
+    const int t0 = tile * kTokens + wave * 32;
+    if (t0 >= T) return;                          // (wave-uniform; no barrier below)
+    const int eb0 = group * kBlocks;              // this workgroup's first block
     const int nb = min(kBlocks, NB - eb0);        // its blocks (>= 1)
     const int S = K / 16;                         // 16-wide K substeps
 
@@ -130,13 +138,23 @@ __global__ __launch_bounds__(256, 1) void router_kernel(const uint16_t* __restri
 
 }  // namespace
 
+bool router_packed_preferred(int T, int E) {
+    // each workgroup's time is set by its own load latency chain, so the
+    // kernel wins while its grid is at most two rounds over the CUs; larger
+    // grids go to the persistent grouped GEMM (same bits either way)
+    const long long groups = ((E + 31) / 32 + kBlocks - 1) / kBlocks;
+    const long long wgs = ((T + kTokens - 1) / kTokens + 7) / 8 * 8 * groups;
+    return wgs <= 2LL * device_cu_count();
+}
+
 hipError_t launch_router_packed(const uint16_t* x, const uint16_t* wg_packed, const float* offset,
                                 int T, int K, int E, float* logits, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
     if (K % 64 || E < 1 || E > MOE_MAX_E) return hipErrorInvalidValue;
     const int groups = ((E + 31) / 32 + kBlocks - 1) / kBlocks;
-    hipLaunchKernelGGL(router_kernel, dim3((unsigned)((T + kTokens - 1) / kTokens), groups),
-                       dim3(256), 0, stream, x, wg_packed, offset, T, K, E, logits);
+    const long long tiles8 = ((T + kTokens - 1) / kTokens + 7) / 8 * 8;   // whole XCD rounds
+    hipLaunchKernelGGL(router_kernel, dim3((unsigned)(tiles8 * groups)), dim3(256), 0, stream, x,
+                       wg_packed, offset, T, K, E, logits);
     return hipGetLastError();
 }
 
