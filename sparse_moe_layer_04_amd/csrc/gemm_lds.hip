@@ -61,6 +61,9 @@ constexpr int kStaticLds = 256;              // reserve for static LDS (scan_sh,
 // tiles with more valid rows than this take the 64-wide stages (MFMA-heavy),
 // the others the 32-wide ones (memory-bound: deeper lookahead)
 constexpr int kWideStageRows = 192;
+// (MXFP8 weights: half the weight bytes per stage, so the 64-wide stages pay
+// off from 129 valid rows; measured 2% faster at the 384-expert workload)
+constexpr int kWideStageRowsFp8 = 128;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -528,7 +531,7 @@ __device__ __forceinline__ void do_tile(LdsTile& t, const GemmArgs& args, int g,
     t.mh = min(MH, (((t.valid + 1) >> 1) + 31) & ~31);
     const int wrows = min(max(t.valid - t.wm * t.mh, 0), t.mh);
     const int ntb = t.n0 < N ? (wrows + 31) / 32 : 0;
-    if (t.valid > kWideStageRows) {
+    if (t.valid > (WF ? kWideStageRowsFp8 : kWideStageRows)) {
         setup_a<AM, 64>(t, args);
         run_tile_ntb<EPI, AM, 64, MAXNTB, WF>(t, ntb);
     } else {
