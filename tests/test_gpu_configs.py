@@ -112,26 +112,36 @@ def test_full_size(cfg):
     free_cuda()
 
 
-def test_full_size_fp8():
-    """The MXFP8 routed-weight mode at the 384-expert workload's full size, in
-    the benchmark's launch configuration (--weights fp8): routes bit-exact,
-    and sampled tokens within 1e-2 x RMS of the oracle run on the oracle's
-    own dequantisation of the fp8 weights of the experts those tokens use."""
-    w = wl.WORKLOADS[2]
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_full_size_fp8(cfg):
+    """The MXFP8 routed-weight mode at full size (the 384-expert layer and
+    the hash-routed T=32768 layer, whose experts take 64-wide stages), in the
+    benchmark's launch configuration (--weights fp8): routes bit-exact, and
+    sampled tokens within 1e-2 x RMS of the oracle run on the oracle's own
+    dequantisation of the fp8 weights of the experts those tokens use."""
+    w = wl.WORKLOADS[cfg]
     print(f"\n[{w.name}, fp8 weights] generating inputs", flush=True)
     inp = wl.make_inputs(w, DEV)
     layer = ops.MoeLayer.from_workload(w, inp, out_dtype=ops.OUT_F32, packed="fp8")
     logits = torch.empty((w.T, w.E), dtype=torch.float32, device=DEV)
     ids = torch.empty((w.T, w.k), dtype=torch.int32, device=DEV)
     wts = torch.empty((w.T, w.k), dtype=torch.float32, device=DEV)
-    y = layer.forward(inp["x"], logits=logits, ids=ids, w=wts)
+    y = layer.forward(inp["x"], input_ids=inp["input_ids"], modality=inp["modality"],
+                      logits=logits, ids=ids, w=wts)
     torch.cuda.synchronize()
     assert int(layer.flags.item()) == 0
-    rid, rw, _ = oracle.route(host(logits), w.k, w.scale, bias=_opt(inp, "score_bias"))
+    rid, rw, _ = oracle.route(host(logits), w.k, w.scale, bias=_opt(inp, "score_bias"),
+                              modality=_opt(inp, "modality"), input_ids=_opt(inp, "input_ids"),
+                              tid2eid=_opt(inp, "tid2eid"), mode=w.mode)
     assert np.array_equal(host(ids), rid)
     assert np.array_equal(host(wts).view(np.uint32), rw.view(np.uint32))
+    # random tokens plus the tokens at the tile boundaries of the busiest expert
+    counts, offsets, _, src, _ = oracle.permute(rid, w.E)
+    e_max = int(np.argmax(counts))
+    lo, hi = int(offsets[e_max]), int(offsets[e_max + 1])
+    edge = [r for r in (lo, lo + 127, lo + 128, lo + 255, lo + 256, hi - 1) if lo <= r < hi]
     rng = np.random.default_rng(77)
-    toks = np.sort(rng.choice(w.T, size=8, replace=False))
+    toks = np.unique(np.concatenate([rng.choice(w.T, size=6, replace=False), src[edge]]))
     experts = np.unique(rid[toks])
     mats = {}
     for key in ("w_gate", "w_up", "w_down"):
