@@ -35,4 +35,8 @@ from .oracle import (  # noqa: F401
     e4m3_encode,
     quant_mxfp8,
     dequant_mxfp8,
+    e2m1_decode,
+    e2m1_encode,
+    quant_mxfp4,
+    dequant_mxfp4,
 )

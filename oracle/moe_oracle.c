@@ -581,3 +581,78 @@ void orc_dequant_mxfp8(const uint8_t* q, const int32_t* x, int64_t R, int K, uin
             w[r * K + k] = orc_f64_to_bf16(
                 ldexp(orc_e4m3_decode(q[r * K + k]), x[r * (K / 32) + k / 32]));
 }
+
+/* ------------------------------------------------------ fp4 expert weights -- */
+/*
+ * MXFP4 (the pages' "MxFP4", OCP Microscaling): blocks of 32 values along K
+ * share one power-of-two scale, each value an OCP E2M1 float (1 sign bit, 2
+ * exponent bits with bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2,
+ * 3, 4, 6; no infinities or NaN).  Scale rule of the OCP specification:
+ *   X = floor(log2(max |v| over the block)) - 2   (2 = E2M1's largest
+ *       exponent), clamped here to [-110, 110] (0 for an all-zero block);
+ *   q = E2M1(v / 2^X), round to nearest, ties to the even code (mantissa
+ *       bit 0), magnitudes beyond 6 saturated to 6.
+ * The dequantised value E2M1(q) * 2^X has at most 2 significant bits and a
+ * normal bf16 exponent, so it is exactly a bf16 value.
+ */
+static const double e2m1_mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double orc_e2m1_decode(uint8_t c)
+{
+    return ((c & 8) ? -1.0 : 1.0) * e2m1_mag[c & 7];
+}
+
+/* nearest magnitude code, ties to the even code; |v| > 6 saturates */
+uint8_t orc_e2m1_encode(double v)
+{
+    const uint8_t sign = signbit(v) ? 8 : 0;
+    const double a = fmin(fabs(v), 6.0);          /* saturate first */
+    int best = 0;
+    for (int c = 1; c < 8; ++c) {
+        const double dc = fabs(a - e2m1_mag[c]), db = fabs(a - e2m1_mag[best]);
+        if (dc < db || (dc == db && (c & 1) == 0))
+            best = c;
+    }
+    return sign | (uint8_t)best;
+}
+
+/* MXFP4 quantisation of bf16 weights [R, K] (K multiple of 32): codes [R, K]
+ * (one per byte, 0..15), block exponents X [R, K/32] */
+void orc_quant_mxfp4(const uint16_t* w, int64_t R, int K, uint8_t* q, int32_t* x)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        for (int b = 0; b < K / 32; ++b) {
+            const uint16_t* v = w + r * K + 32 * b;
+            double amax = 0.0;
+            for (int i = 0; i < 32; ++i) {
+                const double a = fabs(bf16_value(v[i]));
+                if (a > amax)
+                    amax = a;
+            }
+            int X = 0;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);                 /* 2^(ex-1) <= amax < 2^ex */
+                X = (ex - 1) - 2;
+                if (X < -110)
+                    X = -110;
+                if (X > 110)
+                    X = 110;
+            }
+            x[r * (K / 32) + b] = X;
+            for (int i = 0; i < 32; ++i)
+                q[r * K + 32 * b + i] = orc_e2m1_encode(ldexp(bf16_value(v[i]), -X));
+        }
+    }
+}
+
+/* dequantised MXFP4 weights as bf16 bit patterns (exact) */
+void orc_dequant_mxfp4(const uint8_t* q, const int32_t* x, int64_t R, int K, uint16_t* w)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r)
+        for (int k = 0; k < K; ++k)
+            w[r * K + k] = orc_f64_to_bf16(
+                ldexp(orc_e2m1_decode(q[r * K + k]), x[r * (K / 32) + k / 32]));
+}

@@ -65,6 +65,14 @@ def load():
     lib.orc_quant_mxfp8.restype = None
     lib.orc_dequant_mxfp8.argtypes = [P, P, I64, I, P]
     lib.orc_dequant_mxfp8.restype = None
+    lib.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_e2m1_decode.restype = D
+    lib.orc_e2m1_encode.argtypes = [D]
+    lib.orc_e2m1_encode.restype = ctypes.c_uint8
+    lib.orc_quant_mxfp4.argtypes = [P, I64, I, P, P]
+    lib.orc_quant_mxfp4.restype = None
+    lib.orc_dequant_mxfp4.argtypes = [P, P, I64, I, P]
+    lib.orc_dequant_mxfp4.restype = None
     lib.orc_combine.argtypes = [P, P, P, P, I, I, I, P]
     lib.orc_combine.restype = None
     lib.orc_tokens_forward.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, P, I, D, I, P]
@@ -276,4 +284,34 @@ def dequant_mxfp8(q, x):
     K = q.shape[-1]
     w = np.empty(q.shape, np.uint16)
     load().orc_dequant_mxfp8(_p(q), _p(x), q.size // K, K, _p(w))
+    return w
+
+
+def e2m1_decode(code):
+    """Value of an E2M1 code (0..15)."""
+    return float(load().orc_e2m1_decode(int(code)))
+
+
+def e2m1_encode(v):
+    """E2M1 code of v (nearest, ties to the even code, saturating)."""
+    return int(load().orc_e2m1_encode(float(v)))
+
+
+def quant_mxfp4(w):
+    """bf16 bits [..., K] -> (codes uint8 [..., K], block exponents int32 [..., K/32])."""
+    w = _c(w, np.uint16)
+    K = w.shape[-1]
+    q = np.empty(w.shape, np.uint8)
+    x = np.empty(w.shape[:-1] + (K // 32,), np.int32)
+    load().orc_quant_mxfp4(_p(w), w.size // K, K, _p(q), _p(x))
+    return q, x
+
+
+def dequant_mxfp4(q, x):
+    """(codes [..., K], block exponents [..., K/32]) -> dequantised weights as bf16 bits."""
+    q = _c(q, np.uint8)
+    x = _c(x, np.int32)
+    K = q.shape[-1]
+    w = np.empty(q.shape, np.uint16)
+    load().orc_dequant_mxfp4(_p(q), _p(x), q.size // K, K, _p(w))
     return w
