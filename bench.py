@@ -30,7 +30,7 @@ RIDGE = PEAK_BF16 / PEAK_HBM
 
 def stage_work(w, n_nonempty, out_bytes=2, wbytes=2):
     """Algorithmic (minimum) HBM bytes and FLOPs per stage (wbytes: bytes per
-    routed expert weight; MXFP8 weights also read one scale byte per 32)."""
+    routed expert weight; MX weights also read one scale byte per 32)."""
     T, d, E, k, F, Fs = w.T, w.d, w.E, w.k, w.F, w.Fs
     N = T * k
     hash_mode = w.mode == 1
@@ -43,10 +43,10 @@ def stage_work(w, n_nonempty, out_bytes=2, wbytes=2):
     st["permute"] = (N * 4 + 2 * N * 4, 0.0)
     # routed gate/up: weights of the non-empty experts once, every routed row
     # of x once (gathered), h written once
-    st["gate_up_routed"] = (n_nonempty * 2 * F * (d * wbytes + (d // 32 if wbytes == 1 else 0)) +
+    st["gate_up_routed"] = (n_nonempty * 2 * F * (d * wbytes + (d // 32 if wbytes < 2 else 0)) +
                             N * d * 2 + N * F * 2, 2.0 * N * d * 2 * F)
     st["gate_up_shared"] = (2 * Fs * d * 2 + T * d * 2 + T * Fs * 2, 2.0 * T * d * 2 * Fs)
-    st["down_routed"] = (n_nonempty * d * (F * wbytes + (F // 32 if wbytes == 1 else 0)) +
+    st["down_routed"] = (n_nonempty * d * (F * wbytes + (F // 32 if wbytes < 2 else 0)) +
                          N * F * 2 + N * d * 4, 2.0 * N * F * d)
     st["down_shared"] = (d * Fs * 2 + T * Fs * 2 + T * d * 4, 2.0 * T * Fs * d)
     st["combine"] = (N * d * 4 + (T * d * 4 if Fs else 0) + N * 8 + T * d * out_bytes, 0.0)
@@ -143,9 +143,10 @@ def main():
     ap.add_argument("--layout", choices=["packed", "plain"], default="packed",
                     help="weight layout: packed once at load time (moe_pack_weights) or "
                          "the plain [out, in] matrices")
-    ap.add_argument("--weights", choices=["bf16", "fp8"], default="bf16",
-                    help="routed expert weights: bf16, or MXFP8 (E4M3 codes, one power-of-two "
-                         "scale per 32 values of K; moe_pack_weights_fp8; packed layout only)")
+    ap.add_argument("--weights", choices=["bf16", "fp8", "fp4"], default="bf16",
+                    help="routed expert weights: bf16, MXFP8 (E4M3 codes) or MXFP4 (E2M1 codes), "
+                         "one power-of-two scale per 32 values of K (moe_pack_weights_fp8 / "
+                         "_fp4; packed layout only)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle CPU work for the baseline (0: skip)")
     args = ap.parse_args()
@@ -163,10 +164,10 @@ def main():
     print(f"# generating workload {w.name}", file=sys.stderr, flush=True)
     inp = wl.make_inputs(w, dev)
     out_dtype = ops.OUT_F32 if args.out_dtype == "f32" else ops.OUT_BF16
-    if args.weights == "fp8" and args.layout != "packed":
-        ap.error("--weights fp8 needs --layout packed")
+    if args.weights != "bf16" and args.layout != "packed":
+        ap.error("--weights fp8 / fp4 needs --layout packed")
     layer = ops.MoeLayer.from_workload(w, inp, out_dtype=out_dtype,
-                                       packed="fp8" if args.weights == "fp8" else
+                                       packed=args.weights if args.weights != "bf16" else
                                        args.layout == "packed")
     y = torch.empty((w.T, w.d), dtype=torch.float32 if out_dtype == ops.OUT_F32 else torch.bfloat16,
                     device=dev)
@@ -202,7 +203,7 @@ def main():
     counts = torch.bincount(ids.flatten().long(), minlength=w.E).cpu().numpy()
     n_nonempty = int((counts > 0).sum())
     work = stage_work(w, n_nonempty, 4 if out_dtype == ops.OUT_F32 else 2,
-                      wbytes=1 if args.weights == "fp8" else 2)
+                      wbytes={"bf16": 2, "fp8": 1, "fp4": 0.5}[args.weights])
     stages = {}
     for s, name in enumerate(ops.STAGE_NAMES):
         b, f = work[name]
@@ -241,7 +242,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if args.weights == "bf16" else "bf16 activations, MXFP8 (E4M3) routed weights",
+        "dtype": {"bf16": "bf16", "fp8": "bf16 activations, MXFP8 (E4M3) routed weights",
+                  "fp4": "bf16 activations, MXFP4 (E2M1) routed weights"}[args.weights],
         "data": "synthetic",
         "config": dict(w.describe(), out_dtype=args.out_dtype, weight_layout=args.layout,
                        routed_weights=args.weights, non_empty_experts=n_nonempty,

@@ -209,6 +209,27 @@ size_t moe_packed_fp8_scale_bytes(int G, int N, int K, int panel_rows);
 int moe_pack_weights_fp8(const uint16_t* src, int G, int N, int K, int panel_rows, uint8_t* dst,
                          uint8_t* scales, void* stream);
 
+/* MXFP4 routed-expert weights (the pages' "MxFP4"; OCP Microscaling): blocks
+ * of 32 values along K share one power-of-two scale, each value an OCP E2M1
+ * float (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).  Per block:
+ *   X = floor(log2(max |W| over the block)) - 2, clamped to [-110, 110]
+ *       (0 for an all-zero block);
+ *   q = E2M1(W / 2^X), nearest, ties to the even code, saturating at +-6.
+ * The dequantised weight E2M1(q) * 2^X is exactly a bf16 value.
+ *   Codes, panels of P rows: [G][ceil(N/P)][K/32][P/32][64][8 B]; lane l of
+ *   the 512-byte chunk of (K block kb, 32-row block b) holds row
+ *   panel*P + b*32 + l%32, columns 32 kb + 8 (l/32) + {0..7} in bytes 0-3
+ *   and the same + 16 in bytes 4-7, two codes per byte, the lower column in
+ *   the low nibble; rows >= N are zero codes.
+ *   Scales: as moe_pack_weights_fp8 (moe_packed_fp8_scale_bytes bytes).
+ *   src [G,N,K] bf16 (finite); dst moe_packed_fp4_weight_bytes(G,N,K,P)
+ *   bytes; both 16-byte aligned.  K multiple of 64; P 128 (gate, up) or 256
+ *   (down), else 0 / MOE_ERR_UNSUPPORTED.
+ */
+size_t moe_packed_fp4_weight_bytes(int G, int N, int K, int panel_rows);
+int moe_pack_weights_fp4(const uint16_t* src, int G, int N, int K, int panel_rows, uint8_t* dst,
+                         uint8_t* scales, void* stream);
+
 /* ------------------------------------------------------------------------
  * Result return merged by routing weight [TW], plus the always-on shared
  * expert with weight 1 [MS]:
@@ -252,7 +273,8 @@ typedef struct moe_weights {
                                      MOE_WEIGHTS_FP8: as 1, except that w_gate,
                                      w_up, w_down hold moe_pack_weights_fp8
                                      MXFP8 codes (uint8) with the block
-                                     scales below */
+                                     scales below; MOE_WEIGHTS_FP4: the same
+                                     with moe_pack_weights_fp4 MXFP4 codes */
     const uint16_t* w_g;          /* [E,d] bf16 router projection */
     const float* logit_offset;    /* [E] fp32 or NULL, added to the logits */
     const float* score_bias;      /* [n_bias,E] fp32 or NULL (TOPK) */
@@ -263,11 +285,12 @@ typedef struct moe_weights {
     const uint16_t* s_gate;       /* [F_shared,d] bf16 (shared expert) */
     const uint16_t* s_up;         /* [F_shared,d] bf16 */
     const uint16_t* s_down;       /* [d,F_shared] bf16 */
-    const uint8_t* w_gate_scale;  /* MOE_WEIGHTS_FP8: moe_pack_weights_fp8 scales */
-    const uint8_t* w_up_scale;    /* MOE_WEIGHTS_FP8 */
-    const uint8_t* w_down_scale;  /* MOE_WEIGHTS_FP8 */
+    const uint8_t* w_gate_scale;  /* MOE_WEIGHTS_FP8 / FP4: block scales */
+    const uint8_t* w_up_scale;    /* MOE_WEIGHTS_FP8 / FP4 */
+    const uint8_t* w_down_scale;  /* MOE_WEIGHTS_FP8 / FP4 */
 } moe_weights;
 #define MOE_WEIGHTS_FP8 2
+#define MOE_WEIGHTS_FP4 3
 
 /* Workspace for moe_forward (all intermediates: logits, routing, permutation,
  * x_perm, h, y_perm and the shared expert's h and y). */

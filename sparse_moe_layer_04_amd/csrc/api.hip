@@ -311,6 +311,22 @@ int moe_pack_weights_fp8(const uint16_t* src, int G, int N, int K, int panel_row
         launch_pack_weights_fp8(src, dst, scales, G, N, K, panel_rows, as_stream(stream)));
 }
 
+size_t moe_packed_fp4_weight_bytes(int G, int N, int K, int panel_rows) {
+    if (G < 1 || N < 1 || K < 64 || K % 64) return 0;
+    if (panel_rows != 128 && panel_rows != 256) return 0;
+    return packed_fp4_weight_bytes(G, N, K, panel_rows);
+}
+
+int moe_pack_weights_fp4(const uint16_t* src, int G, int N, int K, int panel_rows, uint8_t* dst,
+                         uint8_t* scales, void* stream) {
+    if (G < 1 || N < 1 || K < 64) return MOE_ERR_SHAPE;
+    if (K % 64 || (panel_rows != 128 && panel_rows != 256)) return MOE_ERR_UNSUPPORTED;
+    if (!src || !dst || !scales) return MOE_ERR_NULL;
+    if (!aligned16(src) || !aligned16(dst) || !aligned16(scales)) return MOE_ERR_ALIGN;
+    return hip_status(
+        launch_pack_weights_fp4(src, dst, scales, G, N, K, panel_rows, as_stream(stream)));
+}
+
 int moe_combine(const float* y_perm, const int32_t* dest, const float* topk_w,
                 const float* y_shared, int T, int d, int k, int rows, int out_dtype, void* y,
                 void* stream) {
@@ -336,10 +352,11 @@ static int forward_checks(const moe_cfg* c, const moe_weights* w) {
     if (c->mode != MOE_MODE_TOPK && c->mode != MOE_MODE_HASH) return MOE_ERR_UNSUPPORTED;
     if (c->out_dtype != MOE_OUT_BF16 && c->out_dtype != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
     if (!(c->scale == c->scale)) return MOE_ERR_SHAPE;
-    if (w->packed != 0 && w->packed != 1 && w->packed != MOE_WEIGHTS_FP8)
+    if (w->packed != 0 && w->packed != 1 && w->packed != MOE_WEIGHTS_FP8 &&
+        w->packed != MOE_WEIGHTS_FP4)
         return MOE_ERR_UNSUPPORTED;
-    // fp8 routed weights run on the LDS-staged expert GEMM only
-    if (w->packed == MOE_WEIGHTS_FP8 && !lds_gemm_ok(1, c->E)) return MOE_ERR_UNSUPPORTED;
+    // 8- and 4-bit routed weights run on the LDS-staged expert GEMM only
+    if (w->packed >= MOE_WEIGHTS_FP8 && !lds_gemm_ok(1, c->E)) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -365,13 +382,14 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     if (c->T == 0) return MOE_OK;
     if (!x || !y || !w->w_g || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL;
     if (c->F_shared > 0 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_NULL;
-    const bool fp8 = w->packed == MOE_WEIGHTS_FP8;
-    if (fp8 && (!w->w_gate_scale || !w->w_up_scale || !w->w_down_scale)) return MOE_ERR_NULL;
-    if (fp8 && (!aligned16(w->w_gate_scale) || !aligned16(w->w_up_scale) ||
-                !aligned16(w->w_down_scale)))
+    // routed weight format of the expert GEMMs: 0 bf16, 1 MXFP8, 2 MXFP4
+    const int wfmt = w->packed == MOE_WEIGHTS_FP8 ? 1 : w->packed == MOE_WEIGHTS_FP4 ? 2 : 0;
+    if (wfmt && (!w->w_gate_scale || !w->w_up_scale || !w->w_down_scale)) return MOE_ERR_NULL;
+    if (wfmt && (!aligned16(w->w_gate_scale) || !aligned16(w->w_up_scale) ||
+                 !aligned16(w->w_down_scale)))
         return MOE_ERR_ALIGN;
-    // layout of the bf16 matrices (router, shared expert; routed unless fp8)
-    const int wpk = fp8 ? 1 : w->packed;
+    // layout of the bf16 matrices (router, shared expert; routed unless MX)
+    const int wpk = wfmt ? 1 : w->packed;
     if (c->mode == MOE_MODE_TOPK) {
         if (c->n_bias < 0 || c->n_bias > 2) return MOE_ERR_SHAPE;
         if (c->n_bias > 0 && !w->score_bias) return MOE_ERR_NULL;
@@ -446,7 +464,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g1.w1 = w->w_gate;
     g1.w2 = w->w_up;
     g1.packed = wpk;
-    g1.wfp8 = fp8;
+    g1.wfp8 = wfmt;
     g1.s1 = w->w_gate_scale;
     g1.s2 = w->w_up_scale;
     g1.clamp_limit = c->clamp_limit;
@@ -484,7 +502,7 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g2.N = d;
     g2.w1 = w->w_down;
     g2.packed = wpk;
-    g2.wfp8 = fp8;
+    g2.wfp8 = wfmt;
     g2.s1 = w->w_down_scale;
     g2.out = L.y_perm;
     g2.a_blocked = lds;

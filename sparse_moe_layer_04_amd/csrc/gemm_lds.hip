@@ -73,6 +73,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 //            per wave; the waits count the instructions of later stages.
 //   KB = 64: 2 slots of 64 KB, 1 stage in flight while one computes; per
 //            stage 4 + 4 instructions per wave; every wait is vmcnt(0).
+//   WF = 2 (MXFP4 weights): a quarter of the bytes: one 512-byte chunk per
+//            32-row block per 32 columns (a 16-byte DMA by lanes 0-31).
 //   WF = 1 (MXFP8 weights): the weight stage is half as many bytes (one 1 KB
 //            chunk per 32-row block per 32 columns of K) plus the 8 blocks'
 //            scale bytes (256 per 32 columns: one more DMA instruction for
@@ -88,7 +90,8 @@ struct Stage {
     static constexpr int WI = WF ? KB / 32 : Q;            // weight instrs per wave (1 KB each)
     // (waves w < WI also issue one scale instruction per stage)
     static constexpr int SLOTA = TM * ROWB;
-    static constexpr int SLOTW = WBLK * WI * 1024;
+    static constexpr int CHUNK = WF == 2 ? 512 : 1024;    // bytes per weight instruction
+    static constexpr int SLOTW = WBLK * WI * CHUNK;
     static constexpr int SLOTS_B = WF ? WBLK * (KB / 32) * 32 : 0;   // MXFP8 scale bytes
     static constexpr int SLOT = SLOTA + SLOTW + SLOTS_B;
     static constexpr int SLOTS = KB == 32 ? 4 : 2;
@@ -226,6 +229,28 @@ __device__ __forceinline__ void issue_stage(const LdsTile& t, int j, uint32_t sb
         }
     }
     const int s64 = (j * KB) >> 6, sub0 = ((j * KB) & 63) >> 4;
+    if constexpr (WF == 2) {
+        // fp4 codes: wave w copies block w's 512-byte chunks of MX blocks
+        // kb0 .. kb0 + WI - 1 (lanes 0-31, 16 bytes each) to slot WI w + i
+        const int b = t.wave;
+        const uint8_t* mat = t.bsrc0;
+        int gb = t.blk0 + b;
+        if (EPI == EPI_SWIGLU_BF16 && b >= Pn::BPM) {
+            mat = t.bsrc1;
+            gb -= Pn::BPM;
+        }
+        const int panel = min(gb / Pn::BPP, t.np - 1);
+        const int kb0 = (j * KB) / 32;
+        if (t.lane < 32) {
+#pragma unroll
+            for (int i = 0; i < St::WI; ++i) {
+                const uint8_t* src = mat + (size_t)panel * t.pstride_b +
+                                     (size_t)(kb0 + i) * (Pn::BPP * 512) + (gb % Pn::BPP) * 512 +
+                                     t.lane * 16;
+                dma16(src, base + St::SLOTA + (b * St::WI + i) * 512);
+            }
+        }
+    }
     if constexpr (WF) {
         // fp8 codes: wave w copies block w, chunks c0 .. c0 + WI - 1 (each the
         // 32 columns of one 32-wide K slice, both substeps) to fragment slot
@@ -239,11 +264,14 @@ __device__ __forceinline__ void issue_stage(const LdsTile& t, int j, uint32_t sb
         }
         const int panel = min(gb / Pn::BPP, t.np - 1);
         const int c0 = ((j * KB) & 63) >> 5;
+        if constexpr (WF == 1) {
 #pragma unroll
-        for (int i = 0; i < St::WI; ++i) {
-            const uint8_t* src = mat + (size_t)panel * t.pstride_b + (size_t)s64 * t.wstride_b +
-                                 (gb % Pn::BPP) * 2048 + (c0 + i) * 1024 + t.lane * 16;
-            dma16(src, base + St::SLOTA + (b * St::WI + i) * 1024);
+            for (int i = 0; i < St::WI; ++i) {
+                const uint8_t* src = mat + (size_t)panel * t.pstride_b +
+                                     (size_t)s64 * t.wstride_b + (gb % Pn::BPP) * 2048 +
+                                     (c0 + i) * 1024 + t.lane * 16;
+                dma16(src, base + St::SLOTA + (b * St::WI + i) * 1024);
+            }
         }
         // scale bytes of MX block kb = j KB / 32 + w for all 8 weight blocks
         // (wave w < WI): lanes 8 b' .. 8 b' + 7 copy the 32 rows of block b'
@@ -306,6 +334,18 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 v, float sc) {
     return __builtin_bit_cast(bf16x8, r);
 }
 
+// eight E2M1 codes (nibbles of v, low nibble first) times the MX block scale
+// -> bf16x8 (exact: at most 2 significant bits, normal range; checked on
+// MI355X for every byte and scales 2^-110 .. 2^110)
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t v, float sc) {
+    u32x4 r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 0));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 1));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 2));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 3));
+    return __builtin_bit_cast(bf16x8, r);
+}
+
 template <int EPI, int KB, int NTB, int WF>
 __device__ __forceinline__ void read_operands(const LdsTile& t, uint32_t sbase, int q,
                                               Operands<NTB>& o, float (&msc)[2]) {
@@ -316,7 +356,6 @@ __device__ __forceinline__ void read_operands(const LdsTile& t, uint32_t sbase, 
     const int b0 = (EPI == EPI_SWIGLU_BF16) ? t.wn : 2 * t.wn;
     const int b1 = (EPI == EPI_SWIGLU_BF16) ? Panel<EPI>::BPM + t.wn : 2 * t.wn + 1;
     if constexpr (WF) {
-        const unsigned char* wbase = base + St::SLOTA + t.lane * 16 + (q & 1) * 8;
         // scale byte X + 127 of this lane's row and MX block -> 2^X
         // (scale region: [MX block of the stage][8 weight blocks][32 rows])
         if ((q & 1) == 0) {
@@ -325,8 +364,21 @@ __device__ __forceinline__ void read_operands(const LdsTile& t, uint32_t sbase, 
             msc[0] = __uint_as_float((uint32_t)sbase[b0 * 32] << 23);
             msc[1] = __uint_as_float((uint32_t)sbase[b1 * 32] << 23);
         }
-        o.w0 = fp8x8_to_bf16x8(*(const u32x2*)(wbase + (b0 * St::WI + (q >> 1)) * 1024), msc[0]);
-        o.w1 = fp8x8_to_bf16x8(*(const u32x2*)(wbase + (b1 * St::WI + (q >> 1)) * 1024), msc[1]);
+        if constexpr (WF == 2) {
+            // fp4: lane l's 8 bytes at 8 l of the chunk, substep parity
+            // selects the 4-byte half
+            const unsigned char* wbase = base + St::SLOTA + t.lane * 8 + (q & 1) * 4;
+            o.w0 = fp4x8_to_bf16x8(*(const uint32_t*)(wbase + (b0 * St::WI + (q >> 1)) * 512),
+                                   msc[0]);
+            o.w1 = fp4x8_to_bf16x8(*(const uint32_t*)(wbase + (b1 * St::WI + (q >> 1)) * 512),
+                                   msc[1]);
+        } else {
+            const unsigned char* wbase = base + St::SLOTA + t.lane * 16 + (q & 1) * 8;
+            o.w0 = fp8x8_to_bf16x8(*(const u32x2*)(wbase + (b0 * St::WI + (q >> 1)) * 1024),
+                                   msc[0]);
+            o.w1 = fp8x8_to_bf16x8(*(const u32x2*)(wbase + (b1 * St::WI + (q >> 1)) * 1024),
+                                   msc[1]);
+        }
     } else {
         const unsigned char* wbase = base + St::SLOTA + t.lane * 16;
         o.w0 = *(const bf16x8*)(wbase + (b0 * St::Q + q) * 1024);
@@ -516,11 +568,12 @@ __device__ __forceinline__ void do_tile(LdsTile& t, const GemmArgs& args, int g,
     t.blk0 = n_tile * Pn::BPM;
     t.wstride = (size_t)Pn::BPP * 2048;
     if constexpr (WF) {
-        // fp8 codes: one byte per weight, panels of P rows x K bytes
-        const size_t ebase_b = (size_t)g * t.np * (size_t)Pn::P * t.K;
+        // fp8 codes: one byte per weight, panels of P rows x K bytes (fp4:
+        // half a byte per weight)
+        t.pstride_b = (size_t)Pn::P * t.K / (WF == 2 ? 2 : 1);
+        const size_t ebase_b = (size_t)g * t.np * t.pstride_b;
         t.bsrc0 = (const uint8_t*)args.w1 + ebase_b;
         t.bsrc1 = (const uint8_t*)(EPI == EPI_SWIGLU_BF16 ? args.w2 : args.w1) + ebase_b;
-        t.pstride_b = (size_t)Pn::P * t.K;
         t.wstride_b = (size_t)Pn::BPP * 2048;
         t.sstride = (size_t)(t.K / 32) * Pn::P;
         t.ssrc0 = args.s1 + (size_t)g * t.np * t.sstride;
@@ -700,6 +753,12 @@ hipError_t launch_grouped_gemm_lds(int epilogue, const GemmArgs& g, hipStream_t 
         // fp8 weights: the two routed expert GEMMs of moe_forward (gate/up
         // on gathered token rows, down on the blocked h)
         if (!g.s1 || (epilogue == EPI_SWIGLU_BF16 && !g.s2)) return hipErrorInvalidValue;
+        if (g.wfp8 == 2) {
+            if (epilogue == EPI_SWIGLU_BF16 && am == A_GATHER && g.out_blocked)
+                return launch_lds<EPI_SWIGLU_BF16, A_GATHER, 2>(g, stream);
+            if (epilogue == EPI_F32 && am == A_BLK) return launch_lds<EPI_F32, A_BLK, 2>(g, stream);
+            return hipErrorInvalidValue;
+        }
         if (epilogue == EPI_SWIGLU_BF16 && am == A_GATHER && g.out_blocked)
             return launch_lds<EPI_SWIGLU_BF16, A_GATHER, 1>(g, stream);
         if (epilogue == EPI_F32 && am == A_BLK) return launch_lds<EPI_F32, A_BLK, 1>(g, stream);

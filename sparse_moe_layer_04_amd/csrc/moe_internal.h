@@ -59,8 +59,8 @@ struct GemmArgs {
     int out_blocked;          // SWIGLU out in the blocked activation layout
     uint32_t* sched;          // LDS kernel: 8 per-XCD item counters, 128 B apart,
                               // zero at launch (NULL: static schedule)
-    int wfp8;                 // LDS kernel: w1 / w2 hold MXFP8 codes in the fp8 packed
-                              // layout (moe_pack_weights_fp8), block scales in s1 / s2
+    int wfp8;                 // LDS kernel: 1: w1 / w2 hold MXFP8 codes (moe_pack_weights_fp8),
+                              // 2: MXFP4 codes (moe_pack_weights_fp4); block scales in s1 / s2
     const uint8_t* s1;        // MXFP8 block scale bytes of w1
     const uint8_t* s2;        // MXFP8 block scale bytes of w2 (SWIGLU)
 };
@@ -100,6 +100,10 @@ hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int G, int N,
 size_t packed_fp8_weight_bytes(int G, int N, int K, int P);
 size_t packed_fp8_scale_bytes(int G, int N, int K, int P);
 hipError_t launch_pack_weights_fp8(const uint16_t* src, uint8_t* dst, uint8_t* scales, int G,
+                                   int N, int K, int P, hipStream_t stream);
+// MXFP4 expert weights (E2M1 codes, two per byte; the same scale layout)
+size_t packed_fp4_weight_bytes(int G, int N, int K, int P);
+hipError_t launch_pack_weights_fp4(const uint16_t* src, uint8_t* dst, uint8_t* scales, int G,
                                    int N, int K, int P, hipStream_t stream);
 
 hipError_t launch_route(const float* logits, const float* bias, const uint8_t* modality,

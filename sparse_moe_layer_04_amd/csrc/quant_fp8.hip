@@ -1,5 +1,5 @@
-// One-time quantisation of bf16 expert weights to MXFP8 for the fp8 weight
-// mode of the expert GEMMs.
+// One-time quantisation of bf16 expert weights to MXFP8 (and MXFP4, below)
+// for the 8-bit and 4-bit weight modes of the expert GEMMs.
 //
 // The pages name MXFP8 / MXFP4 weights as the low-precision direction
 // ("Twinkle x Ascend ... DeepSeek-V4 training": functional-expansion
@@ -113,6 +113,79 @@ __global__ __launch_bounds__(256) void mxfp8_pack_kernel(const uint16_t* __restr
             (uint8_t)(X + 127);
 }
 
+// E2M1 code of a finite v: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to
+// the even code (mantissa bit 0), saturating at 6.  Every threshold is an
+// exact midpoint; at a tie the comparison direction picks the even code.
+__device__ __forceinline__ uint32_t e2m1_rne(float v) {
+    const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
+    const float a = fabsf(v);
+    const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                       (uint32_t)(a > 5.0f);
+    return sign | m;
+}
+
+// MXFP4 codes: [G][ceil(N/P)][K/32][P/32][64 lanes][8 bytes]; lane l of the
+// 512-byte chunk of (K block kb, 32-row block b) holds row b*32 + l%32,
+// columns 32 kb + 8 (l/32) + {0..7} in bytes 0-3 and the same + 16 in bytes
+// 4-7, two values per byte, the lower column in the low nibble.  One thread
+// per (row, K block): block exponent, 32 codes (two lanes' 8 bytes), scale.
+__global__ __launch_bounds__(256) void mxfp4_pack_kernel(const uint16_t* __restrict__ src,
+                                                         uint8_t* __restrict__ dst,
+                                                         uint8_t* __restrict__ scales, int N,
+                                                         int K, int P, long long nthreads) {
+    const long long f = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (f >= nthreads) return;
+    const int r = (int)(f & 31);
+    long long q = f >> 5;
+    const int bpp = P / 32;
+    const int b = (int)(q % bpp);
+    q /= bpp;
+    const int KB = K / 32;
+    const int kb = (int)(q % KB);
+    q /= KB;
+    const int np = (N + P - 1) / P;
+    const int panel = (int)(q % np);
+    const long long g = q / np;
+    const int row = panel * P + b * 32 + r;
+    uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};   // lane r, lane r + 32: bytes 0-3, 4-7
+    int X = 0;
+    if (row < N) {
+        const uint16_t* bp = src + (g * N + row) * (long long)K + 32 * kb;
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 w = *(const u32x4*)(bp + 8 * i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+                v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+            }
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        if (amax > 0.0f) {
+            const int e = (int)((__float_as_uint(amax) >> 23) & 0xff) - 127;
+            X = min(max(e - 2, -kMaxExp), kMaxExp);
+        }
+        const float inv = __builtin_ldexpf(1.0f, -X);
+        // column c of the block: lane half h = (c / 8) % 2, word (c / 16),
+        // nibble position c % 8 within that word
+#pragma unroll
+        for (int c = 0; c < 32; ++c) {
+            const uint32_t code = e2m1_rne(v[c] * inv);
+            const int h = (c >> 3) & 1, word = c >> 4, nib = c & 7;
+            if (word == 0) (h ? lo[1] : lo[0]) |= code << (4 * nib);
+            else (h ? hi[1] : hi[0]) |= code << (4 * nib);
+        }
+    }
+    uint8_t* chunk = dst + ((((g * np + panel) * KB + kb) * bpp + b) * 512);
+    *(u32x2*)(chunk + 8 * r) = u32x2{lo[0], hi[0]};
+    *(u32x2*)(chunk + 8 * (r + 32)) = u32x2{lo[1], hi[1]};
+    scales[((g * np + panel) * KB + kb) * (long long)P + b * 32 + r] = (uint8_t)(X + 127);
+}
+
 }  // namespace
 
 size_t packed_fp8_weight_bytes(int G, int N, int K, int P) {
@@ -121,6 +194,19 @@ size_t packed_fp8_weight_bytes(int G, int N, int K, int P) {
 
 size_t packed_fp8_scale_bytes(int G, int N, int K, int P) {
     return packed_fp8_weight_bytes(G, N, K, P) / 32;
+}
+
+size_t packed_fp4_weight_bytes(int G, int N, int K, int P) {
+    return packed_fp8_weight_bytes(G, N, K, P) / 2;
+}
+
+hipError_t launch_pack_weights_fp4(const uint16_t* src, uint8_t* dst, uint8_t* scales, int G,
+                                   int N, int K, int P, hipStream_t stream) {
+    const long long nthreads = (long long)packed_fp8_weight_bytes(G, N, K, P) / 32;
+    if (nthreads == 0) return hipSuccess;
+    hipLaunchKernelGGL(mxfp4_pack_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,
+                       stream, src, dst, scales, N, K, P, nthreads);
+    return hipGetLastError();
 }
 
 hipError_t launch_pack_weights_fp8(const uint16_t* src, uint8_t* dst, uint8_t* scales, int G,

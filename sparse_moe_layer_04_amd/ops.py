@@ -46,8 +46,9 @@ class MoeCfg(ctypes.Structure):
 
 WEIGHT_NAMES = ("w_g", "logit_offset", "score_bias", "tid2eid", "w_gate", "w_up", "w_down",
                 "s_gate", "s_up", "s_down", "w_gate_scale", "w_up_scale", "w_down_scale")
-# moe_weights.packed value of fp8 routed-expert weights (MOE_WEIGHTS_FP8)
+# moe_weights.packed values of MXFP8 / MXFP4 routed-expert weights
 WEIGHTS_FP8 = 2
+WEIGHTS_FP4 = 3
 MATRIX_NAMES = ("w_g", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")
 
 
@@ -90,6 +91,9 @@ def lib():
     L.moe_packed_fp8_scale_bytes.argtypes = [I, I, I, I]
     L.moe_packed_fp8_scale_bytes.restype = S
     L.moe_pack_weights_fp8.argtypes = [P, I, I, I, I, P, P, P]
+    L.moe_packed_fp4_weight_bytes.argtypes = [I, I, I, I]
+    L.moe_packed_fp4_weight_bytes.restype = S
+    L.moe_pack_weights_fp4.argtypes = [P, I, I, I, I, P, P, P]
     L.moe_forward_workspace_size.argtypes = [ctypes.POINTER(MoeCfg)]
     L.moe_forward_workspace_size.restype = S
     L.moe_forward.argtypes = [ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeWeights), P, P, P, P,
@@ -98,7 +102,7 @@ def lib():
     for name in ("moe_gate_logits", "moe_route", "moe_permute", "moe_expert_ffn",
                  "moe_expert_ffn_packed",
                  "moe_combine", "moe_forward", "moe_forward_timed", "moe_pack_weights",
-                 "moe_pack_weights_fp8"):
+                 "moe_pack_weights_fp8", "moe_pack_weights_fp4"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -297,6 +301,24 @@ def pack_weights_fp8(w, panel_rows):
     return codes, scales
 
 
+def pack_weights_fp4(w, panel_rows):
+    """MXFP4 copy (moe_pack_weights_fp4: E2M1 codes in the packed layout, one
+    power-of-two scale per 32 values of K) of bf16 weights [G,N,K] or [N,K];
+    returns (codes uint8 tensor, scale bytes uint8 tensor)."""
+    _need(w, torch.bfloat16, "w")
+    shape = tuple(w.shape)
+    G, N, K = (1,) + shape if w.dim() == 2 else shape
+    nbytes = int(lib().moe_packed_fp4_weight_bytes(G, N, K, panel_rows))
+    if nbytes == 0:
+        raise MoeError(f"cannot pack weights of shape {shape} in panels of {panel_rows}")
+    codes = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(int(lib().moe_packed_fp8_scale_bytes(G, N, K, panel_rows)),
+                         dtype=torch.uint8, device=w.device)
+    _check(lib().moe_pack_weights_fp4(_ptr(w), G, N, K, panel_rows, _ptr(codes), _ptr(scales),
+                                      _stream()), "moe_pack_weights_fp4")
+    return codes, scales
+
+
 class MoeLayer:
     """One fine-grained MoE layer on the device: holds the weights, the config
     and a preallocated workspace; ``forward`` is one C-ABI call."""
@@ -318,19 +340,21 @@ class MoeLayer:
         _opt(self.weights.get("score_bias"), torch.float32, "score_bias")
         _opt(self.weights.get("tid2eid"), torch.int32, "tid2eid")
         fp8 = packed == "fp8"
+        fp4 = packed == "fp4"
         if packed:
             # one-time layout change at load time (moe_pack_weights; with
-            # packed="fp8" the routed expert matrices are quantised to MXFP8
-            # by moe_pack_weights_fp8 instead)
+            # packed="fp8" / "fp4" the routed expert matrices are quantised to
+            # MXFP8 / MXFP4 by moe_pack_weights_fp8 / _fp4 instead)
             for key in MATRIX_NAMES:
                 if self.weights.get(key) is None:
                     continue
-                if fp8 and key in ("w_gate", "w_up", "w_down"):
-                    self.weights[key], self.weights[key + "_scale"] = pack_weights_fp8(
+                if (fp8 or fp4) and key in ("w_gate", "w_up", "w_down"):
+                    pack = pack_weights_fp8 if fp8 else pack_weights_fp4
+                    self.weights[key], self.weights[key + "_scale"] = pack(
                         self.weights[key], PANEL_ROWS[key])
                 else:
                     self.weights[key] = pack_weights(self.weights[key], PANEL_ROWS[key])
-        self.packed = WEIGHTS_FP8 if fp8 else int(bool(packed))
+        self.packed = WEIGHTS_FP8 if fp8 else WEIGHTS_FP4 if fp4 else int(bool(packed))
         self.cw = MoeWeights(packed=self.packed,
                              **{n: _ptr(self.weights.get(n)) for n in WEIGHT_NAMES})
         self.device = self.weights["w_g"].device

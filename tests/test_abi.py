@@ -112,6 +112,10 @@ def test_pack_validation(L):
     assert L.moe_packed_fp8_weight_bytes(2, 100, 128, 128) == 2 * 128 * 128
     assert L.moe_packed_fp8_weight_bytes(1, 8, 100, 128) == 0
     assert L.moe_packed_fp8_scale_bytes(2, 100, 128, 128) == 2 * 128 * 128 // 32
+    assert L.moe_packed_fp4_weight_bytes(2, 100, 128, 128) == 2 * 128 * 128 // 2
+    assert L.moe_pack_weights_fp4(FAKE, 1, 8, 100, 128, FAKE, FAKE, None) == ERR_UNSUPPORTED
+    assert L.moe_pack_weights_fp4(FAKE, 1, 8, 128, 128, FAKE, None, None) == ERR_NULL
+    assert L.moe_pack_weights_fp4(FAKE, 1, 8, 128, 256, FAKE + 2, FAKE, None) == ERR_ALIGN
     assert L.moe_pack_weights_fp8(FAKE, 1, 8, 100, 128, FAKE, FAKE, None) == ERR_UNSUPPORTED
     assert L.moe_pack_weights_fp8(FAKE, 0, 8, 128, 128, FAKE, FAKE, None) == ERR_SHAPE
     assert L.moe_pack_weights_fp8(FAKE, 1, 8, 128, 128, FAKE, None, None) == ERR_NULL
@@ -155,8 +159,10 @@ def test_forward_validation(L):
         setattr(c, field, val)
         assert fwd(c=c) == code, field
     wp = ops.MoeWeights.from_buffer_copy(w)
-    wp.packed = 3
+    wp.packed = 4
     assert fwd(wt=wp) == ERR_UNSUPPORTED
+    wp.packed = ops.WEIGHTS_FP4                      # MXFP4 weights need their block scales
+    assert fwd(wt=wp) == ERR_NULL
     wp.packed = ops.WEIGHTS_FP8                      # fp8 routed weights need their row scales
     assert fwd(wt=wp) == ERR_NULL
     wp.w_gate_scale = wp.w_up_scale = wp.w_down_scale = FAKE + 4

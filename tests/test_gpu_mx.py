@@ -1,6 +1,6 @@
-"""GPU parity of the MXFP8 routed-expert weight mode (E4M3 codes, one
-power-of-two scale per 32 values of K; moe_pack_weights_fp8 + moe_forward
-with packed = MOE_WEIGHTS_FP8) against the oracle:
+"""GPU parity of the MXFP8 and MXFP4 routed-expert weight modes (E4M3 / E2M1
+codes, one power-of-two scale per 32 values of K; moe_pack_weights_fp8 /
+_fp4 + moe_forward with packed = MOE_WEIGHTS_FP8 / _FP4) against the oracle:
 
   - quantisation: codes and block scales bit-exact against the oracle's MX
     quantiser, on random rows plus zero, huge, tiny, saturating and tie
@@ -34,6 +34,26 @@ def unpack_codes(codes, G, N, K, P):
     return a.reshape(G, npan * P, K)
 
 
+def unpack_codes_fp4(codes, G, N, K, P):
+    """[G][ceil(N/P)][K/32][P/32][64][8 B] two codes per byte (low nibble
+    first) -> [G, ceil(N/P)*P, K] codes."""
+    npan = (N + P - 1) // P
+    a = codes.reshape(G, npan, K // 32, P // 32, 2, 32, 2, 4)
+    # axes: g, panel, kb, b, lane_hi, lane_lo, word, byte (+ nibble)
+    n = np.stack([a & 15, a >> 4], axis=-1).reshape(G, npan, K // 32, P // 32, 2, 32, 2, 8)
+    # column of the block = 16 word + 8 lane_hi + nibble
+    n = n.transpose(0, 1, 3, 5, 2, 6, 4, 7)
+    return n.reshape(G, npan * P, K)
+
+
+FORMATS = {
+    "fp8": (lambda w, P: ops.pack_weights_fp8(w, P), unpack_codes, oracle.quant_mxfp8,
+            oracle.dequant_mxfp8),
+    "fp4": (lambda w, P: ops.pack_weights_fp4(w, P), unpack_codes_fp4, oracle.quant_mxfp4,
+            oracle.dequant_mxfp4),
+}
+
+
 def unpack_scales(scales, G, N, K, P):
     """[G][ceil(N/P)][K/32][P/32][32] scale bytes -> block exponents X
     [G, ceil(N/P)*P, K/32]."""
@@ -63,15 +83,17 @@ def weights_with_special_rows(G, N, K, seed):
     return b
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
 @pytest.mark.parametrize("G,N,K,P", [(1, 64, 64, 128), (3, 200, 192, 128), (2, 256, 128, 256),
                                      (5, 96, 320, 256)])
-def test_pack_weights_fp8(G, N, K, P):
+def test_pack_weights_mx(G, N, K, P, fmt):
+    pack, unpack, quant, _ = FORMATS[fmt]
     wb = weights_with_special_rows(G, N, K, seed=G * 1000 + N)
     w = torch.from_numpy(wb.view(np.int16)).to(DEV).view(torch.bfloat16)
-    codes, scales = ops.pack_weights_fp8(w, P)
+    codes, scales = pack(w, P)
     torch.cuda.synchronize()
-    q_ref, x_ref = oracle.quant_mxfp8(wb.reshape(G * N, K))
-    got = unpack_codes(host(codes), G, N, K, P)
+    q_ref, x_ref = quant(wb.reshape(G * N, K))
+    got = unpack(host(codes), G, N, K, P)
     assert np.array_equal(got[:, :N].reshape(G * N, K), q_ref)
     assert not got[:, N:].any()
     xs = unpack_scales(host(scales), G, N, K, P)
@@ -89,23 +111,25 @@ FP8_CASES = [
 ]
 
 
-def _dequantised(inp):
-    """inputs with the routed matrices replaced by their dequantised fp8
+def _dequantised(inp, fmt="fp8"):
+    """inputs with the routed matrices replaced by their dequantised MX
     weights (exact bf16 values, from the oracle's quantiser)."""
+    _, _, quant, dequant = FORMATS[fmt]
     out = dict(inp)
     for key in ("w_gate", "w_up", "w_down"):
         wb = bits(inp[key])
-        q, x = oracle.quant_mxfp8(wb.reshape(-1, wb.shape[-1]))
-        deq = oracle.dequant_mxfp8(q, x).reshape(wb.shape)
+        q, x = quant(wb.reshape(-1, wb.shape[-1]))
+        deq = dequant(q, x).reshape(wb.shape)
         out[key] = torch.from_numpy(deq.view(np.int16)).to(DEV).view(torch.bfloat16)
     return out
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
 @pytest.mark.parametrize("w", FP8_CASES, ids=lambda w: w.name)
-def test_forward_fp8(w):
+def test_forward_mx(w, fmt):
     inp = wl.make_inputs(w, DEV)
-    deq = _dequantised(inp)
-    layer = ops.MoeLayer.from_workload(w, inp, out_dtype=ops.OUT_F32, packed="fp8")
+    deq = _dequantised(inp, fmt)
+    layer = ops.MoeLayer.from_workload(w, inp, out_dtype=ops.OUT_F32, packed=fmt)
     logits = torch.empty((w.T, w.E), dtype=torch.float32, device=DEV)
     ids = torch.empty((w.T, w.k), dtype=torch.int32, device=DEV)
     wts = torch.empty((w.T, w.k), dtype=torch.float32, device=DEV)
@@ -136,8 +160,9 @@ EXACT_COUNTS = [0, 1, 16, 17, 127, 128, 129, 191, 192, 193, 255, 256, 257, 384, 
                 700]
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
 @pytest.mark.parametrize("d,F,k", [(128, 64, 2), (256, 192, 4)])
-def test_forward_fp8_exact_group_sizes(d, F, k):
+def test_forward_mx_exact_group_sizes(d, F, k, fmt):
     slots = np.repeat(np.arange(len(EXACT_COUNTS), dtype=np.int32), EXACT_COUNTS)
     T = len(slots) // k
     table = np.ascontiguousarray(slots.reshape(k, T).T)
@@ -146,8 +171,8 @@ def test_forward_fp8_exact_group_sizes(d, F, k):
     inp = wl.make_inputs(w, DEV)
     inp["input_ids"] = torch.arange(T, dtype=torch.int32, device=DEV)
     inp["tid2eid"] = torch.from_numpy(table).to(DEV)
-    deq = _dequantised(inp)
-    layer = ops.MoeLayer.from_workload(w, inp, out_dtype=ops.OUT_F32, packed="fp8")
+    deq = _dequantised(inp, fmt)
+    layer = ops.MoeLayer.from_workload(w, inp, out_dtype=ops.OUT_F32, packed=fmt)
     ids = torch.empty((w.T, w.k), dtype=torch.int32, device=DEV)
     logits = torch.empty((w.T, w.E), dtype=torch.float32, device=DEV)
     wts = torch.empty((w.T, w.k), dtype=torch.float32, device=DEV)
