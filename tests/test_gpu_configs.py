@@ -112,17 +112,21 @@ def test_full_size(cfg):
     free_cuda()
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
 @pytest.mark.parametrize("cfg", [2, 4])
-def test_full_size_fp8(cfg):
-    """The MXFP8 routed-weight mode at full size (the 384-expert layer and
-    the hash-routed T=32768 layer, whose experts take 64-wide stages), in the
-    benchmark's launch configuration (--weights fp8): routes bit-exact, and
-    sampled tokens within 1e-2 x RMS of the oracle run on the oracle's own
-    dequantisation of the fp8 weights of the experts those tokens use."""
+def test_full_size_mx(cfg, fmt):
+    """The MXFP8 and MXFP4 routed-weight modes at full size (the 384-expert
+    layer and the hash-routed T=32768 layer, whose experts take 64-wide
+    stages), in the benchmark's launch configuration (--weights fp8 / fp4):
+    routes bit-exact, and sampled tokens within 1e-2 x RMS of the oracle run
+    on the oracle's own dequantisation of the weights of the experts those
+    tokens use."""
+    quant, dequant = ((oracle.quant_mxfp8, oracle.dequant_mxfp8) if fmt == "fp8" else
+                      (oracle.quant_mxfp4, oracle.dequant_mxfp4))
     w = wl.WORKLOADS[cfg]
-    print(f"\n[{w.name}, fp8 weights] generating inputs", flush=True)
+    print(f"\n[{w.name}, {fmt} weights] generating inputs", flush=True)
     inp = wl.make_inputs(w, DEV)
-    layer = ops.MoeLayer.from_workload(w, inp, out_dtype=ops.OUT_F32, packed="fp8")
+    layer = ops.MoeLayer.from_workload(w, inp, out_dtype=ops.OUT_F32, packed=fmt)
     logits = torch.empty((w.T, w.E), dtype=torch.float32, device=DEV)
     ids = torch.empty((w.T, w.k), dtype=torch.int32, device=DEV)
     wts = torch.empty((w.T, w.k), dtype=torch.float32, device=DEV)
@@ -147,14 +151,14 @@ def test_full_size_fp8(cfg):
     for key in ("w_gate", "w_up", "w_down"):
         m = bits(inp[key])
         for e in experts:
-            q, ex = oracle.quant_mxfp8(m[e])
-            m[e] = oracle.dequant_mxfp8(q, ex)
+            q, ex = quant(m[e])
+            m[e] = dequant(q, ex)
         mats[key] = m
     shared = [bits(inp[k]) for k in ("s_gate", "s_up", "s_down")]
     yref = oracle.tokens_forward(bits(inp["x"]), toks, rid, rw, mats["w_gate"], mats["w_up"],
                                  mats["w_down"], *shared, w.clamp_limit, w.clamp_mode)
     rel = check_rms(host(y)[toks], yref)
-    print(f"[{w.name}, fp8 weights] {len(toks)} sampled tokens ({len(experts)} experts): "
+    print(f"[{w.name}, {fmt} weights] {len(toks)} sampled tokens ({len(experts)} experts): "
           f"max|y - y_oracle| / rms = {rel:.2e}", flush=True)
     del layer, inp, y, logits, ids, wts, mats
     free_cuda()
