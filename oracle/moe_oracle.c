@@ -39,7 +39,8 @@
  * form; the combine against the dense reductions (single forced expert,
  * identical experts, scale 0); the MXFP8 encoding against torch's
  * float8_e4m3fn (every code, RNE casts, saturated block codes) and numpy's
- * frexp for the block exponent.
+ * frexp for the block exponent; the MXFP4 encoding against the E2M1 value
+ * table of the OCP specification and brute force over its 16 codes.
  */
 #include <math.h>
 #include <stdint.h>
