@@ -9,9 +9,10 @@ The arithmetic lives in ``moe_oracle.c`` (plain C, fp64, built by
 Parity unpinned: the clamp form (symmetric vs gate-above-only), the shared
 expert's form and the init-std reading are readings of what the pages leave
 open; they are configurable, and every other step is pinned by the tests.
-The fp8 weight encoding (OCP MXFP8: E4M3 values, one power-of-two scale per
-32 values along K) follows the OCP specification the pages' "MxFP8" names;
-its exponent clamp to [-110, 110] is this build's reading.
+The microscaling weight encodings (OCP MXFP8: E4M3 values; OCP MXFP4: E2M1
+values; one power-of-two scale per 32 values along K) follow the OCP
+specification that the pages' "MxFP8" and "MxFP4" name; the clamp of the
+shared exponent to [-110, 110] is a reading, not a rule of the pages.
 """
 from .oracle import (  # noqa: F401
     MODE_TOPK,
