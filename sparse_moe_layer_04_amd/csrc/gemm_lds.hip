@@ -555,10 +555,19 @@ __device__ __forceinline__ void do_tile(LdsTile& t, const GemmArgs& args, int g,
                                         int grp_lo, int grp_hi) {
     using Pn = Panel<EPI>;
     const int N = args.N;
-    const int mt = (grp_hi - grp_lo + TM - 1) / TM;
+    // bf16 weights: m-tiles of TM rows, the last one shorter.  MX weights:
+    // the group's rows split evenly over its mt m-tiles (per rows each,
+    // rounded up to 16, the last tile shorter), so the m-tiles of one n-tile
+    // run at the same pace and share their weight reads in L2; measured on
+    // MI355X, 3% faster for MXFP8 weights at the 384-expert workload and 1%
+    // slower for bf16.  Either way per <= TM, and the last tile holds a row:
+    // n > TM (mt - 1) >= per (mt - 1).
+    const int n = grp_hi - grp_lo;
+    const int mt = (n + TM - 1) / TM;
+    const int per = WF != 0 ? ((n + mt - 1) / mt + 15) & ~15 : TM;
     const int n_tile = local / mt, m_tile = local % mt;
-    t.row0 = grp_lo + m_tile * TM;
-    t.valid = min(TM, grp_hi - t.row0);
+    t.row0 = grp_lo + m_tile * per;
+    t.valid = min(per, grp_hi - t.row0);
     // this expert's packed matrices and the n-tile's first block
     t.np = (N + Pn::P - 1) / Pn::P;
     t.pstride = (size_t)Pn::P * t.K;
