@@ -151,7 +151,7 @@ def main():
                     help="seconds of oracle CPU work for the baseline (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the layer runs on one GPU only (no expert-parallel path); --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
