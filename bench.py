@@ -200,6 +200,23 @@ def main():
     stage_ms /= args.steps
     assert int(layer.flags.item()) == 0, "device flagged invalid ids"
 
+    # The same forward with the 256 MB MALL overwritten before every call (a
+    # 512 MiB fill between calls, outside the timed event pair), reported
+    # beside the back-to-back figure: the gap is what cross-call cache reuse
+    # is worth.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    n_cold = min(args.steps, 5)
+    cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n_cold)]
+    for i, (e0, e1) in enumerate(cold):
+        flush.fill_(i + 1)
+        e0.record()
+        fwd()
+        e1.record()
+    torch.cuda.synchronize()
+    ms_cold = sum(e0.elapsed_time(e1) for e0, e1 in cold) / n_cold
+    del flush
+
     counts = torch.bincount(ids.flatten().long(), minlength=w.E).cpu().numpy()
     n_nonempty = int((counts > 0).sum())
     work = stage_work(w, n_nonempty, 4 if out_dtype == ops.OUT_F32 else 2,
@@ -239,6 +256,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_cold_mall": ms_cold,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
