@@ -112,15 +112,24 @@ def test_full_size(cfg):
     free_cuda()
 
 
+def _mx_tile_split(n):
+    """Rows per m-tile of an expert with n rows in the MX weight modes: the
+    rows split evenly over ceil(n / 256) tiles, rounded up to 16."""
+    mt = -(-n // 256)
+    return (-(-n // mt) + 15) & ~15
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "fp4"])
-@pytest.mark.parametrize("cfg", [2, 4])
+@pytest.mark.parametrize("cfg", [2, 3, 4])
 def test_full_size_mx(cfg, fmt):
     """The MXFP8 and MXFP4 routed-weight modes at full size (the 384-expert
-    layer and the hash-routed T=32768 layer, whose experts take 64-wide
-    stages), in the benchmark's launch configuration (--weights fp8 / fp4):
-    routes bit-exact, and sampled tokens within 1e-2 x RMS of the oracle run
-    on the oracle's own dequantisation of the weights of the experts those
-    tokens use."""
+    layer, the skewed multimodal one and the hash-routed T=32768 layer, whose
+    experts take 64-wide stages), in the benchmark's launch configuration
+    (--weights fp8 / fp4): routes bit-exact, and sampled tokens within
+    1e-2 x RMS of the oracle run on the oracle's own dequantisation of the
+    weights of the experts those tokens use.  The sample includes the rows at
+    the tile boundaries of the busiest expert and of a two-tile expert whose
+    tiles are split evenly (fewer than 256 rows each)."""
     quant, dequant = ((oracle.quant_mxfp8, oracle.dequant_mxfp8) if fmt == "fp8" else
                       (oracle.quant_mxfp4, oracle.dequant_mxfp4))
     w = wl.WORKLOADS[cfg]
@@ -144,6 +153,11 @@ def test_full_size_mx(cfg, fmt):
     e_max = int(np.argmax(counts))
     lo, hi = int(offsets[e_max]), int(offsets[e_max + 1])
     edge = [r for r in (lo, lo + 127, lo + 128, lo + 255, lo + 256, hi - 1) if lo <= r < hi]
+    two = [e for e in range(w.E) if 256 < counts[e] and _mx_tile_split(int(counts[e])) < 256]
+    if two:
+        e2 = min(two, key=lambda e: abs(int(counts[e]) - 320))
+        lo2, per = int(offsets[e2]), _mx_tile_split(int(counts[e2]))
+        edge += [lo2 + per - 1, lo2 + per, int(offsets[e2 + 1]) - 1]
     rng = np.random.default_rng(77)
     toks = np.unique(np.concatenate([rng.choice(w.T, size=6, replace=False), src[edge]]))
     experts = np.unique(rid[toks])
