@@ -120,16 +120,17 @@ def _mx_tile_split(n):
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "fp4"])
-@pytest.mark.parametrize("cfg", [2, 3, 4])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_full_size_mx(cfg, fmt):
-    """The MXFP8 and MXFP4 routed-weight modes at full size (the 384-expert
-    layer, the skewed multimodal one and the hash-routed T=32768 layer, whose
-    experts take 64-wide stages), in the benchmark's launch configuration
-    (--weights fp8 / fp4): routes bit-exact, and sampled tokens within
-    1e-2 x RMS of the oracle run on the oracle's own dequantisation of the
-    weights of the experts those tokens use.  The sample includes the rows at
-    the tile boundaries of the busiest expert and of a two-tile expert whose
-    tiles are split evenly (fewer than 256 rows each)."""
+    """The MXFP8 and MXFP4 routed-weight modes at full size (the 64-expert
+    layer, whose ~384-row experts split into two ~192-row tiles; the
+    384-expert layer; the skewed multimodal one; and the hash-routed T=32768
+    layer, whose experts take 64-wide stages), in the benchmark's launch
+    configuration (--weights fp8 / fp4): routes bit-exact, and sampled tokens
+    within 1e-2 x RMS of the oracle run on the oracle's own dequantisation of
+    the weights of the experts those tokens use.  The sample includes the
+    rows at the tile boundaries of the busiest expert and of a two-tile
+    expert whose tiles are split evenly (fewer than 256 rows each)."""
     quant, dequant = ((oracle.quant_mxfp8, oracle.dequant_mxfp8) if fmt == "fp8" else
                       (oracle.quant_mxfp4, oracle.dequant_mxfp4))
     w = wl.WORKLOADS[cfg]
