@@ -8,19 +8,17 @@
 namespace moe {
 
 int device_cu_count() {
-    static int cached_dev = -1;
-    static int cached_cus = 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (dev != cached_dev) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-        cached_cus = cus;
-        cached_dev = dev;
-    }
-    return cached_cus;
+    // (256, the MI355X count, if the query fails)
+    static DeviceSetup setup;
+    long long cus = 0, unused = 0;
+    const hipError_t err = device_setup(setup, cus, unused, [](int dev, long long& v, long long&) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            n = 0;
+        v = n > 0 ? n : 256;
+        return hipSuccess;
+    });
+    return err == hipSuccess ? (int)cus : 256;
 }
 
 namespace {

@@ -405,26 +405,27 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t stream) {
     constexpr int MAXNTB = EPI == EPI_F32_OFFSET ? 4 : MOE_GEMM_MAXNTB;
     constexpr int RING = MOE_GEMM_RING;
     constexpr int APRE = MOE_GEMM_APRE;
-    static int configured_device = -1;
-    static int grid = 0;
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess) return err;
     const size_t lds = kLdsStages * kLdsStage + (size_t)(MOE_MAX_GROUPS + 1) * sizeof(int);
-    if (configured_device != dev) {
-        err = hipFuncSetAttribute((const void*)grouped_gemm_kernel<EPI, PACKED, MAXNTB, RING, APRE>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (err != hipSuccess) return err;
+    // per device, once: the dynamic LDS limit and the grid (all resident
+    // workgroups, whole rounds of the 8 XCDs)
+    static DeviceSetup setup;
+    long long grid = 0, unused = 0;
+    const hipError_t err = device_setup(setup, grid, unused, [lds](int, long long& gr, long long&) {
+        hipError_t e = hipFuncSetAttribute(
+            (const void*)grouped_gemm_kernel<EPI, PACKED, MAXNTB, RING, APRE>,
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
         int occ = 0;
-        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, grouped_gemm_kernel<EPI, PACKED, MAXNTB, RING, APRE>,
-                                                           256, lds);
-        if (err != hipSuccess) return err;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &occ, grouped_gemm_kernel<EPI, PACKED, MAXNTB, RING, APRE>, 256, lds);
+        if (e != hipSuccess) return e;
         if (occ < 1) occ = 1;
-        grid = device_cu_count() * occ;
-        grid = (grid + 7) & ~7;
-        configured_device = dev;
-    }
-    hipLaunchKernelGGL((grouped_gemm_kernel<EPI, PACKED, MAXNTB, RING, APRE>), dim3(grid), dim3(256), lds, stream, g);
+        gr = ((long long)device_cu_count() * occ + 7) & ~7LL;
+        return hipSuccess;
+    });
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((grouped_gemm_kernel<EPI, PACKED, MAXNTB, RING, APRE>), dim3((unsigned)grid),
+                       dim3(256), lds, stream, g);
     return hipGetLastError();
 }
 

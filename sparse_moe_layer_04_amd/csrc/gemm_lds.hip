@@ -718,29 +718,29 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs arg
 
 template <int EPI, int AM, int WF = 0>
 hipError_t launch_lds(const GemmArgs& g, hipStream_t stream) {
-    static int configured_device = -1;
-    static int grid = 0;
-    static size_t static_lds = 0;
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess) return err;
-    if (configured_device != dev) {
+    // per device, once: the dynamic LDS limit and the grid (one workgroup per
+    // CU, whole rounds of the 8 XCDs)
+    static DeviceSetup setup;
+    long long grid = 0, static_lds = 0;
+    const hipError_t err = device_setup(setup, grid, static_lds, [](int, long long& gr,
+                                                                    long long& st) {
         hipFuncAttributes fa;
-        err = hipFuncGetAttributes(&fa, (const void*)grouped_gemm_lds_kernel<EPI, AM, WF>);
-        if (err != hipSuccess) return err;
-        static_lds = fa.sharedSizeBytes;
-        if (static_lds > (size_t)kStaticLds) return hipErrorInvalidValue;
-        err = hipFuncSetAttribute((const void*)grouped_gemm_lds_kernel<EPI, AM, WF>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  kLdsLimit - (int)static_lds);
-        if (err != hipSuccess) return err;
-        grid = (device_cu_count() + 7) & ~7;
-        configured_device = dev;
-    }
+        hipError_t e = hipFuncGetAttributes(&fa, (const void*)grouped_gemm_lds_kernel<EPI, AM, WF>);
+        if (e != hipSuccess) return e;
+        if (fa.sharedSizeBytes > (size_t)kStaticLds) return hipErrorInvalidValue;
+        e = hipFuncSetAttribute((const void*)grouped_gemm_lds_kernel<EPI, AM, WF>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kLdsLimit - (int)fa.sharedSizeBytes);
+        if (e != hipSuccess) return e;
+        st = (long long)fa.sharedSizeBytes;
+        gr = (device_cu_count() + 7) & ~7;
+        return hipSuccess;
+    });
+    if (err != hipSuccess) return err;
     const size_t lds = kRing + (size_t)(g.G + 1) * sizeof(int);
-    if (lds + static_lds > (size_t)kLdsLimit) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((grouped_gemm_lds_kernel<EPI, AM, WF>), dim3(grid), dim3(kThreads), lds,
-                       stream, g);
+    if (lds + (size_t)static_lds > (size_t)kLdsLimit) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((grouped_gemm_lds_kernel<EPI, AM, WF>), dim3((unsigned)grid), dim3(kThreads),
+                       lds, stream, g);
     return hipGetLastError();
 }
 

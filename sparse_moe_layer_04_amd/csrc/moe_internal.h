@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 
 namespace moe {
@@ -31,6 +33,33 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 // ----------------------------------------------------------------- host -----
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
+
+// Per-device one-time set-up (kernel attributes, grid sizes) that is safe
+// when several host threads make their first calls at once: the set-up of a
+// device runs exactly once (std::call_once), later callers wait for it and
+// then read its error code and the two values it stored.  A failed set-up
+// is not retried.
+constexpr int kMaxDevices = 64;
+
+struct DeviceSetup {
+    std::once_flag once[kMaxDevices];
+    hipError_t err[kMaxDevices] = {};
+    long long v0[kMaxDevices] = {};
+    long long v1[kMaxDevices] = {};
+};
+
+// setup(dev, v0, v1) -> hipError_t runs once for the current device.
+template <class F>
+inline hipError_t device_setup(DeviceSetup& s, long long& v0, long long& v1, F&& setup) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(s.once[dev], [&] { s.err[dev] = setup(dev, s.v0[dev], s.v1[dev]); });
+    v0 = s.v0[dev];
+    v1 = s.v1[dev];
+    return s.err[dev];
+}
 
 // Grouped GEMM epilogues.
 enum GemmEpilogue : int {
