@@ -343,10 +343,11 @@ static int forward_checks(const moe_cfg* c, const moe_weights* w) {
     if (!c || !w) return MOE_ERR_NULL;
     if (c->T < 0 || c->E < 1 || c->k < 1 || c->F_shared < 0) return MOE_ERR_SHAPE;
     if (c->E > MOE_MAX_E || c->k > MOE_MAX_K || c->k > c->E) return MOE_ERR_UNSUPPORTED;
+    // (before T k is formed as an int)
+    if ((long long)c->T * c->k >= (1ll << 31)) return MOE_ERR_SHAPE;
     int st = ffn_checks(c->T * c->k, c->d, c->F, c->clamp_limit, c->clamp_mode);
     if (st != MOE_OK) return st;
     if (c->F_shared % 64) return MOE_ERR_UNSUPPORTED;
-    if ((long long)c->T * c->k >= (1ll << 31)) return MOE_ERR_SHAPE;
     if (c->mode != MOE_MODE_TOPK && c->mode != MOE_MODE_HASH) return MOE_ERR_UNSUPPORTED;
     if (c->out_dtype != MOE_OUT_BF16 && c->out_dtype != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
     if (!(c->scale == c->scale)) return MOE_ERR_SHAPE;

@@ -163,7 +163,7 @@ def test_forward_validation(L):
     assert fwd(wt=wp) == ERR_UNSUPPORTED
     wp.packed = ops.WEIGHTS_FP4                      # MXFP4 weights need their block scales
     assert fwd(wt=wp) == ERR_NULL
-    wp.packed = ops.WEIGHTS_FP8                      # fp8 routed weights need their row scales
+    wp.packed = ops.WEIGHTS_FP8                      # MXFP8 weights need their block scales
     assert fwd(wt=wp) == ERR_NULL
     wp.w_gate_scale = wp.w_up_scale = wp.w_down_scale = FAKE + 4
     assert fwd(wt=wp) == ERR_ALIGN
@@ -173,3 +173,6 @@ def test_forward_validation(L):
     assert fwd(c=c) == ERR_NULL                      # hash mode needs input_ids + tid2eid
     c.T = 0
     assert fwd(c=c, x=None, ws=None) == 0
+    c = ops.MoeCfg.from_buffer_copy(cfg)
+    c.T = 1 << 30                                    # T k = 2^31 routed rows: out of range
+    assert fwd(c=c) == ERR_SHAPE
