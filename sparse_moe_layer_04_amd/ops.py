@@ -122,7 +122,11 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
-def _need(t, dtype, name, dims=None):
+def _need(t, dtype, name, dims=None, shape=None):
+    """Checks a tensor handed to the library as a raw pointer: device,
+    dtype, contiguity, rank and (None entries match any size) shape.  The
+    kernels trust these sizes, so a mismatch is an error here rather than an
+    out-of-bounds access on the device."""
     if t is None:
         raise MoeError(f"{name} is required")
     if not t.is_cuda:
@@ -133,22 +137,36 @@ def _need(t, dtype, name, dims=None):
         raise MoeError(f"{name} must be contiguous")
     if dims is not None and t.dim() != dims:
         raise MoeError(f"{name} must have {dims} dims")
+    if shape is not None and (t.dim() != len(shape) or
+                              any(s is not None and s != n for s, n in zip(shape, t.shape))):
+        want = "[" + ", ".join("*" if s is None else str(s) for s in shape) + "]"
+        raise MoeError(f"{name} must be {want}, got {list(t.shape)}")
     return t
 
 
-def _opt(t, dtype, name):
-    return None if t is None else _need(t, dtype, name)
+def _opt(t, dtype, name, shape=None):
+    return None if t is None else _need(t, dtype, name, shape=shape)
+
+
+def _out(t, dtype, name, shape, device):
+    """An output tensor: allocated when None, else checked like an input."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    return _need(t, dtype, name, shape=shape)
+
+
+def _flags(flags):
+    return _opt(flags, torch.int32, "flags", shape=(1,))
 
 
 def gate_logits(x, w_g, logit_offset=None, out=None):
     """logits[T,E] fp32 = x[T,d] @ w_g[E,d]^T (+ logit_offset[E])."""
     _need(x, torch.bfloat16, "x", 2)
-    _need(w_g, torch.bfloat16, "w_g", 2)
-    _opt(logit_offset, torch.float32, "logit_offset")
     T, d = x.shape
+    _need(w_g, torch.bfloat16, "w_g", shape=(None, d))
     E = w_g.shape[0]
-    if out is None:
-        out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _opt(logit_offset, torch.float32, "logit_offset", shape=(E,))
+    out = _out(out, torch.float32, "out", (T, E), x.device)
     _check(lib().moe_gate_logits(_ptr(x), _ptr(w_g), _ptr(logit_offset), T, d, E, _ptr(out),
                                  _stream()), "moe_gate_logits")
     return out
@@ -159,16 +177,19 @@ def route(logits, k, scale, score_bias=None, modality=None, input_ids=None, tid2
     """Returns (topk_ids[T,k] int32, topk_w[T,k] fp32)."""
     _need(logits, torch.float32, "logits", 2)
     T, E = logits.shape
-    _opt(score_bias, torch.float32, "score_bias")
-    _opt(modality, torch.uint8, "modality")
-    _opt(input_ids, torch.int32, "input_ids")
-    _opt(tid2eid, torch.int32, "tid2eid")
-    n_bias = 0 if score_bias is None else score_bias.numel() // E
+    if score_bias is not None and score_bias.dim() == 1:
+        if score_bias.numel() % E:
+            raise MoeError(f"score_bias must hold whole rows of E = {E} values")
+        score_bias = score_bias.view(-1, E)
+    _opt(score_bias, torch.float32, "score_bias", shape=(None, E))
+    _opt(modality, torch.uint8, "modality", shape=(T,))
+    _opt(input_ids, torch.int32, "input_ids", shape=(T,))
+    _opt(tid2eid, torch.int32, "tid2eid", shape=(None, k))
+    _flags(flags)
+    n_bias = 0 if score_bias is None else score_bias.shape[0]
     V = 0 if tid2eid is None else tid2eid.shape[0]
-    if ids is None:
-        ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
-    if w is None:
-        w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    ids = _out(ids, torch.int32, "ids", (T, k), logits.device)
+    w = _out(w, torch.float32, "w", (T, k), logits.device)
     _check(lib().moe_route(_ptr(logits), _ptr(score_bias), _ptr(modality), _ptr(input_ids),
                            _ptr(tid2eid), T, E, k, n_bias, V, mode, float(scale), _ptr(ids),
                            _ptr(w), _ptr(flags), _stream()), "moe_route")
@@ -182,13 +203,15 @@ def permute_workspace_size(T, k, E):
 def permute(topk_ids, x, E, flags=None, workspace=None):
     """Returns dict(counts, offsets, dest, src, x_perm)."""
     _need(topk_ids, torch.int32, "topk_ids", 2)
-    _need(x, torch.bfloat16, "x", 2)
     T, k = topk_ids.shape
+    _need(x, torch.bfloat16, "x", shape=(T, None))
+    _flags(flags)
     d = x.shape[1]
     dev = x.device
     ws_bytes = permute_workspace_size(T, k, E)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _need(workspace, torch.uint8, "workspace", 1)
     out = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
                offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
                dest=torch.empty(T * k, dtype=torch.int32, device=dev),
@@ -206,17 +229,15 @@ def expert_ffn(a, offsets, w_gate, w_up, w_down, clamp_limit=10.0, clamp_mode=CL
     """Grouped FFN: returns (h[rows,F] bf16, y[rows,d] fp32)."""
     _need(a, torch.bfloat16, "a", 2)
     _need(offsets, torch.int32, "offsets", 1)
-    _need(w_gate, torch.bfloat16, "w_gate", 3)
-    _need(w_up, torch.bfloat16, "w_up", 3)
-    _need(w_down, torch.bfloat16, "w_down", 3)
     rows, d = a.shape
+    _need(w_gate, torch.bfloat16, "w_gate", shape=(None, None, d))
     G, F, _ = w_gate.shape
+    _need(w_up, torch.bfloat16, "w_up", shape=(G, F, d))
+    _need(w_down, torch.bfloat16, "w_down", shape=(G, d, F))
     if offsets.numel() != G + 1:
         raise MoeError("offsets must have G + 1 entries")
-    if h is None:
-        h = torch.empty((rows, F), dtype=torch.bfloat16, device=a.device)
-    if y is None:
-        y = torch.empty((rows, d), dtype=torch.float32, device=a.device)
+    h = _out(h, torch.bfloat16, "h", (rows, F), a.device)
+    y = _out(y, torch.float32, "y", (rows, d), a.device)
     _check(lib().moe_expert_ffn(_ptr(a), _ptr(offsets), G, rows, d, F, _ptr(w_gate), _ptr(w_up),
                                 _ptr(w_down), float(clamp_limit), int(clamp_mode), _ptr(h),
                                 _ptr(y), _stream()), "moe_expert_ffn")
@@ -237,10 +258,8 @@ def expert_ffn_packed(a, offsets, w_gate_p, w_up_p, w_down_p, G, F, clamp_limit=
             raise MoeError(f"{name} is not a packed [{G},{n},{k}] matrix (panel_rows {p})")
     if offsets.numel() != G + 1:
         raise MoeError("offsets must have G + 1 entries")
-    if h is None:
-        h = torch.empty((rows, F), dtype=torch.bfloat16, device=a.device)
-    if y is None:
-        y = torch.empty((rows, d), dtype=torch.float32, device=a.device)
+    h = _out(h, torch.bfloat16, "h", (rows, F), a.device)
+    y = _out(y, torch.float32, "y", (rows, d), a.device)
     _check(lib().moe_expert_ffn_packed(_ptr(a), _ptr(offsets), G, rows, d, F, _ptr(w_gate_p),
                                        _ptr(w_up_p), _ptr(w_down_p), float(clamp_limit),
                                        int(clamp_mode), _ptr(h), _ptr(y), _stream()),
@@ -251,14 +270,15 @@ def expert_ffn_packed(a, offsets, w_gate_p, w_up_p, w_down_p, G, F, clamp_limit=
 def combine(y_perm, dest, topk_w, y_shared=None, out_dtype=OUT_BF16, y=None):
     """y[T,d] = y_shared + sum_j topk_w[t,j] * y_perm[dest[t,j]]."""
     _need(y_perm, torch.float32, "y_perm", 2)
-    _need(dest, torch.int32, "dest")
     _need(topk_w, torch.float32, "topk_w", 2)
-    _opt(y_shared, torch.float32, "y_shared")
     T, k = topk_w.shape
     rows, d = y_perm.shape
-    if y is None:
-        dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
-        y = torch.empty((T, d), dtype=dt, device=y_perm.device)
+    _need(dest, torch.int32, "dest")
+    if dest.numel() != T * k:
+        raise MoeError(f"dest must have T k = {T * k} entries")
+    _opt(y_shared, torch.float32, "y_shared", shape=(T, d))
+    dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+    y = _out(y, dt, "y", (T, d), y_perm.device)
     _check(lib().moe_combine(_ptr(y_perm), _ptr(dest), _ptr(topk_w), _ptr(y_shared), T, d, k,
                              rows, int(out_dtype), _ptr(y), _stream()), "moe_combine")
     return y
@@ -330,15 +350,20 @@ class MoeLayer:
                           V=V, scale=float(scale), clamp_limit=float(clamp_limit),
                           clamp_mode=int(clamp_mode), out_dtype=int(out_dtype))
         self.weights = dict(weights)
-        _need(self.weights["w_g"], torch.bfloat16, "w_g", 2)
-        for key in ("w_gate", "w_up", "w_down"):
-            _need(self.weights[key], torch.bfloat16, key, 3)
+        _need(self.weights["w_g"], torch.bfloat16, "w_g", shape=(E, d))
+        _need(self.weights["w_gate"], torch.bfloat16, "w_gate", shape=(E, F, d))
+        _need(self.weights["w_up"], torch.bfloat16, "w_up", shape=(E, F, d))
+        _need(self.weights["w_down"], torch.bfloat16, "w_down", shape=(E, d, F))
         if F_shared > 0:
-            for key in ("s_gate", "s_up", "s_down"):
-                _need(self.weights[key], torch.bfloat16, key, 2)
-        _opt(self.weights.get("logit_offset"), torch.float32, "logit_offset")
-        _opt(self.weights.get("score_bias"), torch.float32, "score_bias")
-        _opt(self.weights.get("tid2eid"), torch.int32, "tid2eid")
+            _need(self.weights["s_gate"], torch.bfloat16, "s_gate", shape=(F_shared, d))
+            _need(self.weights["s_up"], torch.bfloat16, "s_up", shape=(F_shared, d))
+            _need(self.weights["s_down"], torch.bfloat16, "s_down", shape=(d, F_shared))
+        _opt(self.weights.get("logit_offset"), torch.float32, "logit_offset", shape=(E,))
+        if mode == MODE_TOPK and n_bias > 0:
+            _need(self.weights.get("score_bias"), torch.float32, "score_bias",
+                  shape=(n_bias, E))
+        if mode == MODE_HASH:
+            _need(self.weights.get("tid2eid"), torch.int32, "tid2eid", shape=(V, k))
         fp8 = packed == "fp8"
         fp4 = packed == "fp4"
         if packed:
@@ -378,11 +403,13 @@ class MoeLayer:
         _need(x, torch.bfloat16, "x", 2)
         if tuple(x.shape) != (c.T, c.d):
             raise MoeError(f"x must be [{c.T}, {c.d}]")
-        _opt(input_ids, torch.int32, "input_ids")
-        _opt(modality, torch.uint8, "modality")
-        if y is None:
-            dt = torch.float32 if c.out_dtype == OUT_F32 else torch.bfloat16
-            y = torch.empty((c.T, c.d), dtype=dt, device=x.device)
+        _opt(input_ids, torch.int32, "input_ids", shape=(c.T,))
+        _opt(modality, torch.uint8, "modality", shape=(c.T,))
+        _opt(logits, torch.float32, "logits", shape=(c.T, c.E))
+        _opt(ids, torch.int32, "ids", shape=(c.T, c.k))
+        _opt(w, torch.float32, "w", shape=(c.T, c.k))
+        dt = torch.float32 if c.out_dtype == OUT_F32 else torch.bfloat16
+        y = _out(y, dt, "y", (c.T, c.d), x.device)
         ev = None
         if events is not None:
             if len(events) != FORWARD_STAGES + 1:

@@ -361,3 +361,40 @@ def test_expert_ffn_packed(G, d, F, counts):
     h2, y2 = ops.expert_ffn(a, offs_d, wgt, wup, wdn, 10.0)
     assert np.array_equal(bits(h), bits(h2))
     assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
+
+
+def test_binding_rejects_bad_shapes():
+    """The binding checks every tensor's shape before it hands a raw pointer
+    to the library.  Each wrong tensor here is larger than the right one, so
+    a check that failed to raise could not make a kernel read or write out of
+    bounds; the test would only fail."""
+    rng = np.random.default_rng(5)
+    T, d, E, k, F = 64, 128, 8, 2, 64
+    x = _bf16(rng, (T, d), 1.0)
+    w_g = _bf16(rng, (E, d + 64), 0.1)
+    with pytest.raises(ops.MoeError, match="w_g"):
+        ops.gate_logits(x, w_g)
+    logits = torch.zeros((T, E), dtype=torch.float32, device=DEV)
+    modality = torch.zeros(T + 1, dtype=torch.uint8, device=DEV)
+    bias = torch.zeros((2, E), dtype=torch.float32, device=DEV)
+    with pytest.raises(ops.MoeError, match="modality"):
+        ops.route(logits, k, 1.0, score_bias=bias, modality=modality)
+    a = _bf16(rng, (32, d), 1.0)
+    offs = torch.tensor([0, 16, 32], dtype=torch.int32, device=DEV)
+    wg, wd = _bf16(rng, (2, F, d), 0.1), _bf16(rng, (2, d, F), 0.1)
+    with pytest.raises(ops.MoeError, match="w_up"):
+        ops.expert_ffn(a, offs, wg, _bf16(rng, (2, F, d + 64), 0.1), wd)
+    with pytest.raises(ops.MoeError, match="dest"):
+        ops.combine(torch.zeros((T * k, d), dtype=torch.float32, device=DEV),
+                    torch.zeros(T * k + 1, dtype=torch.int32, device=DEV),
+                    torch.zeros((T, k), dtype=torch.float32, device=DEV))
+    w = wl.small(T=T, d=d, E=E, k=k, F=F, seed=3)
+    inp = wl.make_inputs(w, DEV)
+    bad = dict(inp, w_down=_bf16(rng, (E, d, F + 64), 0.1))
+    with pytest.raises(ops.MoeError, match="w_down"):
+        ops.MoeLayer.from_workload(w, bad)
+    layer = ops.MoeLayer.from_workload(w, inp, packed=True)
+    with pytest.raises(ops.MoeError, match="y must be"):
+        layer.forward(inp["x"], y=torch.empty((T + 1, d), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ops.MoeError, match="ids"):
+        layer.forward(inp["x"], ids=torch.empty((T, k + 1), dtype=torch.int32, device=DEV))
