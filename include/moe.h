@@ -33,6 +33,10 @@
  *   - Scratch memory comes from a caller workspace `ws` of at least the
  *     size the matching *_workspace_size() returns (256-byte aligned).  Calls
  *     that share a workspace must not overlap in time.
+ *   - Calls with distinct workspaces and outputs may come from several host
+ *     threads at once, also as the first calls of a process: the library's
+ *     one-time per-device set-up (kernel attributes, grid sizes) runs once
+ *     per device under a lock, and the library keeps no other host state.
  *   - Results are deterministic: the same inputs give the same bits.
  */
 #ifndef MOE_H
