@@ -5,9 +5,11 @@ permutation, routed + shared expert FFNs, combine) over the resident
 synthetic batch of the chosen workload (default: the 384-expert top-6
 V4-Flash-like layer, T=8192, d=4096, F=2048).  Prints one JSON line.
 
-Per-stage times come from HIP events recorded by the library around its
-stages on the launch stream (moe_forward_timed) during the timed steps; the
-roofline object is for the dominant kernel (longest stage).  The CPU baseline
+The K timed steps replay one captured forward (a HIP graph of the library's
+kernels; --eager times K eager calls instead).  Per-stage times come from
+HIP events recorded by the library around its stages on the launch stream
+(moe_forward_timed) during K eager steps; the roofline object is for the
+dominant kernel (longest stage).  The CPU baseline
 times the C oracle on a bounded token sample on the host cores.
 """
 import argparse
@@ -147,6 +149,10 @@ def main():
                     help="routed expert weights: bf16, MXFP8 (E4M3 codes) or MXFP4 (E2M1 codes), "
                          "one power-of-two scale per 32 values of K (moe_pack_weights_fp8 / "
                          "_fp4; packed layout only)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time K eager moe_forward calls instead of K replays of one captured "
+                         "forward (HIP graph); the per-stage breakdown comes from eager calls "
+                         "either way")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle CPU work for the baseline (0: skip)")
     args = ap.parse_args()
@@ -199,6 +205,24 @@ def main():
             stage_ms[s] += evs[s].elapsed_time(evs[s + 1])
     stage_ms /= args.steps
     assert int(layer.flags.item()) == 0, "device flagged invalid ids"
+
+    ms_eager = ms
+    if not args.eager:
+        # one captured forward, replayed K times between the same barriers
+        # (the first call's one-time kernel set-up ran in the warm-up)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fwd()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            graph.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / args.steps
+        assert int(layer.flags.item()) == 0, "device flagged invalid ids"
 
     # The same forward with the 256 MB MALL overwritten before every call (a
     # 512 MiB fill between calls, outside the timed event pair), reported
@@ -257,6 +281,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms,
         "ms_per_step_cold_mall": ms_cold,
+        "ms_per_step_eager": ms_eager,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -264,7 +289,8 @@ def main():
                   "fp4": "bf16 activations, MXFP4 (E2M1) routed weights"}[args.weights],
         "data": "synthetic",
         "config": dict(w.describe(), out_dtype=args.out_dtype, weight_layout=args.layout,
-                       routed_weights=args.weights, non_empty_experts=n_nonempty,
+                       routed_weights=args.weights, graph=not args.eager,
+                       non_empty_experts=n_nonempty,
                        max_rows_per_expert=int(counts.max())),
         "grouped_gemm_tflops": gg_f / gg_t / 1e12,
         "grouped_gemm_mfma_frac": gg_f / gg_t / PEAK_BF16,
