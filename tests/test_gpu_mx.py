@@ -108,6 +108,7 @@ FP8_CASES = [
     wl.small(T=400, d=192, E=32, k=6, F=128, seed=13, scale=2.5, mode=wl.MODE_HASH, V=500,
              zipf_token_s=1.1),
     wl.small(T=600, d=128, E=8, k=2, F=128, seed=15, scale=1.0),   # 2-3 m-tiles per expert
+    wl.small(T=700, d=128, E=1024, k=8, F=64, seed=16, scale=2.5),  # E and k at their maxima
 ]
 
 
