@@ -130,3 +130,11 @@ def route_flips(xb, wg, off, lg_gpu, bias, modality, ids_gpu, k):
 def free_cuda():
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+
+
+def case_id(w):
+    """pytest id of a workload case: its name, seed and any non-default clamp."""
+    s = f"{w.name}-s{w.seed}"
+    if w.clamp_limit != 10.0 or w.clamp_mode != 0:
+        s += f"-L{w.clamp_limit:g}-m{w.clamp_mode}"
+    return s

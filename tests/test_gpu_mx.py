@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import bits, host, bf16_f64, check_rms
+from gpu_util import bits, host, bf16_f64, case_id, check_rms
 from sparse_moe_layer_04_amd import ops, workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -109,6 +109,8 @@ FP8_CASES = [
              zipf_token_s=1.1),
     wl.small(T=600, d=128, E=8, k=2, F=128, seed=15, scale=1.0),   # 2-3 m-tiles per expert
     wl.small(T=700, d=128, E=1024, k=8, F=64, seed=16, scale=2.5),  # E and k at their maxima
+    wl.small(T=300, d=256, E=16, k=4, F=192, seed=18, scale=2.5, clamp_limit=0.5,
+             clamp_mode=1),                                          # the clamp saturates
 ]
 
 
@@ -126,7 +128,7 @@ def _dequantised(inp, fmt="fp8"):
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "fp4"])
-@pytest.mark.parametrize("w", FP8_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("w", FP8_CASES, ids=case_id)
 def test_forward_mx(w, fmt):
     inp = wl.make_inputs(w, DEV)
     deq = _dequantised(inp, fmt)

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import bits, host, bf16_f64, check_logits, check_h, check_rms, ffn_h_bound
+from gpu_util import bits, host, bf16_f64, case_id, check_logits, check_h, check_rms, ffn_h_bound
 from sparse_moe_layer_04_amd import ops, workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -275,6 +275,9 @@ FWD_CASES = [
     # the largest expert count and top-k the library takes (E = 1024, k = 8)
     wl.small(T=700, d=128, E=1024, k=8, F=64, seed=16, scale=2.5, n_bias=2, vision_spans=1,
              span_len=200),
+    # a clamp limit that many gate/up pre-activations exceed, both clamp forms
+    wl.small(T=300, d=256, E=16, k=4, F=192, seed=17, scale=2.5, clamp_limit=0.5),
+    wl.small(T=300, d=256, E=16, k=4, F=192, seed=18, scale=2.5, clamp_limit=0.5, clamp_mode=1),
 ]
 
 
@@ -309,7 +312,7 @@ def _check_forward(w, inp, out_dtype, packed):
     return host(ids)
 
 
-@pytest.mark.parametrize("w", FWD_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("w", FWD_CASES, ids=case_id)
 @pytest.mark.parametrize("out_dtype", [ops.OUT_F32, ops.OUT_BF16])
 @pytest.mark.parametrize("packed", [False, True], ids=["plain", "packed"])
 def test_forward(w, out_dtype, packed):
