@@ -109,6 +109,7 @@ FP8_CASES = [
              zipf_token_s=1.1),
     wl.small(T=600, d=128, E=8, k=2, F=128, seed=15, scale=1.0),   # 2-3 m-tiles per expert
     wl.small(T=700, d=128, E=1024, k=8, F=64, seed=16, scale=2.5),  # E and k at their maxima
+    wl.small(T=1, d=256, E=64, k=6, F=128, seed=19, scale=2.5),     # one token
     wl.small(T=300, d=256, E=16, k=4, F=192, seed=18, scale=2.5, clamp_limit=0.5,
              clamp_mode=1),                                          # the clamp saturates
 ]

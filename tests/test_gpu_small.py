@@ -272,6 +272,10 @@ FWD_CASES = [
     wl.small(T=400, d=192, E=32, k=6, F=128, seed=13, scale=2.5, mode=wl.MODE_HASH, V=500,
              zipf_token_s=1.1),
     wl.small(T=130, d=64, E=1, k=1, F=64, seed=14, F_shared=0),
+    # one and two tokens (decode): one row per routed expert, one or two in
+    # the shared expert
+    wl.small(T=1, d=256, E=64, k=6, F=128, seed=19, scale=2.5),
+    wl.small(T=2, d=128, E=8, k=8, F=64, seed=20, n_bias=2, vision_spans=1, span_len=1),
     # the largest expert count and top-k the library takes (E = 1024, k = 8)
     wl.small(T=700, d=128, E=1024, k=8, F=64, seed=16, scale=2.5, n_bias=2, vision_spans=1,
              span_len=200),
