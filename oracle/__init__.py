@@ -25,6 +25,7 @@ from .oracle import (  # noqa: F401
     score,
     gate_logits,
     route,
+    route_backward,
     permute,
     gather,
     expert_ffn,

@@ -253,6 +253,58 @@ unsigned orc_route(const float* logits, const float* bias, const uint8_t* modali
     return flags;
 }
 
+/* ------------------------------------------------------ routing backward -- */
+/*
+ * Gradient of the routing weights with respect to the router logits: the
+ * first link of MegaGate's backward ("HyperParallel accelerates DeepSeek-V4.1
+ * ...", section 2.3: the gate's normalisation and scaling steps, whose
+ * gradients the fused backward chain carries).  The forward gives
+ *   g_j = S(l[t, ids_j])  (the pinned binary32 sigmoid),
+ *   w_j = scale * g_j / sum_i g_i.
+ * The expert choice is piecewise constant in the logits and the ranking
+ * bias takes no part in w, so only the k selected logits of a token get a
+ * gradient:
+ *   dg_i = (scale / G) * (dw_i - sum_j dw_j g_j / G),   G = sum_j g_j,
+ *   dl[t, ids_i] += dg_i * g_i * (1 - g_i)   (the logistic derivative at the
+ *                                             forward's score value),
+ * and every other entry of the row is 0.  A token whose ids are not all in
+ * [0, E) (dropped by the forward) gets a zero row and sets
+ * ORC_FLAG_BAD_EXPERT_ID.  All arithmetic after S() is fp64.
+ */
+unsigned orc_route_backward(const float* logits, const int32_t* ids, const float* dw,
+                            int T, int E, int k, float scale, double* dl)
+{
+    unsigned flags = 0;
+    double g[64];
+    for (int t = 0; t < T; ++t) {
+        const float* lt = logits + (size_t)t * E;
+        const int32_t* it = ids + (size_t)t * k;
+        const float* dwt = dw + (size_t)t * k;
+        double* out = dl + (size_t)t * E;
+        for (int e = 0; e < E; ++e)
+            out[e] = 0.0;
+        int valid = 1;
+        for (int j = 0; j < k; ++j)
+            if (it[j] < 0 || it[j] >= E)
+                valid = 0;
+        if (!valid) {
+            flags |= ORC_FLAG_BAD_EXPERT_ID;
+            continue;
+        }
+        double G = 0.0, dot = 0.0;
+        for (int j = 0; j < k; ++j) {
+            g[j] = (double)orc_score(lt[it[j]]);
+            G += g[j];
+            dot += (double)dwt[j] * g[j];
+        }
+        for (int j = 0; j < k; ++j) {
+            double dg = (double)scale / G * ((double)dwt[j] - dot / G);
+            out[it[j]] += dg * g[j] * (1.0 - g[j]);
+        }
+    }
+    return flags;
+}
+
 /* ------------------------------------------------------------ permutation -- */
 /*
  * Dispatch (Twinkle: ids from either router become global expert ids ->

@@ -49,6 +49,8 @@ def load():
     lib.orc_gate_logits.restype = None
     lib.orc_route.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, P]
     lib.orc_route.restype = ctypes.c_uint
+    lib.orc_route_backward.argtypes = [P, P, P, I, I, I, F, P]
+    lib.orc_route_backward.restype = ctypes.c_uint
     lib.orc_permute.argtypes = [P, I, I, I, P, P, P, P]
     lib.orc_permute.restype = ctypes.c_uint
     lib.orc_gather.argtypes = [P, P, I64, I, P]
@@ -144,6 +146,20 @@ def route(logits, k, scale, bias=None, modality=None, input_ids=None, tid2eid=No
     flags = load().orc_route(_p(logits), _p(bias), _p(modality), _p(input_ids), _p(tid2eid),
                              T, E, k, n_bias, V, mode, float(scale), _p(ids), _p(w))
     return ids, w, int(flags)
+
+
+def route_backward(logits, ids, dw, scale):
+    """Gradient of the routing weights w.r.t. the logits (orc_route_backward):
+    returns (dlogits[T,E] float64, flags)."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    ids = _c(ids, np.int32)
+    dw = _c(dw, np.float32)
+    k = ids.shape[1]
+    assert ids.shape == (T, k) and dw.shape == (T, k) and k <= 64
+    dl = np.empty((T, E), np.float64)
+    flags = load().orc_route_backward(_p(logits), _p(ids), _p(dw), T, E, k, float(scale), _p(dl))
+    return dl, int(flags)
 
 
 def permute(ids, E):
