@@ -241,6 +241,40 @@ def main():
     ms_cold = sum(e0.elapsed_time(e1) for e0, e1 in cold) / n_cold
     del flush
 
+    # The routing backward (moe_route_backward: the routing weights' gradient
+    # taken back to the logits) on this workload's own forward routes, timed
+    # outside the forward step: 20 calls captured in one graph, replayed
+    # between two events (each call is a few microseconds of device work,
+    # less than the host cost of one call).
+    lg_b = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
+    ids_b = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    layer.forward(inp["x"], input_ids=inp["input_ids"], modality=inp["modality"], logits=lg_b,
+                  ids=ids_b)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    dw_b = torch.randn((w.T, w.k), generator=gen, device=dev)
+    dl_b = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
+    ops.route_backward(lg_b, ids_b, dw_b, w.scale, out=dl_b)
+    torch.cuda.synchronize()
+    n_rb = 20
+    rb_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(rb_graph):
+        for _ in range(n_rb):
+            ops.route_backward(lg_b, ids_b, dw_b, w.scale, out=dl_b)
+    rb_graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    rb_graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    rb_ms = e0.elapsed_time(e1) / n_rb
+    # ids, dw and the k gathered logits read; the whole d_logits row written
+    rb_bytes = w.T * w.k * 12 + w.T * w.E * 4
+    route_backward = {"ms": rb_ms, "GB/s": rb_bytes / rb_ms / 1e6,
+                      "frac_of_hbm_peak": rb_bytes / rb_ms / 1e6 / (PEAK_HBM / 1e9),
+                      "algorithmic_bytes": rb_bytes}
+
     counts = torch.bincount(ids.flatten().long(), minlength=w.E).cpu().numpy()
     n_nonempty = int((counts > 0).sum())
     work = stage_work(w, n_nonempty, 4 if out_dtype == ops.OUT_F32 else 2,
@@ -296,6 +330,7 @@ def main():
         "grouped_gemm_mfma_frac": gg_f / gg_t / PEAK_BF16,
         "roofline": roof,
         "stages": stages,
+        "route_backward": route_backward,
     }
     if args.cpu_budget > 0:
         print("# timing the CPU oracle baseline", file=sys.stderr, flush=True)

@@ -115,6 +115,28 @@ int moe_route(const float* logits, const float* score_bias, const uint8_t* modal
               uint32_t* d_flags, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Routing backward [HP 2.3 MegaGate: the gradient chain of the gate's
+ * normalisation and scaling, the first step of the gate's backward].
+ * Given the forward's logits and routes and the gradient d_topk_w[t,j] of a
+ * loss with respect to topk_w[t,j]:
+ *   g_j = S(logits[t, topk_ids[t,j]]) (the forward's scores), G = sum_j g_j,
+ *   d_logits[t, topk_ids[t,i]] = (scale / G) * (d_topk_w[t,i]
+ *                                 - sum_j d_topk_w[t,j] g_j / G) * g_i (1 - g_i)
+ *   and d_logits[t,e] = 0 for every expert the token did not select (the
+ *   choice is piecewise constant in the logits; the ranking bias takes no
+ *   part in the weights).  fp32 arithmetic, sums in slot order; the bracket
+ *   is evaluated as sum_j g_j (d_topk_w[t,i] - d_topk_w[t,j]) / G, so it is
+ *   exactly 0 when k = 1 or all d_topk_w of a token are equal.
+ *   logits [T,E] fp32; topk_ids [T,k] int32; d_topk_w [T,k] fp32;
+ *   d_logits [T,E] fp32 (every entry written).  A token with an id outside
+ *   [0,E) (as the forward leaves dropped hash tokens) gets a zero row and
+ *   sets MOE_FLAG_BAD_EXPERT_ID.  Same limits on E and k as moe_route.
+ */
+int moe_route_backward(const float* logits, const int32_t* topk_ids, const float* d_topk_w,
+                       int T, int E, int k, float scale, float* d_logits, uint32_t* d_flags,
+                       void* stream);
+
+/* ------------------------------------------------------------------------
  * Token dispatch [TW: ids from either router -> expert_mask -> one dispatch
  * flow; HP 2.3 MegaMoE token dispatch].  On one device the expert-parallel
  * all-to-all becomes a stable counting sort of the (t, j) pairs, t-major, by

@@ -265,6 +265,8 @@ unsigned orc_route(const float* logits, const float* bias, const uint8_t* modali
  * bias takes no part in w, so only the k selected logits of a token get a
  * gradient:
  *   dg_i = (scale / G) * (dw_i - sum_j dw_j g_j / G),   G = sum_j g_j,
+ *        = (scale / G) * sum_j g_j (dw_i - dw_j) / G   (evaluated so: exactly
+ *          0 for k = 1 or equal dw, where the weights are constant),
  *   dl[t, ids_i] += dg_i * g_i * (1 - g_i)   (the logistic derivative at the
  *                                             forward's score value),
  * and every other entry of the row is 0.  A token whose ids are not all in
@@ -291,15 +293,17 @@ unsigned orc_route_backward(const float* logits, const int32_t* ids, const float
             flags |= ORC_FLAG_BAD_EXPERT_ID;
             continue;
         }
-        double G = 0.0, dot = 0.0;
+        double G = 0.0;
         for (int j = 0; j < k; ++j) {
             g[j] = (double)orc_score(lt[it[j]]);
             G += g[j];
-            dot += (double)dwt[j] * g[j];
         }
-        for (int j = 0; j < k; ++j) {
-            double dg = (double)scale / G * ((double)dwt[j] - dot / G);
-            out[it[j]] += dg * g[j] * (1.0 - g[j]);
+        for (int i = 0; i < k; ++i) {
+            double br = 0.0;
+            for (int j = 0; j < k; ++j)
+                br += g[j] * ((double)dwt[i] - (double)dwt[j]);
+            double dg = (double)scale / G * (br / G);
+            out[it[i]] += dg * g[i] * (1.0 - g[i]);
         }
     }
     return flags;

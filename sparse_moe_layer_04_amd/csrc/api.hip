@@ -169,6 +169,18 @@ int moe_route(const float* logits, const float* score_bias, const uint8_t* modal
                                    d_flags, as_stream(stream)));
 }
 
+int moe_route_backward(const float* logits, const int32_t* topk_ids, const float* d_topk_w,
+                       int T, int E, int k, float scale, float* d_logits, uint32_t* d_flags,
+                       void* stream) {
+    if (T < 0 || E < 1 || k < 1) return MOE_ERR_SHAPE;
+    if (E > MOE_MAX_E || k > MOE_MAX_K || k > E) return MOE_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !d_topk_w || !d_logits) return MOE_ERR_NULL;
+    return hip_status(launch_route_backward(logits, topk_ids, d_topk_w, T, E, k, scale, d_logits,
+                                            d_flags, as_stream(stream)));
+}
+
 size_t moe_permute_workspace_size(int T, int k, int E) {
     if (T < 0 || k < 1 || E < 1) return 0;
     return permute_workspace_bytes(T, k, E);

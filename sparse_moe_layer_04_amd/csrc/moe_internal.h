@@ -140,6 +140,10 @@ hipError_t launch_route(const float* logits, const float* bias, const uint8_t* m
                         int n_bias, int V, int mode, float scale, int32_t* ids, float* w,
                         uint32_t* flags, hipStream_t stream);
 
+hipError_t launch_route_backward(const float* logits, const int32_t* ids, const float* dw,
+                                 int T, int E, int k, float scale, float* dl, uint32_t* flags,
+                                 hipStream_t stream);
+
 size_t permute_workspace_bytes(int T, int k, int E);
 hipError_t launch_permute(const int32_t* ids, const uint16_t* x, int T, int d, int E, int k,
                           int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,

@@ -197,6 +197,71 @@ __global__ __launch_bounds__(256) void route_hash_kernel(
     }
 }
 
+// Routing backward ("HyperParallel accelerates DeepSeek-V4.1 ...", section
+// 2.3, MegaGate: the gradient chain of the gate's normalisation and scaling):
+// given dw[t, j] = dLoss/dw_j for the routing weights
+//   w_j = scale * g_j / G,  g_j = S(l[t, ids_j]),  G = sum_j g_j,
+// the logits' gradient is
+//   dl[t, ids_i] = (scale / G) * (dw_i - sum_j dw_j g_j / G) * g_i (1 - g_i)
+// and 0 for the E - k experts the token did not select (the choice is
+// piecewise constant in the logits; the ranking bias takes no part in w).
+// The bracket is evaluated as sum_j g_j (dw_i - dw_j) / G (equal, since
+// sum_j g_j = G): no cancellation between dw_i and the weighted mean, and
+// exactly 0 when k = 1 or all dw are equal, as the weights are then
+// constant.  One wave per token: lane j < k holds slot j; G and the bracket
+// are summed in slot order in fp32; then every lane writes its entries
+// e = lane + 64 i of the row (each entry written once; an expert listed in
+// two slots gets the sum).  A token with an id outside [0, E) gets a zero
+// row and sets MOE_FLAG_BAD_EXPERT_ID.
+__global__ __launch_bounds__(256) void route_backward_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ ids,
+    const float* __restrict__ dw, int T, int E, int k, float scale, float* __restrict__ dl,
+    uint32_t* __restrict__ flags) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;                          // (wave-uniform)
+    int id = -1;
+    float dwj = 0.0f;
+    if (lane < k) {
+        id = ids[(size_t)t * k + lane];
+        dwj = dw[(size_t)t * k + lane];
+    }
+    const bool bad = __builtin_amdgcn_ballot_w64(lane < k && (id < 0 || id >= E)) != 0;
+    float* out = dl + (size_t)t * E;
+    if (bad) {
+        for (int e = lane; e < E; e += 64) out[e] = 0.0f;
+        if (lane == 0 && flags) atomicOr(flags, MOE_FLAG_BAD_EXPERT_ID);
+        return;
+    }
+    const float g = lane < k ? score_fn(logits[(size_t)t * E + id]) : 0.0f;
+    float G = lane_read(g, 0);
+    float br = lane_read(g, 0) * (dwj - lane_read(dwj, 0));
+    for (int j = 1; j < k; ++j) {
+        G = G + lane_read(g, j);
+        br = br + lane_read(g, j) * (dwj - lane_read(dwj, j));
+    }
+    float dlj = 0.0f;
+    if (lane < k) {
+        const float dg = scale / G * (br / G);
+        dlj = dg * (g * (1.0f - g));
+    }
+    // the k (id, gradient) pairs, wave-uniform, read once for the whole row
+    int sid[MOE_MAX_K];
+    float sdl[MOE_MAX_K];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K; ++j) {
+        sid[j] = j < k ? __builtin_amdgcn_readlane(id, j) : -1;
+        sdl[j] = j < k ? lane_read(dlj, j) : 0.0f;
+    }
+    for (int e = lane; e < E; e += 64) {
+        float v = 0.0f;
+#pragma unroll
+        for (int j = 0; j < MOE_MAX_K; ++j)
+            if (sid[j] == e) v = v + sdl[j];
+        out[e] = v;
+    }
+}
+
 template <int NPL>
 void launch_topk(dim3 grid, const float* logits, const float* bias, const uint8_t* modality,
                  int T, int E, int k, int n_bias, float scale, int32_t* ids, float* w,
@@ -232,6 +297,15 @@ hipError_t launch_route(const float* logits, const float* bias, const uint8_t* m
     else
         launch_topk<kMaxPerLane>(grid, logits, bias, modality, T, E, k, n_bias, scale, ids, w,
                                  stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_backward(const float* logits, const int32_t* ids, const float* dw,
+                                 int T, int E, int k, float scale, float* dl, uint32_t* flags,
+                                 hipStream_t stream) {
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(route_backward_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits,
+                       ids, dw, T, E, k, scale, dl, flags);
     return hipGetLastError();
 }
 

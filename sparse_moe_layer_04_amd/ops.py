@@ -77,6 +77,7 @@ def lib():
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_gate_logits.argtypes = [P, P, P, I, I, I, P, P]
     L.moe_route.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, P]
+    L.moe_route_backward.argtypes = [P, P, P, I, I, I, F, P, P, P]
     L.moe_permute_workspace_size.argtypes = [I, I, I]
     L.moe_permute_workspace_size.restype = S
     L.moe_permute.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, S, P]
@@ -194,6 +195,22 @@ def route(logits, k, scale, score_bias=None, modality=None, input_ids=None, tid2
                            _ptr(tid2eid), T, E, k, n_bias, V, mode, float(scale), _ptr(ids),
                            _ptr(w), _ptr(flags), _stream()), "moe_route")
     return ids, w
+
+
+def route_backward(logits, ids, dw, scale, flags=None, out=None):
+    """Gradient of the routing weights with respect to the logits
+    (moe_route_backward): returns d_logits[T,E] fp32 for dw[T,k]."""
+    _need(logits, torch.float32, "logits", 2)
+    T, E = logits.shape
+    _need(ids, torch.int32, "ids", 2)
+    k = ids.shape[1]
+    _need(ids, torch.int32, "ids", shape=(T, k))
+    _need(dw, torch.float32, "dw", shape=(T, k))
+    _flags(flags)
+    out = _out(out, torch.float32, "out", (T, E), logits.device)
+    _check(lib().moe_route_backward(_ptr(logits), _ptr(ids), _ptr(dw), T, E, k, float(scale),
+                                    _ptr(out), _ptr(flags), _stream()), "moe_route_backward")
+    return out
 
 
 def permute_workspace_size(T, k, E):

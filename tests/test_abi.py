@@ -57,6 +57,24 @@ def test_route_validation(L):
     assert route(L, T=0, logits=None, ids=None, w=None) == 0   # empty: nothing to do
 
 
+def test_route_backward_validation(L):
+    def rb(T=4, E=8, k=2, scale=1.0, logits=FAKE, ids=FAKE, dw=FAKE, out=FAKE):
+        return L.moe_route_backward(logits, ids, dw, T, E, k, ctypes.c_float(scale), out, None,
+                                    None)
+    assert rb(k=0) == ERR_SHAPE
+    assert rb(E=0) == ERR_SHAPE
+    assert rb(T=-1) == ERR_SHAPE
+    assert rb(k=9, E=16) == ERR_UNSUPPORTED
+    assert rb(k=3, E=2) == ERR_UNSUPPORTED
+    assert rb(E=2000) == ERR_UNSUPPORTED
+    assert rb(scale=float("nan")) == ERR_SHAPE
+    assert rb(logits=None) == ERR_NULL
+    assert rb(ids=None) == ERR_NULL
+    assert rb(dw=None) == ERR_NULL
+    assert rb(out=None) == ERR_NULL
+    assert rb(T=0, logits=None, ids=None, dw=None, out=None) == 0
+
+
 def test_gate_logits_validation(L):
     assert L.moe_gate_logits(FAKE, FAKE, None, 4, 100, 8, FAKE, None) == ERR_UNSUPPORTED
     assert L.moe_gate_logits(FAKE, FAKE, None, 4, 32, 8, FAKE, None) == ERR_SHAPE

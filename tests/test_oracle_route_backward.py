@@ -79,7 +79,7 @@ def test_constant_weights_have_no_gradient():
     assert np.all(dl == 0.0)                  # k = 1: w = scale whatever the logits
     lg, ids, _ = _case(16, 32, 6, 4)
     dl, _ = oracle.route_backward(lg, ids, np.full((16, 6), 0.75, np.float32), 2.5)
-    assert np.all(np.abs(dl) <= 1e-16)        # equal dw: sum_j w_j = scale is constant
+    assert np.all(dl == 0.0)                  # equal dw: sum_j w_j = scale is constant
 
 
 def test_invalid_ids_zero_row_and_flag():
