@@ -31,6 +31,7 @@ from .oracle import (  # noqa: F401
     expert_ffn,
     expert_ffn_rows,
     combine,
+    combine_backward,
     tokens_forward,
     forward,
     e4m3_decode,

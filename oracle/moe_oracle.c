@@ -494,6 +494,37 @@ void orc_combine(const double* y_perm, const int32_t* dest, const float* w, cons
 }
 
 /*
+ * Backward of the combine (the result return merged by routing weight,
+ * "Twinkle x Ascend ...", section "FSDP2-4D parallel engine adaptation"):
+ * for y[t] = y_shared[t] + sum_j w[t,j] Y_perm[dest[t,j]] and a gradient dy
+ * of the output,
+ *   dY_perm[dest[t,j], o] = w[t,j] * dy[t,o]          (not rounded),
+ *   dw[t,j]               = sum_o dy[t,o] * Y_perm[dest[t,j], o],
+ * and dy_shared = dy.  A pair with dest outside [0, rows) gets dw = 0 and
+ * writes no row; rows no pair maps to are left as they are.  fp64.
+ */
+void orc_combine_backward(const float* dy, const float* y_perm, const int32_t* dest,
+                          const float* w, int T, int d, int k, int rows,
+                          double* dy_perm, double* dw)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            int32_t row = dest[(size_t)t * k + j];
+            double acc = 0.0;
+            if (row >= 0 && row < rows) {
+                for (int o = 0; o < d; ++o) {
+                    double g = (double)dy[(size_t)t * d + o];
+                    acc += g * (double)y_perm[(size_t)row * d + o];
+                    dy_perm[(size_t)row * d + o] = (double)w[(size_t)t * k + j] * g;
+                }
+            }
+            dw[(size_t)t * k + j] = acc;
+        }
+    }
+}
+
+/*
  * The layer output for a list of tokens, from their routing (ids, w):
  *   y[t] = FFN_shared(x[t]) + sum_j w[t,j] * FFN_{ids[t,j]}(x[t]).
  * Identical by definition to permute -> grouped FFN -> combine, because every

@@ -77,6 +77,8 @@ def load():
     lib.orc_dequant_mxfp4.restype = None
     lib.orc_combine.argtypes = [P, P, P, P, I, I, I, P]
     lib.orc_combine.restype = None
+    lib.orc_combine_backward.argtypes = [P, P, P, P, I, I, I, I, P, P]
+    lib.orc_combine_backward.restype = None
     lib.orc_tokens_forward.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, P, I, D, I, P]
     lib.orc_tokens_forward.restype = None
     _LIB = lib
@@ -213,6 +215,24 @@ def expert_ffn_rows(a, rows, experts, w_gate, w_up, w_down, clamp_limit, clamp_m
     load().orc_expert_ffn_rows(_p(a), _p(rows), _p(experts), n, d, F, _p(w_gate), _p(w_up),
                                _p(w_down), float(clamp_limit), int(clamp_mode), _p(h), _p(y))
     return h, y
+
+
+def combine_backward(dy, y_perm, dest, w, dy_perm=None):
+    """Backward of the combine (orc_combine_backward): returns
+    (dy_perm[rows,d] float64, dw[T,k] float64); rows no pair maps to keep the
+    values of `dy_perm` (zeros if None)."""
+    dy = _c(dy, np.float32)
+    y_perm = _c(y_perm, np.float32)
+    dest = _c(dest, np.int32)
+    w = _c(w, np.float32)
+    T, k = w.shape
+    rows, d = y_perm.shape
+    assert dy.shape == (T, d) and dest.size == T * k
+    out = np.zeros((rows, d), np.float64) if dy_perm is None else _c(dy_perm, np.float64).copy()
+    dw = np.empty((T, k), np.float64)
+    load().orc_combine_backward(_p(dy), _p(y_perm), _p(dest), _p(w), T, d, k, rows, _p(out),
+                                _p(dw))
+    return out, dw
 
 
 def combine(y_perm, dest, w, ysh=None):
