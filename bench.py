@@ -248,8 +248,9 @@ def main():
     # less than the host cost of one call).
     lg_b = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
     ids_b = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    wts_b = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
     layer.forward(inp["x"], input_ids=inp["input_ids"], modality=inp["modality"], logits=lg_b,
-                  ids=ids_b)
+                  ids=ids_b, w=wts_b)
     gen = torch.Generator(device=dev)
     gen.manual_seed(7)
     dw_b = torch.randn((w.T, w.k), generator=gen, device=dev)
@@ -274,6 +275,37 @@ def main():
     route_backward = {"ms": rb_ms, "GB/s": rb_bytes / rb_ms / 1e6,
                       "frac_of_hbm_peak": rb_bytes / rb_ms / 1e6 / (PEAK_HBM / 1e9),
                       "algorithmic_bytes": rb_bytes}
+    del rb_graph, dl_b, lg_b
+
+    # The combine backward (moe_combine_backward: the output gradient taken
+    # to the expert outputs and the routing weights) at this workload's
+    # shapes: the forward's routes and weights, random fp32 expert outputs
+    # and output gradient; 5 calls between two events.
+    # (dest of the forward's dispatch: each pair's row in the stable
+    # expert-major order; setup data, computed here with torch)
+    order = torch.argsort(ids_b.flatten().long(), stable=True)
+    dest_b = torch.empty(w.T * w.k, dtype=torch.int32, device=dev)
+    dest_b[order] = torch.arange(w.T * w.k, dtype=torch.int32, device=dev)
+    del order
+    yp_b = torch.randn((w.T * w.k, w.d), generator=gen, device=dev)
+    dy_b = torch.randn((w.T, w.d), generator=gen, device=dev)
+    dyp_b = torch.empty_like(yp_b)
+    dwt_b = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    ops.combine_backward(dy_b, yp_b, dest_b, wts_b, dy_perm=dyp_b, d_topk_w=dwt_b)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        ops.combine_backward(dy_b, yp_b, dest_b, wts_b, dy_perm=dyp_b, d_topk_w=dwt_b)
+    e1.record()
+    torch.cuda.synchronize()
+    cb_ms = e0.elapsed_time(e1) / 5
+    # dy and every routed expert output read, every expert-output gradient
+    # written, dest / w read and d_topk_w written
+    cb_bytes = w.T * w.d * 4 + 2 * w.T * w.k * w.d * 4 + w.T * w.k * 12
+    combine_backward = {"ms": cb_ms, "GB/s": cb_bytes / cb_ms / 1e6,
+                        "frac_of_hbm_peak": cb_bytes / cb_ms / 1e6 / (PEAK_HBM / 1e9),
+                        "algorithmic_bytes": cb_bytes}
+    del yp_b, dy_b, dyp_b, dest_b
 
     counts = torch.bincount(ids.flatten().long(), minlength=w.E).cpu().numpy()
     n_nonempty = int((counts > 0).sum())
@@ -331,6 +363,7 @@ def main():
         "roofline": roof,
         "stages": stages,
         "route_backward": route_backward,
+        "combine_backward": combine_backward,
     }
     if args.cpu_budget > 0:
         print("# timing the CPU oracle baseline", file=sys.stderr, flush=True)

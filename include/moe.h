@@ -270,6 +270,24 @@ int moe_combine(const float* y_perm, const int32_t* dest, const float* topk_w,
                 void* stream);
 
 /* ------------------------------------------------------------------------
+ * Combine backward [TW: the merge by routing weight; its gradients feed
+ * the expert outputs and, through moe_route_backward, the router].  For a
+ * gradient dy of the layer output y = y_shared + sum_j w[t,j] y_perm[dest]:
+ *   dy_perm[dest[t,j], o] = fl32(topk_w[t,j] * dy[t,o]),
+ *   d_topk_w[t,j] = sum_o dy[t,o] * y_perm[dest[t,j], o]   (fp32 fma
+ *                   partials reduced over the workgroup in a fixed order),
+ *   and the shared expert's output gradient is dy itself (nothing to do).
+ *   dy [T,d] fp32; y_perm [rows,d] fp32 (the forward's expert outputs);
+ *   dest [T*k] int32; topk_w [T,k] fp32; dy_perm [rows,d] fp32 (rows that
+ *   no pair maps to are left untouched); d_topk_w [T,k] fp32 (written).
+ *   A pair with dest outside [0, rows) gets d_topk_w = 0 and writes no
+ *   row.  d multiple of 8, k <= 8; dy, y_perm and dy_perm 16-byte aligned.
+ */
+int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* dest,
+                         const float* topk_w, int T, int d, int k, int rows, float* dy_perm,
+                         float* d_topk_w, void* stream);
+
+/* ------------------------------------------------------------------------
  * Whole layer forward: gate logits -> route -> permute -> grouped FFN (routed
  * experts) and FFN (shared expert) -> combine.
  */

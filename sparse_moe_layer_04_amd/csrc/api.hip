@@ -351,6 +351,21 @@ int moe_combine(const float* y_perm, const int32_t* dest, const float* topk_w,
                                      as_stream(stream)));
 }
 
+int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* dest,
+                         const float* topk_w, int T, int d, int k, int rows, float* dy_perm,
+                         float* d_topk_w, void* stream) {
+    if (T < 0 || d < 8 || k < 1 || rows < 0) return MOE_ERR_SHAPE;
+    if (k > MOE_MAX_K || d % 8) return MOE_ERR_UNSUPPORTED;
+    if ((long long)rows * d >= (1ll << 40) || (long long)T * d >= (1ll << 40)) return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!dy || !dest || !topk_w || !d_topk_w || (rows > 0 && (!y_perm || !dy_perm)))
+        return MOE_ERR_NULL;
+    if (!aligned16(dy) || (y_perm && !aligned16(y_perm)) || (dy_perm && !aligned16(dy_perm)))
+        return MOE_ERR_ALIGN;
+    return hip_status(launch_combine_backward(dy, y_perm, dest, topk_w, T, d, k, rows, dy_perm,
+                                              d_topk_w, as_stream(stream)));
+}
+
 static int forward_checks(const moe_cfg* c, const moe_weights* w) {
     if (!c || !w) return MOE_ERR_NULL;
     if (c->T < 0 || c->E < 1 || c->k < 1 || c->F_shared < 0) return MOE_ERR_SHAPE;

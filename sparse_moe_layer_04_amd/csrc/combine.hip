@@ -75,7 +75,77 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
 }
 
+// Backward of the combine: for a gradient dy of the output,
+//   dy_perm[dest[t, j], o] = w[t, j] * dy[t, o]   (one fp32 rounding),
+//   dw[t, j] = sum_o dy[t, o] * y_perm[dest[t, j], o]
+// (the shared expert's gradient is dy itself).  One workgroup per token;
+// each thread owns 4 consecutive columns per 1024-column pass: it reads dy
+// and each source row once, writes the k gradient rows and accumulates its
+// k partial dot products by fma; the workgroup then adds the partials in a
+// fixed tree order (the same bits on every run).  A pair whose dest is
+// outside [0, rows) gets dw = 0 and writes nothing.
+__global__ __launch_bounds__(256) void combine_backward_kernel(
+    const float* __restrict__ dy, const float* __restrict__ y_perm,
+    const int32_t* __restrict__ dest, const float* __restrict__ w, int d, int k, int rows,
+    float* __restrict__ dy_perm, float* __restrict__ dw) {
+    __shared__ float red[MOE_MAX_K][256];
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    int rj[MOE_MAX_K];
+    float wj[MOE_MAX_K], part[MOE_MAX_K];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K; ++j) {
+        rj[j] = -1;
+        wj[j] = 0.0f;
+        part[j] = 0.0f;
+        if (j < k) {
+            const int r = dest[(size_t)t * k + j];
+            if (r >= 0 && r < rows) {
+                rj[j] = r;
+                wj[j] = w[(size_t)t * k + j];
+            }
+        }
+    }
+    for (int c = tid * 4; c < d; c += 1024) {
+        const f32x4 g = __builtin_nontemporal_load((const f32x4*)(dy + (size_t)t * d + c));
+#pragma unroll
+        for (int j = 0; j < MOE_MAX_K; ++j) {
+            if (rj[j] < 0) continue;
+            const f32x4 v =
+                __builtin_nontemporal_load((const f32x4*)(y_perm + (size_t)rj[j] * d + c));
+            f32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                part[j] = __builtin_fmaf(g[i], v[i], part[j]);
+                o[i] = wj[j] * g[i];
+            }
+            *(f32x4*)(dy_perm + (size_t)rj[j] * d + c) = o;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K; ++j) red[j][tid] = part[j];
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (tid < s) {
+#pragma unroll
+            for (int j = 0; j < MOE_MAX_K; ++j)
+                if (j < k) red[j][tid] = red[j][tid] + red[j][tid + s];
+        }
+        __syncthreads();
+    }
+    if (tid < k) dw[(size_t)t * k + tid] = red[tid][0];
+}
+
 }  // namespace
+
+hipError_t launch_combine_backward(const float* dy, const float* y_perm, const int32_t* dest,
+                                   const float* w, int T, int d, int k, int rows, float* dy_perm,
+                                   float* dw, hipStream_t stream) {
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(combine_backward_kernel, dim3(T), dim3(256), 0, stream, dy, y_perm, dest,
+                       w, d, k, rows, dy_perm, dw);
+    return hipGetLastError();
+}
 
 hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* w,
                           const float* y_shared, int T, int d, int k, int rows, int out_dtype,

@@ -140,6 +140,10 @@ hipError_t launch_route(const float* logits, const float* bias, const uint8_t* m
                         int n_bias, int V, int mode, float scale, int32_t* ids, float* w,
                         uint32_t* flags, hipStream_t stream);
 
+hipError_t launch_combine_backward(const float* dy, const float* y_perm, const int32_t* dest,
+                                   const float* w, int T, int d, int k, int rows, float* dy_perm,
+                                   float* dw, hipStream_t stream);
+
 hipError_t launch_route_backward(const float* logits, const int32_t* ids, const float* dw,
                                  int T, int E, int k, float scale, float* dl, uint32_t* flags,
                                  hipStream_t stream);

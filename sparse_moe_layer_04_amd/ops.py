@@ -78,6 +78,7 @@ def lib():
     L.moe_gate_logits.argtypes = [P, P, P, I, I, I, P, P]
     L.moe_route.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, P]
     L.moe_route_backward.argtypes = [P, P, P, I, I, I, F, P, P, P]
+    L.moe_combine_backward.argtypes = [P, P, P, P, I, I, I, I, P, P, P]
     L.moe_permute_workspace_size.argtypes = [I, I, I]
     L.moe_permute_workspace_size.restype = S
     L.moe_permute.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, S, P]
@@ -299,6 +300,28 @@ def combine(y_perm, dest, topk_w, y_shared=None, out_dtype=OUT_BF16, y=None):
     _check(lib().moe_combine(_ptr(y_perm), _ptr(dest), _ptr(topk_w), _ptr(y_shared), T, d, k,
                              rows, int(out_dtype), _ptr(y), _stream()), "moe_combine")
     return y
+
+
+def combine_backward(dy, y_perm, dest, topk_w, dy_perm=None, d_topk_w=None):
+    """Backward of the combine (moe_combine_backward): returns
+    (dy_perm[rows,d] fp32, d_topk_w[T,k] fp32).  A new dy_perm starts at
+    zero, so rows no pair maps to are 0."""
+    _need(topk_w, torch.float32, "topk_w", 2)
+    T, k = topk_w.shape
+    _need(y_perm, torch.float32, "y_perm", 2)
+    rows, d = y_perm.shape
+    _need(dy, torch.float32, "dy", shape=(T, d))
+    _need(dest, torch.int32, "dest")
+    if dest.numel() != T * k:
+        raise MoeError(f"dest must have T k = {T * k} entries")
+    if dy_perm is None:
+        dy_perm = torch.zeros((rows, d), dtype=torch.float32, device=dy.device)
+    _need(dy_perm, torch.float32, "dy_perm", shape=(rows, d))
+    d_topk_w = _out(d_topk_w, torch.float32, "d_topk_w", (T, k), dy.device)
+    _check(lib().moe_combine_backward(_ptr(dy), _ptr(y_perm), _ptr(dest), _ptr(topk_w), T, d, k,
+                                      rows, _ptr(dy_perm), _ptr(d_topk_w), _stream()),
+           "moe_combine_backward")
+    return dy_perm, d_topk_w
 
 
 # panel height each matrix is packed with for moe_forward

@@ -152,6 +152,22 @@ def test_combine_validation(L):
     assert comb(T=0, yp=None, y=None) == 0
 
 
+def test_combine_backward_validation(L):
+    def cb(T=4, d=64, k=2, rows=8, dy=FAKE, yp=FAKE, dyp=FAKE, dw=FAKE):
+        return L.moe_combine_backward(dy, yp, FAKE, FAKE, T, d, k, rows, dyp, dw, None)
+    assert cb(k=0) == ERR_SHAPE
+    assert cb(rows=-1) == ERR_SHAPE
+    assert cb(k=9) == ERR_UNSUPPORTED
+    assert cb(d=12) == ERR_UNSUPPORTED
+    assert cb(dy=None) == ERR_NULL
+    assert cb(yp=None) == ERR_NULL
+    assert cb(dyp=None) == ERR_NULL
+    assert cb(dw=None) == ERR_NULL
+    assert cb(dy=FAKE + 4) == ERR_ALIGN
+    assert cb(dyp=FAKE + 8) == ERR_ALIGN
+    assert cb(T=0, dy=None, yp=None, dyp=None, dw=None) == 0
+
+
 def test_forward_validation(L):
     cfg = ops.MoeCfg(T=8, d=128, E=8, k=2, F=64, F_shared=64, mode=0, n_bias=1, V=0, scale=1.0,
                      clamp_limit=10.0, clamp_mode=0, out_dtype=0)
