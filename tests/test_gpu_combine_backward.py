@@ -80,3 +80,25 @@ def test_combine_backward_full_size_sampled():
     got_rows = host(dyp[torch.from_numpy(rows_s.astype(np.int64)).to(DEV)])
     assert np.array_equal(got_rows, ry.astype(np.float32))
     assert np.all(np.abs(host(dw)[tok] - rw) <= _dw_bound(host(dy)[tok], yp_s, local, d))
+
+
+def test_gather_backward_is_combine_with_unit_weights():
+    """The backward of the dispatch gather (x_perm[row] = x[src[row]]) adds
+    each token's k row gradients: moe_combine with unit weights and no shared
+    term, checked against fp64 autograd of the gather."""
+    T, d, k, E = 300, 256, 6, 64
+    rng = np.random.default_rng(8)
+    ids = torch.from_numpy(np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
+                           .astype(np.int32)).to(DEV)
+    perm = ops.permute(ids, torch.zeros((T, 8), dtype=torch.bfloat16, device=DEV), E)
+    dxp = rng.normal(0, 1, (T * k, d)).astype(np.float32)
+    dx = ops.combine(torch.from_numpy(dxp).to(DEV), perm["dest"],
+                     torch.ones((T, k), dtype=torch.float32, device=DEV), out_dtype=ops.OUT_F32)
+    torch.cuda.synchronize()
+    X = torch.zeros((T, d), dtype=torch.float64, requires_grad=True)
+    src = torch.from_numpy(host(perm["src"]).astype(np.int64))
+    (X[src] * torch.from_numpy(dxp.astype(np.float64))).sum().backward()
+    ref = X.grad.numpy()
+    mag = np.zeros((T, d))
+    np.add.at(mag, host(perm["src"]), np.abs(dxp.astype(np.float64)))
+    assert np.all(np.abs(host(dx) - ref) <= k * 2.0 ** -24 * mag)
