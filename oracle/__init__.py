@@ -32,6 +32,7 @@ from .oracle import (  # noqa: F401
     expert_ffn_rows,
     combine,
     combine_backward,
+    swiglu_backward,
     tokens_forward,
     forward,
     e4m3_decode,

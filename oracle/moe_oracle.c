@@ -367,6 +367,38 @@ void orc_gather(const uint16_t* x, const int32_t* src, int64_t rows, int d, uint
     }
 }
 
+/* ------------------------------------------------------ SwiGLU backward -- */
+/*
+ * Backward of the clamped SwiGLU between the expert matmuls ("HyperParallel
+ * accelerates DeepSeek-V4.1 ...", section 2.3, MegaMoE: SwiGLU with the V4.1
+ * clamp).  For h = silu(cg(G)) * cu(U) with the clamps of ffn_row and a
+ * gradient dh of h:
+ *   dU = dh * silu(cg(G)) * [U inside [-L, L]],
+ *   dG = dh * cu(U) * silu'(cg(G)) * [G inside the gate clamp's range],
+ *   silu'(z) = s (1 + z (1 - s)),  s = 1 / (1 + exp(-z)),
+ * a clamp passing its gradient on the closed range (as at the limits the
+ * clamp is the identity from the inside).  fp64 from fp32 inputs.
+ */
+void orc_swiglu_backward(const float* gate, const float* up, const float* dh, int64_t n,
+                         double L, int clamp_mode, double* dgate, double* dup)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        double g = gate[i], u = up[i], gh = dh[i];
+        int g_in = clamp_mode == 0 ? (g >= -L && g <= L) : (g <= L);
+        int u_in = (u >= -L && u <= L);
+        double gc = g, uc = u;
+        if (gc > L) gc = L;
+        if (clamp_mode == 0 && gc < -L) gc = -L;
+        if (uc > L) uc = L;
+        if (uc < -L) uc = -L;
+        double sg = 1.0 / (1.0 + exp(-gc));
+        double silu = gc * sg;
+        dup[i] = u_in ? gh * silu : 0.0;
+        dgate[i] = g_in ? gh * uc * sg * (1.0 + gc * (1.0 - sg)) : 0.0;
+    }
+}
+
 /* ------------------------------------------------------------- expert FFN -- */
 /*
  * One expert on one activation row a[0..d):

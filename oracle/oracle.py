@@ -78,6 +78,8 @@ def load():
     lib.orc_combine.argtypes = [P, P, P, P, I, I, I, P]
     lib.orc_combine.restype = None
     lib.orc_combine_backward.argtypes = [P, P, P, P, I, I, I, I, P, P]
+    lib.orc_swiglu_backward.argtypes = [P, P, P, I64, D, I, P, P]
+    lib.orc_swiglu_backward.restype = None
     lib.orc_combine_backward.restype = None
     lib.orc_tokens_forward.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, P, I, D, I, P]
     lib.orc_tokens_forward.restype = None
@@ -233,6 +235,20 @@ def combine_backward(dy, y_perm, dest, w, dy_perm=None):
     load().orc_combine_backward(_p(dy), _p(y_perm), _p(dest), _p(w), T, d, k, rows, _p(out),
                                 _p(dw))
     return out, dw
+
+
+def swiglu_backward(gate, up, dh, clamp_limit, clamp_mode=0):
+    """Backward of the clamped SwiGLU (orc_swiglu_backward): returns
+    (dgate, dup) float64 arrays of the inputs' shape."""
+    gate = _c(gate, np.float32)
+    up = _c(up, np.float32)
+    dh = _c(dh, np.float32)
+    assert gate.shape == up.shape == dh.shape
+    dg = np.empty(gate.shape, np.float64)
+    du = np.empty(gate.shape, np.float64)
+    load().orc_swiglu_backward(_p(gate), _p(up), _p(dh), gate.size, float(clamp_limit),
+                               int(clamp_mode), _p(dg), _p(du))
+    return dg, du
 
 
 def combine(y_perm, dest, w, ysh=None):
