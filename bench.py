@@ -307,6 +307,29 @@ def main():
                         "algorithmic_bytes": cb_bytes}
     del yp_b, dy_b, dyp_b, dest_b
 
+    # The clamped-SwiGLU backward (moe_swiglu_backward) at this workload's
+    # [T k, F] pre-activation shape: random fp32 gate/up pre-activations and
+    # h gradient; 5 calls between two events.
+    sb_shape = (w.T * w.k, w.F)
+    g_sb = torch.randn(sb_shape, generator=gen, device=dev) * 4
+    u_sb = torch.randn(sb_shape, generator=gen, device=dev) * 4
+    dh_sb = torch.randn(sb_shape, generator=gen, device=dev)
+    dg_sb, du_sb = torch.empty_like(g_sb), torch.empty_like(g_sb)
+    ops.swiglu_backward(g_sb, u_sb, dh_sb, w.clamp_limit, w.clamp_mode, dgate=dg_sb, dup=du_sb)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        ops.swiglu_backward(g_sb, u_sb, dh_sb, w.clamp_limit, w.clamp_mode, dgate=dg_sb,
+                            dup=du_sb)
+    e1.record()
+    torch.cuda.synchronize()
+    sb_ms = e0.elapsed_time(e1) / 5
+    sb_bytes = 20 * w.T * w.k * w.F          # three fp32 inputs read, two written
+    swiglu_backward = {"ms": sb_ms, "GB/s": sb_bytes / sb_ms / 1e6,
+                       "frac_of_hbm_peak": sb_bytes / sb_ms / 1e6 / (PEAK_HBM / 1e9),
+                       "algorithmic_bytes": sb_bytes}
+    del g_sb, u_sb, dh_sb, dg_sb, du_sb
+
     counts = torch.bincount(ids.flatten().long(), minlength=w.E).cpu().numpy()
     n_nonempty = int((counts > 0).sum())
     work = stage_work(w, n_nonempty, 4 if out_dtype == ops.OUT_F32 else 2,
@@ -364,6 +387,7 @@ def main():
         "stages": stages,
         "route_backward": route_backward,
         "combine_backward": combine_backward,
+        "swiglu_backward": swiglu_backward,
     }
     if args.cpu_budget > 0:
         print("# timing the CPU oracle baseline", file=sys.stderr, flush=True)

@@ -288,6 +288,23 @@ int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* de
                          float* d_topk_w, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Clamped-SwiGLU backward [HP 2.3 MegaMoE: SwiGLU with the V4.1 clamp].
+ * For h = silu(cg(gate)) * cu(up), the clamps of moe_expert_ffn (limit L,
+ * clamp_mode), and a gradient dh of h, elementwise:
+ *   dup   = dh * silu(cg(gate)) * [up inside [-L, L]],
+ *   dgate = dh * cu(up) * silu'(cg(gate)) * [gate inside the gate clamp's
+ *           range ([-L, L], or (-inf, L] for MOE_CLAMP_GATE_UPPER)],
+ *   silu'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z); a clamp passes its
+ *   gradient on the closed range.  fp32 arithmetic.
+ *   gate, up, dh, dgate, dup: n fp32 values each (n a multiple of 4; the
+ *   [rows, F] pre-activations of the gate/up matmul and their gradients),
+ *   16-byte aligned.  L > 0 (+inf disables the clamp).
+ */
+int moe_swiglu_backward(const float* gate, const float* up, const float* dh, int64_t n,
+                        float clamp_limit, int clamp_mode, float* dgate, float* dup,
+                        void* stream);
+
+/* ------------------------------------------------------------------------
  * Whole layer forward: gate logits -> route -> permute -> grouped FFN (routed
  * experts) and FFN (shared expert) -> combine.
  */

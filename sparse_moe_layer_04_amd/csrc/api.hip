@@ -366,6 +366,23 @@ int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* de
                                               d_topk_w, as_stream(stream)));
 }
 
+int moe_swiglu_backward(const float* gate, const float* up, const float* dh, int64_t n,
+                        float clamp_limit, int clamp_mode, float* dgate, float* dup,
+                        void* stream) {
+    if (n < 0) return MOE_ERR_SHAPE;
+    if (n % 4) return MOE_ERR_UNSUPPORTED;
+    if (!(clamp_limit > 0.0f)) return MOE_ERR_SHAPE;  // also rejects NaN
+    if (clamp_mode != MOE_CLAMP_SYMMETRIC && clamp_mode != MOE_CLAMP_GATE_UPPER)
+        return MOE_ERR_UNSUPPORTED;
+    if (n == 0) return MOE_OK;
+    if (!gate || !up || !dh || !dgate || !dup) return MOE_ERR_NULL;
+    if (!aligned16(gate) || !aligned16(up) || !aligned16(dh) || !aligned16(dgate) ||
+        !aligned16(dup))
+        return MOE_ERR_ALIGN;
+    return hip_status(launch_swiglu_backward(gate, up, dh, (long long)n, clamp_limit, clamp_mode,
+                                             dgate, dup, as_stream(stream)));
+}
+
 static int forward_checks(const moe_cfg* c, const moe_weights* w) {
     if (!c || !w) return MOE_ERR_NULL;
     if (c->T < 0 || c->E < 1 || c->k < 1 || c->F_shared < 0) return MOE_ERR_SHAPE;

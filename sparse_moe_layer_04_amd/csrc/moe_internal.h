@@ -140,6 +140,10 @@ hipError_t launch_route(const float* logits, const float* bias, const uint8_t* m
                         int n_bias, int V, int mode, float scale, int32_t* ids, float* w,
                         uint32_t* flags, hipStream_t stream);
 
+hipError_t launch_swiglu_backward(const float* gate, const float* up, const float* dh,
+                                  long long n, float clamp_limit, int clamp_mode, float* dgate,
+                                  float* dup, hipStream_t stream);
+
 hipError_t launch_combine_backward(const float* dy, const float* y_perm, const int32_t* dest,
                                    const float* w, int T, int d, int k, int rows, float* dy_perm,
                                    float* dw, hipStream_t stream);

@@ -79,6 +79,7 @@ def lib():
     L.moe_route.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, P]
     L.moe_route_backward.argtypes = [P, P, P, I, I, I, F, P, P, P]
     L.moe_combine_backward.argtypes = [P, P, P, P, I, I, I, I, P, P, P]
+    L.moe_swiglu_backward.argtypes = [P, P, P, ctypes.c_int64, F, I, P, P, P]
     L.moe_permute_workspace_size.argtypes = [I, I, I]
     L.moe_permute_workspace_size.restype = S
     L.moe_permute.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, S, P]
@@ -322,6 +323,22 @@ def combine_backward(dy, y_perm, dest, topk_w, dy_perm=None, d_topk_w=None):
                                       rows, _ptr(dy_perm), _ptr(d_topk_w), _stream()),
            "moe_combine_backward")
     return dy_perm, d_topk_w
+
+
+def swiglu_backward(gate, up, dh, clamp_limit=10.0, clamp_mode=CLAMP_SYMMETRIC, dgate=None,
+                    dup=None):
+    """Backward of the clamped SwiGLU (moe_swiglu_backward): returns
+    (dgate, dup), fp32 tensors of gate's shape."""
+    _need(gate, torch.float32, "gate")
+    shape = tuple(gate.shape)
+    _need(up, torch.float32, "up", shape=shape)
+    _need(dh, torch.float32, "dh", shape=shape)
+    dgate = _out(dgate, torch.float32, "dgate", shape, gate.device)
+    dup = _out(dup, torch.float32, "dup", shape, gate.device)
+    _check(lib().moe_swiglu_backward(_ptr(gate), _ptr(up), _ptr(dh), gate.numel(),
+                                     float(clamp_limit), int(clamp_mode), _ptr(dgate), _ptr(dup),
+                                     _stream()), "moe_swiglu_backward")
+    return dgate, dup
 
 
 # panel height each matrix is packed with for moe_forward

@@ -168,6 +168,20 @@ def test_combine_backward_validation(L):
     assert cb(T=0, dy=None, yp=None, dyp=None, dw=None) == 0
 
 
+def test_swiglu_backward_validation(L):
+    def sb(n=64, lim=10.0, mode=0, g=FAKE, dg=FAKE):
+        return L.moe_swiglu_backward(g, FAKE, FAKE, n, ctypes.c_float(lim), mode, dg, FAKE, None)
+    assert sb(n=-4) == ERR_SHAPE
+    assert sb(n=6) == ERR_UNSUPPORTED
+    assert sb(lim=0.0) == ERR_SHAPE
+    assert sb(lim=float("nan")) == ERR_SHAPE
+    assert sb(mode=2) == ERR_UNSUPPORTED
+    assert sb(g=None) == ERR_NULL
+    assert sb(dg=None) == ERR_NULL
+    assert sb(g=FAKE + 4) == ERR_ALIGN
+    assert sb(n=0, g=None, dg=None) == 0
+
+
 def test_forward_validation(L):
     cfg = ops.MoeCfg(T=8, d=128, E=8, k=2, F=64, F_shared=64, mode=0, n_bias=1, V=0, scale=1.0,
                      clamp_limit=10.0, clamp_mode=0, out_dtype=0)
