@@ -33,6 +33,7 @@ from .oracle import (  # noqa: F401
     combine,
     combine_backward,
     swiglu_backward,
+    grouped_gemm,
     tokens_forward,
     forward,
     e4m3_decode,

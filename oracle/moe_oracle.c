@@ -367,6 +367,33 @@ void orc_gather(const uint16_t* x, const int32_t* src, int64_t rows, int d, uint
     }
 }
 
+/* ---------------------------------------------------------- grouped GEMM -- */
+/*
+ * One grouped matmul of the expert FFN's shape, out = A W_g^T per group
+ * ("HyperParallel accelerates DeepSeek-V4.1 ...", section 2.3, MegaMoE: the
+ * expert matmuls; in the backward the same product gives the input
+ * gradients, dH = dY W_down = dY (W_down^T)^T):
+ *   out[r, n] = sum_k a[r, k] * w[g, n, k]   for offsets[g] <= r < offsets[g+1],
+ * a and w bf16, exact products summed in fp64.  Rows outside every group
+ * are left as they are.
+ */
+void orc_grouped_gemm(const uint16_t* a, const int32_t* offsets, int G, int K, int N,
+                      const uint16_t* w, double* out)
+{
+    for (int g = 0; g < G; ++g) {
+        const uint16_t* wg = w + (size_t)g * N * K;
+#pragma omp parallel for schedule(static)
+        for (int r = offsets[g]; r < offsets[g + 1]; ++r) {
+            for (int n = 0; n < N; ++n) {
+                double acc = 0.0;
+                for (int k = 0; k < K; ++k)
+                    acc += bf16_value(a[(size_t)r * K + k]) * bf16_value(wg[(size_t)n * K + k]);
+                out[(size_t)r * N + n] = acc;
+            }
+        }
+    }
+}
+
 /* ------------------------------------------------------ SwiGLU backward -- */
 /*
  * Backward of the clamped SwiGLU between the expert matmuls ("HyperParallel

@@ -79,6 +79,8 @@ def load():
     lib.orc_combine.restype = None
     lib.orc_combine_backward.argtypes = [P, P, P, P, I, I, I, I, P, P]
     lib.orc_swiglu_backward.argtypes = [P, P, P, I64, D, I, P, P]
+    lib.orc_grouped_gemm.argtypes = [P, P, I, I, I, P, P]
+    lib.orc_grouped_gemm.restype = None
     lib.orc_swiglu_backward.restype = None
     lib.orc_combine_backward.restype = None
     lib.orc_tokens_forward.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, P, I, D, I, P]
@@ -235,6 +237,20 @@ def combine_backward(dy, y_perm, dest, w, dy_perm=None):
     load().orc_combine_backward(_p(dy), _p(y_perm), _p(dest), _p(w), T, d, k, rows, _p(out),
                                 _p(dw))
     return out, dw
+
+
+def grouped_gemm(a, offsets, w, out=None):
+    """out[r] = a[r] @ w[g].T for the rows of group g (bf16 bits in, fp64
+    out); rows outside every group keep `out`'s values (zeros if None)."""
+    a = _bf16(a)
+    offsets = _c(offsets, np.int32)
+    w = _bf16(w)
+    G, N, K = w.shape
+    rows = a.shape[0]
+    assert a.shape[1] == K and offsets.shape == (G + 1,)
+    res = np.zeros((rows, N), np.float64) if out is None else _c(out, np.float64).copy()
+    load().orc_grouped_gemm(_p(a), _p(offsets), G, K, N, _p(w), _p(res))
+    return res
 
 
 def swiglu_backward(gate, up, dh, clamp_limit, clamp_mode=0):
