@@ -305,6 +305,20 @@ int moe_swiglu_backward(const float* gate, const float* up, const float* dh, int
                         void* stream);
 
 /* ------------------------------------------------------------------------
+ * Grouped matmul on packed weights [HP 2.3 MegaMoE: the expert matmuls].
+ *   out[r, n] = sum_k a[r,k] * W[g, n, k]  for offsets[g] <= r < offsets[g+1],
+ *   bf16 products, fp32 accumulation (the expert FFN's MFMA chain); rows
+ *   outside every group are left untouched.  In the backward it gives the
+ *   expert GEMMs' input gradients: dH = dY W_down with W = W_down^T
+ *   ([G, F, d]), and the gate/up input gradient with W = [W_gate | W_up]^T.
+ *   a [rows, K] bf16 row-major; offsets [G+1] int32 device; w_packed =
+ *   moe_pack_weights(W [G, N, K], panel_rows 256); out [rows, N] fp32.
+ *   K, N multiples of 64; a, w_packed, out 16-byte aligned.  No workspace.
+ */
+int moe_grouped_gemm_packed(const uint16_t* a, const int32_t* offsets, int G, int rows, int K,
+                            int N, const uint16_t* w_packed, float* out, void* stream);
+
+/* ------------------------------------------------------------------------
  * Whole layer forward: gate logits -> route -> permute -> grouped FFN (routed
  * experts) and FFN (shared expert) -> combine.
  */

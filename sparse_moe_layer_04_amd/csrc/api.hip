@@ -366,6 +366,30 @@ int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* de
                                               d_topk_w, as_stream(stream)));
 }
 
+int moe_grouped_gemm_packed(const uint16_t* a, const int32_t* offsets, int G, int rows, int K,
+                            int N, const uint16_t* w_packed, float* out, void* stream) {
+    if (G < 1 || rows < 0 || K < 64 || N < 64) return MOE_ERR_SHAPE;
+    if (K % 64 || N % 64) return MOE_ERR_UNSUPPORTED;
+    if (G > MOE_MAX_GROUPS || G > grouped_gemm_lds_max_groups()) return MOE_ERR_UNSUPPORTED;
+    if ((long long)rows * K >= (1ll << 40) || (long long)rows * N >= (1ll << 40))
+        return MOE_ERR_SHAPE;
+    if (rows == 0) return MOE_OK;
+    if (!a || !offsets || !w_packed || !out) return MOE_ERR_NULL;
+    if (!aligned16(a) || !aligned16(w_packed) || !aligned16(out)) return MOE_ERR_ALIGN;
+    // the LDS-staged expert GEMM, fp32 output, static schedule (no workspace)
+    GemmArgs g{};
+    g.a = a;
+    g.offsets = offsets;
+    g.G = G;
+    g.rows = rows;
+    g.K = K;
+    g.N = N;
+    g.w1 = w_packed;
+    g.packed = 1;
+    g.out = out;
+    return hip_status(launch_grouped_gemm_lds(EPI_F32, g, as_stream(stream)));
+}
+
 int moe_swiglu_backward(const float* gate, const float* up, const float* dh, int64_t n,
                         float clamp_limit, int clamp_mode, float* dgate, float* dup,
                         void* stream) {

@@ -80,6 +80,7 @@ def lib():
     L.moe_route_backward.argtypes = [P, P, P, I, I, I, F, P, P, P]
     L.moe_combine_backward.argtypes = [P, P, P, P, I, I, I, I, P, P, P]
     L.moe_swiglu_backward.argtypes = [P, P, P, ctypes.c_int64, F, I, P, P, P]
+    L.moe_grouped_gemm_packed.argtypes = [P, P, I, I, I, I, P, P, P]
     L.moe_permute_workspace_size.argtypes = [I, I, I]
     L.moe_permute_workspace_size.restype = S
     L.moe_permute.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, S, P]
@@ -323,6 +324,23 @@ def combine_backward(dy, y_perm, dest, topk_w, dy_perm=None, d_topk_w=None):
                                       rows, _ptr(dy_perm), _ptr(d_topk_w), _stream()),
            "moe_combine_backward")
     return dy_perm, d_topk_w
+
+
+def grouped_gemm_packed(a, offsets, w_packed, G, N, out=None):
+    """out[r] = a[r] @ W[g].T for the rows of group g (moe_grouped_gemm_packed;
+    w_packed = pack_weights(W [G, N, K], 256)); a new `out` starts at zero."""
+    _need(a, torch.bfloat16, "a", 2)
+    rows, K = a.shape
+    _need(offsets, torch.int32, "offsets", shape=(G + 1,))
+    _need(w_packed, torch.bfloat16, "w_packed", 1)
+    if w_packed.numel() * 2 != lib().moe_packed_weight_bytes(G, N, K, 256):
+        raise MoeError(f"w_packed is not a packed [{G},{N},{K}] matrix (panel_rows 256)")
+    if out is None:
+        out = torch.zeros((rows, N), dtype=torch.float32, device=a.device)
+    _need(out, torch.float32, "out", shape=(rows, N))
+    _check(lib().moe_grouped_gemm_packed(_ptr(a), _ptr(offsets), G, rows, K, N, _ptr(w_packed),
+                                         _ptr(out), _stream()), "moe_grouped_gemm_packed")
+    return out
 
 
 def swiglu_backward(gate, up, dh, clamp_limit=10.0, clamp_mode=CLAMP_SYMMETRIC, dgate=None,

@@ -168,6 +168,21 @@ def test_combine_backward_validation(L):
     assert cb(T=0, dy=None, yp=None, dyp=None, dw=None) == 0
 
 
+def test_grouped_gemm_packed_validation(L):
+    def gg(G=2, rows=8, K=64, N=64, a=FAKE, w=FAKE, out=FAKE):
+        return L.moe_grouped_gemm_packed(a, FAKE, G, rows, K, N, w, out, None)
+    assert gg(G=0) == ERR_SHAPE
+    assert gg(rows=-1) == ERR_SHAPE
+    assert gg(K=32) == ERR_SHAPE
+    assert gg(K=96) == ERR_UNSUPPORTED
+    assert gg(N=100) == ERR_UNSUPPORTED
+    assert gg(G=5000) == ERR_UNSUPPORTED
+    assert gg(a=None) == ERR_NULL
+    assert gg(w=None) == ERR_NULL
+    assert gg(out=FAKE + 4) == ERR_ALIGN
+    assert gg(rows=0, a=None, w=None, out=None) == 0
+
+
 def test_swiglu_backward_validation(L):
     def sb(n=64, lim=10.0, mode=0, g=FAKE, dg=FAKE):
         return L.moe_swiglu_backward(g, FAKE, FAKE, n, ctypes.c_float(lim), mode, dg, FAKE, None)
