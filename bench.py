@@ -330,6 +330,33 @@ def main():
                        "algorithmic_bytes": sb_bytes}
     del g_sb, u_sb, dh_sb, dg_sb, du_sb
 
+    # The down projection's input gradient dH = dY W_down per expert
+    # (moe_grouped_gemm_packed with W_down^T packed once) at this workload's
+    # group sizes: random bf16 dY; 3 calls between two events.
+    counts_b = torch.bincount(ids_b.flatten().long(), minlength=w.E)
+    offs_b = torch.zeros(w.E + 1, dtype=torch.int32, device=dev)
+    offs_b[1:] = torch.cumsum(counts_b, 0).to(torch.int32)
+    wdT_b = ops.pack_weights(inp["w_down"].transpose(1, 2).contiguous(), 256)
+    dY_b = torch.randn((w.T * w.k, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    dH_b = torch.empty((w.T * w.k, w.F), dtype=torch.float32, device=dev)
+    ops.grouped_gemm_packed(dY_b, offs_b, wdT_b, w.E, w.F, out=dH_b)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(3):
+        ops.grouped_gemm_packed(dY_b, offs_b, wdT_b, w.E, w.F, out=dH_b)
+    e1.record()
+    torch.cuda.synchronize()
+    dg_ms = e0.elapsed_time(e1) / 3
+    nz_b = int((counts_b > 0).sum().item())
+    dg_flops = 2.0 * w.T * w.k * w.d * w.F
+    dg_bytes = nz_b * w.F * w.d * 2 + w.T * w.k * w.d * 2 + w.T * w.k * w.F * 4
+    down_dgrad = {"ms": dg_ms, "TFLOP/s": dg_flops / dg_ms / 1e9,
+                  "GB/s": dg_bytes / dg_ms / 1e6,
+                  "frac_of_hbm_peak": dg_bytes / dg_ms / 1e6 / (PEAK_HBM / 1e9),
+                  "frac_of_mfma_peak": dg_flops / dg_ms / 1e9 / (PEAK_BF16 / 1e12),
+                  "algorithmic_bytes": dg_bytes, "flops": dg_flops}
+    del wdT_b, dY_b, dH_b
+
     counts = torch.bincount(ids.flatten().long(), minlength=w.E).cpu().numpy()
     n_nonempty = int((counts > 0).sum())
     work = stage_work(w, n_nonempty, 4 if out_dtype == ops.OUT_F32 else 2,
@@ -388,6 +415,7 @@ def main():
         "route_backward": route_backward,
         "combine_backward": combine_backward,
         "swiglu_backward": swiglu_backward,
+        "down_dgrad": down_dgrad,
     }
     if args.cpu_budget > 0:
         print("# timing the CPU oracle baseline", file=sys.stderr, flush=True)
