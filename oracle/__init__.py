@@ -34,6 +34,8 @@ from .oracle import (  # noqa: F401
     combine_backward,
     swiglu_backward,
     grouped_gemm,
+    grouped_wgrad,
+    grouped_wgrad_entries,
     tokens_forward,
     forward,
     e4m3_decode,

@@ -394,6 +394,53 @@ void orc_grouped_gemm(const uint16_t* a, const int32_t* offsets, int G, int K, i
     }
 }
 
+/* ------------------------------------------------ grouped weight gradient -- */
+/*
+ * Weight gradient of a grouped matmul ("HyperParallel accelerates
+ * DeepSeek-V4.1 ...", section 2.3, MegaMoE: the expert matmuls, whose weights
+ * a training step updates; section 03: the training run).  For the forward
+ * out = A W_g^T per group (orc_grouped_gemm) and a gradient dy of out, the
+ * chain rule gives
+ *   dw[g, m, k] = sum_{offsets[g] <= r < offsets[g+1]} dy[r, m] * a[r, k],
+ * dy and a bf16, exact products summed in fp64.  A group without rows gets a
+ * zero gradient.  With dy = dY, a = H it is the down projection's dW_down;
+ * with dy = dG or dU, a = X (the dispatched tokens) dW_gate or dW_up; with a
+ * single group of T rows, dy = the router logits' gradient and a = x, it is
+ * the router projection's dW_g.
+ */
+void orc_grouped_wgrad(const uint16_t* dy, const uint16_t* a, const int32_t* offsets, int G,
+                       int M, int K, double* dw)
+{
+    for (int g = 0; g < G; ++g) {
+        const int lo = offsets[g], hi = offsets[g + 1];
+        double* dwg = dw + (size_t)g * M * K;
+#pragma omp parallel for schedule(static)
+        for (int m = 0; m < M; ++m) {
+            for (int k = 0; k < K; ++k) {
+                double acc = 0.0;
+                for (int r = lo; r < hi; ++r)
+                    acc += bf16_value(dy[(size_t)r * M + m]) * bf16_value(a[(size_t)r * K + k]);
+                dwg[(size_t)m * K + k] = acc;
+            }
+        }
+    }
+}
+
+/* The same definition at n listed entries (g[i], m[i], k[i]) only, for
+ * sampled checks at sizes where the whole gradient is too large. */
+void orc_grouped_wgrad_entries(const uint16_t* dy, const uint16_t* a, const int32_t* offsets,
+                               int M, int K, const int32_t* g, const int32_t* m, const int32_t* k,
+                               int64_t n, double* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        double acc = 0.0;
+        for (int r = offsets[g[i]]; r < offsets[g[i] + 1]; ++r)
+            acc += bf16_value(dy[(size_t)r * M + m[i]]) * bf16_value(a[(size_t)r * K + k[i]]);
+        out[i] = acc;
+    }
+}
+
 /* ------------------------------------------------------ SwiGLU backward -- */
 /*
  * Backward of the clamped SwiGLU between the expert matmuls ("HyperParallel
@@ -632,9 +679,9 @@ void orc_tokens_forward(const uint16_t* x, const int64_t* tokens, int n, int d, 
 /* ------------------------------------------------------ fp8 expert weights -- */
 /*
  * 8-bit expert weights.  The pages name MXFP8 / MXFP4 as the low-precision
- * direction ("Twinkle x Ascend ... DeepSeek-V4 training", functional-
- * expansion section; the V4-Flash checkpoints ship in FP4/FP8, quick-start
- * section) without restating the format.  MXFP8 is the OCP Microscaling
+ * direction ("CANN DeepSeek-V4 training optimisation", outlook section,
+ * functional-expansion bullets; the V4-Flash checkpoints ship in FP4/FP8,
+ * quick-start section of "Twinkle x Ascend ... DeepSeek-V4 training") without restating the format.  MXFP8 is the OCP Microscaling
  * format: blocks of 32 consecutive values along K share one power-of-two
  * scale (E8M0), each value an OCP 8-bit float E4M3 ("E4M3FN": 1 sign bit, 4
  * exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities,

@@ -81,6 +81,10 @@ def load():
     lib.orc_swiglu_backward.argtypes = [P, P, P, I64, D, I, P, P]
     lib.orc_grouped_gemm.argtypes = [P, P, I, I, I, P, P]
     lib.orc_grouped_gemm.restype = None
+    lib.orc_grouped_wgrad.argtypes = [P, P, P, I, I, I, P]
+    lib.orc_grouped_wgrad.restype = None
+    lib.orc_grouped_wgrad_entries.argtypes = [P, P, P, I, I, P, P, P, I64, P]
+    lib.orc_grouped_wgrad_entries.restype = None
     lib.orc_swiglu_backward.restype = None
     lib.orc_combine_backward.restype = None
     lib.orc_tokens_forward.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, P, I, D, I, P]
@@ -251,6 +255,29 @@ def grouped_gemm(a, offsets, w, out=None):
     res = np.zeros((rows, N), np.float64) if out is None else _c(out, np.float64).copy()
     load().orc_grouped_gemm(_p(a), _p(offsets), G, K, N, _p(w), _p(res))
     return res
+
+
+def grouped_wgrad(dy, a, offsets):
+    """dw[g] = dy[rows of g]^T a[rows of g] (fp64) for bf16 dy [rows, M] and
+    a [rows, K]: the weight gradient of out = a W_g^T per group."""
+    dy, a = _bf16(dy), _bf16(a)
+    offsets = _c(offsets, np.int32)
+    G = offsets.shape[0] - 1
+    M, K = dy.shape[1], a.shape[1]
+    dw = np.empty((G, M, K), np.float64)
+    load().orc_grouped_wgrad(_p(dy), _p(a), _p(offsets), G, M, K, _p(dw))
+    return dw
+
+
+def grouped_wgrad_entries(dy, a, offsets, g, m, k):
+    """grouped_wgrad at the listed entries (g[i], m[i], k[i]) only."""
+    dy, a = _bf16(dy), _bf16(a)
+    offsets = _c(offsets, np.int32)
+    g, m, k = _c(g, np.int32), _c(m, np.int32), _c(k, np.int32)
+    out = np.empty(g.shape[0], np.float64)
+    load().orc_grouped_wgrad_entries(_p(dy), _p(a), _p(offsets), dy.shape[1], a.shape[1], _p(g),
+                                     _p(m), _p(k), g.shape[0], _p(out))
+    return out
 
 
 def swiglu_backward(gate, up, dh, clamp_limit, clamp_mode=0):
