@@ -38,7 +38,9 @@ def stage_work(w, n_nonempty, out_bytes=2, wbytes=2):
     hash_mode = w.mode == 1
     st = {}
     st["router_gemm"] = (T * d * 2 + E * d * 2 + T * E * 4, 2.0 * T * d * E)
-    route_bytes = T * E * 4 + T * k * 8 + (T * 4 + T * k * 4 if hash_mode else 0)
+    # TopK reads every logit; Hash reads the token id, its table row and the
+    # k logits at the table's ids; both write ids and weights
+    route_bytes = (T * 4 + T * k * 4 + T * k * 4 if hash_mode else T * E * 4) + T * k * 8
     st["route"] = (route_bytes, 0.0)
     # the forward's permutation writes dest/src only (the routed gate/up GEMM
     # gathers the token rows through src)
@@ -92,6 +94,44 @@ def load_traffic(stage, workload_name):
     if not ent or ent.get("source_digest") != kernel_source_digest(stage):
         return None
     return ent.get("bytes_per_launch")
+
+
+def routing_diagnostics(w, inp, logits, ids, gap=1e-6):
+    """Near-ties and route flips of the benchmarked forward (TopK routing),
+    computed after the timed region with plain torch fp64 arithmetic:
+      near_ties   - tokens whose k-th and (k+1)-th biased scores, from the
+                    forward's own fp32 logits, differ by less than `gap`;
+      route_flips - tokens whose expert set under logits accumulated in fp64
+                    (x W_g^T + offset) differs from the forward's set.
+    None for hash routing (no ranking)."""
+    import torch
+    if w.mode == 1:
+        return None
+    bias = inp["score_bias"]
+    rows = None
+    if bias is not None:
+        rows = bias.double()[inp["modality"].long()] if (
+            inp["modality"] is not None and bias.shape[0] > 1) else bias.double()[:1]
+
+    def ranked(lg):
+        r = torch.sigmoid(lg.double())
+        if rows is not None:
+            r = r + rows
+        return r
+
+    r = ranked(logits)
+    top = torch.topk(r, w.k + 1, dim=1).values
+    near = int((top[:, w.k - 1] - top[:, w.k] < gap).sum().item())
+    lg64 = inp["x"].double() @ inp["w_g"].double().T
+    if inp["logit_offset"] is not None:
+        lg64 = lg64 + inp["logit_offset"].double()
+    ids64 = torch.topk(ranked(lg64), w.k, dim=1).indices
+    flips = int((torch.sort(ids64, dim=1).values !=
+                 torch.sort(ids.long(), dim=1).values).any(dim=1).sum().item())
+    return {"near_ties": near, "route_flips": flips, "gap": gap,
+            "how": "near_ties: k-th minus (k+1)-th biased score < gap under the forward's fp32 "
+                   "logits; route_flips: tokens whose expert set under fp64-accumulated logits "
+                   "differs from the forward's (torch fp64, outside the timed region)"}
 
 
 def cpu_baseline(w, inp, budget_s, seed=123):
@@ -275,6 +315,8 @@ def main():
     route_backward = {"ms": rb_ms, "GB/s": rb_bytes / rb_ms / 1e6,
                       "frac_of_hbm_peak": rb_bytes / rb_ms / 1e6 / (PEAK_HBM / 1e9),
                       "algorithmic_bytes": rb_bytes}
+    # near-ties and route flips of this forward's routing (not timed)
+    routing = routing_diagnostics(w, inp, lg_b, ids_b)
     del rb_graph, dl_b, lg_b
 
     # The combine backward (moe_combine_backward: the output gradient taken
@@ -416,6 +458,7 @@ def main():
         "combine_backward": combine_backward,
         "swiglu_backward": swiglu_backward,
         "down_dgrad": down_dgrad,
+        "routing": routing,
     }
     if args.cpu_budget > 0:
         print("# timing the CPU oracle baseline", file=sys.stderr, flush=True)

@@ -18,6 +18,8 @@
  *         by routing weight.
  *   [MS]  "MindSpore HyperParallel one-click DeepSeek-V4.1-Flash", section 01:
  *         one shared expert plus 384 routed experts, 6 routed per token.
+ *   [CN]  "CANN DeepSeek-V4 training optimisation", outlook section,
+ *         functional-expansion bullets: MxFP8 / MxFP4 low-precision weights.
  *
  * Conventions (all entry points):
  *   - Tensor arguments are DEVICE pointers owned by the caller, row-major and
@@ -208,8 +210,10 @@ int moe_pack_weights(const uint16_t* src, int G, int N, int K, int panel_rows, u
 
 /* ------------------------------------------------------------------------
  * MXFP8 routed-expert weights (a one-time conversion at weight-load time).
- * The pages name MXFP8 / MXFP4 expert weights ("Twinkle x Ascend",
- * functional-expansion section; FP4/FP8 checkpoints in the quick start);
+ * The pages name MXFP8 / MXFP4 expert weights ("CANN DeepSeek-V4 training
+ * optimisation", outlook section, functional-expansion bullets; the FP4/FP8
+ * checkpoints in the quick start of "Twinkle x Ascend ... DeepSeek-V4
+ * training");
  * MXFP8 is the OCP Microscaling format: blocks of 32 values along K (the
  * input dimension) share one power-of-two scale, each value an OCP E4M3
  * float (bias 7, subnormals, no infinities, largest finite 448).  Per block,
@@ -368,8 +372,21 @@ typedef struct moe_weights {
 #define MOE_WEIGHTS_FP4 3
 
 /* Workspace for moe_forward (all intermediates: logits, routing, permutation,
- * x_perm, h, y_perm and the shared expert's h and y). */
+ * x_perm, h, y_perm and the shared expert's h and y) [HP 2.3 MegaMoE: one
+ * workspace reused across the fused chain].  moe_workspace_size is the same
+ * size under the name of the layer's one workspace; 0 for an invalid cfg
+ * (NULL, T < 0, E < 1 or k < 1). */
 size_t moe_forward_workspace_size(const moe_cfg* cfg);
+size_t moe_workspace_size(const moe_cfg* cfg);
+
+/* Reads the device error-flag word (the MOE_FLAG_* bits that moe_route,
+ * moe_permute, moe_route_backward and moe_forward OR into *d_flags) into
+ * *out after all work queued on `stream` so far has completed.  Unlike every
+ * other entry point it synchronises the host with the stream (a checking or
+ * test call, not a per-step one).  d_flags is a device uint32; out a host
+ * pointer.  MOE_ERR_NULL if either is NULL, MOE_ERR_HIP if the copy or the
+ * synchronisation fails (then *out is not written). */
+int moe_read_error_flags(const uint32_t* d_flags, void* stream, uint32_t* out);
 
 /* x [T,d] bf16; input_ids [T] int32 (HASH) or NULL; modality [T] u8 or NULL;
  * y [T,d] (bf16 or fp32 per out_dtype).  Optional outputs (NULL = kept in the

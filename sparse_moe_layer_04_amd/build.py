@@ -7,6 +7,8 @@ linked into one shared library next to this file.  Flags:
                                  is a fixed sequence of IEEE operations)
   -Xclang -target-feature -Xclang -packed-fp32-ops
                                  no packed-fp32 instructions
+  -Werror=inline-asm             inline assembly must not clobber reserved
+                                 registers (the LDS copies save and restore M0)
 """
 import concurrent.futures as cf
 import glob
@@ -23,7 +25,7 @@ ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-Wall", "-Wno-unused-function"]
+          "-Wall", "-Wno-unused-function", "-Werror=inline-asm"]
 
 
 def sources():

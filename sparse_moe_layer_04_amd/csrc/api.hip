@@ -116,6 +116,19 @@ FwdWs forward_layout(const moe_cfg* c, char* base) {
 }
 
 }  // namespace
+
+int permute_arg_checks(const int32_t* topk_ids, const uint16_t* x, int T, int d, int E, int k,
+                       const int32_t* counts, const int32_t* offsets, const int32_t* dest,
+                       const int32_t* src, const uint16_t* x_perm) {
+    if (T < 0 || d < 8 || E < 1 || k < 1) return MOE_ERR_SHAPE;
+    if (E > MOE_MAX_E || k > MOE_MAX_K || d % 8) return MOE_ERR_UNSUPPORTED;
+    if ((long long)T * k >= (1ll << 31)) return MOE_ERR_SHAPE;
+    if (!counts || !offsets) return MOE_ERR_NULL;
+    if (T > 0 && (!topk_ids || !x || !dest || !src || !x_perm)) return MOE_ERR_NULL;
+    if (T > 0 && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -189,15 +202,11 @@ size_t moe_permute_workspace_size(int T, int k, int E) {
 int moe_permute(const int32_t* topk_ids, const uint16_t* x, int T, int d, int E, int k,
                 int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src, uint16_t* x_perm,
                 uint32_t* d_flags, void* ws, size_t ws_bytes, void* stream) {
-    if (T < 0 || d < 8 || E < 1 || k < 1) return MOE_ERR_SHAPE;
-    if (E > MOE_MAX_E || k > MOE_MAX_K || d % 8) return MOE_ERR_UNSUPPORTED;
-    if ((long long)T * k >= (1ll << 31)) return MOE_ERR_SHAPE;
-    if (!counts || !offsets) return MOE_ERR_NULL;
+    int st = permute_arg_checks(topk_ids, x, T, d, E, k, counts, offsets, dest, src, x_perm);
+    if (st != MOE_OK) return st;
     if (!ws && permute_workspace_bytes(T, k, E) > 0) return MOE_ERR_NULL;
-    if (T > 0 && (!topk_ids || !x || !dest || !src || !x_perm)) return MOE_ERR_NULL;
     if (((uintptr_t)ws & 255u) || ws_bytes < permute_workspace_bytes(T, k, E))
         return MOE_ERR_WORKSPACE;
-    if (T > 0 && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_ALIGN;
     return hip_status(launch_permute(topk_ids, x, T, d, E, k, counts, offsets, dest, src, x_perm,
                                      d_flags, ws, as_stream(stream)));
 }
@@ -430,6 +439,19 @@ static int forward_checks(const moe_cfg* c, const moe_weights* w) {
 size_t moe_forward_workspace_size(const moe_cfg* cfg) {
     if (!cfg || cfg->T < 0 || cfg->E < 1 || cfg->k < 1) return 0;
     return forward_layout(cfg, nullptr).total;
+}
+
+size_t moe_workspace_size(const moe_cfg* cfg) { return moe_forward_workspace_size(cfg); }
+
+int moe_read_error_flags(const uint32_t* d_flags, void* stream, uint32_t* out) {
+    if (!d_flags || !out) return MOE_ERR_NULL;
+    uint32_t v = 0;
+    hipStream_t s = as_stream(stream);
+    if (hipMemcpyAsync(&v, d_flags, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+    *out = v;
+    return MOE_OK;
 }
 
 int moe_forward(const moe_cfg* c, const moe_weights* w, const uint16_t* x,

@@ -410,7 +410,7 @@ hipError_t launch_epi(const GemmArgs& g, hipStream_t stream) {
     // workgroups, whole rounds of the 8 XCDs)
     static DeviceSetup setup;
     long long grid = 0, unused = 0;
-    const hipError_t err = device_setup(setup, grid, unused, [lds](int, long long& gr, long long&) {
+    const hipError_t err = device_setup(setup, grid, unused, [](int, long long& gr, long long&) {
         hipError_t e = hipFuncSetAttribute(
             (const void*)grouped_gemm_kernel<EPI, PACKED, MAXNTB, RING, APRE>,
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

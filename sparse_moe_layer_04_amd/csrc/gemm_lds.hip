@@ -128,22 +128,39 @@ __device__ __forceinline__ int swz(int r) {
 // 1 KB direct-to-LDS copy: lane l's 16 bytes from gaddr go to LDS byte
 // lds_byte + 16 l.
 // (lds_byte must be wave-uniform; readfirstlane makes that visible)
+// M0 carries the LDS address of the copy.  The compiler may keep a value of
+// its own in M0, so the block saves M0 in an SGPR of its own, sets it, issues
+// the copy (one wait state after the M0 write, as the hardware requires) and
+// restores it: M0 leaves the block as it came in.  The copy takes its LDS
+// address from M0 when it issues, so the restore does not disturb it.
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_byte) {
     const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_byte);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :
-                 : "s"(m0v), "v"(gaddr)
-                 : "memory", "m0");
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0v), "v"(gaddr)
+        : "memory");
 }
 
 // 4-byte direct-to-LDS copy: lane l's 4 bytes from gaddr go to LDS byte
-// lds_byte + 4 l (only the active lanes copy)
+// lds_byte + 4 l (only the active lanes copy); M0 handled as in dma16
 __device__ __forceinline__ void dma4(const void* gaddr, uint32_t lds_byte) {
     const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_byte);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-                 :
-                 : "s"(m0v), "v"(gaddr)
-                 : "memory", "m0");
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0v), "v"(gaddr)
+        : "memory");
 }
 
 // wait until at most N of this wave's memory operations are outstanding

@@ -153,6 +153,11 @@ hipError_t launch_route_backward(const float* logits, const int32_t* ids, const 
                                  hipStream_t stream);
 
 size_t permute_workspace_bytes(int T, int k, int E);
+// moe_permute's argument checks other than the workspace (MOE_OK or the
+// error code)
+int permute_arg_checks(const int32_t* topk_ids, const uint16_t* x, int T, int d, int E, int k,
+                       const int32_t* counts, const int32_t* offsets, const int32_t* dest,
+                       const int32_t* src, const uint16_t* x_perm);
 hipError_t launch_permute(const int32_t* ids, const uint16_t* x, int T, int d, int E, int k,
                           int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
                           uint16_t* x_perm, uint32_t* flags, void* ws, hipStream_t stream,

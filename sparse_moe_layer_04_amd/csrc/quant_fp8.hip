@@ -2,8 +2,9 @@
 // for the 8-bit and 4-bit weight modes of the expert GEMMs.
 //
 // The pages name MXFP8 / MXFP4 weights as the low-precision direction
-// ("Twinkle x Ascend ... DeepSeek-V4 training": functional-expansion
-// section; FP4/FP8 checkpoints in the quick start).  MXFP8 (OCP
+// ("CANN DeepSeek-V4 training optimisation": outlook section,
+// functional-expansion bullets; FP4/FP8 checkpoints in the quick start of
+// "Twinkle x Ascend ... DeepSeek-V4 training").  MXFP8 (OCP
 // Microscaling): blocks of 32 values along K share one power-of-two scale,
 // each value an OCP E4M3 float (bias 7, subnormals, no infinities, largest
 // finite 448).  Scale rule of the OCP specification: X = floor(log2(block

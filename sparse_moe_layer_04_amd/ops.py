@@ -100,6 +100,9 @@ def lib():
     L.moe_pack_weights_fp4.argtypes = [P, I, I, I, I, P, P, P]
     L.moe_forward_workspace_size.argtypes = [ctypes.POINTER(MoeCfg)]
     L.moe_forward_workspace_size.restype = S
+    L.moe_workspace_size.argtypes = [ctypes.POINTER(MoeCfg)]
+    L.moe_workspace_size.restype = S
+    L.moe_read_error_flags.argtypes = [P, P, ctypes.POINTER(ctypes.c_uint32)]
     L.moe_forward.argtypes = [ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeWeights), P, P, P, P,
                               P, P, P, P, P, S, P]
     L.moe_forward_timed.argtypes = L.moe_forward.argtypes + [P]
@@ -110,6 +113,17 @@ def lib():
         getattr(L, name).restype = I
     _lib = L
     return L
+
+
+def read_error_flags(flags):
+    """The device error-flag word (MOE_FLAG_* bits) after the work queued on
+    the current stream so far (moe_read_error_flags: synchronises with the
+    stream)."""
+    _need(flags, torch.int32, "flags", shape=(1,))
+    out = ctypes.c_uint32(0)
+    _check(lib().moe_read_error_flags(_ptr(flags), _stream(), ctypes.byref(out)),
+           "moe_read_error_flags")
+    return int(out.value)
 
 
 def _check(status, what):

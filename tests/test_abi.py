@@ -239,3 +239,21 @@ def test_forward_validation(L):
     c = ops.MoeCfg.from_buffer_copy(cfg)
     c.T = 1 << 30                                    # T k = 2^31 routed rows: out of range
     assert fwd(c=c) == ERR_SHAPE
+
+
+def test_workspace_size_and_error_flag_reader(L):
+    """moe_workspace_size is the forward's workspace under the layer's one
+    name (0 for an invalid cfg); moe_read_error_flags rejects NULL pointers
+    before any HIP call."""
+    cfg = ops.MoeCfg(T=8192, d=4096, E=384, k=6, F=2048, F_shared=2048, mode=0, n_bias=1, V=0,
+                     scale=2.5, clamp_limit=10.0, clamp_mode=0, out_dtype=0)
+    a = L.moe_workspace_size(ctypes.byref(cfg))
+    assert a == L.moe_forward_workspace_size(ctypes.byref(cfg)) and a > 0
+    assert L.moe_workspace_size(None) == 0
+    bad = ops.MoeCfg.from_buffer_copy(cfg)
+    bad.k = 0
+    assert L.moe_workspace_size(ctypes.byref(bad)) == 0
+    out = ctypes.c_uint32(7)
+    assert L.moe_read_error_flags(None, None, ctypes.byref(out)) == ERR_NULL
+    assert L.moe_read_error_flags(FAKE, None, None) == ERR_NULL
+    assert out.value == 7

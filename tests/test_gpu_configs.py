@@ -9,10 +9,12 @@ weights, one moe_forward call):
   - the dispatch permutation (counts, offsets, dest, src) bit-exact and every
     gathered row byte-equal to its token row;
   - router logits on sampled rows within the fp32 accumulation bound;
-  - the layer output (fp32 mode) on sampled tokens - a seeded random sample
-    plus the tokens at the tile boundaries of the most loaded expert -
-    within 1e-2 x RMS of the oracle; the bf16 output within one bf16 rounding
-    of that bound.
+  - the layer output (fp32 mode) within 1e-2 x RMS of the oracle: every
+    token of the 64-expert layer; at the larger ones a token set that covers
+    every non-empty expert and, for every m-tile of the expert GEMMs, its
+    first and last row and the rows on both sides of its wave-half split
+    (plus the shared expert's tile boundaries and a seeded random sample);
+    the bf16 output within one bf16 rounding of that bound.
 Near-ties (k-th vs (k+1)-th biased score gap below 1e-6) are counted and
 printed (they are bit-exact here because both sides use the same logits).
 Route flips are counted and printed too: the tokens whose expert set under
@@ -37,6 +39,51 @@ DEV = torch.device("cuda")
 
 def _opt(inp, key):
     return None if inp[key] is None else host(inp[key])
+
+
+TM = 256   # activation rows per expert-GEMM tile
+
+
+def _bf16_tile_split(n):
+    """Rows per m-tile of an expert with n rows for bf16 weights: TM (the
+    last tile shorter)."""
+    return TM
+
+
+def _mx_tile_split(n):
+    """Rows per m-tile of an expert with n rows in the MX weight modes: the
+    rows split evenly over ceil(n / 256) tiles, rounded up to 16."""
+    mt = -(-n // TM)
+    return (-(-n // mt) + 15) & ~15
+
+
+def tile_edge_rows(lo, hi, per):
+    """Rows of the expert segment [lo, hi) at the edges of its m-tiles of
+    `per` rows: each tile's first and last row and the rows on both sides of
+    the split between its two wave halves (each half takes
+    min(128, ceil(valid / 2) rounded up to 32) rows)."""
+    out = []
+    for r0 in range(lo, hi, per):
+        valid = min(per, hi - r0)
+        mh = min(TM // 2, (((valid + 1) >> 1) + 31) & ~31)
+        out += [r0, r0 + valid - 1]
+        if mh < valid:
+            out += [r0 + mh - 1, r0 + mh]
+    return out
+
+
+def coverage_tokens(counts, offsets, src, split, T, rng, n_random=32):
+    """Tokens whose outputs cover every non-empty expert and every m-tile
+    edge of the routed expert GEMMs (rows of the dispatch order mapped to
+    their tokens through src), the shared expert's tile edges (its single
+    group of T rows) and n_random seeded random tokens."""
+    rows = []
+    for e in np.nonzero(counts)[0]:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        rows += tile_edge_rows(lo, hi, split(hi - lo))
+    toks = [src[np.asarray(rows, np.int64)], np.asarray(tile_edge_rows(0, T, TM), np.int64),
+            rng.choice(T, size=min(n_random, T), replace=False)]
+    return np.unique(np.concatenate(toks).astype(np.int64))
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
@@ -93,12 +140,14 @@ def test_full_size(cfg):
     rows = np.sort(rng.choice(w.T, size=48, replace=False))
     check_logits(xb, bits(inp["w_g"]), _opt(inp, "logit_offset"), lg, rows)
 
-    # layer output on sampled tokens (random + tile boundaries of the busiest expert)
-    e_max = int(np.argmax(counts))
-    lo, hi = int(offsets[e_max]), int(offsets[e_max + 1])
-    edge = [r for r in (lo, lo + 31, lo + 32, lo + 127, lo + 128, lo + 255, lo + 256, hi - 1)
-            if lo <= r < hi]
-    toks = np.unique(np.concatenate([rng.choice(w.T, size=40, replace=False), src[edge]]))
+    # layer output: every token of the 64-expert layer; at the larger ones
+    # every non-empty expert and every m-tile edge of the expert GEMMs
+    if cfg == 1:
+        toks = np.arange(w.T, dtype=np.int64)
+    else:
+        toks = coverage_tokens(counts, offsets, src, _bf16_tile_split, w.T, rng)
+    covered = np.unique(rid[toks])
+    assert set(np.nonzero(counts)[0]) <= set(covered.tolist())
     shared = [bits(inp[k]) if inp[k] is not None else None for k in ("s_gate", "s_up", "s_down")]
     yref = oracle.tokens_forward(xb, toks, rid, rw, bits(inp["w_gate"]), bits(inp["w_up"]),
                                  bits(inp["w_down"]), *shared, w.clamp_limit, w.clamp_mode)
@@ -106,17 +155,23 @@ def test_full_size(cfg):
     rms = np.sqrt(np.mean(yref ** 2))
     err16 = np.abs(bf16_f64(bits(y16))[toks] - yref)
     assert np.all(err16 <= 2.0 ** -8 * np.abs(yref) + 1e-2 * rms)
-    print(f"[{w.name}] {len(toks)} sampled tokens: max|y - y_oracle| / rms = {rel:.2e}",
-          flush=True)
+    print(f"[{w.name}, bf16 weights] {len(toks)} of {w.T} tokens, {len(covered)} experts "
+          f"(all non-empty): max|y - y_oracle| / rms = {rel:.2e}", flush=True)
     del layer, inp, y, y16, logits, ids, wts
     free_cuda()
 
 
-def _mx_tile_split(n):
-    """Rows per m-tile of an expert with n rows in the MX weight modes: the
-    rows split evenly over ceil(n / 256) tiles, rounded up to 16."""
-    mt = -(-n // 256)
-    return (-(-n // mt) + 15) & ~15
+def _dequant_experts(m, experts, quant, dequant):
+    """The oracle's dequantisation of the listed experts' matrices, in place
+    (host threads over experts; each call is one C routine)."""
+    import concurrent.futures as cf
+
+    def one(e):
+        q, ex = quant(m[e])
+        m[e] = dequant(q, ex)
+
+    with cf.ThreadPoolExecutor(max_workers=16) as ex:
+        list(ex.map(one, [int(e) for e in experts]))
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "fp4"])
@@ -126,11 +181,10 @@ def test_full_size_mx(cfg, fmt):
     layer, whose ~384-row experts split into two ~192-row tiles; the
     384-expert layer; the skewed multimodal one; and the hash-routed T=32768
     layer, whose experts take 64-wide stages), in the benchmark's launch
-    configuration (--weights fp8 / fp4): routes bit-exact, and sampled tokens
-    within 1e-2 x RMS of the oracle run on the oracle's own dequantisation of
-    the weights of the experts those tokens use.  The sample includes the
-    rows at the tile boundaries of the busiest expert and of a two-tile
-    expert whose tiles are split evenly (fewer than 256 rows each)."""
+    configuration (--weights fp8 / fp4): routes bit-exact, and the outputs of
+    a token set covering every non-empty expert and every m-tile edge (tiles
+    split evenly in these modes) within 1e-2 x RMS of the oracle run on the
+    oracle's own dequantisation of every expert's weights."""
     quant, dequant = ((oracle.quant_mxfp8, oracle.dequant_mxfp8) if fmt == "fp8" else
                       (oracle.quant_mxfp4, oracle.dequant_mxfp4))
     w = wl.WORKLOADS[cfg]
@@ -149,31 +203,21 @@ def test_full_size_mx(cfg, fmt):
                               tid2eid=_opt(inp, "tid2eid"), mode=w.mode)
     assert np.array_equal(host(ids), rid)
     assert np.array_equal(host(wts).view(np.uint32), rw.view(np.uint32))
-    # random tokens plus the tokens at the tile boundaries of the busiest expert
     counts, offsets, _, src, _ = oracle.permute(rid, w.E)
-    e_max = int(np.argmax(counts))
-    lo, hi = int(offsets[e_max]), int(offsets[e_max + 1])
-    edge = [r for r in (lo, lo + 127, lo + 128, lo + 255, lo + 256, hi - 1) if lo <= r < hi]
-    two = [e for e in range(w.E) if 256 < counts[e] and _mx_tile_split(int(counts[e])) < 256]
-    if two:
-        e2 = min(two, key=lambda e: abs(int(counts[e]) - 320))
-        lo2, per = int(offsets[e2]), _mx_tile_split(int(counts[e2]))
-        edge += [lo2 + per - 1, lo2 + per, int(offsets[e2 + 1]) - 1]
     rng = np.random.default_rng(77)
-    toks = np.unique(np.concatenate([rng.choice(w.T, size=6, replace=False), src[edge]]))
+    toks = coverage_tokens(counts, offsets, src, _mx_tile_split, w.T, rng)
     experts = np.unique(rid[toks])
+    assert set(np.nonzero(counts)[0]) <= set(experts.tolist())
     mats = {}
     for key in ("w_gate", "w_up", "w_down"):
         m = bits(inp[key])
-        for e in experts:
-            q, ex = quant(m[e])
-            m[e] = dequant(q, ex)
+        _dequant_experts(m, experts, quant, dequant)
         mats[key] = m
     shared = [bits(inp[k]) for k in ("s_gate", "s_up", "s_down")]
     yref = oracle.tokens_forward(bits(inp["x"]), toks, rid, rw, mats["w_gate"], mats["w_up"],
                                  mats["w_down"], *shared, w.clamp_limit, w.clamp_mode)
     rel = check_rms(host(y)[toks], yref)
-    print(f"[{w.name}, {fmt} weights] {len(toks)} sampled tokens ({len(experts)} experts): "
-          f"max|y - y_oracle| / rms = {rel:.2e}", flush=True)
+    print(f"[{w.name}, {fmt} weights] {len(toks)} of {w.T} tokens, {len(experts)} experts "
+          f"(all non-empty): max|y - y_oracle| / rms = {rel:.2e}", flush=True)
     del layer, inp, y, logits, ids, wts, mats
     free_cuda()

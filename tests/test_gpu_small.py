@@ -90,6 +90,8 @@ def test_route_hash_bad_ids():
     assert np.array_equal(host(ids), rid)
     assert np.array_equal(host(w), rw)
     assert int(flags.item()) == rf == 3
+    # the C-ABI reader of the flag word gives the same bits
+    assert ops.read_error_flags(flags) == 3
 
 
 # --------------------------------------------------------------- permute ----
