@@ -58,6 +58,7 @@ extern "C" {
 #define MOE_ERR_WORKSPACE (-4)   /* workspace missing, misaligned or too small */
 #define MOE_ERR_HIP (-5)         /* a HIP runtime call failed */
 #define MOE_ERR_ALIGN (-6)       /* a tensor pointer is not 16-byte aligned */
+#define MOE_ERR_SCRATCH (-7)     /* more scratch than the static array holds */
 
 #define MOE_MODE_TOPK 0 /* sigmoid score + bias-ranked top-k */
 #define MOE_MODE_HASH 1 /* ids from tid2eid[input_ids] */
@@ -158,6 +159,24 @@ size_t moe_permute_workspace_size(int T, int k, int E);
 int moe_permute(const int32_t* topk_ids, const uint16_t* x, int T, int d, int E, int k,
                 int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
                 uint16_t* x_perm, uint32_t* d_flags, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_permute for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, checks, results and errors as moe_permute, without the
+ * workspace: the permutation's scratch (chunk ranks, chunk histogram and
+ * bases: moe_permute_workspace_size(T, k, E) bytes) lives in a static
+ * device array of MOE_NOALLOC_SCRATCH_BYTES that each GPU the library runs
+ * on holds until the process ends.  The call allocates nothing; a call whose
+ * scratch would exceed the array returns MOE_ERR_SCRATCH before any launch.
+ * Every call on one GPU shares that GPU's array (no part of it needs to
+ * start at zero; it keeps the last call's contents), so calls that overlap
+ * in time on one GPU race: the caller serialises them (one stream, or
+ * events between streams).  The first call on a device looks up the array's
+ * device address once (a host call, not an allocation). */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+int moe_permute_noalloc(const int32_t* topk_ids, const uint16_t* x, int T, int d, int E, int k,
+                        int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
+                        uint16_t* x_perm, uint32_t* d_flags, void* stream);
 
 /* ------------------------------------------------------------------------
  * Grouped expert FFN [HP 2.3 MegaMoE: two expert matmuls with SwiGLU and the

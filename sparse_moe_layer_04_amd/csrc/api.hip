@@ -144,6 +144,8 @@ const char* moe_status_string(int status) {
         case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case MOE_ERR_HIP: return "HIP runtime error";
         case MOE_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+        case MOE_ERR_SCRATCH:
+            return "the call needs more scratch than the library's static scratch array holds";
         default: return "unknown status";
     }
 }

@@ -84,6 +84,7 @@ def lib():
     L.moe_permute_workspace_size.argtypes = [I, I, I]
     L.moe_permute_workspace_size.restype = S
     L.moe_permute.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, S, P]
+    L.moe_permute_noalloc.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P]
     L.moe_expert_ffn.argtypes = [P, P, I, I, I, I, P, P, P, F, I, P, P, P]
     L.moe_expert_ffn_packed.argtypes = L.moe_expert_ffn.argtypes
     L.moe_combine.argtypes = [P, P, P, P, I, I, I, I, I, P, P]
@@ -255,6 +256,30 @@ def permute(topk_ids, x, E, flags=None, workspace=None):
                              _ptr(out["offsets"]), _ptr(out["dest"]), _ptr(out["src"]),
                              _ptr(out["x_perm"]), _ptr(flags), _ptr(workspace),
                              workspace.numel(), _stream()), "moe_permute")
+    return out
+
+
+def permute_noalloc(topk_ids, x, E, flags=None, out=None):
+    """moe_permute_noalloc (the permutation with its scratch in the library's
+    static device array): returns dict(counts, offsets, dest, src, x_perm).
+    `out` may hold preallocated outputs (a dict of the same keys), so that the
+    call itself allocates nothing."""
+    _need(topk_ids, torch.int32, "topk_ids", 2)
+    T, k = topk_ids.shape
+    _need(x, torch.bfloat16, "x", shape=(T, None))
+    _flags(flags)
+    d = x.shape[1]
+    dev = x.device
+    out = dict(out or {})
+    out["counts"] = _out(out.get("counts"), torch.int32, "counts", (E,), dev)
+    out["offsets"] = _out(out.get("offsets"), torch.int32, "offsets", (E + 1,), dev)
+    out["dest"] = _out(out.get("dest"), torch.int32, "dest", (T * k,), dev)
+    out["src"] = _out(out.get("src"), torch.int32, "src", (T * k,), dev)
+    out["x_perm"] = _out(out.get("x_perm"), torch.bfloat16, "x_perm", (T * k, d), dev)
+    _check(lib().moe_permute_noalloc(_ptr(topk_ids), _ptr(x), T, d, E, k, _ptr(out["counts"]),
+                                     _ptr(out["offsets"]), _ptr(out["dest"]), _ptr(out["src"]),
+                                     _ptr(out["x_perm"]), _ptr(flags), _stream()),
+           "moe_permute_noalloc")
     return out
 
 

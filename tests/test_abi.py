@@ -257,3 +257,21 @@ def test_workspace_size_and_error_flag_reader(L):
     assert L.moe_read_error_flags(None, None, ctypes.byref(out)) == ERR_NULL
     assert L.moe_read_error_flags(FAKE, None, None) == ERR_NULL
     assert out.value == 7
+
+
+def test_permute_noalloc_validation(L):
+    """moe_permute_noalloc: moe_permute's checks, and a call whose scratch
+    exceeds the static array is rejected before any launch."""
+    def pn(T=64, d=64, E=8, k=2, ids=FAKE, x=FAKE, counts=FAKE, offsets=FAKE, xp=FAKE):
+        return L.moe_permute_noalloc(ids, x, T, d, E, k, counts, offsets, FAKE, FAKE, xp, None,
+                                     None)
+    assert pn(k=0) == ERR_SHAPE
+    assert pn(E=2000) == ERR_UNSUPPORTED
+    assert pn(d=12) == ERR_UNSUPPORTED
+    assert pn(counts=None) == ERR_NULL
+    assert pn(ids=None) == ERR_NULL
+    assert pn(x=FAKE + 2) == ERR_ALIGN
+    T, k, E = 1 << 17, 8, 1024                # chunk histogram alone: 32 MiB
+    assert ops.permute_workspace_size(T, k, E) > 8 << 20
+    assert pn(T=T, k=k, E=E) == -7
+    assert "scratch" in L.moe_status_string(-7).decode()
