@@ -36,6 +36,10 @@ from .oracle import (  # noqa: F401
     grouped_gemm,
     grouped_wgrad,
     grouped_wgrad_entries,
+    router_backward,
+    round_bf16,
+    add,
+    layer_backward,
     tokens_forward,
     forward,
     e4m3_decode,

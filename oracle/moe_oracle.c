@@ -441,6 +441,51 @@ void orc_grouped_wgrad_entries(const uint16_t* dy, const uint16_t* a, const int3
     }
 }
 
+/* ---------------------------------------------------- router backward -- */
+/*
+ * Gradients of the router projection l = x W_g^T ("HyperParallel accelerates
+ * DeepSeek-V4.1 ...", section 2.3, MegaGate: the projection matmul that
+ * feeds the gate) for a gradient dl of the logits:
+ *   dx[t, i]  = sum_e dl[t, e] * w_g[e, i]
+ *   dwg[e, i] = sum_t dl[t, e] * x[t, i]
+ * dl in fp64 (the routing backward's output), x and w_g bf16, fp64 sums over
+ * every expert / token (the plain dense definition).
+ */
+void orc_router_backward(const double* dl, const uint16_t* x, const uint16_t* wg, int T, int d,
+                         int E, double* dx, double* dwg)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t)
+        for (int i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int e = 0; e < E; ++e)
+                acc += dl[(size_t)t * E + e] * bf16_value(wg[(size_t)e * d + i]);
+            dx[(size_t)t * d + i] = acc;
+        }
+#pragma omp parallel for schedule(static)
+    for (int e = 0; e < E; ++e)
+        for (int i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int t = 0; t < T; ++t)
+                acc += dl[(size_t)t * E + e] * bf16_value(x[(size_t)t * d + i]);
+            dwg[(size_t)e * d + i] = acc;
+        }
+}
+
+/* n values rounded to bf16 (nearest, ties to even): the precision in which a
+ * gradient enters the matrix cores in the backward. */
+void orc_round_bf16_array(const double* v, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f64_to_bf16(v[i]);
+}
+
+/* out = a + b elementwise (fp64): the sum of the gradient contributions that
+ * reach the same tensor along different paths of the layer. */
+void orc_add_f64(const double* a, const double* b, int64_t n, double* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = a[i] + b[i];
+}
+
 /* ------------------------------------------------------ SwiGLU backward -- */
 /*
  * Backward of the clamped SwiGLU between the expert matmuls ("HyperParallel

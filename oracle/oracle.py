@@ -81,6 +81,12 @@ def load():
     lib.orc_swiglu_backward.argtypes = [P, P, P, I64, D, I, P, P]
     lib.orc_grouped_gemm.argtypes = [P, P, I, I, I, P, P]
     lib.orc_grouped_gemm.restype = None
+    lib.orc_router_backward.argtypes = [P, P, P, I, I, I, P, P]
+    lib.orc_router_backward.restype = None
+    lib.orc_round_bf16_array.argtypes = [P, I64, P]
+    lib.orc_round_bf16_array.restype = None
+    lib.orc_add_f64.argtypes = [P, P, I64, P]
+    lib.orc_add_f64.restype = None
     lib.orc_grouped_wgrad.argtypes = [P, P, P, I, I, I, P]
     lib.orc_grouped_wgrad.restype = None
     lib.orc_grouped_wgrad_entries.argtypes = [P, P, P, I, I, P, P, P, I64, P]
@@ -255,6 +261,99 @@ def grouped_gemm(a, offsets, w, out=None):
     res = np.zeros((rows, N), np.float64) if out is None else _c(out, np.float64).copy()
     load().orc_grouped_gemm(_p(a), _p(offsets), G, K, N, _p(w), _p(res))
     return res
+
+
+def router_backward(dl, x, wg):
+    """(dx[T,d], dwg[E,d]) float64: gradients of l = x w_g^T for dl[T,E]."""
+    dl = _c(dl, np.float64)
+    x, wg = _bf16(x), _bf16(wg)
+    T, E = dl.shape
+    d = x.shape[1]
+    dx = np.empty((T, d), np.float64)
+    dwg = np.empty((E, d), np.float64)
+    load().orc_router_backward(_p(dl), _p(x), _p(wg), T, d, E, _p(dx), _p(dwg))
+    return dx, dwg
+
+
+def round_bf16(v):
+    """float64 values rounded to bf16 (nearest even), returned as bits."""
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    load().orc_round_bf16_array(_p(v), v.size, _p(out))
+    return out
+
+
+def add(a, b):
+    """a + b (float64), elementwise."""
+    a, b = _c(a, np.float64), _c(b, np.float64)
+    assert a.shape == b.shape
+    out = np.empty(a.shape, np.float64)
+    load().orc_add_f64(_p(a), _p(b), a.size, _p(out))
+    return out
+
+
+def _t(w):
+    """[G, N, K] bf16 bits -> [G, K, N] (the transposed matrices; data movement)."""
+    return np.ascontiguousarray(np.swapaxes(_bf16(w), -1, -2))
+
+
+def layer_backward(x, logits, k, scale, w_g, w_gate, w_up, w_down, s_gate, s_up, s_down, dy,
+                   clamp_limit=10.0, clamp_mode=0, bias=None, modality=None, input_ids=None,
+                   tid2eid=None, mode=MODE_TOPK):
+    """Gradients of the whole layer for an output gradient dy[T,d] (fp32),
+    chaining the pinned backward pieces in the reverse order of the forward.
+    The forward's values come from `forward` (routes from the given logits).
+    Gradients enter the matrix products as bf16 (round_bf16) and the fp32
+    intermediates of the GPU path (expert outputs, pre-activations, their
+    gradients, the routing-weight gradient) are passed as fp32, so the chain
+    follows the precision at which each product is taken.  Returns a dict:
+    dx, dw_g, dw_gate, dw_up, dw_down, ds_gate, ds_up, ds_down (float64) and
+    dx_routed, dx_shared, dx_router (the three parts of dx)."""
+    x = _bf16(x)
+    T, d = x.shape
+    f = forward(x, logits, k, scale, w_gate, w_up, w_down, s_gate, s_up, s_down, clamp_limit,
+                clamp_mode, bias, modality, input_ids, tid2eid, mode)
+    w_gate, w_up, w_down = _bf16(w_gate), _bf16(w_up), _bf16(w_down)
+    offs, dest, h, xp = f["offsets"], f["dest"], f["h"], f["x_perm"]
+    dy = _c(dy, np.float32)
+    out = {}
+    # combine: y = ysh + sum_j w_j y_perm[dest_j]
+    dyp, dtw = combine_backward(dy, f["y_perm"], dest, f["w"])
+    dyp16 = round_bf16(dyp)
+    # down projection y_perm = h W_down^T
+    out["dw_down"] = grouped_wgrad(dyp16, h, offs)
+    dh = grouped_gemm(dyp16, offs, _t(w_down))
+    # clamped SwiGLU h = silu(cg(G)) cu(U), G = x_perm W_gate^T, U = x_perm W_up^T
+    G = grouped_gemm(xp, offs, w_gate)
+    U = grouped_gemm(xp, offs, w_up)
+    dG, dU = swiglu_backward(G, U, dh, clamp_limit, clamp_mode)
+    dG16, dU16 = round_bf16(dG), round_bf16(dU)
+    out["dw_gate"] = grouped_wgrad(dG16, xp, offs)
+    out["dw_up"] = grouped_wgrad(dU16, xp, offs)
+    dxp = grouped_gemm(np.concatenate([dG16, dU16], axis=1), offs,
+                       _t(np.concatenate([w_gate, w_up], axis=1)))
+    # dispatch: x_perm[row] = x[src[row]]; its backward sums each token's rows
+    out["dx_routed"] = combine(dxp, dest, np.ones((T, k), np.float32))
+    # routing weights -> logits -> router projection
+    dl, _ = route_backward(logits, f["ids"], dtw, scale)
+    out["dx_router"], out["dw_g"] = router_backward(dl, x, w_g)
+    # shared expert on x
+    sg, su, sd = _bf16(s_gate), _bf16(s_up), _bf16(s_down)
+    one = np.array([0, T], np.int32)
+    hs, _ = expert_ffn(x, one, sg[None], su[None], sd[None], clamp_limit, clamp_mode)
+    dy16 = round_bf16(dy)
+    out["ds_down"] = grouped_wgrad(dy16, hs, one)[0]
+    dhs = grouped_gemm(dy16, one, _t(sd[None]))
+    Gs = grouped_gemm(x, one, sg[None])
+    Us = grouped_gemm(x, one, su[None])
+    dGs, dUs = swiglu_backward(Gs, Us, dhs, clamp_limit, clamp_mode)
+    dGs16, dUs16 = round_bf16(dGs), round_bf16(dUs)
+    out["ds_gate"] = grouped_wgrad(dGs16, x, one)[0]
+    out["ds_up"] = grouped_wgrad(dUs16, x, one)[0]
+    out["dx_shared"] = grouped_gemm(np.concatenate([dGs16, dUs16], axis=1), one,
+                                    _t(np.concatenate([sg, su], axis=0)[None]))
+    out["dx"] = add(add(out["dx_routed"], out["dx_shared"]), out["dx_router"])
+    return out
 
 
 def grouped_wgrad(dy, a, offsets):
