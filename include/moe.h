@@ -342,6 +342,24 @@ int moe_grouped_gemm_packed(const uint16_t* a, const int32_t* offsets, int G, in
                             int N, const uint16_t* w_packed, float* out, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Grouped weight gradient [HP 2.3 MegaMoE: the expert matmuls, whose weights
+ * the training step of HP 03 updates].  For the grouped matmul
+ * out[r, :] = a[r, :] W_g^T on the rows of group g and a gradient dy of out:
+ *   dw[g, m, k] = sum_{offsets[g] <= r < offsets[g+1]} dy[r, m] * a[r, k]
+ * bf16 products, fp32 accumulation; a group without rows gets zeros (every
+ * entry of dw is written).  dW_down = dY^T H (dy = dY [rows, d], a = H
+ * [rows, F]), dW_gate = dG^T X and dW_up = dU^T X (dy = the pre-activation
+ * gradients, a = the dispatched token rows), and with G = 1 the shared
+ * expert's matrices and the router's dW_g = dlogits^T x.
+ *   dy [rows, M] bf16, a [rows, K] bf16 row-major; offsets [G+1] int32 in
+ *   DEVICE memory (entries clamped into [0, rows]; NULL allowed when G = 1:
+ *   one group [0, rows)); dw [G, M, K] fp32.  M, K multiples of 8; dy, a, dw
+ *   16-byte aligned.  No workspace.
+ */
+int moe_grouped_wgrad(const uint16_t* dy, const uint16_t* a, const int32_t* offsets, int G,
+                      int rows, int M, int K, float* dw, void* stream);
+
+/* ------------------------------------------------------------------------
  * Whole layer forward: gate logits -> route -> permute -> grouped FFN (routed
  * experts) and FFN (shared expert) -> combine.
  */

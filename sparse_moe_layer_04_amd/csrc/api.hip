@@ -64,7 +64,12 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 inline bool lds_gemm_ok(int packed, int G) {
     return packed && G <= grouped_gemm_lds_max_groups();
 }
+#ifndef MOE_EXPERT_GEMM_FLAT
+#define MOE_EXPERT_GEMM_FLAT 1
+#endif
 inline hipError_t expert_gemm(int epi, const GemmArgs& g, hipStream_t s) {
+    if (MOE_EXPERT_GEMM_FLAT && g.packed && !g.wfp8 && g.G <= grouped_gemm_flat_max_groups())
+        return launch_grouped_gemm_flat(epi, g, s);
     return lds_gemm_ok(g.packed, g.G) ? launch_grouped_gemm_lds(epi, g, s)
                                       : launch_grouped_gemm(epi, g, s);
 }
@@ -399,6 +404,19 @@ int moe_grouped_gemm_packed(const uint16_t* a, const int32_t* offsets, int G, in
     g.packed = 1;
     g.out = out;
     return hip_status(launch_grouped_gemm_lds(EPI_F32, g, as_stream(stream)));
+}
+
+int moe_grouped_wgrad(const uint16_t* dy, const uint16_t* a, const int32_t* offsets, int G,
+                      int rows, int M, int K, float* dw, void* stream) {
+    if (G < 1 || rows < 0 || M < 8 || K < 8) return MOE_ERR_SHAPE;
+    if (M % 8 || K % 8) return MOE_ERR_UNSUPPORTED;
+    if ((long long)rows * M >= (1ll << 40) || (long long)rows * K >= (1ll << 40) ||
+        (long long)G * M * K >= (1ll << 40))
+        return MOE_ERR_SHAPE;
+    if (!dw || (rows > 0 && (!dy || !a))) return MOE_ERR_NULL;
+    if (G > 1 && !offsets) return MOE_ERR_NULL;
+    if ((dy && !aligned16(dy)) || (a && !aligned16(a)) || !aligned16(dw)) return MOE_ERR_ALIGN;
+    return hip_status(launch_grouped_wgrad(dy, a, offsets, G, rows, M, K, dw, as_stream(stream)));
 }
 
 int moe_swiglu_backward(const float* gate, const float* up, const float* dh, int64_t n,

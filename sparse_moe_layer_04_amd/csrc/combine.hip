@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             const int r = dest[(size_t)t * k + j];
             if (r >= 0 && r < rows) {
                 rj[j] = r;
-                wj[j] = w[(size_t)t * k + j];
+                wj[j] = w ? w[(size_t)t * k + j] : 1.0f;
             }
         }
     }
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
             const int r = dest[(size_t)t * k + j];
             if (r >= 0 && r < rows) {
                 rj[j] = r;
-                wj[j] = w[(size_t)t * k + j];
+                wj[j] = w ? w[(size_t)t * k + j] : 1.0f;
             }
         }
     }

@@ -1,0 +1,596 @@
+// Grouped expert GEMM on packed bf16 weights, "flat" form: weights stream
+// from memory straight into the MFMA operand registers of the one wave that
+// uses them; only the activation rows go through LDS ("HyperParallel
+// accelerates DeepSeek-V4.1 ...", section 2.3, MegaMoE: the two expert
+// matmuls and the clamped SwiGLU between them).
+//
+// Problem: for each expert g and activation row r in [lo_g, hi_g),
+//   out[r, n] = sum_k A[r, k] * W[g, n, k]
+// with W in the moe_pack_weights panel layout (P = 128 rows for the gate and
+// up matrices, P = 256 for the down matrix) and A row-major, in the blocked
+// activation layout, or gathered (row r of A is row gather[r] of a row-major
+// matrix: the dispatch permutation applied while loading).
+//
+// Why this shape.  With a few hundred rows per expert the expert GEMMs are
+// bound by streaming the weights from HBM: every weight element is used
+// against all rows of its tile, once.  So:
+//   - a tile is up to 128 activation rows x 512 weight rows (SwiGLU: 256
+//     features x {gate, up}); wave w of the 8 owns 64 weight rows (SwiGLU: the
+//     gate and up rows of 32 features, so the epilogue needs no exchange;
+//     down: two 32-row blocks) against every row of the tile: up to 2 x 4
+//     MFMA 32x32 accumulators per wave;
+//   - each weight element feeds exactly one wave, so the packed 1 KB
+//     fragments (one per 16-wide K substep and 32-row block, lane-ordered)
+//     are loaded by that wave straight into its operand registers, one
+//     64-wide stage (4 substeps) ahead: plain coalesced 16-byte loads, no
+//     LDS round trip and no second read of the weights by another wave;
+//   - the activation rows are shared by all 8 waves, so they go through a
+//     2-slot LDS ring: each stage (128 rows x 64 columns, 16 KB) is loaded
+//     into registers two stages ahead and written to LDS one stage ahead,
+//     one barrier per stage.  512 weight rows per tile halve how often an
+//     expert's rows are restaged compared with 256-row tiles.
+// Every memory operation is an ordinary compiler-visible load or store, so
+// the compiler's vmcnt/lgkmcnt waits are exact; loads past the end of K or of
+// a group read clamped, valid addresses so the load count per stage is fixed.
+//
+// LDS swizzle: row r of a slot is 128 bytes (8 chunks of 16 B); chunk c is
+// stored at c ^ ((r >> 1) & 7), so the 16 lanes one LDS cycle serves in an
+// MFMA operand read (16 rows of one chunk index) hit distinct banks.
+//
+// Scheduling: persistent grid (one workgroup per CU); every workgroup builds
+// the per-expert item prefix in LDS from the device offsets; items are
+// ordered (expert, n-tile, m-tile), the 8 XCDs take contiguous ranges of
+// equal item count and inside an XCD the workgroups claim items from a
+// per-XCD counter (or, without counters, take every (grid/8)-th item).
+#include <type_traits>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int FM = 128;                  // activation rows per tile
+constexpr int FN = 512;                  // weight rows per tile
+constexpr int FK = 64;                   // K columns per stage
+constexpr int FQ = FK / 16;              // MFMA substeps per stage
+constexpr int FNTB = FM / 32;            // 32-row activation blocks per tile
+constexpr int kFThreads = 512;           // 8 waves
+constexpr int kRowBytes = FK * 2;        // LDS bytes per activation row
+constexpr int kSlotBytes = FM * kRowBytes;
+constexpr int kRingBytes = 2 * kSlotBytes;
+// fp32 epilogue staging: one 32-row block of the tile's outputs, rows padded
+// by 16 bytes so that the 32 rows one MFMA accumulator spans land in
+// distinct banks
+constexpr int kEpiRow = FN * 4 + 16;
+constexpr int kEpiBytes = 32 * kEpiRow;
+constexpr int kLdsFixed = kRingBytes + kEpiBytes;
+constexpr int kFLdsLimit = 160 * 1024;
+constexpr int kFStaticLds = 256;
+
+enum FAMode : int { FA_ROW = 0, FA_BLK = 1, FA_GATHER = 2 };
+
+template <int EPI>
+struct FPanel {
+    static constexpr int P = (EPI == EPI_SWIGLU_BF16) ? 128 : 256;  // packed panel rows
+    static constexpr int BPP = P / 32;                               // 32-row blocks per panel
+    // outputs (features for SwiGLU, output rows for down) per tile
+    static constexpr int TN = (EPI == EPI_SWIGLU_BF16) ? FN / 2 : FN;
+};
+
+__device__ __forceinline__ float fclamp_sym(float v, float L) { return fminf(fmaxf(v, -L), L); }
+
+__device__ __forceinline__ int fswz(int r) { return (r >> 1) & 7; }
+
+// Per-workgroup state of one tile.
+struct FlatTile {
+    int lane, wave, half, l32, tid;
+    int K, N;
+    int row0, valid;       // first activation row of the tile, rows in it
+    int ntb;               // 32-row activation blocks holding a valid row
+    int n0;                // first output (feature / output row) of this wave
+    const uint16_t* wp0;   // this wave's block-0 fragments at stage 0 (lane offset included)
+    const uint16_t* wp1;   // block 1 (SwiGLU: the up block)
+    size_t wstage;         // elements per 64-wide K stage of one panel
+    size_t a_off[2];       // this thread's activation source (elements) at stage 0
+    int a_rows;            // activation rows this thread stages (0..2, wave-uniform)
+    int a_step;            // elements per stage of the activation source
+};
+
+template <int NTB>
+struct FOps {
+    bf16x8 a[NTB];
+};
+
+// activation fragments of substep q (one 16-wide K slice) of the slot
+template <int NTB>
+__device__ __forceinline__ void read_act(const unsigned char* slot, const FlatTile& t, int q,
+                                         FOps<NTB>& o) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+        const int r = tb * 32 + t.l32;
+        const int c = (2 * q + t.half) ^ fswz(r);
+        o.a[tb] = *(const bf16x8*)(slot + r * kRowBytes + c * 16);
+    }
+}
+
+template <int NTB>
+__device__ __forceinline__ void mfma_step(const bf16x8& w0, const bf16x8& w1, const FOps<NTB>& o,
+                                          f32x16 (&acc)[2][FNTB]) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+        acc[0][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w0, o.a[tb], acc[0][tb], 0, 0, 0);
+        acc[1][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w1, o.a[tb], acc[1][tb], 0, 0, 0);
+    }
+}
+
+// fp32 outputs (down projection): each 32-row block goes through LDS so that
+// every store instruction writes 1 KB of one output row (the accumulator
+// layout gives each lane 16 bytes in each of 32 rows 4 * N bytes apart).
+// Barrier-uniform: every wave runs it whatever its columns.
+template <int NTB>
+__device__ __forceinline__ void flat_epilogue_f32(const GemmArgs& args, const FlatTile& t,
+                                                  const f32x16 (&acc)[2][FNTB],
+                                                  unsigned char* stg) {
+    const int N = t.N;
+    const int nl0 = 64 * t.wave;                   // this wave's first column in the tile
+    const int nbase = t.n0 - nl0;                  // the tile's first output column
+    float* out = (float*)args.out;
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+        __syncthreads();                           // the previous block's reads are done
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int c = nl0 + 32 * b + 8 * qq + 4 * t.half;
+                f32x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = acc[b][tb][4 * qq + i];
+                *(f32x4*)(stg + t.l32 * kEpiRow + c * 4) = v;
+            }
+        __syncthreads();
+        // wave w stores rows 4 w .. 4 w + 3 of the block: 2 x 1 KB per row
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int row = 4 * t.wave + rr;
+            const int rl = tb * 32 + row;
+            if (rl >= t.valid) continue;
+            float* orow = out + (size_t)(t.row0 + rl) * N + nbase;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int c = 256 * h + 4 * t.lane;
+                if (nbase + c < N)
+                    *(f32x4*)(orow + c) = *(const f32x4*)(stg + row * kEpiRow + c * 4);
+            }
+        }
+    }
+}
+
+template <int EPI, int AM, int NTB>
+__device__ __forceinline__ void flat_epilogue(const GemmArgs& args, const FlatTile& t,
+                                              const f32x16 (&acc)[2][FNTB]) {
+    const int N = t.N;
+    if (t.n0 >= N) return;
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+        const int rl = tb * 32 + t.l32;
+        if (rl >= t.valid) continue;
+        const size_t r = (size_t)(t.row0 + rl);
+        if constexpr (EPI == EPI_SWIGLU_BF16) {
+            const float L = args.clamp_limit;
+            uint16_t* out = (uint16_t*)args.out;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int n = t.n0 + 8 * qq + 4 * t.half;
+                if (args.out_g) {
+                    // the fp32 pre-activations, before the clamps (saved for
+                    // the backward)
+                    f32x4 gs, us;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        gs[i] = acc[0][tb][4 * qq + i];
+                        us[i] = acc[1][tb][4 * qq + i];
+                    }
+                    *(f32x4*)(args.out_g + r * N + n) = gs;
+                    *(f32x4*)(args.out_u + r * N + n) = us;
+                }
+                uint32_t packed[2];
+#pragma unroll
+                for (int i = 0; i < 4; i += 2) {
+                    uint16_t hb[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        float gv = acc[0][tb][4 * qq + i + u];
+                        float uv = acc[1][tb][4 * qq + i + u];
+                        gv = args.clamp_mode == MOE_CLAMP_SYMMETRIC ? fclamp_sym(gv, L)
+                                                                    : fminf(gv, L);
+                        uv = fclamp_sym(uv, L);
+                        const float silu = gv / (1.0f + __expf(-gv));
+                        hb[u] = f32_to_bf16(silu * uv);
+                    }
+                    packed[i >> 1] = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
+                }
+                uint16_t* dst = AM != FA_ROW ? out + blocked_index(r, n, N) : out + r * N + n;
+                *(u32x2*)dst = u32x2{packed[0], packed[1]};
+            }
+        } else {
+            float* orow = (float*)args.out + r * N;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int n = t.n0 + 32 * b + 8 * qq + 4 * t.half;
+                    f32x4 v;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = acc[b][tb][4 * qq + i];
+                    *(f32x4*)(orow + n) = v;
+                }
+        }
+    }
+}
+
+// Pipeline depths (defaults; the build may override them):
+//   FLAT_R   weight substeps in flight per wave (register ring; 4 or 8)
+//   FLAT_AD  stages the activation loads run ahead of their LDS write (1, 2)
+//   FLAT_OB  activation operand buffers (2: read one substep ahead)
+#ifndef FLAT_R
+#define FLAT_R 4
+#endif
+#ifndef FLAT_AD
+#define FLAT_AD 2
+#endif
+#ifndef FLAT_OB
+#define FLAT_OB 2
+#endif
+
+// K loop and epilogue of one tile for NTB valid 32-row blocks.
+//   stage j: barrier (slot j % 2 holds stage j); load the activations of
+//   stage j + AD into registers; for each substep u = 4 j + q: read its
+//   activation fragments from LDS and multiply (with two operand buffers the
+//   multiply lags the read by one substep, so every LDS read latency hides
+//   behind the other substep's MFMAs); after the MFMAs of substep u, its weight
+//   register slot (u % R) takes the weights of substep u + R.  Finally stage
+//   j + 1's activations (loaded AD - 1 stages earlier) go to slot (j + 1) % 2.
+// The stage loop is unrolled by two, so every ring index is static.
+template <int EPI, int AM, int NTB>
+__device__ __forceinline__ void flat_tile(const GemmArgs& args, const FlatTile& t,
+                                          unsigned char* ring) {
+    constexpr int R = FLAT_R, AD = FLAT_AD, OB = FLAT_OB;
+    static_assert(R == 4 || R == 8, "weight ring of one or two stages");
+    static_assert(AD == 1 || AD == 2, "activation depth");
+    static_assert(OB == 1 || OB == 2, "operand buffers");
+    f32x16 acc[2][FNTB];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int tb = 0; tb < FNTB; ++tb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[b][tb][i] = 0.0f;
+    const int S = t.K / FK;
+    const uint16_t* a = args.a;
+
+    bf16x8 w0[R], w1[R];
+    u32x4 areg[AD][2];
+
+    // weights of global substep u (stage u / 4, substep u % 4), clamped to K
+    auto load_w = [&](int u, bf16x8& d0, bf16x8& d1) {
+        const int j = min(u >> 2, S - 1);
+        const size_t off = (size_t)j * t.wstage + (size_t)(u & 3) * 512;
+        d0 = *(const bf16x8*)(t.wp0 + off);
+        d1 = *(const bf16x8*)(t.wp1 + off);
+    };
+    auto load_a = [&](int j, u32x4 (&d)[2]) {
+        const size_t off = (size_t)min(j, S - 1) * t.a_step;
+        d[0] = *(const u32x4*)(a + t.a_off[0] + off);
+        if (t.a_rows > 1) d[1] = *(const u32x4*)(a + t.a_off[1] + off);
+    };
+    auto store_a = [&](int j, const u32x4 (&d)[2]) {
+        unsigned char* slot = ring + (j & 1) * kSlotBytes;
+        const int c = t.tid & 7;
+        const int r0 = t.tid >> 3;
+        *(u32x4*)(slot + r0 * kRowBytes + ((c ^ fswz(r0)) << 4)) = d[0];
+        if (t.a_rows > 1) {
+            const int r1 = r0 + 64;
+            *(u32x4*)(slot + r1 * kRowBytes + ((c ^ fswz(r1)) << 4)) = d[1];
+        }
+    };
+
+    // prologue: weights of substeps 0 .. R - 1; activations of stages
+    // 0 .. AD - 1 (stage 0 into slot 0)
+#pragma unroll
+    for (int u = 0; u < R; ++u) load_w(u, w0[u], w1[u]);
+    if (t.a_rows > 0) {
+#pragma unroll
+        for (int p = 0; p < AD; ++p) load_a(p, areg[p]);
+        store_a(0, areg[0]);
+    }
+
+    FOps<NTB> o[OB];
+    auto stage = [&](int j, auto par) {
+        constexpr int P = decltype(par)::value;   // j % 2
+        __syncthreads();
+        const unsigned char* slot = ring + P * kSlotBytes;
+        // activation registers: stage j's set was written to LDS at the end
+        // of stage j - 1; it now takes stage j + AD
+        if (t.a_rows > 0) load_a(j + AD, areg[AD == 2 ? P : 0]);
+#pragma unroll
+        for (int q = 0; q < FQ; ++q) {
+            const int u = 4 * j + q;
+            if constexpr (OB == 2) {
+                read_act<NTB>(slot, t, q, o[q & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (q > 0 || j > 0) {
+                    // previous substep u - 1, its weight slot, then refill
+                    const int ps = (P * 4 + q + R - 1) % R;
+                    mfma_step<NTB>(w0[ps], w1[ps], o[(q + 1) & 1], acc);
+                    load_w(u - 1 + R, w0[ps], w1[ps]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                read_act<NTB>(slot, t, q, o[0]);
+                const int cs = (P * 4 + q) % R;
+                mfma_step<NTB>(w0[cs], w1[cs], o[0], acc);
+                load_w(u + R, w0[cs], w1[cs]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (t.a_rows > 0 && j + 1 < S) {
+            if constexpr (AD == 2) {
+                store_a(j + 1, areg[P ^ 1]);
+            } else {
+                store_a(j + 1, areg[0]);
+            }
+        }
+        // the last substep of the K loop (its operands were read at q = 3)
+        if constexpr (OB == 2) {
+            if (j == S - 1) {
+                constexpr int ls = (P * 4 + 3) % R;
+                mfma_step<NTB>(w0[ls], w1[ls], o[1], acc);
+            }
+        }
+    };
+    for (int j = 0; j < S; j += 2) {
+        stage(j, std::integral_constant<int, 0>());
+        if (j + 1 < S) stage(j + 1, std::integral_constant<int, 1>());
+    }
+    if constexpr (EPI == EPI_F32) {
+        flat_epilogue_f32<NTB>(args, t, acc, ring + kRingBytes);
+    } else {
+        flat_epilogue<EPI, AM, NTB>(args, t, acc);
+    }
+}
+
+template <int EPI, int AM, int NT>
+__device__ __forceinline__ void flat_tile_ntb(const GemmArgs& args, const FlatTile& t,
+                                              unsigned char* ring) {
+    if constexpr (NT == 1) {
+        flat_tile<EPI, AM, 1>(args, t, ring);
+    } else {
+        if (t.ntb >= NT) flat_tile<EPI, AM, NT>(args, t, ring);
+        else flat_tile_ntb<EPI, AM, NT - 1>(args, t, ring);
+    }
+}
+
+// Set up and run the tile of item `local` of group g (rows [grp_lo, grp_hi)).
+// A group's rows split evenly over its ceil(n / 128) m-tiles (rounded up to
+// 32 rows), so its m-tiles run at the same pace.
+template <int EPI, int AM>
+__device__ __forceinline__ void flat_item(const GemmArgs& args, FlatTile& t, unsigned char* ring,
+                                          int g, int local, int grp_lo, int grp_hi) {
+    using Pn = FPanel<EPI>;
+    const int n = grp_hi - grp_lo;
+    const int mt = (n + FM - 1) / FM;
+    const int per = ((n + mt - 1) / mt + 31) & ~31;
+    const int n_tile = local / mt, m_tile = local % mt;
+    t.row0 = grp_lo + m_tile * per;
+    t.valid = min(per, grp_hi - t.row0);
+    t.ntb = (t.valid + 31) >> 5;
+    // this wave's weight blocks
+    const int np = (t.N + Pn::P - 1) / Pn::P;
+    const size_t pstride = (size_t)Pn::P * t.K;
+    const size_t ebase = (size_t)g * np * pstride;
+    t.wstage = (size_t)Pn::BPP * 2048;
+    const uint16_t* m0;
+    const uint16_t* m1;
+    int blk0, blk1;
+    if constexpr (EPI == EPI_SWIGLU_BF16) {
+        // features [32 fb, 32 fb + 32) of the gate and the up matrix
+        const int fb = n_tile * (Pn::TN / 32) + t.wave;
+        t.n0 = fb * 32;
+        m0 = args.w1 + ebase;
+        m1 = args.w2 + ebase;
+        blk0 = blk1 = fb;
+    } else {
+        // output rows [32 wb, 32 wb + 64)
+        const int wb = n_tile * (Pn::TN / 32) + 2 * t.wave;
+        t.n0 = wb * 32;
+        m0 = m1 = args.w1 + ebase;
+        blk0 = wb;
+        blk1 = wb + 1;
+    }
+    // (blocks past the matrix end read the last panel; never stored)
+    const int p0 = min(blk0 / Pn::BPP, np - 1), p1 = min(blk1 / Pn::BPP, np - 1);
+    t.wp0 = m0 + (size_t)p0 * pstride + (size_t)(blk0 % Pn::BPP) * 2048 + t.lane * 8;
+    t.wp1 = m1 + (size_t)p1 * pstride + (size_t)(blk1 % Pn::BPP) * 2048 + t.lane * 8;
+    // activation staging: thread tid copies 16 B chunk (tid % 8) of rows
+    // tid / 8 and tid / 8 + 64 (rows past the tile read its last valid row);
+    // a wave stages its second row group only if the tile reaches it
+    const int c = t.tid & 7;
+    const int r0 = t.tid >> 3;
+    const int rows_needed = t.ntb * 32;
+    t.a_rows = (r0 - (t.lane >> 3) < rows_needed) + (r0 - (t.lane >> 3) + 64 < rows_needed);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const size_t grow = (size_t)(t.row0 + min(r0 + 64 * i, t.valid - 1));
+        size_t e;
+        if (AM == FA_BLK) e = blocked_index(grow, c * 8, t.K);
+        else if (AM == FA_GATHER) e = (size_t)args.gather[grow] * t.K + c * 8;
+        else e = grow * t.K + c * 8;
+        t.a_off[i] = e;
+    }
+    // per 64-wide stage: two 32-column blocks (blocked) or 64 elements
+    t.a_step = AM == FA_BLK ? 1024 : FK;
+    flat_tile_ntb<EPI, AM, FNTB>(args, t, ring);
+}
+
+template <int EPI, int AM>
+__global__ __launch_bounds__(kFThreads) void grouped_gemm_flat_kernel(GemmArgs args) {
+    using Pn = FPanel<EPI>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int scan_sh[8];
+    __shared__ int next_item;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = args.G, rows = args.rows, N = args.N;
+    const int* offs = args.offsets;
+    int* item_prefix = (int*)(smem + kLdsFixed);   // [G + 1]
+    const int NT = (N + Pn::TN - 1) / Pn::TN;
+
+    auto group_rows = [&](int g, int& lo, int& hi) {
+        lo = 0;
+        hi = rows;
+        if (offs) {
+            lo = min(max(offs[g], 0), rows);
+            hi = max(lo, min(max(offs[g + 1], 0), rows));
+        }
+    };
+
+    // per-group item counts -> exclusive prefix in LDS
+    {
+        const int per = (G + kFThreads - 1) / kFThreads;
+        const int g0 = tid * per;
+        int local = 0;
+        for (int g = g0; g < g0 + per && g < G; ++g) {
+            int lo, hi;
+            group_rows(g, lo, hi);
+            const int items = NT * ((hi - lo + FM - 1) / FM);
+            item_prefix[g] = items;
+            local += items;
+        }
+        int x = local;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) scan_sh[wave] = x;
+        __syncthreads();
+        int wbase = 0, total = 0;
+        for (int w = 0; w < 8; ++w) {
+            if (w < wave) wbase += scan_sh[w];
+            total += scan_sh[w];
+        }
+        int run = wbase + x - local;
+        for (int g = g0; g < g0 + per && g < G; ++g) {
+            const int v = item_prefix[g];
+            item_prefix[g] = run;
+            run += v;
+        }
+        if (tid == 0) item_prefix[G] = total;
+        __syncthreads();
+    }
+
+    const int xcd = blockIdx.x & 7;
+    const int per_xcd = gridDim.x >> 3;
+    const long long Q = item_prefix[G];
+    const int item_lo = (int)(Q * xcd / 8), item_hi = (int)(Q * (xcd + 1) / 8);
+
+    FlatTile t;
+    t.tid = tid;
+    t.lane = lane;
+    t.wave = wave;
+    t.half = lane >> 5;
+    t.l32 = lane & 31;
+    t.K = args.K;
+    t.N = N;
+    unsigned* ctr = args.sched ? args.sched + xcd * 32 : nullptr;
+
+    int q;
+    if (ctr) {
+        if (tid == 0) next_item = item_lo + (int)atomicAdd(ctr, 1u);
+        __syncthreads();
+        q = next_item;
+    } else {
+        q = item_lo + (blockIdx.x >> 3);
+    }
+    while (q < item_hi) {
+        // claim the next item now; its id is published after this tile
+        unsigned claimed = 0;
+        if (ctr && tid == 0) claimed = atomicAdd(ctr, 1u);
+        int g = 0;
+        {
+            int lo = 0, hi = G;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (item_prefix[mid] <= q) lo = mid; else hi = mid - 1;
+            }
+            g = lo;
+        }
+        int grp_lo, grp_hi;
+        group_rows(g, grp_lo, grp_hi);
+        flat_item<EPI, AM>(args, t, smem, g, q - item_prefix[g], grp_lo, grp_hi);
+        // every wave is past its last LDS read of this tile before the next
+        // tile's prologue writes slot 0, and the claimed id is visible
+        __syncthreads();
+        if (ctr && tid == 0) next_item = item_lo + (int)claimed;
+        __syncthreads();
+        q = ctr ? next_item : q + per_xcd;
+    }
+}
+
+template <int EPI, int AM>
+hipError_t launch_flat(const GemmArgs& g, hipStream_t stream) {
+    static DeviceSetup setup;
+    long long grid = 0, static_lds = 0;
+    const hipError_t err = device_setup(setup, grid, static_lds, [](int, long long& gr,
+                                                                    long long& st) {
+        hipFuncAttributes fa;
+        hipError_t e = hipFuncGetAttributes(&fa, (const void*)grouped_gemm_flat_kernel<EPI, AM>);
+        if (e != hipSuccess) return e;
+        if (fa.sharedSizeBytes > (size_t)kFStaticLds) return hipErrorInvalidValue;
+        e = hipFuncSetAttribute((const void*)grouped_gemm_flat_kernel<EPI, AM>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kFLdsLimit - (int)fa.sharedSizeBytes);
+        if (e != hipSuccess) return e;
+        st = (long long)fa.sharedSizeBytes;
+        gr = (device_cu_count() + 7) & ~7;
+        return hipSuccess;
+    });
+    if (err != hipSuccess) return err;
+    const size_t lds = kLdsFixed + (size_t)(g.G + 1) * sizeof(int);
+    if (lds + (size_t)static_lds > (size_t)kFLdsLimit) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((grouped_gemm_flat_kernel<EPI, AM>), dim3((unsigned)grid), dim3(kFThreads),
+                       lds, stream, g);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int grouped_gemm_flat_max_groups() {
+    return (kFLdsLimit - kFStaticLds - kLdsFixed) / (int)sizeof(int) - 1;
+}
+
+hipError_t launch_grouped_gemm_flat(int epilogue, const GemmArgs& g, hipStream_t stream) {
+    if (g.K % FK != 0 || g.G < 1 || g.wfp8) return hipErrorInvalidValue;
+    if ((g.out_g != nullptr) != (g.out_u != nullptr)) return hipErrorInvalidValue;
+    if (g.out_g && epilogue != EPI_SWIGLU_BF16) return hipErrorInvalidValue;
+    if (g.gather && g.a_blocked) return hipErrorInvalidValue;
+    const int am = g.gather ? FA_GATHER : g.a_blocked ? FA_BLK : FA_ROW;
+    switch (epilogue) {
+        case EPI_SWIGLU_BF16:
+            // h is blocked exactly when the activations are not plain row-major
+            if (g.out_blocked != (am != FA_ROW)) return hipErrorInvalidValue;
+            if (am == FA_GATHER) return launch_flat<EPI_SWIGLU_BF16, FA_GATHER>(g, stream);
+            if (am == FA_BLK) return launch_flat<EPI_SWIGLU_BF16, FA_BLK>(g, stream);
+            return launch_flat<EPI_SWIGLU_BF16, FA_ROW>(g, stream);
+        case EPI_F32:
+            if (am == FA_GATHER) return launch_flat<EPI_F32, FA_GATHER>(g, stream);
+            if (am == FA_BLK) return launch_flat<EPI_F32, FA_BLK>(g, stream);
+            return launch_flat<EPI_F32, FA_ROW>(g, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace moe

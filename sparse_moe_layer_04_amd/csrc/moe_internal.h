@@ -92,6 +92,8 @@ struct GemmArgs {
                               // 2: MXFP4 codes (moe_pack_weights_fp4); block scales in s1 / s2
     const uint8_t* s1;        // MXFP8 block scale bytes of w1
     const uint8_t* s2;        // MXFP8 block scale bytes of w2 (SWIGLU)
+    float* out_g;             // flat kernel, SWIGLU: [rows, N] fp32 gate pre-activations
+    float* out_u;             // ... and up pre-activations (both or neither; NULL: not saved)
 };
 // per-launch scheduling counters of the LDS-staged expert GEMM
 constexpr int kSchedWords = 8 * 32;
@@ -121,6 +123,11 @@ bool router_packed_preferred(int T, int E);
 // G <= grouped_gemm_lds_max_groups().
 hipError_t launch_grouped_gemm_lds(int epilogue, const GemmArgs& g, hipStream_t stream);
 int grouped_gemm_lds_max_groups();
+// Expert GEMMs on packed bf16 weights, weights streamed into registers and
+// only the activation rows staged in LDS (128 x 512 tiles).  Takes
+// G <= grouped_gemm_flat_max_groups().
+hipError_t launch_grouped_gemm_flat(int epilogue, const GemmArgs& g, hipStream_t stream);
+int grouped_gemm_flat_max_groups();
 size_t packed_weight_elems(int G, int N, int K, int P);
 hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int G, int N, int K, int P,
                                hipStream_t stream);
@@ -152,6 +159,28 @@ hipError_t launch_route_backward(const float* logits, const int32_t* ids, const 
                                  int T, int E, int k, float scale, float* dl, uint32_t* flags,
                                  hipStream_t stream);
 
+// dw[g] = dy[rows of g]^T a[rows of g] (fp32), every group's dw written;
+// row r of dy at dy + r * ld_dy, of a at a + r * ld_a
+hipError_t launch_grouped_wgrad(const uint16_t* dy, const uint16_t* a, const int32_t* offsets,
+                                int G, int rows, int M, int K, float* dw, hipStream_t stream,
+                                int ld_dy = 0, int ld_a = 0);
+// the clamped-SwiGLU backward for rows x F pre-activations with bf16 outputs
+// side by side: dgu[r, f] = dG, dgu[r, F + f] = dU (row stride 2F); the same
+// fp32 arithmetic as launch_swiglu_backward, rounded once to bf16
+hipError_t launch_swiglu_backward_bf16(const float* gate, const float* up, const float* dh,
+                                       long long rows, int F, float clamp_limit, int clamp_mode,
+                                       uint16_t* dgu, hipStream_t stream);
+// dst[i] = bf16(src[i]) (nearest even), n values
+hipError_t launch_cast_bf16(const float* src, long long n, uint16_t* dst, hipStream_t stream);
+// router projection gradients from the logits' gradient dl [T, E] (fp32),
+// using that dl is zero off each token's selected experts:
+//   dx[t, :] += sum_j dl[t, ids_j] w_g[ids_j, :]          (accumulated into dx)
+//   dwg[e, :] = sum_{rows r of expert e} dl[src_r, e] x[src_r, :]
+hipError_t launch_router_backward(const float* dl, const int32_t* ids, const int32_t* offsets,
+                                  const int32_t* src, const uint16_t* x, const uint16_t* wg,
+                                  int T, int d, int E, int k, float* dx, float* dwg,
+                                  hipStream_t stream);
+
 size_t permute_workspace_bytes(int T, int k, int E);
 // moe_permute's argument checks other than the workspace (MOE_OK or the
 // error code)
@@ -165,6 +194,7 @@ hipError_t launch_permute(const int32_t* ids, const uint16_t* x, int T, int d, i
 // (x_perm may be NULL: dest/src only; the rank kernel also clears
 // zero[0, nzero): the expert GEMMs' counters)
 
+// (w may be NULL: every weight 1, the dispatch gather's backward)
 hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* w,
                           const float* y_shared, int T, int d, int k, int rows, int out_dtype,
                           void* y, hipStream_t stream);

@@ -1,0 +1,196 @@
+// Grouped weight gradient ("HyperParallel accelerates DeepSeek-V4.1 ...",
+// section 2.3, MegaMoE: the expert matmuls, whose weights a training step
+// updates; section 03: the training run):
+//   dw[g, m, k] = sum_{offsets[g] <= r < offsets[g+1]} dy[r, m] * a[r, k]
+// for the forward out = a W_g^T per group.  dy [rows, M] and a [rows, K] bf16
+// row-major, fp32 accumulation on the matrix cores, dw [G, M, K] fp32 (a group
+// without rows gets zeros).  One kernel gives the expert down projection's
+// dW_down = dY^T H, the gate/up matrices' dW_gate = dG^T X and dW_up = dU^T X,
+// the shared expert's (one group) and the router projection's dW_g =
+// dlogits^T x (one group of T rows).
+//
+// The contraction runs over each group's rows, the slow index of both inputs.
+// A workgroup (4 waves) computes a 128 (m) x 128 (k) tile of one group's dw,
+// walking the group's rows in chunks of 32:
+//   - a chunk of dy (32 rows x 128 m) and of a (32 rows x 128 k) is copied
+//     row-major into LDS (16-byte coalesced loads; rows past the group end are
+//     zeros), two chunk slots, one barrier per chunk;
+//   - the MFMA operands need 8 consecutive rows of one column per lane
+//     (v_mfma_f32_32x32x16_bf16: operand A = a, so each lane's accumulator
+//     holds 4 consecutive k of one m and the stores are 16 bytes), gathered
+//     with 16-bit LDS reads; LDS rows are padded to 272 bytes, so the two
+//     half-waves (rows 8 apart) read distinct banks;
+//   - wave (wm, wk) owns 64 m x 64 k (2 x 2 accumulators).
+// Grid: one workgroup per (group, m-tile, k-tile), mapped so that each XCD
+// (workgroup id mod 8) takes a contiguous range of tiles: the tiles of one
+// group share that XCD's L2 for their dy and a rows.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int WT = 128;                 // tile: m and k extent
+constexpr int WR = 32;                  // rows per chunk
+constexpr int kWThreads = 256;
+constexpr int kWRow = WT * 2 + 16;      // LDS bytes per staged row (padded)
+constexpr int kWOperand = WR * kWRow;   // one operand chunk
+constexpr int kWSlot = 2 * kWOperand;   // dy + a chunk
+
+struct WgradArgs {
+    const uint16_t* dy;
+    const uint16_t* a;
+    const int32_t* offsets;  // [G + 1] or NULL (one group [0, rows))
+    int G, rows, M, K;
+    int ld_dy, ld_a;         // row strides (elements) of dy and a
+    int mt, kt;              // tiles per group along m and k
+    long long tiles;         // G * mt * kt
+    float* dw;
+};
+
+// 8 rows (row0 .. row0 + 7) of column `col` of a staged operand chunk as one
+// MFMA operand (bf16x8)
+__device__ __forceinline__ bf16x8 gather8(const unsigned char* chunk, int row0, int col) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = *(const uint16_t*)(chunk + (row0 + 2 * i) * kWRow + col * 2);
+        const uint32_t hi = *(const uint16_t*)(chunk + (row0 + 2 * i + 1) * kWRow + col * 2);
+        r[i] = lo | (hi << 16);
+    }
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+__global__ __launch_bounds__(kWThreads) void grouped_wgrad_kernel(WgradArgs args) {
+    __shared__ __align__(16) unsigned char lds[2 * kWSlot];
+    // XCD-contiguous tile order: workgroup b runs on XCD b % 8
+    const long long per = (long long)gridDim.x / 8;
+    const long long tile = (long long)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (tile >= args.tiles) return;
+    const int kt_i = (int)(tile % args.kt);
+    const int mt_i = (int)((tile / args.kt) % args.mt);
+    const int g = (int)(tile / ((long long)args.kt * args.mt));
+    const int M = args.M, K = args.K;
+    const int m0 = mt_i * WT, k0 = kt_i * WT;
+    int lo = 0, hi = args.rows;
+    if (args.offsets) {
+        lo = min(max(args.offsets[g], 0), args.rows);
+        hi = max(lo, min(max(args.offsets[g + 1], 0), args.rows));
+    }
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wk = wave & 1;
+    const int half = lane >> 5, l32 = lane & 31;
+
+    f32x16 acc[2][2];   // [k block][m block]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // staging: thread tid copies 16-byte chunk (tid % 16) of chunk rows
+    // tid / 16 and tid / 16 + 16 of both operands (columns past M / K and rows
+    // past the group end stage zeros)
+    const int sc = tid & 15, sr = tid >> 4;
+    const int cm = m0 + 8 * sc, ck = k0 + 8 * sc;
+    const bool m_in = cm < M, k_in = ck < K;
+    u32x4 st[2][2];     // [operand: dy, a][row group]
+    auto load_chunk = [&](int r0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = r0 + sr + 16 * i;
+            const bool in = r < hi;
+            u32x4 z = {0u, 0u, 0u, 0u};
+            st[0][i] = (in && m_in) ? *(const u32x4*)(args.dy + (size_t)r * args.ld_dy + cm) : z;
+            st[1][i] = (in && k_in) ? *(const u32x4*)(args.a + (size_t)r * args.ld_a + ck) : z;
+        }
+    };
+    auto store_chunk = [&](int slot) {
+        unsigned char* base = lds + slot * kWSlot;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            *(u32x4*)(base + (sr + 16 * i) * kWRow + sc * 16) = st[0][i];
+            *(u32x4*)(base + kWOperand + (sr + 16 * i) * kWRow + sc * 16) = st[1][i];
+        }
+    };
+
+    const int nchunks = (hi - lo + WR - 1) / WR;
+    if (nchunks > 0) {
+        load_chunk(lo);
+        store_chunk(0);
+    }
+    for (int c = 0; c < nchunks; ++c) {
+        __syncthreads();
+        if (c + 1 < nchunks) load_chunk(lo + (c + 1) * WR);
+        const unsigned char* dyc = lds + (c & 1) * kWSlot;
+        const unsigned char* ac = dyc + kWOperand;
+#pragma unroll
+        for (int s = 0; s < WR / 16; ++s) {
+            const int row0 = 16 * s + 8 * half;
+            bf16x8 fa[2], fd[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                fa[i] = gather8(ac, row0, 64 * wk + 32 * i + l32);
+                fd[i] = gather8(dyc, row0, 64 * wm + 32 * i + l32);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fd[j], acc[i][j],
+                                                                        0, 0, 0);
+        }
+        if (c + 1 < nchunks) store_chunk((c + 1) & 1);
+    }
+
+    // accumulator element e of lane l: k = 8 (e / 4) + 4 half + e % 4 within
+    // the k block, m = l32 within the m block
+    float* out = args.dw + (size_t)g * M * K;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = m0 + 64 * wm + 32 * j + l32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int k = k0 + 64 * wk + 32 * i + 8 * qq + 4 * half;
+                if (k >= K) continue;
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * qq + e];
+                *(f32x4*)(out + (size_t)m * K + k) = v;
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_grouped_wgrad(const uint16_t* dy, const uint16_t* a, const int32_t* offsets,
+                                int G, int rows, int M, int K, float* dw, hipStream_t stream,
+                                int ld_dy, int ld_a) {
+    WgradArgs args;
+    args.ld_dy = ld_dy > 0 ? ld_dy : M;
+    args.ld_a = ld_a > 0 ? ld_a : K;
+    if (args.ld_dy < M || args.ld_a < K || args.ld_dy % 8 || args.ld_a % 8)
+        return hipErrorInvalidValue;
+    args.dy = dy;
+    args.a = a;
+    args.offsets = offsets;
+    args.G = G;
+    args.rows = rows;
+    args.M = M;
+    args.K = K;
+    args.mt = (M + WT - 1) / WT;
+    args.kt = (K + WT - 1) / WT;
+    args.tiles = (long long)G * args.mt * args.kt;
+    args.dw = dw;
+    const long long per = (args.tiles + 7) / 8;
+    if (8 * per > 0x7fffffffll) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(grouped_wgrad_kernel, dim3((unsigned)(8 * per)), dim3(kWThreads), 0, stream,
+                       args);
+    return hipGetLastError();
+}
+
+}  // namespace moe

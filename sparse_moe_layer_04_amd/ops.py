@@ -81,6 +81,7 @@ def lib():
     L.moe_combine_backward.argtypes = [P, P, P, P, I, I, I, I, P, P, P]
     L.moe_swiglu_backward.argtypes = [P, P, P, ctypes.c_int64, F, I, P, P, P]
     L.moe_grouped_gemm_packed.argtypes = [P, P, I, I, I, I, P, P, P]
+    L.moe_grouped_wgrad.argtypes = [P, P, P, I, I, I, I, P, P]
     L.moe_permute_workspace_size.argtypes = [I, I, I]
     L.moe_permute_workspace_size.restype = S
     L.moe_permute.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, P, S, P]
@@ -379,6 +380,25 @@ def grouped_gemm_packed(a, offsets, w_packed, G, N, out=None):
     _need(out, torch.float32, "out", shape=(rows, N))
     _check(lib().moe_grouped_gemm_packed(_ptr(a), _ptr(offsets), G, rows, K, N, _ptr(w_packed),
                                          _ptr(out), _stream()), "moe_grouped_gemm_packed")
+    return out
+
+
+def grouped_wgrad(dy, a, offsets, G=None, out=None):
+    """dw[g] = dy[rows of g]^T a[rows of g] (fp32 [G, M, K]) for bf16 dy
+    [rows, M] and a [rows, K]: the weight gradient of a grouped matmul.
+    offsets [G+1] int32 (device) or None for one group of all rows."""
+    _need(dy, torch.bfloat16, "dy", 2)
+    rows, M = dy.shape
+    _need(a, torch.bfloat16, "a", shape=(rows, None))
+    K = a.shape[1]
+    if offsets is None:
+        G = 1
+    else:
+        _need(offsets, torch.int32, "offsets", 1)
+        G = offsets.numel() - 1
+    out = _out(out, torch.float32, "out", (G, M, K), dy.device)
+    _check(lib().moe_grouped_wgrad(_ptr(dy), _ptr(a), _ptr(offsets), G, rows, M, K, _ptr(out),
+                                   _stream()), "moe_grouped_wgrad")
     return out
 
 

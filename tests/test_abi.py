@@ -275,3 +275,18 @@ def test_permute_noalloc_validation(L):
     assert ops.permute_workspace_size(T, k, E) > 8 << 20
     assert pn(T=T, k=k, E=E) == -7
     assert "scratch" in L.moe_status_string(-7).decode()
+
+
+def test_grouped_wgrad_validation(L):
+    def wg(G=2, rows=64, M=64, K=64, dy=FAKE, a=FAKE, offs=FAKE, dw=FAKE):
+        return L.moe_grouped_wgrad(dy, a, offs, G, rows, M, K, dw, None)
+    assert wg(G=0) == ERR_SHAPE
+    assert wg(rows=-1) == ERR_SHAPE
+    assert wg(M=4) == ERR_SHAPE
+    assert wg(M=68) == ERR_UNSUPPORTED
+    assert wg(K=100) == ERR_UNSUPPORTED
+    assert wg(dw=None) == ERR_NULL
+    assert wg(dy=None) == ERR_NULL
+    assert wg(offs=None) == ERR_NULL                 # several groups need offsets
+    assert wg(a=FAKE + 8) == ERR_ALIGN
+    assert wg(G=1 << 20, M=4096, K=4096) == ERR_SHAPE
