@@ -299,7 +299,7 @@ def _t(w):
 
 def layer_backward(x, logits, k, scale, w_g, w_gate, w_up, w_down, s_gate, s_up, s_down, dy,
                    clamp_limit=10.0, clamp_mode=0, bias=None, modality=None, input_ids=None,
-                   tid2eid=None, mode=MODE_TOPK):
+                   tid2eid=None, mode=MODE_TOPK, weight_grads=True):
     """Gradients of the whole layer for an output gradient dy[T,d] (fp32),
     chaining the pinned backward pieces in the reverse order of the forward.
     The forward's values come from `forward` (routes from the given logits).
@@ -308,7 +308,9 @@ def layer_backward(x, logits, k, scale, w_g, w_gate, w_up, w_down, s_gate, s_up,
     gradients, the routing-weight gradient) are passed as fp32, so the chain
     follows the precision at which each product is taken.  Returns a dict:
     dx, dw_g, dw_gate, dw_up, dw_down, ds_gate, ds_up, ds_down (float64) and
-    dx_routed, dx_shared, dx_router (the three parts of dx)."""
+    dx_routed, dx_shared, dx_router (the three parts of dx).  With
+    weight_grads=False the expert weight gradients are skipped (each token's
+    dx depends only on that token, so dx can be checked on a token subset)."""
     x = _bf16(x)
     T, d = x.shape
     f = forward(x, logits, k, scale, w_gate, w_up, w_down, s_gate, s_up, s_down, clamp_limit,
@@ -321,15 +323,17 @@ def layer_backward(x, logits, k, scale, w_g, w_gate, w_up, w_down, s_gate, s_up,
     dyp, dtw = combine_backward(dy, f["y_perm"], dest, f["w"])
     dyp16 = round_bf16(dyp)
     # down projection y_perm = h W_down^T
-    out["dw_down"] = grouped_wgrad(dyp16, h, offs)
+    if weight_grads:
+        out["dw_down"] = grouped_wgrad(dyp16, h, offs)
     dh = grouped_gemm(dyp16, offs, _t(w_down))
     # clamped SwiGLU h = silu(cg(G)) cu(U), G = x_perm W_gate^T, U = x_perm W_up^T
     G = grouped_gemm(xp, offs, w_gate)
     U = grouped_gemm(xp, offs, w_up)
     dG, dU = swiglu_backward(G, U, dh, clamp_limit, clamp_mode)
     dG16, dU16 = round_bf16(dG), round_bf16(dU)
-    out["dw_gate"] = grouped_wgrad(dG16, xp, offs)
-    out["dw_up"] = grouped_wgrad(dU16, xp, offs)
+    if weight_grads:
+        out["dw_gate"] = grouped_wgrad(dG16, xp, offs)
+        out["dw_up"] = grouped_wgrad(dU16, xp, offs)
     dxp = grouped_gemm(np.concatenate([dG16, dU16], axis=1), offs,
                        _t(np.concatenate([w_gate, w_up], axis=1)))
     # dispatch: x_perm[row] = x[src[row]]; its backward sums each token's rows
@@ -337,19 +341,25 @@ def layer_backward(x, logits, k, scale, w_g, w_gate, w_up, w_down, s_gate, s_up,
     # routing weights -> logits -> router projection
     dl, _ = route_backward(logits, f["ids"], dtw, scale)
     out["dx_router"], out["dw_g"] = router_backward(dl, x, w_g)
-    # shared expert on x
+    # shared expert on x (none: no shared gradients, no dx part)
+    if s_gate is None:
+        out["dx_shared"] = np.zeros((T, d), np.float64)
+        out["dx"] = add(out["dx_routed"], out["dx_router"])
+        return out
     sg, su, sd = _bf16(s_gate), _bf16(s_up), _bf16(s_down)
     one = np.array([0, T], np.int32)
     hs, _ = expert_ffn(x, one, sg[None], su[None], sd[None], clamp_limit, clamp_mode)
     dy16 = round_bf16(dy)
-    out["ds_down"] = grouped_wgrad(dy16, hs, one)[0]
+    if weight_grads:
+        out["ds_down"] = grouped_wgrad(dy16, hs, one)[0]
     dhs = grouped_gemm(dy16, one, _t(sd[None]))
     Gs = grouped_gemm(x, one, sg[None])
     Us = grouped_gemm(x, one, su[None])
     dGs, dUs = swiglu_backward(Gs, Us, dhs, clamp_limit, clamp_mode)
     dGs16, dUs16 = round_bf16(dGs), round_bf16(dUs)
-    out["ds_gate"] = grouped_wgrad(dGs16, x, one)[0]
-    out["ds_up"] = grouped_wgrad(dUs16, x, one)[0]
+    if weight_grads:
+        out["ds_gate"] = grouped_wgrad(dGs16, x, one)[0]
+        out["ds_up"] = grouped_wgrad(dUs16, x, one)[0]
     out["dx_shared"] = grouped_gemm(np.concatenate([dGs16, dUs16], axis=1), one,
                                     _t(np.concatenate([sg, su], axis=0)[None]))
     out["dx"] = add(add(out["dx_routed"], out["dx_shared"]), out["dx_router"])
