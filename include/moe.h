@@ -447,6 +447,68 @@ int moe_forward_timed(const moe_cfg* cfg, const moe_weights* w, const uint16_t* 
                       float* logits_out, int32_t* ids_out, float* w_out, uint32_t* d_flags,
                       void* ws, size_t ws_bytes, void* stream, void* const* events);
 
+/* ------------------------------------------------------------------------
+ * Whole layer backward [HP 2.3: MegaGate's fused backward chain of the gate's
+ * normalisation gradients, MegaMoE's expert matmuls; HP 03: the training run
+ * whose step this is].  For an output gradient dy of moe_forward's output y,
+ * the gradients of y with respect to x and every weight.  The forward's
+ * intermediates are recomputed from x (router logits, routes, dispatch,
+ * expert pre-activations, h, expert outputs); then, in reverse order:
+ *   combine:      dy_perm[dest[t,j]] = w[t,j] dy[t], d_w[t,j] = <dy[t], y_perm[dest]>
+ *   down:         dW_down[e] = dy_perm_e^T h_e,  dh = dy_perm W_down
+ *   SwiGLU:       dG, dU from dh through the clamps (moe_swiglu_backward)
+ *   gate / up:    dW_gate[e] = dG_e^T x_e, dW_up[e] = dU_e^T x_e,
+ *                 dx_perm = dG W_gate + dU W_up
+ *   dispatch:     dx[t] = sum_j dx_perm[dest[t,j]]
+ *   routing:      d_logits from d_w (moe_route_backward)
+ *   router:       dx[t] += d_logits[t] W_g, dW_g = d_logits^T x
+ *   shared:       the same FFN chain on x with dy (dWs_*, dx += its input
+ *                 gradient).
+ * Gradients enter the matrix products as bf16 (round to nearest even), as
+ * the activations do; every product accumulates in fp32; the outputs are
+ * fp32.  The ranking bias and the logit offset get no gradient (the bias
+ * only ranks; the offset is a fixed input), nor does the hash table.
+ *   cfg, w: as moe_forward, with w->packed == 1 (bf16 packed weights); x,
+ *   input_ids, modality: the forward's inputs; dy [T,d] fp32.
+ *   bw: the weights in the layouts of the input-gradient products, each
+ *   written once per weight update by moe_pack_weights with panel_rows 256:
+ *     w_g        [E,d] bf16 router weights, plain row-major;
+ *     w_down_t   W_down^T, [E,F,d];
+ *     w_gu_t     [W_gate; W_up]^T per expert, [E,d,2F] (column o of
+ *                expert e: W_gate[e][:,o] then W_up[e][:,o]);
+ *     s_down_t   Ws_down^T [F_shared,d]; s_gu_t [Ws_gate; Ws_up]^T [d,2F_shared]
+ *                (NULL when F_shared = 0).
+ *   g: outputs, all fp32, every entry written: dx [T,d], dw_g [E,d], dw_gate
+ *   and dw_up [E,F,d], dw_down [E,d,F], ds_gate and ds_up [F_shared,d],
+ *   ds_down [d,F_shared] (NULL when F_shared = 0).
+ *   ws: moe_backward_workspace_size(cfg) bytes, 256-byte aligned.  With T = 0
+ *   nothing is written.  d multiple of 8; E <= 1024.
+ */
+typedef struct moe_bwd_weights {
+    const uint16_t* w_g;
+    const uint16_t* w_down_t;
+    const uint16_t* w_gu_t;
+    const uint16_t* s_down_t;
+    const uint16_t* s_gu_t;
+} moe_bwd_weights;
+
+typedef struct moe_grads {
+    float* dx;
+    float* dw_g;
+    float* dw_gate;
+    float* dw_up;
+    float* dw_down;
+    float* ds_gate;
+    float* ds_up;
+    float* ds_down;
+} moe_grads;
+
+size_t moe_backward_workspace_size(const moe_cfg* cfg);
+int moe_backward(const moe_cfg* cfg, const moe_weights* w, const moe_bwd_weights* bw,
+                 const uint16_t* x, const int32_t* input_ids, const uint8_t* modality,
+                 const float* dy, const moe_grads* g, uint32_t* d_flags, void* ws,
+                 size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

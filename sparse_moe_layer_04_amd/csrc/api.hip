@@ -120,6 +120,102 @@ FwdWs forward_layout(const moe_cfg* c, char* base) {
     return w;
 }
 
+// moe_backward workspace layout (N = T k routed rows)
+struct BwdWs {
+    float* logits;      // [T, E]
+    int32_t* ids;       // [T, k]
+    float* w;           // [T, k]
+    float* dtw;         // [T, k] routing-weight gradient
+    float* dl;          // [T, E] logit gradient
+    int32_t* counts;    // [E]
+    int32_t* offsets;   // [E + 1]
+    int32_t* dest;      // [N]
+    int32_t* src;       // [N]
+    uint16_t* x_perm;   // [N, d] bf16
+    float* g;           // [N, F] gate pre-activations
+    float* u;           // [N, F] up pre-activations
+    uint16_t* h;        // [N, F] bf16
+    float* y_perm;      // [N, d]
+    float* dyp;         // [N, d] fp32 expert-output gradient (later: dx_perm)
+    uint16_t* dyp16;    // [N, d] bf16
+    float* dh;          // [N, F]
+    uint16_t* dgu;      // [N, 2F] bf16
+    float* gs;          // [T, Fs]
+    float* us;          // [T, Fs]
+    uint16_t* hs;       // [T, Fs] bf16
+    uint16_t* dy16;     // [T, d] bf16
+    float* dhs;         // [T, Fs]
+    uint16_t* dgus;     // [T, 2Fs] bf16
+    float* dxs;         // [T, d] shared expert's input gradient
+    void* perm;
+    uint32_t* sched;    // 8 x kSchedWords expert GEMM counters
+    size_t total;
+};
+
+BwdWs backward_layout(const moe_cfg* c, char* base) {
+    const size_t T = (size_t)c->T, N = (size_t)c->T * c->k, d = c->d, F = c->F;
+    const size_t Fs = c->F_shared > 0 ? c->F_shared : 0;
+    size_t off = 0;
+    BwdWs w;
+    auto take = [&](size_t bytes) {
+        char* p = base ? base + off : nullptr;
+        off += align256(bytes);
+        return (void*)p;
+    };
+    w.logits = (float*)take(T * c->E * 4);
+    w.ids = (int32_t*)take(N * 4);
+    w.w = (float*)take(N * 4);
+    w.dtw = (float*)take(N * 4);
+    w.dl = (float*)take(T * c->E * 4);
+    w.counts = (int32_t*)take((size_t)c->E * 4);
+    w.offsets = (int32_t*)take((size_t)(c->E + 1) * 4);
+    w.dest = (int32_t*)take(N * 4);
+    w.src = (int32_t*)take(N * 4);
+    w.x_perm = (uint16_t*)take(N * d * 2);
+    w.g = (float*)take(N * F * 4);
+    w.u = (float*)take(N * F * 4);
+    w.h = (uint16_t*)take(N * F * 2);
+    w.y_perm = (float*)take(N * d * 4);
+    w.dyp = (float*)take(N * d * 4);
+    w.dyp16 = (uint16_t*)take(N * d * 2);
+    w.dh = (float*)take(N * F * 4);
+    w.dgu = (uint16_t*)take(N * 2 * F * 2);
+    w.gs = (float*)take(T * Fs * 4);
+    w.us = (float*)take(T * Fs * 4);
+    w.hs = (uint16_t*)take(T * Fs * 2);
+    w.dy16 = (uint16_t*)take(T * d * 2);
+    w.dhs = (float*)take(T * Fs * 4);
+    w.dgus = (uint16_t*)take(T * 2 * Fs * 2);
+    w.dxs = (float*)take(Fs ? T * d * 4 : 0);
+    w.perm = take(permute_workspace_bytes(c->T, c->k, c->E));
+    w.sched = (uint32_t*)take(8 * kSchedWords * sizeof(uint32_t));
+    w.total = off;
+    return w;
+}
+
+// one expert GEMM on the flat kernel with row-major activations
+hipError_t flat_gemm(int epi, const uint16_t* a, const int32_t* offsets, int G, int rows, int K,
+                     int N, const uint16_t* w1, const uint16_t* w2, float L, int cmode, void* out,
+                     float* out_g, float* out_u, uint32_t* sched, hipStream_t s) {
+    GemmArgs g{};
+    g.a = a;
+    g.offsets = offsets;
+    g.G = G;
+    g.rows = rows;
+    g.K = K;
+    g.N = N;
+    g.w1 = w1;
+    g.w2 = w2;
+    g.packed = 1;
+    g.clamp_limit = L;
+    g.clamp_mode = cmode;
+    g.out = out;
+    g.out_g = out_g;
+    g.out_u = out_u;
+    g.sched = sched;
+    return launch_grouped_gemm_flat(epi, g, s);
+}
+
 }  // namespace
 
 int permute_arg_checks(const int32_t* topk_ids, const uint16_t* x, int T, int d, int E, int k,
@@ -638,6 +734,146 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
                             c->out_dtype, y, s)) != hipSuccess)
         return MOE_ERR_HIP;
     if (!mark(8)) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+size_t moe_backward_workspace_size(const moe_cfg* cfg) {
+    if (!cfg || cfg->T < 0 || cfg->E < 1 || cfg->k < 1 || cfg->F_shared < 0) return 0;
+    return backward_layout(cfg, nullptr).total;
+}
+
+int moe_backward(const moe_cfg* c, const moe_weights* w, const moe_bwd_weights* bw,
+                 const uint16_t* x, const int32_t* input_ids, const uint8_t* modality,
+                 const float* dy, const moe_grads* gr, uint32_t* d_flags, void* ws,
+                 size_t ws_bytes, void* stream) {
+    int st = forward_checks(c, w);
+    if (st != MOE_OK) return st;
+    if (!bw || !gr) return MOE_ERR_NULL;
+    if (w->packed != 1) return MOE_ERR_UNSUPPORTED;   // bf16 packed weights only
+    if (c->E > grouped_gemm_flat_max_groups()) return MOE_ERR_UNSUPPORTED;
+    if (c->T == 0) return MOE_OK;
+    const int Fs = c->F_shared;
+    if (!x || !dy || !w->w_g || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL;
+    if (!bw->w_g || !bw->w_down_t || !bw->w_gu_t) return MOE_ERR_NULL;
+    if (!gr->dx || !gr->dw_g || !gr->dw_gate || !gr->dw_up || !gr->dw_down) return MOE_ERR_NULL;
+    if (Fs > 0 && (!w->s_gate || !w->s_up || !w->s_down || !bw->s_down_t || !bw->s_gu_t ||
+                   !gr->ds_gate || !gr->ds_up || !gr->ds_down))
+        return MOE_ERR_NULL;
+    if (c->mode == MOE_MODE_TOPK) {
+        if (c->n_bias < 0 || c->n_bias > 2) return MOE_ERR_SHAPE;
+        if (c->n_bias > 0 && !w->score_bias) return MOE_ERR_NULL;
+    } else {
+        if (!input_ids || !w->tid2eid) return MOE_ERR_NULL;
+        if (c->V < 1) return MOE_ERR_SHAPE;
+    }
+    if (c->d % 8) return MOE_ERR_UNSUPPORTED;
+    if (!ws) return MOE_ERR_NULL;
+    BwdWs L = backward_layout(c, (char*)ws);
+    if (((uintptr_t)ws & 255u) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    const void* al[] = {x, dy, w->w_g, w->w_gate, w->w_up, w->w_down, bw->w_g, bw->w_down_t,
+                        bw->w_gu_t, gr->dx, gr->dw_g, gr->dw_gate, gr->dw_up, gr->dw_down};
+    for (const void* p : al)
+        if (!aligned16(p)) return MOE_ERR_ALIGN;
+    if (Fs > 0) {
+        const void* as[] = {w->s_gate, w->s_up, w->s_down, bw->s_down_t, bw->s_gu_t, gr->ds_gate,
+                            gr->ds_up, gr->ds_down};
+        for (const void* p : as)
+            if (!aligned16(p)) return MOE_ERR_ALIGN;
+    }
+
+    hipStream_t s = as_stream(stream);
+    const int T = c->T, d = c->d, E = c->E, k = c->k, F = c->F;
+    const int N = T * k;
+    const float Lc = c->clamp_limit;
+    const int cm = c->clamp_mode;
+    uint32_t* sch = L.sched;
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+
+    // ---- recompute the forward's intermediates
+    if (router_packed_preferred(T, E)) {
+        if (!ok(launch_router_packed(x, w->w_g, w->logit_offset, T, d, E, L.logits, s)))
+            return MOE_ERR_HIP;
+    } else {
+        GemmArgs gl{};
+        gl.a = x;
+        gl.G = 1;
+        gl.rows = T;
+        gl.K = d;
+        gl.N = E;
+        gl.w1 = w->w_g;
+        gl.packed = 1;
+        gl.offset = w->logit_offset;
+        gl.out = L.logits;
+        if (!ok(launch_grouped_gemm(EPI_F32_OFFSET, gl, s))) return MOE_ERR_HIP;
+    }
+    if (!ok(launch_route(L.logits, c->n_bias > 0 ? w->score_bias : nullptr, modality, input_ids,
+                         w->tid2eid, T, E, k, c->n_bias, c->V, c->mode, c->scale, L.ids, L.w,
+                         d_flags, s)))
+        return MOE_ERR_HIP;
+    if (!ok(launch_permute(L.ids, x, T, d, E, k, L.counts, L.offsets, L.dest, L.src, L.x_perm,
+                           d_flags, L.perm, s, sch, 8 * kSchedWords)))
+        return MOE_ERR_HIP;
+    // gate/up with the pre-activations saved, h row-major; then y_perm
+    if (!ok(flat_gemm(EPI_SWIGLU_BF16, L.x_perm, L.offsets, E, N, d, F, w->w_gate, w->w_up, Lc,
+                      cm, L.h, L.g, L.u, sch, s)))
+        return MOE_ERR_HIP;
+    if (!ok(flat_gemm(EPI_F32, L.h, L.offsets, E, N, F, d, w->w_down, nullptr, Lc, cm, L.y_perm,
+                      nullptr, nullptr, sch + kSchedWords, s)))
+        return MOE_ERR_HIP;
+
+    // ---- combine -> expert outputs and routing weights
+    if (!ok(launch_combine_backward(dy, L.y_perm, L.dest, L.w, T, d, k, N, L.dyp, L.dtw, s)))
+        return MOE_ERR_HIP;
+    if (!ok(launch_cast_bf16(L.dyp, (long long)N * d, L.dyp16, s))) return MOE_ERR_HIP;
+    // ---- down projection: weight and input gradients
+    if (!ok(launch_grouped_wgrad(L.dyp16, L.h, L.offsets, E, N, d, F, gr->dw_down, s)))
+        return MOE_ERR_HIP;
+    if (!ok(flat_gemm(EPI_F32, L.dyp16, L.offsets, E, N, d, F, bw->w_down_t, nullptr, Lc, cm,
+                      L.dh, nullptr, nullptr, sch + 2 * kSchedWords, s)))
+        return MOE_ERR_HIP;
+    // ---- clamped SwiGLU, then gate/up weight and input gradients
+    if (!ok(launch_swiglu_backward_bf16(L.g, L.u, L.dh, N, F, Lc, cm, L.dgu, s)))
+        return MOE_ERR_HIP;
+    if (!ok(launch_grouped_wgrad(L.dgu, L.x_perm, L.offsets, E, N, F, d, gr->dw_gate, s, 2 * F)))
+        return MOE_ERR_HIP;
+    if (!ok(launch_grouped_wgrad(L.dgu + F, L.x_perm, L.offsets, E, N, F, d, gr->dw_up, s, 2 * F)))
+        return MOE_ERR_HIP;
+    float* dxp = L.dyp;  // (dy_perm is no longer needed: its rows take dx_perm)
+    if (!ok(flat_gemm(EPI_F32, L.dgu, L.offsets, E, N, 2 * F, d, bw->w_gu_t, nullptr, Lc, cm, dxp,
+                      nullptr, nullptr, sch + 3 * kSchedWords, s)))
+        return MOE_ERR_HIP;
+
+    // ---- shared expert on x with dy
+    if (Fs > 0) {
+        if (!ok(flat_gemm(EPI_SWIGLU_BF16, x, nullptr, 1, T, d, Fs, w->s_gate, w->s_up, Lc, cm,
+                          L.hs, L.gs, L.us, sch + 4 * kSchedWords, s)))
+            return MOE_ERR_HIP;
+        if (!ok(launch_cast_bf16(dy, (long long)T * d, L.dy16, s))) return MOE_ERR_HIP;
+        if (!ok(launch_grouped_wgrad(L.dy16, L.hs, nullptr, 1, T, d, Fs, gr->ds_down, s)))
+            return MOE_ERR_HIP;
+        if (!ok(flat_gemm(EPI_F32, L.dy16, nullptr, 1, T, d, Fs, bw->s_down_t, nullptr, Lc, cm,
+                          L.dhs, nullptr, nullptr, sch + 5 * kSchedWords, s)))
+            return MOE_ERR_HIP;
+        if (!ok(launch_swiglu_backward_bf16(L.gs, L.us, L.dhs, T, Fs, Lc, cm, L.dgus, s)))
+            return MOE_ERR_HIP;
+        if (!ok(launch_grouped_wgrad(L.dgus, x, nullptr, 1, T, Fs, d, gr->ds_gate, s, 2 * Fs)))
+            return MOE_ERR_HIP;
+        if (!ok(launch_grouped_wgrad(L.dgus + Fs, x, nullptr, 1, T, Fs, d, gr->ds_up, s, 2 * Fs)))
+            return MOE_ERR_HIP;
+        if (!ok(flat_gemm(EPI_F32, L.dgus, nullptr, 1, T, 2 * Fs, d, bw->s_gu_t, nullptr, Lc, cm,
+                          L.dxs, nullptr, nullptr, sch + 6 * kSchedWords, s)))
+            return MOE_ERR_HIP;
+    }
+    // ---- dx = (each token's dx_perm rows, unit weights) + shared expert's
+    if (!ok(launch_combine(dxp, L.dest, nullptr, Fs > 0 ? L.dxs : nullptr, T, d, k, N, MOE_OUT_F32,
+                           gr->dx, s)))
+        return MOE_ERR_HIP;
+    // ---- routing weights -> logits -> router projection
+    if (!ok(launch_route_backward(L.logits, L.ids, L.dtw, T, E, k, c->scale, L.dl, d_flags, s)))
+        return MOE_ERR_HIP;
+    if (!ok(launch_router_backward(L.dl, L.ids, L.offsets, L.src, x, bw->w_g, T, d, E, k, gr->dx,
+                                   gr->dw_g, s)))
+        return MOE_ERR_HIP;
     return MOE_OK;
 }
 

@@ -56,6 +56,18 @@ class MoeWeights(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_int)] + [(n, ctypes.c_void_p) for n in WEIGHT_NAMES]
 
 
+BWD_WEIGHT_NAMES = ("w_g", "w_down_t", "w_gu_t", "s_down_t", "s_gu_t")
+GRAD_NAMES = ("dx", "dw_g", "dw_gate", "dw_up", "dw_down", "ds_gate", "ds_up", "ds_down")
+
+
+class MoeBwdWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in BWD_WEIGHT_NAMES]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_NAMES]
+
+
 def declared_functions():
     """Names of the functions include/moe.h declares."""
     text = open(HEADER).read()
@@ -108,6 +120,11 @@ def lib():
     L.moe_forward.argtypes = [ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeWeights), P, P, P, P,
                               P, P, P, P, P, S, P]
     L.moe_forward_timed.argtypes = L.moe_forward.argtypes + [P]
+    L.moe_backward_workspace_size.argtypes = [ctypes.POINTER(MoeCfg)]
+    L.moe_backward_workspace_size.restype = S
+    L.moe_backward.argtypes = [ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeWeights),
+                               ctypes.POINTER(MoeBwdWeights), P, P, P, P,
+                               ctypes.POINTER(MoeGrads), P, P, S, P]
     for name in ("moe_gate_logits", "moe_route", "moe_permute", "moe_expert_ffn",
                  "moe_expert_ffn_packed",
                  "moe_combine", "moe_forward", "moe_forward_timed", "moe_pack_weights",
@@ -484,6 +501,8 @@ class MoeLayer:
                           V=V, scale=float(scale), clamp_limit=float(clamp_limit),
                           clamp_mode=int(clamp_mode), out_dtype=int(out_dtype))
         self.weights = dict(weights)
+        self.plain = dict(weights)     # the [out, in] matrices (for the backward's layouts)
+        self.bw = None
         _need(self.weights["w_g"], torch.bfloat16, "w_g", shape=(E, d))
         _need(self.weights["w_gate"], torch.bfloat16, "w_gate", shape=(E, F, d))
         _need(self.weights["w_up"], torch.bfloat16, "w_up", shape=(E, F, d))
@@ -520,6 +539,54 @@ class MoeLayer:
         self.ws_bytes = int(lib().moe_forward_workspace_size(ctypes.byref(self.cfg)))
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         self.flags = torch.zeros(1, dtype=torch.int32, device=self.device)
+
+    def backward_weights(self):
+        """The weights in the layouts of the backward's input-gradient
+        products (moe_bwd_weights): packed once per weight update from the
+        [out, in] matrices (transposed and concatenated copies, then
+        moe_pack_weights with 256-row panels)."""
+        if self.bw is None:
+            p = self.plain
+            bw = dict(w_g=p["w_g"].contiguous(),
+                      w_down_t=pack_weights(p["w_down"].transpose(1, 2).contiguous(), 256),
+                      w_gu_t=pack_weights(torch.cat([p["w_gate"], p["w_up"]], dim=1)
+                                          .transpose(1, 2).contiguous(), 256))
+            if self.cfg.F_shared > 0:
+                bw["s_down_t"] = pack_weights(p["s_down"].t().contiguous(), 256)
+                bw["s_gu_t"] = pack_weights(torch.cat([p["s_gate"], p["s_up"]], dim=0)
+                                            .t().contiguous(), 256)
+            self.bw = bw
+            self.cbw = MoeBwdWeights(**{n: _ptr(bw.get(n)) for n in BWD_WEIGHT_NAMES})
+            self.bws_bytes = int(lib().moe_backward_workspace_size(ctypes.byref(self.cfg)))
+            self.bworkspace = torch.empty(self.bws_bytes, dtype=torch.uint8, device=self.device)
+        return self.bw
+
+    def backward(self, x, dy, input_ids=None, modality=None, grads=None):
+        """Gradients of the layer output for an output gradient dy [T, d]
+        fp32 (one moe_backward call): dict with dx, dw_g, dw_gate, dw_up,
+        dw_down and, with a shared expert, ds_gate, ds_up, ds_down (fp32)."""
+        c = self.cfg
+        if self.packed != 1:
+            raise MoeError("moe_backward takes bf16 packed weights (packed=True)")
+        _need(x, torch.bfloat16, "x", shape=(c.T, c.d))
+        _need(dy, torch.float32, "dy", shape=(c.T, c.d))
+        _opt(input_ids, torch.int32, "input_ids", shape=(c.T,))
+        _opt(modality, torch.uint8, "modality", shape=(c.T,))
+        self.backward_weights()
+        shapes = dict(dx=(c.T, c.d), dw_g=(c.E, c.d), dw_gate=(c.E, c.F, c.d),
+                      dw_up=(c.E, c.F, c.d), dw_down=(c.E, c.d, c.F))
+        if c.F_shared > 0:
+            shapes.update(ds_gate=(c.F_shared, c.d), ds_up=(c.F_shared, c.d),
+                          ds_down=(c.d, c.F_shared))
+        grads = dict(grads or {})
+        for n, shp in shapes.items():
+            grads[n] = _out(grads.get(n), torch.float32, n, shp, x.device)
+        cg = MoeGrads(**{n: _ptr(grads.get(n)) for n in GRAD_NAMES})
+        _check(lib().moe_backward(ctypes.byref(c), ctypes.byref(self.cw), ctypes.byref(self.cbw),
+                                  _ptr(x), _ptr(input_ids), _ptr(modality), _ptr(dy),
+                                  ctypes.byref(cg), _ptr(self.flags), _ptr(self.bworkspace),
+                                  self.bws_bytes, _stream()), "moe_backward")
+        return grads
 
     @classmethod
     def from_workload(cls, w, inputs, out_dtype=OUT_BF16, packed=False):
