@@ -193,6 +193,11 @@ def main():
                     help="time K eager moe_forward calls instead of K replays of one captured "
                          "forward (HIP graph); the per-stage breakdown comes from eager calls "
                          "either way")
+    ap.add_argument("--extras", choices=["all", "none", "backward"], default="all",
+                    help="after the forward's timing, also time the backward pieces, the weight "
+                         "gradient and the whole layer backward (all), only the layer backward "
+                         "(backward), or nothing (none: a fixed set of forward calls for "
+                         "profiling)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle CPU work for the baseline (0: skip)")
     args = ap.parse_args()
@@ -281,123 +286,178 @@ def main():
     ms_cold = sum(e0.elapsed_time(e1) for e0, e1 in cold) / n_cold
     del flush
 
-    # The routing backward (moe_route_backward: the routing weights' gradient
-    # taken back to the logits) on this workload's own forward routes, timed
-    # outside the forward step: 20 calls captured in one graph, replayed
-    # between two events (each call is a few microseconds of device work,
-    # less than the host cost of one call).
-    lg_b = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
-    ids_b = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
-    wts_b = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
-    layer.forward(inp["x"], input_ids=inp["input_ids"], modality=inp["modality"], logits=lg_b,
-                  ids=ids_b, w=wts_b)
+    route_backward = combine_backward = swiglu_backward = down_dgrad = wgrad_down = None
+    routing = None
     gen = torch.Generator(device=dev)
     gen.manual_seed(7)
-    dw_b = torch.randn((w.T, w.k), generator=gen, device=dev)
-    dl_b = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
-    ops.route_backward(lg_b, ids_b, dw_b, w.scale, out=dl_b)
-    torch.cuda.synchronize()
-    n_rb = 20
-    rb_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(rb_graph):
-        for _ in range(n_rb):
-            ops.route_backward(lg_b, ids_b, dw_b, w.scale, out=dl_b)
-    rb_graph.replay()
-    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    rb_graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    rb_ms = e0.elapsed_time(e1) / n_rb
-    # ids, dw and the k gathered logits read; the whole d_logits row written
-    rb_bytes = w.T * w.k * 12 + w.T * w.E * 4
-    route_backward = {"ms": rb_ms, "GB/s": rb_bytes / rb_ms / 1e6,
-                      "frac_of_hbm_peak": rb_bytes / rb_ms / 1e6 / (PEAK_HBM / 1e9),
-                      "algorithmic_bytes": rb_bytes}
-    # near-ties and route flips of this forward's routing (not timed)
-    routing = routing_diagnostics(w, inp, lg_b, ids_b)
-    del rb_graph, dl_b, lg_b
+    if args.extras == "all":
+        # The routing backward (moe_route_backward: the routing weights' gradient
+        # taken back to the logits) on this workload's own forward routes, timed
+        # outside the forward step: 20 calls captured in one graph, replayed
+        # between two events (each call is a few microseconds of device work,
+        # less than the host cost of one call).
+        lg_b = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
+        ids_b = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+        wts_b = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+        layer.forward(inp["x"], input_ids=inp["input_ids"], modality=inp["modality"], logits=lg_b,
+                      ids=ids_b, w=wts_b)
+        dw_b = torch.randn((w.T, w.k), generator=gen, device=dev)
+        dl_b = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
+        ops.route_backward(lg_b, ids_b, dw_b, w.scale, out=dl_b)
+        torch.cuda.synchronize()
+        n_rb = 20
+        rb_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(rb_graph):
+            for _ in range(n_rb):
+                ops.route_backward(lg_b, ids_b, dw_b, w.scale, out=dl_b)
+        rb_graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        rb_graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        rb_ms = e0.elapsed_time(e1) / n_rb
+        # ids, dw and the k gathered logits read; the whole d_logits row written
+        rb_bytes = w.T * w.k * 12 + w.T * w.E * 4
+        route_backward = {"ms": rb_ms, "GB/s": rb_bytes / rb_ms / 1e6,
+                          "frac_of_hbm_peak": rb_bytes / rb_ms / 1e6 / (PEAK_HBM / 1e9),
+                          "algorithmic_bytes": rb_bytes}
+        # near-ties and route flips of this forward's routing (not timed)
+        routing = routing_diagnostics(w, inp, lg_b, ids_b)
+        del rb_graph, dl_b, lg_b
 
-    # The combine backward (moe_combine_backward: the output gradient taken
-    # to the expert outputs and the routing weights) at this workload's
-    # shapes: the forward's routes and weights, random fp32 expert outputs
-    # and output gradient; 5 calls between two events.
-    # (dest of the forward's dispatch: each pair's row in the stable
-    # expert-major order; setup data, computed here with torch)
-    order = torch.argsort(ids_b.flatten().long(), stable=True)
-    dest_b = torch.empty(w.T * w.k, dtype=torch.int32, device=dev)
-    dest_b[order] = torch.arange(w.T * w.k, dtype=torch.int32, device=dev)
-    del order
-    yp_b = torch.randn((w.T * w.k, w.d), generator=gen, device=dev)
-    dy_b = torch.randn((w.T, w.d), generator=gen, device=dev)
-    dyp_b = torch.empty_like(yp_b)
-    dwt_b = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
-    ops.combine_backward(dy_b, yp_b, dest_b, wts_b, dy_perm=dyp_b, d_topk_w=dwt_b)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(5):
+        # The combine backward (moe_combine_backward: the output gradient taken
+        # to the expert outputs and the routing weights) at this workload's
+        # shapes: the forward's routes and weights, random fp32 expert outputs
+        # and output gradient; 5 calls between two events.
+        # (dest of the forward's dispatch: each pair's row in the stable
+        # expert-major order; setup data, computed here with torch)
+        order = torch.argsort(ids_b.flatten().long(), stable=True)
+        dest_b = torch.empty(w.T * w.k, dtype=torch.int32, device=dev)
+        dest_b[order] = torch.arange(w.T * w.k, dtype=torch.int32, device=dev)
+        del order
+        yp_b = torch.randn((w.T * w.k, w.d), generator=gen, device=dev)
+        dy_b = torch.randn((w.T, w.d), generator=gen, device=dev)
+        dyp_b = torch.empty_like(yp_b)
+        dwt_b = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
         ops.combine_backward(dy_b, yp_b, dest_b, wts_b, dy_perm=dyp_b, d_topk_w=dwt_b)
-    e1.record()
-    torch.cuda.synchronize()
-    cb_ms = e0.elapsed_time(e1) / 5
-    # dy and every routed expert output read, every expert-output gradient
-    # written, dest / w read and d_topk_w written
-    cb_bytes = w.T * w.d * 4 + 2 * w.T * w.k * w.d * 4 + w.T * w.k * 12
-    combine_backward = {"ms": cb_ms, "GB/s": cb_bytes / cb_ms / 1e6,
-                        "frac_of_hbm_peak": cb_bytes / cb_ms / 1e6 / (PEAK_HBM / 1e9),
-                        "algorithmic_bytes": cb_bytes}
-    del yp_b, dy_b, dyp_b, dest_b
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            ops.combine_backward(dy_b, yp_b, dest_b, wts_b, dy_perm=dyp_b, d_topk_w=dwt_b)
+        e1.record()
+        torch.cuda.synchronize()
+        cb_ms = e0.elapsed_time(e1) / 5
+        # dy and every routed expert output read, every expert-output gradient
+        # written, dest / w read and d_topk_w written
+        cb_bytes = w.T * w.d * 4 + 2 * w.T * w.k * w.d * 4 + w.T * w.k * 12
+        combine_backward = {"ms": cb_ms, "GB/s": cb_bytes / cb_ms / 1e6,
+                            "frac_of_hbm_peak": cb_bytes / cb_ms / 1e6 / (PEAK_HBM / 1e9),
+                            "algorithmic_bytes": cb_bytes}
+        del yp_b, dy_b, dyp_b, dest_b
 
-    # The clamped-SwiGLU backward (moe_swiglu_backward) at this workload's
-    # [T k, F] pre-activation shape: random fp32 gate/up pre-activations and
-    # h gradient; 5 calls between two events.
-    sb_shape = (w.T * w.k, w.F)
-    g_sb = torch.randn(sb_shape, generator=gen, device=dev) * 4
-    u_sb = torch.randn(sb_shape, generator=gen, device=dev) * 4
-    dh_sb = torch.randn(sb_shape, generator=gen, device=dev)
-    dg_sb, du_sb = torch.empty_like(g_sb), torch.empty_like(g_sb)
-    ops.swiglu_backward(g_sb, u_sb, dh_sb, w.clamp_limit, w.clamp_mode, dgate=dg_sb, dup=du_sb)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(5):
-        ops.swiglu_backward(g_sb, u_sb, dh_sb, w.clamp_limit, w.clamp_mode, dgate=dg_sb,
-                            dup=du_sb)
-    e1.record()
-    torch.cuda.synchronize()
-    sb_ms = e0.elapsed_time(e1) / 5
-    sb_bytes = 20 * w.T * w.k * w.F          # three fp32 inputs read, two written
-    swiglu_backward = {"ms": sb_ms, "GB/s": sb_bytes / sb_ms / 1e6,
-                       "frac_of_hbm_peak": sb_bytes / sb_ms / 1e6 / (PEAK_HBM / 1e9),
-                       "algorithmic_bytes": sb_bytes}
-    del g_sb, u_sb, dh_sb, dg_sb, du_sb
+        # The clamped-SwiGLU backward (moe_swiglu_backward) at this workload's
+        # [T k, F] pre-activation shape: random fp32 gate/up pre-activations and
+        # h gradient; 5 calls between two events.
+        sb_shape = (w.T * w.k, w.F)
+        g_sb = torch.randn(sb_shape, generator=gen, device=dev) * 4
+        u_sb = torch.randn(sb_shape, generator=gen, device=dev) * 4
+        dh_sb = torch.randn(sb_shape, generator=gen, device=dev)
+        dg_sb, du_sb = torch.empty_like(g_sb), torch.empty_like(g_sb)
+        ops.swiglu_backward(g_sb, u_sb, dh_sb, w.clamp_limit, w.clamp_mode, dgate=dg_sb, dup=du_sb)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            ops.swiglu_backward(g_sb, u_sb, dh_sb, w.clamp_limit, w.clamp_mode, dgate=dg_sb,
+                                dup=du_sb)
+        e1.record()
+        torch.cuda.synchronize()
+        sb_ms = e0.elapsed_time(e1) / 5
+        sb_bytes = 20 * w.T * w.k * w.F          # three fp32 inputs read, two written
+        swiglu_backward = {"ms": sb_ms, "GB/s": sb_bytes / sb_ms / 1e6,
+                           "frac_of_hbm_peak": sb_bytes / sb_ms / 1e6 / (PEAK_HBM / 1e9),
+                           "algorithmic_bytes": sb_bytes}
+        del g_sb, u_sb, dh_sb, dg_sb, du_sb
 
-    # The down projection's input gradient dH = dY W_down per expert
-    # (moe_grouped_gemm_packed with W_down^T packed once) at this workload's
-    # group sizes: random bf16 dY; 3 calls between two events.
-    counts_b = torch.bincount(ids_b.flatten().long(), minlength=w.E)
-    offs_b = torch.zeros(w.E + 1, dtype=torch.int32, device=dev)
-    offs_b[1:] = torch.cumsum(counts_b, 0).to(torch.int32)
-    wdT_b = ops.pack_weights(inp["w_down"].transpose(1, 2).contiguous(), 256)
-    dY_b = torch.randn((w.T * w.k, w.d), generator=gen, device=dev).to(torch.bfloat16)
-    dH_b = torch.empty((w.T * w.k, w.F), dtype=torch.float32, device=dev)
-    ops.grouped_gemm_packed(dY_b, offs_b, wdT_b, w.E, w.F, out=dH_b)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(3):
+        # The down projection's input gradient dH = dY W_down per expert
+        # (moe_grouped_gemm_packed with W_down^T packed once) at this workload's
+        # group sizes: random bf16 dY; 3 calls between two events.
+        counts_b = torch.bincount(ids_b.flatten().long(), minlength=w.E)
+        offs_b = torch.zeros(w.E + 1, dtype=torch.int32, device=dev)
+        offs_b[1:] = torch.cumsum(counts_b, 0).to(torch.int32)
+        wdT_b = ops.pack_weights(inp["w_down"].transpose(1, 2).contiguous(), 256)
+        dY_b = torch.randn((w.T * w.k, w.d), generator=gen, device=dev).to(torch.bfloat16)
+        dH_b = torch.empty((w.T * w.k, w.F), dtype=torch.float32, device=dev)
         ops.grouped_gemm_packed(dY_b, offs_b, wdT_b, w.E, w.F, out=dH_b)
-    e1.record()
-    torch.cuda.synchronize()
-    dg_ms = e0.elapsed_time(e1) / 3
-    nz_b = int((counts_b > 0).sum().item())
-    dg_flops = 2.0 * w.T * w.k * w.d * w.F
-    dg_bytes = nz_b * w.F * w.d * 2 + w.T * w.k * w.d * 2 + w.T * w.k * w.F * 4
-    down_dgrad = {"ms": dg_ms, "TFLOP/s": dg_flops / dg_ms / 1e9,
-                  "GB/s": dg_bytes / dg_ms / 1e6,
-                  "frac_of_hbm_peak": dg_bytes / dg_ms / 1e6 / (PEAK_HBM / 1e9),
-                  "frac_of_mfma_peak": dg_flops / dg_ms / 1e9 / (PEAK_BF16 / 1e12),
-                  "algorithmic_bytes": dg_bytes, "flops": dg_flops}
-    del wdT_b, dY_b, dH_b
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(3):
+            ops.grouped_gemm_packed(dY_b, offs_b, wdT_b, w.E, w.F, out=dH_b)
+        e1.record()
+        torch.cuda.synchronize()
+        dg_ms = e0.elapsed_time(e1) / 3
+        nz_b = int((counts_b > 0).sum().item())
+        dg_flops = 2.0 * w.T * w.k * w.d * w.F
+        dg_bytes = nz_b * w.F * w.d * 2 + w.T * w.k * w.d * 2 + w.T * w.k * w.F * 4
+        down_dgrad = {"ms": dg_ms, "TFLOP/s": dg_flops / dg_ms / 1e9,
+                      "GB/s": dg_bytes / dg_ms / 1e6,
+                      "frac_of_hbm_peak": dg_bytes / dg_ms / 1e6 / (PEAK_HBM / 1e9),
+                      "frac_of_mfma_peak": dg_flops / dg_ms / 1e9 / (PEAK_BF16 / 1e12),
+                      "algorithmic_bytes": dg_bytes, "flops": dg_flops}
+        del wdT_b, dH_b
+
+        # The down projection's weight gradient dW_down[e] = dY_e^T H_e
+        # (moe_grouped_wgrad) at this workload's group sizes: random bf16 dY and
+        # H; 3 calls between two events.
+        H_b = torch.randn((w.T * w.k, w.F), generator=gen, device=dev).to(torch.bfloat16)
+        dW_b = torch.empty((w.E, w.d, w.F), dtype=torch.float32, device=dev)
+        ops.grouped_wgrad(dY_b, H_b, offs_b, out=dW_b)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(3):
+            ops.grouped_wgrad(dY_b, H_b, offs_b, out=dW_b)
+        e1.record()
+        torch.cuda.synchronize()
+        wg_ms = e0.elapsed_time(e1) / 3
+        wg_flops = 2.0 * w.T * w.k * w.d * w.F
+        # every dW entry written once (fp32), dY and H read once
+        wg_bytes = w.E * w.d * w.F * 4 + w.T * w.k * (w.d + w.F) * 2
+        wgrad_down = {"ms": wg_ms, "TFLOP/s": wg_flops / wg_ms / 1e9,
+                      "GB/s": wg_bytes / wg_ms / 1e6,
+                      "frac_of_hbm_peak": wg_bytes / wg_ms / 1e6 / (PEAK_HBM / 1e9),
+                      "frac_of_mfma_peak": wg_flops / wg_ms / 1e9 / (PEAK_BF16 / 1e12),
+                      "algorithmic_bytes": wg_bytes, "flops": wg_flops}
+        del dY_b, H_b, dW_b
+        torch.cuda.empty_cache()
+
+    # The whole layer backward (moe_backward: the forward's intermediates
+    # recomputed, then every gradient) for a random fp32 output gradient;
+    # 1 warm-up call (it also packs the transposed weights once), then 3
+    # calls between two events.
+    layer_backward = None
+    if args.extras in ("all", "backward") and args.weights == "bf16" and args.layout == "packed":
+        dyb = torch.randn((w.T, w.d), generator=gen, device=dev)
+        grads = layer.backward(inp["x"], dyb, input_ids=inp["input_ids"],
+                               modality=inp["modality"])
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(3):
+            layer.backward(inp["x"], dyb, input_ids=inp["input_ids"], modality=inp["modality"],
+                           grads=grads)
+        e1.record()
+        torch.cuda.synchronize()
+        lb_ms = e0.elapsed_time(e1) / 3
+        assert int(layer.flags.item()) == 0, "device flagged invalid ids"
+        # forward recomputation (expert products once) plus the input- and
+        # weight-gradient products: 3x the forward's FLOPs on the experts
+        fw_flops = 2.0 * w.T * (w.k * 3 * w.d * w.F + 3 * w.d * w.Fs)
+        layer_backward = {"ms": lb_ms, "tokens/s": w.T / (lb_ms * 1e-3),
+                          "TFLOP/s": 3 * fw_flops / lb_ms / 1e9,
+                          "note": "forward recomputed inside; 3x the expert FFN FLOPs"}
+        del grads, dyb
+        layer.bw = layer.bworkspace = None
+        torch.cuda.empty_cache()
 
     counts = torch.bincount(ids.flatten().long(), minlength=w.E).cpu().numpy()
     n_nonempty = int((counts > 0).sum())
@@ -458,6 +518,8 @@ def main():
         "combine_backward": combine_backward,
         "swiglu_backward": swiglu_backward,
         "down_dgrad": down_dgrad,
+        "wgrad_down": wgrad_down,
+        "layer_backward": layer_backward,
         "routing": routing,
     }
     if args.cpu_budget > 0:

@@ -198,8 +198,8 @@ int moe_expert_ffn(const uint16_t* a, const int32_t* offsets, int G, int rows, i
                    float clamp_limit, int clamp_mode, uint16_t* h, float* y, void* stream);
 
 /* The same grouped FFN on weights in the moe_pack_weights layout (w_gate,
- * w_up with panel_rows 128, w_down with 256), computed by the LDS-staged
- * expert GEMM that moe_forward uses for packed weights.  Arguments, layouts
+ * w_up with panel_rows 128, w_down with 256), computed by the expert GEMM
+ * that moe_forward uses for packed weights.  Arguments, layouts
  * and results as moe_expert_ffn (h row-major).  It takes no
  * workspace, so its workgroups split the tiles statically (moe_forward
  * balances them with counters in its workspace); the arithmetic, and so every

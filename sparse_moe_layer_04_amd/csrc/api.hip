@@ -67,8 +67,26 @@ inline bool lds_gemm_ok(int packed, int G) {
 #ifndef MOE_EXPERT_GEMM_FLAT
 #define MOE_EXPERT_GEMM_FLAT 1
 #endif
+// packed bf16 weights without a workspace (static schedule): the flat kernel
+// when its LDS holds the group table, else the LDS-staged one
+inline hipError_t packed_gemm(int epi, const GemmArgs& g, hipStream_t s) {
+    if (MOE_EXPERT_GEMM_FLAT && g.G <= grouped_gemm_flat_max_groups())
+        return launch_grouped_gemm_flat(epi, g, s);
+    return launch_grouped_gemm_lds(epi, g, s);
+}
+#ifndef MOE_EXPERT_GEMM_FLAT_MX
+#define MOE_EXPERT_GEMM_FLAT_MX 1
+#endif
+// the flat kernel takes MX weights in the two routed GEMMs of the forward:
+// gate/up on gathered token rows into blocked h, down on blocked h
+inline bool flat_mx_ok(int epi, const GemmArgs& g) {
+    return MOE_EXPERT_GEMM_FLAT_MX && !g.out_g &&
+           ((epi == EPI_SWIGLU_BF16 && g.gather && g.out_blocked && !g.a_blocked) ||
+            (epi == EPI_F32 && !g.gather && g.a_blocked));
+}
 inline hipError_t expert_gemm(int epi, const GemmArgs& g, hipStream_t s) {
-    if (MOE_EXPERT_GEMM_FLAT && g.packed && !g.wfp8 && g.G <= grouped_gemm_flat_max_groups())
+    if (MOE_EXPERT_GEMM_FLAT && g.packed && g.G <= grouped_gemm_flat_max_groups() &&
+        (!g.wfp8 || flat_mx_ok(epi, g)))
         return launch_grouped_gemm_flat(epi, g, s);
     return lds_gemm_ok(g.packed, g.G) ? launch_grouped_gemm_lds(epi, g, s)
                                       : launch_grouped_gemm(epi, g, s);
@@ -381,7 +399,7 @@ int moe_expert_ffn_packed(const uint16_t* a, const int32_t* offsets, int G, int 
     g1.clamp_limit = clamp_limit;
     g1.clamp_mode = clamp_mode;
     g1.out = h;
-    hipError_t e = launch_grouped_gemm_lds(EPI_SWIGLU_BF16, g1, s);
+    hipError_t e = packed_gemm(EPI_SWIGLU_BF16, g1, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     GemmArgs g2{};
     g2.a = h;
@@ -393,7 +411,7 @@ int moe_expert_ffn_packed(const uint16_t* a, const int32_t* offsets, int G, int 
     g2.w1 = w_down;
     g2.packed = 1;
     g2.out = y;
-    return hip_status(launch_grouped_gemm_lds(EPI_F32, g2, s));
+    return hip_status(packed_gemm(EPI_F32, g2, s));
 }
 
 size_t moe_packed_weight_bytes(int G, int N, int K, int panel_rows) {
@@ -499,7 +517,7 @@ int moe_grouped_gemm_packed(const uint16_t* a, const int32_t* offsets, int G, in
     g.w1 = w_packed;
     g.packed = 1;
     g.out = out;
-    return hip_status(launch_grouped_gemm_lds(EPI_F32, g, as_stream(stream)));
+    return hip_status(packed_gemm(EPI_F32, g, as_stream(stream)));
 }
 
 int moe_grouped_wgrad(const uint16_t* dy, const uint16_t* a, const int32_t* offsets, int G,

@@ -94,6 +94,13 @@ struct FlatTile {
     size_t a_off[2];       // this thread's activation source (elements) at stage 0
     int a_rows;            // activation rows this thread stages (0..2, wave-uniform)
     int a_step;            // elements per stage of the activation source
+    // MXFP8 / MXFP4 weights: this wave's code chunks and scale bytes
+    const uint8_t* cp0;    // block 0 codes at K block 0 (lane offset included)
+    const uint8_t* cp1;    // block 1
+    size_t cstage;         // fp8: bytes per 64-wide K stage of a panel; fp4: per K block
+    const uint8_t* sp0;    // block 0 scale byte of this lane's row at K block 0
+    const uint8_t* sp1;
+    int sstep;             // scale bytes per K block (the panel's rows)
 };
 
 template <int NTB>
@@ -252,10 +259,12 @@ __device__ __forceinline__ void flat_epilogue(const GemmArgs& args, const FlatTi
 //   register slot (u % R) takes the weights of substep u + R.  Finally stage
 //   j + 1's activations (loaded AD - 1 stages earlier) go to slot (j + 1) % 2.
 // The stage loop is unrolled by two, so every ring index is static.
-template <int EPI, int AM, int NTB>
+template <int EPI, int AM, int NTB, int WF>
 __device__ __forceinline__ void flat_tile(const GemmArgs& args, const FlatTile& t,
                                           unsigned char* ring) {
-    constexpr int R = FLAT_R, AD = FLAT_AD, OB = FLAT_OB;
+    // (MX weights: one stage of code chunks in flight, operands read one
+    // substep ahead)
+    constexpr int R = WF ? 4 : FLAT_R, AD = FLAT_AD, OB = WF ? 2 : FLAT_OB;
     static_assert(R == 4 || R == 8, "weight ring of one or two stages");
     static_assert(AD == 1 || AD == 2, "activation depth");
     static_assert(OB == 1 || OB == 2, "operand buffers");
@@ -269,8 +278,36 @@ __device__ __forceinline__ void flat_tile(const GemmArgs& args, const FlatTile& 
     const int S = t.K / FK;
     const uint16_t* a = args.a;
 
-    bf16x8 w0[R], w1[R];
+    bf16x8 w0[WF ? 1 : R], w1[WF ? 1 : R];
     u32x4 areg[AD][2];
+    // MX weights: the code chunks (32 K columns = one MX block, both of its
+    // substeps) of one stage for both blocks, and their scale bytes X + 127
+    using CodeT = typename std::conditional<WF == 2, u32x2, u32x4>::type;
+    CodeT cw0[2], cw1[2];
+    uint32_t sc0[2], sc1[2];
+    auto load_c = [&](int j, int c) {
+        const int jj = min(j, S - 1);
+        const int kb = 2 * jj + c;
+        const size_t off = WF == 1 ? (size_t)jj * t.cstage + (size_t)c * 1024
+                                   : (size_t)kb * t.cstage;
+        cw0[c] = *(const CodeT*)(t.cp0 + off);
+        cw1[c] = *(const CodeT*)(t.cp1 + off);
+        sc0[c] = t.sp0[(size_t)kb * t.sstep];
+        sc1[c] = t.sp1[(size_t)kb * t.sstep];
+    };
+    // the bf16 operands of substep pq of the stage in the code ring: exact
+    // (the scaled code is a bf16 value)
+    auto decode = [&](int pq, bf16x8& d0, bf16x8& d1) {
+        const int c = pq >> 1, hh = pq & 1;
+        const float f0 = __uint_as_float(sc0[c] << 23), f1 = __uint_as_float(sc1[c] << 23);
+        if constexpr (WF == 1) {
+            d0 = fp8x8_to_bf16x8(u32x2{cw0[c][2 * hh], cw0[c][2 * hh + 1]}, f0);
+            d1 = fp8x8_to_bf16x8(u32x2{cw1[c][2 * hh], cw1[c][2 * hh + 1]}, f1);
+        } else if constexpr (WF == 2) {
+            d0 = fp4x8_to_bf16x8(cw0[c][hh], f0);
+            d1 = fp4x8_to_bf16x8(cw1[c][hh], f1);
+        }
+    };
 
     // weights of global substep u (stage u / 4, substep u % 4), clamped to K
     auto load_w = [&](int u, bf16x8& d0, bf16x8& d1) {
@@ -297,8 +334,13 @@ __device__ __forceinline__ void flat_tile(const GemmArgs& args, const FlatTile& 
 
     // prologue: weights of substeps 0 .. R - 1; activations of stages
     // 0 .. AD - 1 (stage 0 into slot 0)
+    if constexpr (WF) {
+        load_c(0, 0);
+        load_c(0, 1);
+    } else {
 #pragma unroll
-    for (int u = 0; u < R; ++u) load_w(u, w0[u], w1[u]);
+        for (int u = 0; u < R; ++u) load_w(u, w0[u], w1[u]);
+    }
     if (t.a_rows > 0) {
 #pragma unroll
         for (int p = 0; p < AD; ++p) load_a(p, areg[p]);
@@ -320,10 +362,21 @@ __device__ __forceinline__ void flat_tile(const GemmArgs& args, const FlatTile& 
                 read_act<NTB>(slot, t, q, o[q & 1]);
                 __builtin_amdgcn_sched_barrier(0);
                 if (q > 0 || j > 0) {
-                    // previous substep u - 1, its weight slot, then refill
-                    const int ps = (P * 4 + q + R - 1) % R;
-                    mfma_step<NTB>(w0[ps], w1[ps], o[(q + 1) & 1], acc);
-                    load_w(u - 1 + R, w0[ps], w1[ps]);
+                    if constexpr (WF) {
+                        // previous substep pq of stage jp; after the second
+                        // substep of a code chunk the chunk takes stage jp + 1
+                        const int pq = (q + 3) & 3;
+                        const int jp = q > 0 ? j : j - 1;
+                        bf16x8 d0, d1;
+                        decode(pq, d0, d1);
+                        mfma_step<NTB>(d0, d1, o[(q + 1) & 1], acc);
+                        if (pq & 1) load_c(jp + 1, pq >> 1);
+                    } else {
+                        // previous substep u - 1, its weight slot, then refill
+                        const int ps = (P * 4 + q + R - 1) % R;
+                        mfma_step<NTB>(w0[ps], w1[ps], o[(q + 1) & 1], acc);
+                        load_w(u - 1 + R, w0[ps], w1[ps]);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             } else {
@@ -344,8 +397,14 @@ __device__ __forceinline__ void flat_tile(const GemmArgs& args, const FlatTile& 
         // the last substep of the K loop (its operands were read at q = 3)
         if constexpr (OB == 2) {
             if (j == S - 1) {
-                constexpr int ls = (P * 4 + 3) % R;
-                mfma_step<NTB>(w0[ls], w1[ls], o[1], acc);
+                if constexpr (WF) {
+                    bf16x8 d0, d1;
+                    decode(3, d0, d1);
+                    mfma_step<NTB>(d0, d1, o[1], acc);
+                } else {
+                    constexpr int ls = (P * 4 + 3) % R;
+                    mfma_step<NTB>(w0[ls], w1[ls], o[1], acc);
+                }
             }
         }
     };
@@ -360,21 +419,21 @@ __device__ __forceinline__ void flat_tile(const GemmArgs& args, const FlatTile& 
     }
 }
 
-template <int EPI, int AM, int NT>
+template <int EPI, int AM, int NT, int WF>
 __device__ __forceinline__ void flat_tile_ntb(const GemmArgs& args, const FlatTile& t,
                                               unsigned char* ring) {
     if constexpr (NT == 1) {
-        flat_tile<EPI, AM, 1>(args, t, ring);
+        flat_tile<EPI, AM, 1, WF>(args, t, ring);
     } else {
-        if (t.ntb >= NT) flat_tile<EPI, AM, NT>(args, t, ring);
-        else flat_tile_ntb<EPI, AM, NT - 1>(args, t, ring);
+        if (t.ntb >= NT) flat_tile<EPI, AM, NT, WF>(args, t, ring);
+        else flat_tile_ntb<EPI, AM, NT - 1, WF>(args, t, ring);
     }
 }
 
 // Set up and run the tile of item `local` of group g (rows [grp_lo, grp_hi)).
 // A group's rows split evenly over its ceil(n / 128) m-tiles (rounded up to
 // 32 rows), so its m-tiles run at the same pace.
-template <int EPI, int AM>
+template <int EPI, int AM, int WF>
 __device__ __forceinline__ void flat_item(const GemmArgs& args, FlatTile& t, unsigned char* ring,
                                           int g, int local, int grp_lo, int grp_hi) {
     using Pn = FPanel<EPI>;
@@ -412,6 +471,26 @@ __device__ __forceinline__ void flat_item(const GemmArgs& args, FlatTile& t, uns
     const int p0 = min(blk0 / Pn::BPP, np - 1), p1 = min(blk1 / Pn::BPP, np - 1);
     t.wp0 = m0 + (size_t)p0 * pstride + (size_t)(blk0 % Pn::BPP) * 2048 + t.lane * 8;
     t.wp1 = m1 + (size_t)p1 * pstride + (size_t)(blk1 % Pn::BPP) * 2048 + t.lane * 8;
+    if constexpr (WF) {
+        // MX codes: fp8 [panel][K/64][P/32][2 chunks][64 lanes][16 B]; fp4
+        // [panel][K/32][P/32][64 lanes][8 B]; scales [panel][K/32][P/32][32]
+        const size_t pstride_b = (size_t)Pn::P * t.K / (WF == 2 ? 2 : 1);
+        const size_t ebase_b = (size_t)g * np * pstride_b;
+        const uint8_t* c0 = (const uint8_t*)args.w1 + ebase_b;
+        const uint8_t* c1 =
+            (const uint8_t*)(EPI == EPI_SWIGLU_BF16 ? args.w2 : args.w1) + ebase_b;
+        const size_t bsz = WF == 1 ? 2048 : 512;        // bytes per block per stage / K block
+        const size_t lsz = WF == 1 ? 16 : 8;            // bytes per lane
+        t.cstage = (size_t)Pn::BPP * bsz;
+        t.cp0 = c0 + (size_t)p0 * pstride_b + (size_t)(blk0 % Pn::BPP) * bsz + t.lane * lsz;
+        t.cp1 = c1 + (size_t)p1 * pstride_b + (size_t)(blk1 % Pn::BPP) * bsz + t.lane * lsz;
+        const size_t sstride = (size_t)(t.K / 32) * Pn::P;
+        const uint8_t* s0 = args.s1 + (size_t)g * np * sstride;
+        const uint8_t* s1 = (EPI == EPI_SWIGLU_BF16 ? args.s2 : args.s1) + (size_t)g * np * sstride;
+        t.sp0 = s0 + (size_t)p0 * sstride + (size_t)(blk0 % Pn::BPP) * 32 + t.l32;
+        t.sp1 = s1 + (size_t)p1 * sstride + (size_t)(blk1 % Pn::BPP) * 32 + t.l32;
+        t.sstep = Pn::P;
+    }
     // activation staging: thread tid copies 16 B chunk (tid % 8) of rows
     // tid / 8 and tid / 8 + 64 (rows past the tile read its last valid row);
     // a wave stages its second row group only if the tile reaches it
@@ -430,10 +509,10 @@ __device__ __forceinline__ void flat_item(const GemmArgs& args, FlatTile& t, uns
     }
     // per 64-wide stage: two 32-column blocks (blocked) or 64 elements
     t.a_step = AM == FA_BLK ? 1024 : FK;
-    flat_tile_ntb<EPI, AM, FNTB>(args, t, ring);
+    flat_tile_ntb<EPI, AM, FNTB, WF>(args, t, ring);
 }
 
-template <int EPI, int AM>
+template <int EPI, int AM, int WF>
 __global__ __launch_bounds__(kFThreads) void grouped_gemm_flat_kernel(GemmArgs args) {
     using Pn = FPanel<EPI>;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -530,7 +609,7 @@ __global__ __launch_bounds__(kFThreads) void grouped_gemm_flat_kernel(GemmArgs a
         }
         int grp_lo, grp_hi;
         group_rows(g, grp_lo, grp_hi);
-        flat_item<EPI, AM>(args, t, smem, g, q - item_prefix[g], grp_lo, grp_hi);
+        flat_item<EPI, AM, WF>(args, t, smem, g, q - item_prefix[g], grp_lo, grp_hi);
         // every wave is past its last LDS read of this tile before the next
         // tile's prologue writes slot 0, and the claimed id is visible
         __syncthreads();
@@ -540,17 +619,17 @@ __global__ __launch_bounds__(kFThreads) void grouped_gemm_flat_kernel(GemmArgs a
     }
 }
 
-template <int EPI, int AM>
+template <int EPI, int AM, int WF = 0>
 hipError_t launch_flat(const GemmArgs& g, hipStream_t stream) {
     static DeviceSetup setup;
     long long grid = 0, static_lds = 0;
     const hipError_t err = device_setup(setup, grid, static_lds, [](int, long long& gr,
                                                                     long long& st) {
         hipFuncAttributes fa;
-        hipError_t e = hipFuncGetAttributes(&fa, (const void*)grouped_gemm_flat_kernel<EPI, AM>);
+        hipError_t e = hipFuncGetAttributes(&fa, (const void*)grouped_gemm_flat_kernel<EPI, AM, WF>);
         if (e != hipSuccess) return e;
         if (fa.sharedSizeBytes > (size_t)kFStaticLds) return hipErrorInvalidValue;
-        e = hipFuncSetAttribute((const void*)grouped_gemm_flat_kernel<EPI, AM>,
+        e = hipFuncSetAttribute((const void*)grouped_gemm_flat_kernel<EPI, AM, WF>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize,
                                 kFLdsLimit - (int)fa.sharedSizeBytes);
         if (e != hipSuccess) return e;
@@ -561,7 +640,7 @@ hipError_t launch_flat(const GemmArgs& g, hipStream_t stream) {
     if (err != hipSuccess) return err;
     const size_t lds = kLdsFixed + (size_t)(g.G + 1) * sizeof(int);
     if (lds + (size_t)static_lds > (size_t)kFLdsLimit) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((grouped_gemm_flat_kernel<EPI, AM>), dim3((unsigned)grid), dim3(kFThreads),
+    hipLaunchKernelGGL((grouped_gemm_flat_kernel<EPI, AM, WF>), dim3((unsigned)grid), dim3(kFThreads),
                        lds, stream, g);
     return hipGetLastError();
 }
@@ -573,7 +652,23 @@ int grouped_gemm_flat_max_groups() {
 }
 
 hipError_t launch_grouped_gemm_flat(int epilogue, const GemmArgs& g, hipStream_t stream) {
-    if (g.K % FK != 0 || g.G < 1 || g.wfp8) return hipErrorInvalidValue;
+    if (g.K % FK != 0 || g.G < 1) return hipErrorInvalidValue;
+    if (g.wfp8) {
+        // MX weights: the two routed expert GEMMs of moe_forward (gate/up on
+        // gathered token rows, down on the blocked h)
+        if (g.wfp8 != 1 && g.wfp8 != 2) return hipErrorInvalidValue;
+        if (!g.s1 || (epilogue == EPI_SWIGLU_BF16 && !g.s2) || g.out_g) return hipErrorInvalidValue;
+        const bool gu = epilogue == EPI_SWIGLU_BF16 && g.gather && g.out_blocked && !g.a_blocked;
+        const bool dn = epilogue == EPI_F32 && !g.gather && g.a_blocked;
+        if (g.wfp8 == 1) {
+            if (gu) return launch_flat<EPI_SWIGLU_BF16, FA_GATHER, 1>(g, stream);
+            if (dn) return launch_flat<EPI_F32, FA_BLK, 1>(g, stream);
+        } else {
+            if (gu) return launch_flat<EPI_SWIGLU_BF16, FA_GATHER, 2>(g, stream);
+            if (dn) return launch_flat<EPI_F32, FA_BLK, 2>(g, stream);
+        }
+        return hipErrorInvalidValue;
+    }
     if ((g.out_g != nullptr) != (g.out_u != nullptr)) return hipErrorInvalidValue;
     if (g.out_g && epilogue != EPI_SWIGLU_BF16) return hipErrorInvalidValue;
     if (g.gather && g.a_blocked) return hipErrorInvalidValue;

@@ -65,7 +65,6 @@ constexpr int kWideStageRows = 192;
 // off from 129 valid rows; measured 2% faster at the 384-expert workload)
 constexpr int kWideStageRowsFp8 = 128;
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Pipeline of one stage width KB (32 or 64 columns of K per stage).
 //   KB = 32: 4 slots of 32 KB (16 KB activations + 16 KB weights), 3 stages
@@ -333,35 +332,6 @@ struct Operands {
     bf16x8 w0, w1, a[NTB];
 };
 
-// eight E4M3 codes (bytes of v, in order) times the MX block scale sc (a
-// power of two in [2^-110, 2^110]) -> bf16x8.  The products have at most 4
-// significant bits and a normal exponent, so the conversion is exact (on
-// MI355X it gives the upper halves of the exact fp32 products, checked for
-// every code and scales 2^-110 .. 2^110).
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 v, float sc) {
-    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], sc, false);
-    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], sc, true);
-    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], sc, false);
-    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], sc, true);
-    u32x4 r;
-    r[0] = __builtin_bit_cast(uint32_t, p0);
-    r[1] = __builtin_bit_cast(uint32_t, p1);
-    r[2] = __builtin_bit_cast(uint32_t, p2);
-    r[3] = __builtin_bit_cast(uint32_t, p3);
-    return __builtin_bit_cast(bf16x8, r);
-}
-
-// eight E2M1 codes (nibbles of v, low nibble first) times the MX block scale
-// -> bf16x8 (exact: at most 2 significant bits, normal range; checked on
-// MI355X for every byte and scales 2^-110 .. 2^110)
-__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t v, float sc) {
-    u32x4 r;
-    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 0));
-    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 1));
-    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 2));
-    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 3));
-    return __builtin_bit_cast(bf16x8, r);
-}
 
 template <int EPI, int KB, int NTB, int WF>
 __device__ __forceinline__ void read_operands(const LdsTile& t, uint32_t sbase, int q,
