@@ -63,10 +63,10 @@ STAGE_SOURCES = {
     "router_gemm": ("router.hip", "moe_internal.h"),
     "route": ("route.hip", "moe_internal.h"),
     "permute": ("permute.hip", "moe_internal.h"),
-    "gate_up_routed": ("gemm_lds.hip", "moe_internal.h"),
-    "gate_up_shared": ("gemm_lds.hip", "moe_internal.h"),
-    "down_routed": ("gemm_lds.hip", "moe_internal.h"),
-    "down_shared": ("gemm_lds.hip", "moe_internal.h"),
+    "gate_up_routed": ("gemm_flat.hip", "moe_internal.h"),
+    "gate_up_shared": ("gemm_flat.hip", "moe_internal.h"),
+    "down_routed": ("gemm_flat.hip", "moe_internal.h"),
+    "down_shared": ("gemm_flat.hip", "moe_internal.h"),
     "combine": ("combine.hip", "moe_internal.h"),
 }
 
