@@ -12,18 +12,27 @@
 // The contraction runs over each group's rows, the slow index of both inputs.
 // A workgroup (4 waves) computes a 128 (m) x 128 (k) tile of one group's dw,
 // walking the group's rows in chunks of 32:
-//   - a chunk of dy (32 rows x 128 m) and of a (32 rows x 128 k) is copied
-//     row-major into LDS (16-byte coalesced loads; rows past the group end are
-//     zeros), two chunk slots, one barrier per chunk;
+//   - a chunk of dy (32 rows x 128 m) and of a (32 rows x 128 k) is loaded
+//     two chunks ahead into registers (16-byte coalesced loads; rows past the
+//     group end are zeros) and copied row-major into one of two LDS slots,
+//     one barrier per chunk;
 //   - the MFMA operands need 8 consecutive rows of one column per lane
 //     (v_mfma_f32_32x32x16_bf16: operand A = a, so each lane's accumulator
 //     holds 4 consecutive k of one m and the stores are 16 bytes), gathered
 //     with 16-bit LDS reads; LDS rows are padded to 272 bytes, so the two
 //     half-waves (rows 8 apart) read distinct banks;
-//   - wave (wm, wk) owns 64 m x 64 k (2 x 2 accumulators).
+//   - wave (wm, wk) owns 64 m x 64 k (2 x 2 accumulators);
+//   - the fp32 tile (64 KB, as many bytes as the tile reads at 128 rows, so
+//     the writes dominate the traffic) leaves through LDS in two halves of
+//     64 rows: every store instruction writes two whole 512-byte row
+//     segments, non-temporal (the gradient is not read again by this step).
+// Four waves per SIMD (the register budget is capped for it): a tile's
+// chunks are few, so the memory latency is hidden by the other tiles.
 // Grid: one workgroup per (group, m-tile, k-tile), mapped so that each XCD
 // (workgroup id mod 8) takes a contiguous range of tiles: the tiles of one
 // group share that XCD's L2 for their dy and a rows.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -60,7 +69,8 @@ __device__ __forceinline__ bf16x8 gather8(const unsigned char* chunk, int row0, 
     return __builtin_bit_cast(bf16x8, r);
 }
 
-__global__ __launch_bounds__(kWThreads) void grouped_wgrad_kernel(WgradArgs args) {
+__global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void grouped_wgrad_kernel(WgradArgs args) {
     __shared__ __align__(16) unsigned char lds[2 * kWSlot];
     // XCD-contiguous tile order: workgroup b runs on XCD b % 8
     const long long per = (long long)gridDim.x / 8;
@@ -95,35 +105,41 @@ __global__ __launch_bounds__(kWThreads) void grouped_wgrad_kernel(WgradArgs args
     const int sc = tid & 15, sr = tid >> 4;
     const int cm = m0 + 8 * sc, ck = k0 + 8 * sc;
     const bool m_in = cm < M, k_in = ck < K;
-    u32x4 st[2][2];     // [operand: dy, a][row group]
-    auto load_chunk = [&](int r0) {
+    u32x4 st[2][2][2];  // [register set][operand: dy, a][row group]
+    auto load_chunk = [&](int r0, auto set) {
+        constexpr int S = decltype(set)::value;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int r = r0 + sr + 16 * i;
             const bool in = r < hi;
             u32x4 z = {0u, 0u, 0u, 0u};
-            st[0][i] = (in && m_in) ? *(const u32x4*)(args.dy + (size_t)r * args.ld_dy + cm) : z;
-            st[1][i] = (in && k_in) ? *(const u32x4*)(args.a + (size_t)r * args.ld_a + ck) : z;
+            st[S][0][i] = (in && m_in) ? *(const u32x4*)(args.dy + (size_t)r * args.ld_dy + cm) : z;
+            st[S][1][i] = (in && k_in) ? *(const u32x4*)(args.a + (size_t)r * args.ld_a + ck) : z;
         }
     };
-    auto store_chunk = [&](int slot) {
+    auto store_chunk = [&](int slot, auto set) {
+        constexpr int S = decltype(set)::value;
         unsigned char* base = lds + slot * kWSlot;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            *(u32x4*)(base + (sr + 16 * i) * kWRow + sc * 16) = st[0][i];
-            *(u32x4*)(base + kWOperand + (sr + 16 * i) * kWRow + sc * 16) = st[1][i];
+            *(u32x4*)(base + (sr + 16 * i) * kWRow + sc * 16) = st[S][0][i];
+            *(u32x4*)(base + kWOperand + (sr + 16 * i) * kWRow + sc * 16) = st[S][1][i];
         }
     };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
 
+    // chunk c is staged from register set c % 2 into LDS slot c % 2; its
+    // global loads are issued two chunks ahead
     const int nchunks = (hi - lo + WR - 1) / WR;
-    if (nchunks > 0) {
-        load_chunk(lo);
-        store_chunk(0);
-    }
-    for (int c = 0; c < nchunks; ++c) {
+    if (nchunks > 0) load_chunk(lo, I0());
+    if (nchunks > 1) load_chunk(lo + WR, I1());
+    if (nchunks > 0) store_chunk(0, I0());
+    auto step = [&](int c, auto par) {
+        constexpr int P = decltype(par)::value;
         __syncthreads();
-        if (c + 1 < nchunks) load_chunk(lo + (c + 1) * WR);
-        const unsigned char* dyc = lds + (c & 1) * kWSlot;
+        if (c + 2 < nchunks) load_chunk(lo + (c + 2) * WR, par);
+        const unsigned char* dyc = lds + P * kWSlot;
         const unsigned char* ac = dyc + kWOperand;
 #pragma unroll
         for (int s = 0; s < WR / 16; ++s) {
@@ -141,27 +157,51 @@ __global__ __launch_bounds__(kWThreads) void grouped_wgrad_kernel(WgradArgs args
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fd[j], acc[i][j],
                                                                         0, 0, 0);
         }
-        if (c + 1 < nchunks) store_chunk((c + 1) & 1);
+        if (c + 1 < nchunks) store_chunk(P ^ 1, std::integral_constant<int, P ^ 1>());
+    };
+    for (int c = 0; c < nchunks; c += 2) {
+        step(c, I0());
+        if (c + 1 < nchunks) step(c + 1, I1());
     }
 
-    // accumulator element e of lane l: k = 8 (e / 4) + 4 half + e % 4 within
-    // the k block, m = l32 within the m block
+    // output through LDS in two halves of 64 m rows (the chunk slots hold
+    // 64 rows x 128 k fp32): the waves of half wm write their accumulators
+    // (element e of lane l: k = 8 (e / 4) + 4 half + e % 4 of the k block,
+    // m = l32 of the m block), then all 256 threads store whole 512-byte row
+    // segments
     float* out = args.dw + (size_t)g * M * K;
+    constexpr int kORow = WT * 4 + 16;
+    static_assert(64 * kORow <= 2 * kWSlot, "output half fits the chunk slots");
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int m = m0 + 64 * wm + 32 * j + l32;
-        if (m >= M) continue;
+    for (int h = 0; h < 2; ++h) {
+        __syncthreads();
+        if (wm == h) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int k = k0 + 64 * wk + 32 * i + 8 * qq + 4 * half;
-                if (k >= K) continue;
-                f32x4 v;
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * qq + e];
-                *(f32x4*)(out + (size_t)m * K + k) = v;
+                    for (int qq = 0; qq < 4; ++qq) {
+                        f32x4 v;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * qq + e];
+                        const int r = 32 * j + l32;
+                        const int kk = 64 * wk + 32 * i + 8 * qq + 4 * half;
+                        *(f32x4*)(lds + r * kORow + kk * 4) = v;
+                    }
+        }
+        __syncthreads();
+        const int c4 = tid & 31;
+        const int k = k0 + 4 * c4;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int r = 8 * p + (tid >> 5);
+            const int m = m0 + 64 * h + r;
+            if (m < M && k < K) {
+                const f32x4 v = *(const f32x4*)(lds + r * kORow + c4 * 16);
+                __builtin_nontemporal_store(v, (f32x4*)(out + (size_t)m * K + k));
             }
+        }
     }
 }
 
