@@ -16,14 +16,20 @@ CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off",
           "-fopenmp", "-fPIC", "-shared", "-Wall"]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = ["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"]
+# AddressSanitizer + UndefinedBehaviorSanitizer build (tests/test_sanitizers.py)
+SANITIZE = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+            "-fno-omit-frame-pointer"]
+
+
+def build(verbose: bool = False, lib: str = LIB, sanitize: bool = False) -> str:
+    tmp = lib + ".tmp"
+    flags = [f for f in CFLAGS if not (sanitize and f == "-O2")] + (SANITIZE if sanitize else [])
+    cmd = ["gcc", *flags, SRC, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -21,7 +21,9 @@ _LIB = None
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "libmoe_oracle.so")
+    # MOE_ORACLE_LIBRARY: another build of the same source (the sanitizer
+    # build of tests/test_sanitizers.py)
+    return os.environ.get("MOE_ORACLE_LIBRARY", os.path.join(_HERE, "libmoe_oracle.so"))
 
 
 def load():
