@@ -42,6 +42,9 @@ from .oracle import (  # noqa: F401
     layer_backward,
     tokens_forward,
     forward,
+    forward_a8w4,
+    tokens_forward_a8w4,
+    quant_dequant_mxfp8,
     e4m3_decode,
     e4m3_encode,
     quant_mxfp8,

@@ -462,6 +462,80 @@ def forward(x, logits, k, scale, w_gate, w_up, w_down, s_gate=None, s_up=None, s
                 x_perm=x_perm, h=h, y_perm=y_perm, ysh=ysh, y=y, flags=f1 | f2)
 
 
+def quant_dequant_mxfp8(a):
+    """bf16 bits [..., K] -> their MXFP8 values (quantise along K in blocks of
+    32, then dequantise) as bf16 bits; exact (see orc_quant_mxfp8)."""
+    q, x = quant_mxfp8(a)
+    return dequant_mxfp8(q, x)
+
+
+def forward_a8w4(x, logits, k, scale, w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None,
+                 clamp_limit=10.0, clamp_mode=0, bias=None, modality=None, input_ids=None,
+                 tid2eid=None, mode=MODE_TOPK):
+    """Whole layer in the A8W4 reading ("CANN DeepSeek-V4 training
+    optimisation", outlook, functional-expansion bullets: FP8 and A8W4
+    low-precision training on MxFP8 / MxFP4): the routed experts' weights are
+    given as their (dequantised) MXFP4 values and both routed expert matmuls
+    take MXFP8 activations: each token's row of x is quantised along d before
+    gate/up, each row of h (the bf16 SwiGLU output) along F before down.  The
+    router, routing, dispatch, the shared expert (bf16, on x itself) and the
+    combine are those of forward().  Returns forward()'s dict plus x8 (the
+    quantised x, bf16 bits) and h8 (the quantised h)."""
+    x = _bf16(x)
+    E = np.asarray(logits).shape[1]
+    ids, w, f1 = route(logits, k, scale, bias, modality, input_ids, tid2eid, mode)
+    counts, offsets, dest, src, f2 = permute(ids, E)
+    x8 = quant_dequant_mxfp8(x)
+    x_perm = gather(x8, src)
+    h, _ = expert_ffn(x_perm, offsets, w_gate, w_up, w_down, clamp_limit, clamp_mode)
+    h8 = quant_dequant_mxfp8(h)
+    y_perm = grouped_gemm(h8, offsets, w_down)
+    ysh = None
+    if s_gate is not None:
+        T = x.shape[0]
+        _, ysh = expert_ffn(x, np.array([0, T], np.int32), _bf16(s_gate)[None],
+                            _bf16(s_up)[None], _bf16(s_down)[None], clamp_limit, clamp_mode)
+    y = combine(y_perm, dest, w, ysh)
+    return dict(ids=ids, w=w, counts=counts, offsets=offsets, dest=dest, src=src,
+                x_perm=x_perm, x8=x8, h=h, h8=h8, y_perm=y_perm, ysh=ysh, y=y, flags=f1 | f2)
+
+
+def tokens_forward_a8w4(x, tokens, ids, w, w_gate, w_up, w_down, s_gate, s_up, s_down,
+                        clamp_limit, clamp_mode=0):
+    """forward_a8w4's output for the listed tokens from their routing (ids,
+    w): the token's quantised row through each of its k experts, h quantised,
+    the down products combined with the routing weights in slot order in
+    fp64, plus the shared expert on the unquantised row."""
+    x = _bf16(x)
+    tokens = _c(tokens, np.int64)
+    ids = _c(ids, np.int32)
+    w = _c(w, np.float32)
+    n, k = tokens.shape[0], ids.shape[1]
+    E = _bf16(w_gate).shape[0]
+    x8 = quant_dequant_mxfp8(x[tokens])
+    # (token, slot) pairs grouped by expert (valid ids only)
+    pt = np.repeat(np.arange(n), k)
+    pe = ids[tokens].reshape(-1)
+    ok = (pe >= 0) & (pe < E)
+    order = np.argsort(np.where(ok, pe, E), kind="stable")[: int(ok.sum())]
+    counts = np.bincount(pe[order], minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a = x8[pt[order]]
+    h, _ = expert_ffn(a, offsets, w_gate, w_up, w_down, clamp_limit, clamp_mode)
+    yp = grouped_gemm(quant_dequant_mxfp8(h), offsets, w_down)
+    y_pair = np.zeros((n * k, x.shape[1]), np.float64)
+    y_pair[order] = yp
+    wt = np.where(ok, w[tokens].reshape(-1).astype(np.float64), 0.0)
+    y = np.zeros((n, x.shape[1]), np.float64)
+    for j in range(k):
+        y += wt[j::k, None] * y_pair[j::k]
+    if s_gate is not None:
+        _, ysh = expert_ffn(x[tokens], np.array([0, n], np.int32), _bf16(s_gate)[None],
+                            _bf16(s_up)[None], _bf16(s_down)[None], clamp_limit, clamp_mode)
+        y += ysh
+    return y
+
+
 def e4m3_decode(code):
     """Value of an E4M3 code (float; NaN for S.1111.111)."""
     return float(load().orc_e4m3_decode(int(code)))
