@@ -27,12 +27,14 @@ if ROOT not in sys.path:
 
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # FLOP/s, MI355X dense bf16 MFMA
-RIDGE = PEAK_BF16 / PEAK_HBM
+PEAK_FP8 = 5.0e15          # FLOP/s, MI355X dense fp8 MFMA
 
 
-def stage_work(w, n_nonempty, out_bytes=2, wbytes=2):
+def stage_work(w, n_nonempty, out_bytes=2, wbytes=2, abytes=2):
     """Algorithmic (minimum) HBM bytes and FLOPs per stage (wbytes: bytes per
-    routed expert weight; MX weights also read one scale byte per 32)."""
+    routed expert weight; MX weights also read one scale byte per 32; abytes:
+    bytes per routed-GEMM activation, 1 for MXFP8 activations plus one scale
+    byte per 32, whose quantisation of x is part of the permute stage)."""
     T, d, E, k, F, Fs = w.T, w.d, w.E, w.k, w.F, w.Fs
     N = T * k
     hash_mode = w.mode == 1
@@ -44,14 +46,16 @@ def stage_work(w, n_nonempty, out_bytes=2, wbytes=2):
     st["route"] = (route_bytes, 0.0)
     # the forward's permutation writes dest/src only (the routed gate/up GEMM
     # gathers the token rows through src)
-    st["permute"] = (N * 4 + 2 * N * 4, 0.0)
+    a_sc = 1.0 / 32 if abytes < 2 else 0.0
+    st["permute"] = (N * 4 + 2 * N * 4 + (T * d * (2 + 1 + a_sc) if abytes < 2 else 0), 0.0)
     # routed gate/up: weights of the non-empty experts once, every routed row
     # of x once (gathered), h written once
     st["gate_up_routed"] = (n_nonempty * 2 * F * (d * wbytes + (d // 32 if wbytes < 2 else 0)) +
-                            N * d * 2 + N * F * 2, 2.0 * N * d * 2 * F)
+                            N * d * (abytes + a_sc) + N * F * (abytes + a_sc),
+                            2.0 * N * d * 2 * F)
     st["gate_up_shared"] = (2 * Fs * d * 2 + T * d * 2 + T * Fs * 2, 2.0 * T * d * 2 * Fs)
     st["down_routed"] = (n_nonempty * d * (F * wbytes + (F // 32 if wbytes < 2 else 0)) +
-                         N * F * 2 + N * d * 4, 2.0 * N * F * d)
+                         N * F * (abytes + a_sc) + N * d * 4, 2.0 * N * F * d)
     st["down_shared"] = (d * Fs * 2 + T * Fs * 2 + T * d * 4, 2.0 * T * Fs * d)
     st["combine"] = (N * d * 4 + (T * d * 4 if Fs else 0) + N * 8 + T * d * out_bytes, 0.0)
     return st
@@ -185,10 +189,11 @@ def main():
     ap.add_argument("--layout", choices=["packed", "plain"], default="packed",
                     help="weight layout: packed once at load time (moe_pack_weights) or "
                          "the plain [out, in] matrices")
-    ap.add_argument("--weights", choices=["bf16", "fp8", "fp4"], default="bf16",
+    ap.add_argument("--weights", choices=["bf16", "fp8", "fp4", "a8w4"], default="bf16",
                     help="routed expert weights: bf16, MXFP8 (E4M3 codes) or MXFP4 (E2M1 codes), "
                          "one power-of-two scale per 32 values of K (moe_pack_weights_fp8 / "
-                         "_fp4; packed layout only)")
+                         "_fp4; packed layout only); a8w4: MXFP4 weights and MXFP8 "
+                         "activations on the scaled MX matrix cores")
     ap.add_argument("--eager", action="store_true",
                     help="time K eager moe_forward calls instead of K replays of one captured "
                          "forward (HIP graph); the per-stage breakdown comes from eager calls "
@@ -462,12 +467,16 @@ def main():
     counts = torch.bincount(ids.flatten().long(), minlength=w.E).cpu().numpy()
     n_nonempty = int((counts > 0).sum())
     work = stage_work(w, n_nonempty, 4 if out_dtype == ops.OUT_F32 else 2,
-                      wbytes={"bf16": 2, "fp8": 1, "fp4": 0.5}[args.weights])
+                      wbytes={"bf16": 2, "fp8": 1, "fp4": 0.5, "a8w4": 0.5}[args.weights],
+                      abytes=1 if args.weights == "a8w4" else 2)
+    # matrix-core peak of the routed GEMMs: bf16, or fp8 for MXFP8 activations
+    peak_mm = PEAK_FP8 if args.weights == "a8w4" else PEAK_BF16
     stages = {}
     for s, name in enumerate(ops.STAGE_NAMES):
         b, f = work[name]
         t = stage_ms[s] * 1e-3
-        bound = "mfma" if f > 0 and f / b > RIDGE else "hbm"
+        routed = name in ("gate_up_routed", "down_routed")
+        bound = "mfma" if f > 0 and f / b > (peak_mm if routed else PEAK_BF16) / PEAK_HBM else "hbm"
         stages[name] = {"ms": round(float(stage_ms[s]), 4), "GB/s": round(b / t / 1e9, 1) if t else None,
                         "TFLOP/s": round(f / t / 1e12, 1) if t and f else None, "bound": bound}
     dom = max(range(nst), key=lambda s: stage_ms[s])
@@ -475,7 +484,8 @@ def main():
     b, f = work[dname]
     t = stage_ms[dom] * 1e-3
     if stages[dname]["bound"] == "mfma":
-        roof = {"bound": "mfma", "achieved": f / t / 1e12, "peak": PEAK_BF16 / 1e12,
+        pk = peak_mm if dname in ("gate_up_routed", "down_routed") else PEAK_BF16
+        roof = {"bound": "mfma", "achieved": f / t / 1e12, "peak": pk / 1e12,
                 "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": b / t / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
@@ -504,14 +514,16 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8": "bf16 activations, MXFP8 (E4M3) routed weights",
-                  "fp4": "bf16 activations, MXFP4 (E2M1) routed weights"}[args.weights],
+                  "fp4": "bf16 activations, MXFP4 (E2M1) routed weights",
+                  "a8w4": "MXFP8 (E4M3) activations x MXFP4 (E2M1) routed weights on the "
+                          "scaled MX matrix cores; router and shared expert bf16"}[args.weights],
         "data": "synthetic",
         "config": dict(w.describe(), out_dtype=args.out_dtype, weight_layout=args.layout,
                        routed_weights=args.weights, graph=not args.eager,
                        non_empty_experts=n_nonempty,
                        max_rows_per_expert=int(counts.max())),
         "grouped_gemm_tflops": gg_f / gg_t / 1e12,
-        "grouped_gemm_mfma_frac": gg_f / gg_t / PEAK_BF16,
+        "grouped_gemm_mfma_frac": gg_f / gg_t / peak_mm,
         "roofline": roof,
         "stages": stages,
         "route_backward": route_backward,

@@ -209,6 +209,27 @@ int moe_expert_ffn_packed(const uint16_t* a, const int32_t* offsets, int G, int 
                           const uint16_t* w_down, float clamp_limit, int clamp_mode, uint16_t* h,
                           float* y, void* stream);
 
+/* The grouped FFN in the A8W4 mode [CN outlook: A8W4 on MxFP8 / MxFP4] on
+ * the scaled MX matrix cores: activations as MXFP8 (moe_quantize_mxfp8 of
+ * a), weights as MXFP4 (moe_pack_weights_fp4 codes and scales; panel_rows
+ * 128 for w_gate / w_up, 256 for w_down).  For every group g and row r:
+ *   G, U as moe_expert_ffn on the dequantised a8 and weights (exact products,
+ *   fp32 accumulation), clamped; h = bf16(silu(G) U), then h8 / h_scale =
+ *   its MXFP8 quantisation along F (the rule of moe_quantize_mxfp8);
+ *   y[r,o] = sum_f h8~[r,f] w_down~[g,o,f] (fp32), h8~ the dequantised h8.
+ *   a8 [rows,d] uint8 codes + a_scale [rows,d/32] scale bytes; offsets [G+1]
+ *   int32 in DEVICE memory (as moe_expert_ffn); h8 [rows,F] uint8 codes,
+ *   h_scale [rows,F/32] scale bytes, y [rows,d] fp32 (written for rows
+ *   inside a group only).  d, F multiples of 128; a8, h8, y and the weight
+ *   codes 16-byte aligned, the scale arrays 4-byte aligned.  moe_forward
+ *   with MOE_WEIGHTS_A8W4 runs this chain on the routed rows (gathered
+ *   through the dispatch permutation). */
+int moe_expert_ffn_a8w4(const uint8_t* a8, const uint8_t* a_scale, const int32_t* offsets, int G,
+                        int rows, int d, int F, const uint8_t* w_gate, const uint8_t* w_up,
+                        const uint8_t* w_down, const uint8_t* s_gate, const uint8_t* s_up,
+                        const uint8_t* s_down, float clamp_limit, int clamp_mode, uint8_t* h8,
+                        uint8_t* h_scale, float* y, void* stream);
+
 /* ------------------------------------------------------------------------
  * Weight packing (a one-time layout change at weight-load time, not part of
  * the per-step computation).  Rewrites G matrices W[g] of [N,K] bf16 ([out,
@@ -278,6 +299,19 @@ int moe_pack_weights_fp8(const uint16_t* src, int G, int N, int K, int panel_row
 size_t moe_packed_fp4_weight_bytes(int G, int N, int K, int panel_rows);
 int moe_pack_weights_fp4(const uint16_t* src, int G, int N, int K, int panel_rows, uint8_t* dst,
                          uint8_t* scales, void* stream);
+
+/* MXFP8 quantisation of activation rows [CN outlook: A8W4, MxFP8 activations]
+ * (the rule of moe_pack_weights_fp8, along K): for every row of a and block
+ * of 32 consecutive values, X = floor(log2(max |v|)) - 8 clamped to
+ * [-110, 110] (0 for an all-zero block), codes[r, c] = E4M3(a[r, c] / 2^X)
+ * rounded to nearest even and saturated to +-448, scales[r, c / 32] = X + 127.
+ *   a [rows, K] bf16 (16-byte aligned), codes [rows, K] uint8 (16-byte
+ *   aligned), scales [rows, K / 32] uint8; rows >= 0, K > 0 a multiple of 32.
+ * NaN inputs give unspecified codes.  Enqueued on `stream`; the caller owns
+ * every buffer.  MOE_ERR_SHAPE / MOE_ERR_NULL / MOE_ERR_ALIGN on bad
+ * arguments (nothing enqueued). */
+int moe_quantize_mxfp8(const uint16_t* a, long long rows, int K, uint8_t* codes, uint8_t* scales,
+                       void* stream);
 
 /* ------------------------------------------------------------------------
  * Result return merged by routing weight [TW], plus the always-on shared
@@ -390,7 +424,18 @@ typedef struct moe_weights {
                                      w_up, w_down hold moe_pack_weights_fp8
                                      MXFP8 codes (uint8) with the block
                                      scales below; MOE_WEIGHTS_FP4: the same
-                                     with moe_pack_weights_fp4 MXFP4 codes */
+                                     with moe_pack_weights_fp4 MXFP4 codes;
+                                     MOE_WEIGHTS_A8W4: the MXFP4 weights of
+                                     MOE_WEIGHTS_FP4 and MXFP8 activations
+                                     for both routed expert matmuls [CN
+                                     outlook: A8W4 on MxFP8 / MxFP4]: each
+                                     token's row of x is quantised along d
+                                     (as moe_quantize_mxfp8) before gate/up
+                                     and each routed row of h (the bf16
+                                     SwiGLU output) along F before down, on
+                                     the scaled MX matrix cores; d and F
+                                     multiples of 128; the shared expert
+                                     stays bf16 */
     const uint16_t* w_g;          /* [E,d] bf16 router projection */
     const float* logit_offset;    /* [E] fp32 or NULL, added to the logits */
     const float* score_bias;      /* [n_bias,E] fp32 or NULL (TOPK) */
@@ -407,6 +452,7 @@ typedef struct moe_weights {
 } moe_weights;
 #define MOE_WEIGHTS_FP8 2
 #define MOE_WEIGHTS_FP4 3
+#define MOE_WEIGHTS_A8W4 4
 
 /* Workspace for moe_forward (all intermediates: logits, routing, permutation,
  * x_perm, h, y_perm and the shared expert's h and y) [HP 2.3 MegaMoE: one

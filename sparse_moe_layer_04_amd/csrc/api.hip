@@ -85,6 +85,7 @@ inline bool flat_mx_ok(int epi, const GemmArgs& g) {
             (epi == EPI_F32 && !g.gather && g.a_blocked));
 }
 inline hipError_t expert_gemm(int epi, const GemmArgs& g, hipStream_t s) {
+    if (g.wfp8 == 3) return launch_grouped_gemm_flat(epi, g, s);   // A8W4: flat kernel only
     if (MOE_EXPERT_GEMM_FLAT && g.packed && g.G <= grouped_gemm_flat_max_groups() &&
         (!g.wfp8 || flat_mx_ok(epi, g)))
         return launch_grouped_gemm_flat(epi, g, s);
@@ -108,6 +109,9 @@ struct FwdWs {
     float* ys;
     void* perm;
     uint32_t* sched;  // 4 x kSchedWords expert GEMM counters
+    uint8_t* x8;      // A8W4: [T, d] MXFP8 codes of x
+    uint8_t* x8s;     // [T, d / 32] their scale bytes
+    uint8_t* h8s;     // [T k, F / 32] scale bytes of the MXFP8 h (codes in h)
     size_t total;
 };
 
@@ -134,6 +138,9 @@ FwdWs forward_layout(const moe_cfg* c, char* base) {
     w.ys = (float*)take(c->F_shared > 0 ? T * c->d * 4 : 0);
     w.perm = take(permute_workspace_bytes(c->T, c->k, c->E));
     w.sched = (uint32_t*)take(4 * kSchedWords * sizeof(uint32_t));
+    w.x8 = (uint8_t*)take(T * c->d);
+    w.x8s = (uint8_t*)take(T * (c->d / 32));
+    w.h8s = (uint8_t*)take(N * (c->F / 32));
     w.total = off;
     return w;
 }
@@ -467,6 +474,15 @@ int moe_pack_weights_fp4(const uint16_t* src, int G, int N, int K, int panel_row
         launch_pack_weights_fp4(src, dst, scales, G, N, K, panel_rows, as_stream(stream)));
 }
 
+int moe_quantize_mxfp8(const uint16_t* a, long long rows, int K, uint8_t* codes, uint8_t* scales,
+                       void* stream) {
+    if (rows < 0 || K <= 0 || K % 32 || rows * (long long)K >= (1ll << 40)) return MOE_ERR_SHAPE;
+    if (rows == 0) return MOE_OK;
+    if (!a || !codes || !scales) return MOE_ERR_NULL;
+    if (!aligned16(a) || !aligned16(codes)) return MOE_ERR_ALIGN;
+    return hip_status(launch_quant_rows_mxfp8(a, rows, K, codes, scales, as_stream(stream)));
+}
+
 int moe_combine(const float* y_perm, const int32_t* dest, const float* topk_w,
                 const float* y_shared, int T, int d, int k, int rows, int out_dtype, void* y,
                 void* stream) {
@@ -494,6 +510,61 @@ int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* de
         return MOE_ERR_ALIGN;
     return hip_status(launch_combine_backward(dy, y_perm, dest, topk_w, T, d, k, rows, dy_perm,
                                               d_topk_w, as_stream(stream)));
+}
+
+int moe_expert_ffn_a8w4(const uint8_t* a8, const uint8_t* a_scale, const int32_t* offsets, int G,
+                        int rows, int d, int F, const uint8_t* w_gate, const uint8_t* w_up,
+                        const uint8_t* w_down, const uint8_t* s_gate, const uint8_t* s_up,
+                        const uint8_t* s_down, float clamp_limit, int clamp_mode, uint8_t* h8,
+                        uint8_t* h_scale, float* y, void* stream) {
+    if (G < 1) return MOE_ERR_SHAPE;
+    if (G > MOE_MAX_GROUPS || G > grouped_gemm_flat_max_groups()) return MOE_ERR_UNSUPPORTED;
+    int st = ffn_checks(rows, d, F, clamp_limit, clamp_mode);
+    if (st != MOE_OK) return st;
+    if (d % 128 || F % 128) return MOE_ERR_UNSUPPORTED;
+    if (rows == 0) return MOE_OK;
+    if (!a8 || !a_scale || !offsets || !w_gate || !w_up || !w_down || !s_gate || !s_up ||
+        !s_down || !h8 || !h_scale || !y)
+        return MOE_ERR_NULL;
+    if (!aligned16(a8) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+        !aligned16(h8) || !aligned16(y) || ((uintptr_t)a_scale & 3u) || ((uintptr_t)h_scale & 3u))
+        return MOE_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    // no workspace: static schedule (sched = NULL)
+    GemmArgs g1{};
+    g1.a8 = a8;
+    g1.a_scale = a_scale;
+    g1.offsets = offsets;
+    g1.G = G;
+    g1.rows = rows;
+    g1.K = d;
+    g1.N = F;
+    g1.w1 = (const uint16_t*)w_gate;
+    g1.w2 = (const uint16_t*)w_up;
+    g1.s1 = s_gate;
+    g1.s2 = s_up;
+    g1.packed = 1;
+    g1.wfp8 = 3;
+    g1.clamp_limit = clamp_limit;
+    g1.clamp_mode = clamp_mode;
+    g1.out = h8;
+    g1.out_scale = h_scale;
+    hipError_t e = launch_grouped_gemm_flat(EPI_SWIGLU_BF16, g1, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    GemmArgs g2{};
+    g2.a8 = h8;
+    g2.a_scale = h_scale;
+    g2.offsets = offsets;
+    g2.G = G;
+    g2.rows = rows;
+    g2.K = F;
+    g2.N = d;
+    g2.w1 = (const uint16_t*)w_down;
+    g2.s1 = s_down;
+    g2.packed = 1;
+    g2.wfp8 = 3;
+    g2.out = y;
+    return hip_status(launch_grouped_gemm_flat(EPI_F32, g2, s));
 }
 
 int moe_grouped_gemm_packed(const uint16_t* a, const int32_t* offsets, int G, int rows, int K,
@@ -563,9 +634,16 @@ static int forward_checks(const moe_cfg* c, const moe_weights* w) {
     if (c->out_dtype != MOE_OUT_BF16 && c->out_dtype != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
     if (!(c->scale == c->scale)) return MOE_ERR_SHAPE;
     if (w->packed != 0 && w->packed != 1 && w->packed != MOE_WEIGHTS_FP8 &&
-        w->packed != MOE_WEIGHTS_FP4)
+        w->packed != MOE_WEIGHTS_FP4 && w->packed != MOE_WEIGHTS_A8W4)
         return MOE_ERR_UNSUPPORTED;
-    // 8- and 4-bit routed weights run on the LDS-staged expert GEMM only
+    if (w->packed == MOE_WEIGHTS_A8W4) {
+        // the flat expert GEMM on 128-wide K stages
+        if (c->E > grouped_gemm_flat_max_groups() || c->d % 128 || c->F % 128)
+            return MOE_ERR_UNSUPPORTED;
+        return MOE_OK;
+    }
+    // 8- and 4-bit routed weights need the group table of the LDS-staged
+    // expert GEMM (their fallback)
     if (w->packed >= MOE_WEIGHTS_FP8 && !lds_gemm_ok(1, c->E)) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -606,7 +684,10 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     if (!x || !y || !w->w_g || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL;
     if (c->F_shared > 0 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_NULL;
     // routed weight format of the expert GEMMs: 0 bf16, 1 MXFP8, 2 MXFP4
-    const int wfmt = w->packed == MOE_WEIGHTS_FP8 ? 1 : w->packed == MOE_WEIGHTS_FP4 ? 2 : 0;
+    const int wfmt = w->packed == MOE_WEIGHTS_FP8    ? 1
+                     : w->packed == MOE_WEIGHTS_FP4  ? 2
+                     : w->packed == MOE_WEIGHTS_A8W4 ? 3
+                                                     : 0;
     if (wfmt && (!w->w_gate_scale || !w->w_up_scale || !w->w_down_scale)) return MOE_ERR_NULL;
     if (wfmt && (!aligned16(w->w_gate_scale) || !aligned16(w->w_up_scale) ||
                  !aligned16(w->w_down_scale)))
@@ -666,11 +747,15 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     // The LDS-staged expert GEMM gathers the token rows through src (no
     // x_perm copy) and passes h in the blocked layout; the register-direct
     // kernel (plain weights) reads a row-major x_perm.  The permutation's
-    // first kernel also clears the expert GEMMs' scheduling counters.
-    const bool lds = lds_gemm_ok(wpk, E);
+    // first kernel also clears the expert GEMMs' scheduling counters.  A8W4:
+    // the rows of x are quantised to MXFP8 once, and gathered as codes.
+    const bool a8 = wfmt == 3;
+    const bool lds = lds_gemm_ok(wpk, E) && !a8;
     if ((e = launch_permute(ids, x, T, d, E, k, L.counts, L.offsets, L.dest, L.src,
-                            lds ? nullptr : L.x_perm, d_flags, L.perm, s, L.sched,
+                            lds || a8 ? nullptr : L.x_perm, d_flags, L.perm, s, L.sched,
                             4 * kSchedWords)) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (a8 && (e = launch_quant_rows_mxfp8(x, T, d, L.x8, L.x8s, s)) != hipSuccess)
         return MOE_ERR_HIP;
     if (!mark(3)) return MOE_ERR_HIP;
     const int rows = T * k;
@@ -695,6 +780,13 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g1.out = L.h;
     g1.out_blocked = lds;
     g1.sched = L.sched;
+    if (a8) {
+        // MXFP8 x rows through src, h written as MXFP8 codes (in h) + scales
+        g1.gather = L.src;
+        g1.a8 = L.x8;
+        g1.a_scale = L.x8s;
+        g1.out_scale = L.h8s;
+    }
     if ((e = expert_gemm(EPI_SWIGLU_BF16, g1, s)) != hipSuccess) return MOE_ERR_HIP;
     if (!mark(4)) return MOE_ERR_HIP;
     // 5. shared expert gate/up
@@ -730,6 +822,10 @@ int moe_forward_timed(const moe_cfg* c, const moe_weights* w, const uint16_t* x,
     g2.out = L.y_perm;
     g2.a_blocked = lds;
     g2.sched = L.sched + 2 * kSchedWords;
+    if (a8) {
+        g2.a8 = (const uint8_t*)L.h;
+        g2.a_scale = L.h8s;
+    }
     if ((e = expert_gemm(EPI_F32, g2, s)) != hipSuccess) return MOE_ERR_HIP;
     if (!mark(6)) return MOE_ERR_HIP;
     // 7. shared expert down

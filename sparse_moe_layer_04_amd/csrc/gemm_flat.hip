@@ -63,7 +63,11 @@ constexpr int kRingBytes = 2 * kSlotBytes;
 // distinct banks
 constexpr int kEpiRow = FN * 4 + 16;
 constexpr int kEpiBytes = 32 * kEpiRow;
-constexpr int kLdsFixed = kRingBytes + kEpiBytes;
+// A8W4: fp8 activations, 128 K columns per stage (128 bytes per row, the
+// bf16 stage's slot size) and their scale bytes (4 MX blocks per row)
+constexpr int FK8 = 128;
+constexpr int kScaleSlot = FM * 4;
+constexpr int kLdsFixed = kRingBytes + kEpiBytes + 2 * kScaleSlot;
 constexpr int kFLdsLimit = 160 * 1024;
 constexpr int kFStaticLds = 256;
 
@@ -101,6 +105,7 @@ struct FlatTile {
     const uint8_t* sp0;    // block 0 scale byte of this lane's row at K block 0
     const uint8_t* sp1;
     int sstep;             // scale bytes per K block (the panel's rows)
+    size_t s_off;          // A8W4: scale bytes of the activation row this thread stages
 };
 
 template <int NTB>
@@ -419,14 +424,206 @@ __device__ __forceinline__ void flat_tile(const GemmArgs& args, const FlatTile& 
     }
 }
 
+// ---------------------------------------------------------------- A8W4 ----
+// MXFP8 activations x MXFP4 weights on the scaled MX matrix cores
+// (v_mfma_scale_f32_32x32x64_f8f6f4: D[n, t] += sum over 64 K of A[n, k]
+// 2^(sa - 127) B[k, t] 2^(sb - 127), the scales per 32-wide K block).
+// Operand lanes (lane l: row / column l % 32, h = l / 32):
+//   A, E2M1 weights: the 32 values K [32 h, 32 h + 32) of the step, 8 per
+//     dword, low nibble first (dwords 0-3);
+//   B, E4M3 activations: bytes 0-15 are K [16 h, 16 h + 16), bytes 16-31 are
+//     K [32 + 16 h, 32 + 16 h + 16);
+//   scale operand of lane l: the E8M0 scale of K block h of its row / column.
+// The MXFP4 packed weights hold, per K block and 32-row block, 8 bytes for
+// lane l' (row l' % 32): K [8 h', 8 h' + 8) and [16 + 8 h', 16 + 8 h' + 8);
+// lane (n, h) therefore takes the bytes of lanes n and n + 32 of block
+// 4 j + 2 s + h (stage j, step s) and interleaves their dwords into K order.
+// Each output accumulates over ascending 64-wide steps; the accumulator
+// layout is the bf16 kernel's, so the epilogues are shared (SwiGLU writes h
+// as MXFP8 codes and scales for the down projection).
+// activation operands of step s of the stage in `slot` (32 bytes per lane
+// per 32-row block); the scale operands come from one 4-byte word per row
+template <int NTB>
+__device__ __forceinline__ void read_b8(const unsigned char* slot, const FlatTile& t, int s,
+                                        v8i (&b)[NTB]) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+        const int r = tb * 32 + t.l32;
+        const int c1 = (4 * s + t.half) ^ fswz(r), c2 = (4 * s + 2 + t.half) ^ fswz(r);
+        const u32x4 lo = *(const u32x4*)(slot + r * kRowBytes + (c1 << 4));
+        const u32x4 hi = *(const u32x4*)(slot + r * kRowBytes + (c2 << 4));
+        b[tb] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+}
+
+// the 2 x NTB scaled MFMAs of step S: weight scale bytes packed as
+// [block 0 step 0, block 0 step 1, block 1 step 0, block 1 step 1] (byte
+// selected by the operand's byte select), activation scale words shifted so
+// that byte 2 S is this lane's block
+template <int NTB, int S>
+__device__ __forceinline__ void mfma_a8w4(const u32x4& w0, const u32x4& w1, uint32_t ws,
+                                          const v8i (&b)[NTB], const uint32_t (&as)[NTB],
+                                          f32x16 (&acc)[2][FNTB]) {
+    const v8i a0 = {(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], 0, 0, 0, 0};
+    const v8i a1 = {(int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3], 0, 0, 0, 0};
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+        acc[0][tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            a0, b[tb], acc[0][tb], 4, 0, S, (int)ws, 2 * S, (int)as[tb]);
+        acc[1][tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            a1, b[tb], acc[1][tb], 4, 0, 2 + S, (int)ws, 2 * S, (int)as[tb]);
+    }
+}
+
+// SwiGLU epilogue of the A8W4 gate/up GEMM: h = SwiGLU(clamped g, u) rounded
+// to bf16 (as the bf16 path's h), then MXFP8 along the features: the wave's
+// 32 features of a row are one MX block, held by lanes l and l ^ 32.
+template <int NTB>
+__device__ __forceinline__ void flat_epilogue_h8(const GemmArgs& args, const FlatTile& t,
+                                                 const f32x16 (&acc)[2][FNTB]) {
+    const int N = t.N;
+    if (t.n0 >= N) return;                         // (wave-uniform)
+    const float L = args.clamp_limit;
+    uint8_t* out = (uint8_t*)args.out;
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+        float hv[16];
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            float gv = acc[0][tb][e], uv = acc[1][tb][e];
+            gv = args.clamp_mode == MOE_CLAMP_SYMMETRIC ? fclamp_sym(gv, L) : fminf(gv, L);
+            uv = fclamp_sym(uv, L);
+            const float silu = gv / (1.0f + __expf(-gv));
+            hv[e] = bf16_to_f32(f32_to_bf16(silu * uv));
+            amax = fmaxf(amax, fabsf(hv[e]));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const int X = mx8_exponent(amax);
+        const float inv = __builtin_ldexpf(1.0f, -X);
+        const int rl = tb * 32 + t.l32;
+        if (rl >= t.valid) continue;
+        const size_t r = (size_t)(t.row0 + rl);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) word |= e4m3_rne(hv[4 * qq + i] * inv) << (8 * i);
+            *(uint32_t*)(out + r * N + t.n0 + 8 * qq + 4 * t.half) = word;
+        }
+        if (t.half == 0) args.out_scale[r * (N / 32) + t.n0 / 32] = (uint8_t)(X + 127);
+    }
+}
+
+// K loop and epilogue of one A8W4 tile: 128-wide stages, one barrier each;
+// per stage and wave two 64-wide steps of 2 x NTB scaled MFMAs.  The
+// activation codes (and scale words) of stage j + 2 are loaded during stage
+// j and written to LDS at the end of stage j + 1; the weights of stage j + 2
+// are loaded into the register set of stage j right after its MFMAs.
+template <int EPI, int AM, int NTB>
+__device__ __forceinline__ void flat_tile_a8(const GemmArgs& args, const FlatTile& t,
+                                             unsigned char* ring) {
+    f32x16 acc[2][FNTB];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int tb = 0; tb < FNTB; ++tb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[b][tb][i] = 0.0f;
+    const int S = t.K / FK8;
+    const uint8_t* a8 = args.a8;
+    unsigned char* sring = ring + kRingBytes + kEpiBytes;
+
+    u32x4 wq[2][2][2];       // [set][step][block]
+    uint32_t wsc[2];         // [set]: scale bytes (block 0 step 0, 0 1, 1 0, 1 1)
+    auto load_w = [&](int j, auto set) {
+        constexpr int W = decltype(set)::value;
+        const int jj = min(j, S - 1);
+        uint32_t sc = 0;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const size_t kb = (size_t)(4 * jj + 2 * s);
+            const size_t off = kb * t.cstage;
+            const u32x2 o0 = *(const u32x2*)(t.cp0 + off), p0 = *(const u32x2*)(t.cp0 + off + 256);
+            const u32x2 o1 = *(const u32x2*)(t.cp1 + off), p1 = *(const u32x2*)(t.cp1 + off + 256);
+            wq[W][s][0] = u32x4{o0[0], p0[0], o0[1], p0[1]};
+            wq[W][s][1] = u32x4{o1[0], p1[0], o1[1], p1[1]};
+            sc |= (uint32_t)t.sp0[kb * t.sstep] << (8 * s);
+            sc |= (uint32_t)t.sp1[kb * t.sstep] << (8 * (2 + s));
+        }
+        wsc[W] = sc;
+    };
+    u32x4 areg[2][2];
+    uint32_t sreg[2];
+    auto load_a = [&](int j, u32x4 (&d)[2], uint32_t& sd) {
+        const size_t jj = (size_t)min(j, S - 1);
+        if (t.a_rows > 0) d[0] = *(const u32x4*)(a8 + t.a_off[0] + jj * FK8);
+        if (t.a_rows > 1) d[1] = *(const u32x4*)(a8 + t.a_off[1] + jj * FK8);
+        if (t.tid < FM) sd = *(const uint32_t*)(args.a_scale + t.s_off + 4 * jj);
+    };
+    auto store_a = [&](int j, const u32x4 (&d)[2], uint32_t sd) {
+        unsigned char* slot = ring + (j & 1) * kSlotBytes;
+        const int c = t.tid & 7;
+        const int r0 = t.tid >> 3;
+        if (t.a_rows > 0) *(u32x4*)(slot + r0 * kRowBytes + ((c ^ fswz(r0)) << 4)) = d[0];
+        if (t.a_rows > 1) {
+            const int r1 = r0 + 64;
+            *(u32x4*)(slot + r1 * kRowBytes + ((c ^ fswz(r1)) << 4)) = d[1];
+        }
+        if (t.tid < FM) *(uint32_t*)(sring + (j & 1) * kScaleSlot + t.tid * 4) = sd;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    load_w(0, I0());
+    load_w(1, I1());
+    load_a(0, areg[0], sreg[0]);
+    load_a(1, areg[1], sreg[1]);
+    store_a(0, areg[0], sreg[0]);
+
+    v8i b[NTB];
+    uint32_t as[NTB];
+    auto stage = [&](int j, auto par) {
+        constexpr int P = decltype(par)::value;   // j % 2
+        __syncthreads();
+        const unsigned char* slot = ring + P * kSlotBytes;
+        const unsigned char* sslot = sring + P * kScaleSlot;
+        load_a(j + 2, areg[P], sreg[P]);
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+            as[tb] = *(const uint32_t*)(sslot + (tb * 32 + t.l32) * 4) >> (8 * t.half);
+        read_b8<NTB>(slot, t, 0, b);
+        mfma_a8w4<NTB, 0>(wq[P][0][0], wq[P][0][1], wsc[P], b, as, acc);
+        read_b8<NTB>(slot, t, 1, b);
+        mfma_a8w4<NTB, 1>(wq[P][1][0], wq[P][1][1], wsc[P], b, as, acc);
+        load_w(j + 2, par);
+        if (j + 1 < S) store_a(j + 1, areg[P ^ 1], sreg[P ^ 1]);
+    };
+    for (int j = 0; j < S; j += 2) {
+        stage(j, I0());
+        if (j + 1 < S) stage(j + 1, I1());
+    }
+    if constexpr (EPI == EPI_F32) {
+        flat_epilogue_f32<NTB>(args, t, acc, ring + kRingBytes);
+    } else {
+        flat_epilogue_h8<NTB>(args, t, acc);
+    }
+}
+
 template <int EPI, int AM, int NT, int WF>
 __device__ __forceinline__ void flat_tile_ntb(const GemmArgs& args, const FlatTile& t,
                                               unsigned char* ring) {
     if constexpr (NT == 1) {
-        flat_tile<EPI, AM, 1, WF>(args, t, ring);
+        if constexpr (WF == 3) flat_tile_a8<EPI, AM, 1>(args, t, ring);
+        else flat_tile<EPI, AM, 1, WF>(args, t, ring);
     } else {
-        if (t.ntb >= NT) flat_tile<EPI, AM, NT, WF>(args, t, ring);
-        else flat_tile_ntb<EPI, AM, NT - 1, WF>(args, t, ring);
+        if (t.ntb >= NT) {
+            if constexpr (WF == 3) flat_tile_a8<EPI, AM, NT>(args, t, ring);
+            else flat_tile<EPI, AM, NT, WF>(args, t, ring);
+        } else {
+            flat_tile_ntb<EPI, AM, NT - 1, WF>(args, t, ring);
+        }
     }
 }
 
@@ -474,7 +671,7 @@ __device__ __forceinline__ void flat_item(const GemmArgs& args, FlatTile& t, uns
     if constexpr (WF) {
         // MX codes: fp8 [panel][K/64][P/32][2 chunks][64 lanes][16 B]; fp4
         // [panel][K/32][P/32][64 lanes][8 B]; scales [panel][K/32][P/32][32]
-        const size_t pstride_b = (size_t)Pn::P * t.K / (WF == 2 ? 2 : 1);
+        const size_t pstride_b = (size_t)Pn::P * t.K / (WF >= 2 ? 2 : 1);
         const size_t ebase_b = (size_t)g * np * pstride_b;
         const uint8_t* c0 = (const uint8_t*)args.w1 + ebase_b;
         const uint8_t* c1 =
@@ -482,13 +679,18 @@ __device__ __forceinline__ void flat_item(const GemmArgs& args, FlatTile& t, uns
         const size_t bsz = WF == 1 ? 2048 : 512;        // bytes per block per stage / K block
         const size_t lsz = WF == 1 ? 16 : 8;            // bytes per lane
         t.cstage = (size_t)Pn::BPP * bsz;
-        t.cp0 = c0 + (size_t)p0 * pstride_b + (size_t)(blk0 % Pn::BPP) * bsz + t.lane * lsz;
-        t.cp1 = c1 + (size_t)p1 * pstride_b + (size_t)(blk1 % Pn::BPP) * bsz + t.lane * lsz;
+        // (A8W4: lane (n, h) reads the bytes of lanes n and n + 32 of K block
+        // 2 s' + h, so the lane offset is n's and block h is folded in)
+        const size_t lane_b = WF == 3 ? (size_t)t.l32 * lsz + (size_t)t.half * t.cstage
+                                      : (size_t)t.lane * lsz;
+        t.cp0 = c0 + (size_t)p0 * pstride_b + (size_t)(blk0 % Pn::BPP) * bsz + lane_b;
+        t.cp1 = c1 + (size_t)p1 * pstride_b + (size_t)(blk1 % Pn::BPP) * bsz + lane_b;
         const size_t sstride = (size_t)(t.K / 32) * Pn::P;
         const uint8_t* s0 = args.s1 + (size_t)g * np * sstride;
         const uint8_t* s1 = (EPI == EPI_SWIGLU_BF16 ? args.s2 : args.s1) + (size_t)g * np * sstride;
-        t.sp0 = s0 + (size_t)p0 * sstride + (size_t)(blk0 % Pn::BPP) * 32 + t.l32;
-        t.sp1 = s1 + (size_t)p1 * sstride + (size_t)(blk1 % Pn::BPP) * 32 + t.l32;
+        const size_t lane_s = (size_t)t.l32 + (WF == 3 ? (size_t)t.half * Pn::P : 0);
+        t.sp0 = s0 + (size_t)p0 * sstride + (size_t)(blk0 % Pn::BPP) * 32 + lane_s;
+        t.sp1 = s1 + (size_t)p1 * sstride + (size_t)(blk1 % Pn::BPP) * 32 + lane_s;
         t.sstep = Pn::P;
     }
     // activation staging: thread tid copies 16 B chunk (tid % 8) of rows
@@ -502,10 +704,24 @@ __device__ __forceinline__ void flat_item(const GemmArgs& args, FlatTile& t, uns
     for (int i = 0; i < 2; ++i) {
         const size_t grow = (size_t)(t.row0 + min(r0 + 64 * i, t.valid - 1));
         size_t e;
-        if (AM == FA_BLK) e = blocked_index(grow, c * 8, t.K);
-        else if (AM == FA_GATHER) e = (size_t)args.gather[grow] * t.K + c * 8;
-        else e = grow * t.K + c * 8;
+        if constexpr (WF == 3) {
+            // fp8 codes: bytes, 16 per chunk
+            const size_t src = AM == FA_GATHER ? (size_t)args.gather[grow] : grow;
+            e = src * t.K + c * 16;
+        } else if (AM == FA_BLK) {
+            e = blocked_index(grow, c * 8, t.K);
+        } else if (AM == FA_GATHER) {
+            e = (size_t)args.gather[grow] * t.K + c * 8;
+        } else {
+            e = grow * t.K + c * 8;
+        }
         t.a_off[i] = e;
+    }
+    if constexpr (WF == 3) {
+        // scale bytes of tile row tid (threads 0 .. FM - 1)
+        const size_t grow = (size_t)(t.row0 + min(t.tid, t.valid - 1));
+        const size_t src = AM == FA_GATHER ? (size_t)args.gather[grow] : grow;
+        t.s_off = src * (size_t)(t.K / 32);
     }
     // per 64-wide stage: two 32-column blocks (blocked) or 64 elements
     t.a_step = AM == FA_BLK ? 1024 : FK;
@@ -653,6 +869,18 @@ int grouped_gemm_flat_max_groups() {
 
 hipError_t launch_grouped_gemm_flat(int epilogue, const GemmArgs& g, hipStream_t stream) {
     if (g.K % FK != 0 || g.G < 1) return hipErrorInvalidValue;
+    if (g.wfp8 == 3) {
+        // A8W4: gate/up on MXFP8 rows (gathered or row-major) into MXFP8 h,
+        // down on row-major MXFP8 h; MXFP4 weights
+        if (g.K % FK8 || !g.a8 || !g.a_scale || !g.s1 || g.out_g || g.a_blocked ||
+            g.out_blocked)
+            return hipErrorInvalidValue;
+        if (epilogue == EPI_SWIGLU_BF16 && g.s2 && g.out_scale && g.N % 32 == 0)
+            return g.gather ? launch_flat<EPI_SWIGLU_BF16, FA_GATHER, 3>(g, stream)
+                            : launch_flat<EPI_SWIGLU_BF16, FA_ROW, 3>(g, stream);
+        if (epilogue == EPI_F32 && !g.gather) return launch_flat<EPI_F32, FA_ROW, 3>(g, stream);
+        return hipErrorInvalidValue;
+    }
     if (g.wfp8) {
         // MX weights: the two routed expert GEMMs of moe_forward (gate/up on
         // gathered token rows, down on the blocked h)

@@ -17,6 +17,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 
 // fp32 -> bf16 bits, round to nearest even (quiet NaN kept NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
@@ -100,6 +101,37 @@ enum GemmEpilogue : int {
     EPI_F32_OFFSET = 2,   // out = fp32(A W1^T + offset[n])
 };
 
+// OCP E4M3 code of a finite v: round to nearest, ties to even, saturating
+// at +-448 (subnormal codes below 2^-6, spacing 2^-9)
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    const float a = fabsf(v);
+    if (a >= 448.0f) return sign | 0x7eu;
+    if (a < 0x1p-6f) {
+        const float m = __builtin_rintf(a * 512.0f);   // exact product; 0 .. 8
+        return sign | (uint32_t)m;                     // 8 = code 0x08, the smallest normal
+    }
+    const uint32_t ua = __float_as_uint(a);
+    int E = (int)(ua >> 23) - 127;
+    const uint32_t mant = ua & 0x7fffffu;
+    uint32_t r = (mant + 0x7ffffu + ((mant >> 20) & 1u)) >> 20;   // 3 bits, ties to even
+    if (r == 8u) {
+        r = 0u;
+        E += 1;
+    }
+    if (E > 8 || (E == 8 && r > 6u)) return sign | 0x7eu;
+    return sign | ((uint32_t)(E + 7) << 3) | r;
+}
+
+// MXFP8 block exponent X = floor(log2 amax) - 8 clamped to [-110, 110], 0
+// for an all-zero block (the scale byte is X + 127).  floor(log2) from the
+// exponent field: a subnormal amax is below 2^-126 and clamps anyway.
+__device__ __forceinline__ int mx8_exponent(float amax) {
+    if (!(amax > 0.0f)) return 0;
+    const int e = (int)((__float_as_uint(amax) >> 23) & 0xff) - 127;
+    return min(max(e - 8, -110), 110);
+}
+
 struct GemmArgs {
     const uint16_t* a;        // [rows, K] bf16 activations ([a_rows, K] when gathered)
     const int32_t* offsets;   // [G+1] device group row offsets, or NULL: one group [0, rows)
@@ -126,6 +158,11 @@ struct GemmArgs {
     const uint8_t* s2;        // MXFP8 block scale bytes of w2 (SWIGLU)
     float* out_g;             // flat kernel, SWIGLU: [rows, N] fp32 gate pre-activations
     float* out_u;             // ... and up pre-activations (both or neither; NULL: not saved)
+    // A8W4 (wfp8 == 3, flat kernel): MXFP8 activations and MXFP4 weights
+    const uint8_t* a8;        // [rows (a_rows when gathered), K] E4M3 codes
+    const uint8_t* a_scale;   // [.., K / 32] block scale bytes X + 127 of a8
+    uint8_t* out_scale;       // SWIGLU: out is [rows, N] E4M3 codes of h, these its
+                              // [rows, N / 32] scale bytes
 };
 // per-launch scheduling counters of the LDS-staged expert GEMM
 constexpr int kSchedWords = 8 * 32;
@@ -167,6 +204,10 @@ hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int G, int N,
 // MXFP8 expert weights (E4M3 codes, one power-of-two scale per 32 values of K)
 size_t packed_fp8_weight_bytes(int G, int N, int K, int P);
 size_t packed_fp8_scale_bytes(int G, int N, int K, int P);
+// MXFP8 quantisation of bf16 rows [rows, K] (K multiple of 32): E4M3 codes
+// [rows, K] and scale bytes X + 127 [rows, K / 32]
+hipError_t launch_quant_rows_mxfp8(const uint16_t* a, long long rows, int K, uint8_t* codes,
+                                   uint8_t* scales, hipStream_t stream);
 hipError_t launch_pack_weights_fp8(const uint16_t* src, uint8_t* dst, uint8_t* scales, int G,
                                    int N, int K, int P, hipStream_t stream);
 // MXFP4 expert weights (E2M1 codes, two per byte; the same scale layout)

@@ -27,29 +27,7 @@
 namespace moe {
 namespace {
 
-constexpr float kE4M3Max = 448.0f;
 constexpr int kMaxExp = 110;
-
-// E4M3 code of a finite v, round to nearest even, saturating
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-    const float a = fabsf(v);
-    if (a >= kE4M3Max) return sign | 0x7eu;
-    if (a < 0x1p-6f) {                          // subnormal codes, spacing 2^-9
-        const float m = __builtin_rintf(a * 512.0f);   // exact product; 0 .. 8
-        return sign | (uint32_t)m;              // 8 = code 0x08, the smallest normal
-    }
-    const uint32_t ua = __float_as_uint(a);
-    int E = (int)(ua >> 23) - 127;
-    const uint32_t mant = ua & 0x7fffffu;
-    uint32_t r = (mant + 0x7ffffu + ((mant >> 20) & 1u)) >> 20;   // 3 bits, ties to even
-    if (r == 8u) {
-        r = 0u;
-        E += 1;
-    }
-    if (E > 8 || (E == 8 && r > 6u)) return sign | 0x7eu;
-    return sign | ((uint32_t)(E + 7) << 3) | r;
-}
 
 // One thread per 16-byte chunk of codes (16 values of one MX block of one
 // row): block exponent from all 32 values of the block, then its 16 codes;
@@ -88,12 +66,7 @@ __global__ __launch_bounds__(256) void mxfp8_pack_kernel(const uint16_t* __restr
                 amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xffff0000u)));
             }
         }
-        if (amax > 0.0f) {
-            // floor(log2(amax)) from the exponent field (subnormal amax is
-            // below 2^-126 and clamps to -110 anyway)
-            const int e = (int)((__float_as_uint(amax) >> 23) & 0xff) - 127;
-            X = min(max(e - 8, -kMaxExp), kMaxExp);
-        }
+        X = mx8_exponent(amax);
         const float inv = __builtin_ldexpf(1.0f, -X);   // exact power of two
         const uint16_t* rp = bp + 8 * (lane >> 5);
 #pragma unroll
@@ -187,7 +160,60 @@ __global__ __launch_bounds__(256) void mxfp4_pack_kernel(const uint16_t* __restr
     scales[((g * np + panel) * KB + kb) * (long long)P + b * 32 + r] = (uint8_t)(X + 127);
 }
 
+// MXFP8 quantisation of activation rows (the A8W4 mode's x): one thread per
+// MX block of 32 values of one row, 64 bytes in (four 16-byte loads), 32
+// codes and one scale byte out.
+__global__ __launch_bounds__(256) void mxfp8_rows_kernel(const uint16_t* __restrict__ a,
+                                                         uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales,
+                                                         long long nblocks) {
+    const long long b = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (b >= nblocks) return;
+    const uint16_t* bp = a + b * 32;
+    u32x4 w[4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        w[v] = *(const u32x4*)(bp + 8 * v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            amax = fmaxf(amax, fabsf(__uint_as_float(w[v][i] << 16)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(w[v][i] & 0xffff0000u)));
+        }
+    }
+    const int X = mx8_exponent(amax);
+    const float inv = __builtin_ldexpf(1.0f, -X);       // exact power of two
+    u32x4 out[2];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+            // elements 8 v + 2 i .. 8 v + 2 i + 3: one 32-bit word of codes
+            uint32_t word = 0;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const uint32_t lo = e4m3_rne(__uint_as_float(w[v][i + u] << 16) * inv);
+                const uint32_t hi = e4m3_rne(__uint_as_float(w[v][i + u] & 0xffff0000u) * inv);
+                word |= (lo | (hi << 8)) << (16 * u);
+            }
+            out[v >> 1][2 * (v & 1) + (i >> 1)] = word;
+        }
+    *(u32x4*)(codes + b * 32) = out[0];
+    *(u32x4*)(codes + b * 32 + 16) = out[1];
+    scales[b] = (uint8_t)(X + 127);
+}
+
 }  // namespace
+
+hipError_t launch_quant_rows_mxfp8(const uint16_t* a, long long rows, int K, uint8_t* codes,
+                                   uint8_t* scales, hipStream_t stream) {
+    if (rows < 0 || K % 32) return hipErrorInvalidValue;
+    const long long nblocks = rows * (K / 32);
+    if (nblocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(mxfp8_rows_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0,
+                       stream, a, codes, scales, nblocks);
+    return hipGetLastError();
+}
 
 size_t packed_fp8_weight_bytes(int G, int N, int K, int P) {
     return (size_t)G * (size_t)((N + P - 1) / P) * P * (size_t)K;

@@ -49,6 +49,7 @@ WEIGHT_NAMES = ("w_g", "logit_offset", "score_bias", "tid2eid", "w_gate", "w_up"
 # moe_weights.packed values of MXFP8 / MXFP4 routed-expert weights
 WEIGHTS_FP8 = 2
 WEIGHTS_FP4 = 3
+WEIGHTS_A8W4 = 4
 MATRIX_NAMES = ("w_g", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")
 
 
@@ -112,6 +113,8 @@ def lib():
     L.moe_packed_fp4_weight_bytes.argtypes = [I, I, I, I]
     L.moe_packed_fp4_weight_bytes.restype = S
     L.moe_pack_weights_fp4.argtypes = [P, I, I, I, I, P, P, P]
+    L.moe_quantize_mxfp8.argtypes = [P, ctypes.c_longlong, I, P, P, P]
+    L.moe_expert_ffn_a8w4.argtypes = [P, P, P, I, I, I, I, P, P, P, P, P, P, F, I, P, P, P, P]
     L.moe_forward_workspace_size.argtypes = [ctypes.POINTER(MoeCfg)]
     L.moe_forward_workspace_size.restype = S
     L.moe_workspace_size.argtypes = [ctypes.POINTER(MoeCfg)]
@@ -128,7 +131,8 @@ def lib():
     for name in ("moe_gate_logits", "moe_route", "moe_permute", "moe_expert_ffn",
                  "moe_expert_ffn_packed",
                  "moe_combine", "moe_forward", "moe_forward_timed", "moe_pack_weights",
-                 "moe_pack_weights_fp8", "moe_pack_weights_fp4"):
+                 "moe_pack_weights_fp8", "moe_pack_weights_fp4", "moe_quantize_mxfp8",
+                 "moe_expert_ffn_a8w4"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -472,6 +476,40 @@ def pack_weights_fp8(w, panel_rows):
     return codes, scales
 
 
+def quantize_mxfp8(a, codes=None, scales=None):
+    """MXFP8 quantisation of bf16 rows a [rows, K] along K (moe_quantize_mxfp8):
+    returns (codes uint8 [rows, K], scale bytes X + 127 uint8 [rows, K/32])."""
+    _need(a, torch.bfloat16, "a", 2)
+    rows, K = a.shape
+    codes = _out(codes, torch.uint8, "codes", (rows, K), a.device)
+    scales = _out(scales, torch.uint8, "scales", (rows, K // 32), a.device)
+    _check(lib().moe_quantize_mxfp8(_ptr(a), rows, K, _ptr(codes), _ptr(scales), _stream()),
+           "moe_quantize_mxfp8")
+    return codes, scales
+
+
+def expert_ffn_a8w4(a8, a_scale, offsets, w_gate, w_up, w_down, G, F, clamp_limit=10.0,
+                    clamp_mode=CLAMP_SYMMETRIC):
+    """Grouped FFN in the A8W4 mode (moe_expert_ffn_a8w4): a8 / a_scale from
+    quantize_mxfp8, w_* = (codes, scales) pairs from pack_weights_fp4
+    (panel rows 128, 128, 256).  Returns (h8 uint8 [rows, F], h_scale uint8
+    [rows, F/32], y fp32 [rows, d])."""
+    _need(a8, torch.uint8, "a8", 2)
+    rows, d = a8.shape
+    _need(a_scale, torch.uint8, "a_scale", shape=(rows, d // 32))
+    _need(offsets, torch.int32, "offsets", shape=(G + 1,))
+    dev = a8.device
+    h8 = torch.empty((rows, F), dtype=torch.uint8, device=dev)
+    hs = torch.empty((rows, F // 32), dtype=torch.uint8, device=dev)
+    y = torch.zeros((rows, d), dtype=torch.float32, device=dev)
+    (cg, sg), (cu, su), (cd, sd) = w_gate, w_up, w_down
+    _check(lib().moe_expert_ffn_a8w4(_ptr(a8), _ptr(a_scale), _ptr(offsets), G, rows, d, F,
+                                     _ptr(cg), _ptr(cu), _ptr(cd), _ptr(sg), _ptr(su), _ptr(sd),
+                                     float(clamp_limit), int(clamp_mode), _ptr(h8), _ptr(hs),
+                                     _ptr(y), _stream()), "moe_expert_ffn_a8w4")
+    return h8, hs, y
+
+
 def pack_weights_fp4(w, panel_rows):
     """MXFP4 copy (moe_pack_weights_fp4: E2M1 codes in the packed layout, one
     power-of-two scale per 32 values of K) of bf16 weights [G,N,K] or [N,K];
@@ -518,11 +556,13 @@ class MoeLayer:
         if mode == MODE_HASH:
             _need(self.weights.get("tid2eid"), torch.int32, "tid2eid", shape=(V, k))
         fp8 = packed == "fp8"
-        fp4 = packed == "fp4"
+        a8w4 = packed == "a8w4"
+        fp4 = packed == "fp4" or a8w4
         if packed:
             # one-time layout change at load time (moe_pack_weights; with
             # packed="fp8" / "fp4" the routed expert matrices are quantised to
-            # MXFP8 / MXFP4 by moe_pack_weights_fp8 / _fp4 instead)
+            # MXFP8 / MXFP4 by moe_pack_weights_fp8 / _fp4 instead; "a8w4":
+            # MXFP4 weights and MXFP8 activations)
             for key in MATRIX_NAMES:
                 if self.weights.get(key) is None:
                     continue
@@ -532,7 +572,8 @@ class MoeLayer:
                         self.weights[key], PANEL_ROWS[key])
                 else:
                     self.weights[key] = pack_weights(self.weights[key], PANEL_ROWS[key])
-        self.packed = WEIGHTS_FP8 if fp8 else WEIGHTS_FP4 if fp4 else int(bool(packed))
+        self.packed = (WEIGHTS_FP8 if fp8 else WEIGHTS_A8W4 if a8w4 else WEIGHTS_FP4 if fp4
+                       else int(bool(packed)))
         self.cw = MoeWeights(packed=self.packed,
                              **{n: _ptr(self.weights.get(n)) for n in WEIGHT_NAMES})
         self.device = self.weights["w_g"].device

@@ -140,6 +140,32 @@ def test_pack_validation(L):
     assert L.moe_pack_weights_fp8(FAKE, 1, 8, 128, 256, FAKE + 2, FAKE, None) == ERR_ALIGN
 
 
+def test_quantize_mxfp8_validation(L):
+    assert L.moe_quantize_mxfp8(FAKE, 4, 48, FAKE, FAKE, None) == ERR_SHAPE      # K % 32
+    assert L.moe_quantize_mxfp8(FAKE, -1, 64, FAKE, FAKE, None) == ERR_SHAPE
+    assert L.moe_quantize_mxfp8(FAKE, 4, 0, FAKE, FAKE, None) == ERR_SHAPE
+    assert L.moe_quantize_mxfp8(FAKE, 1 << 35, 64, FAKE, FAKE, None) == ERR_SHAPE
+    assert L.moe_quantize_mxfp8(None, 4, 64, FAKE, FAKE, None) == ERR_NULL
+    assert L.moe_quantize_mxfp8(FAKE, 4, 64, FAKE, None, None) == ERR_NULL
+    assert L.moe_quantize_mxfp8(FAKE + 2, 4, 64, FAKE, FAKE, None) == ERR_ALIGN
+    assert L.moe_quantize_mxfp8(FAKE, 4, 64, FAKE + 8, FAKE, None) == ERR_ALIGN
+    assert L.moe_quantize_mxfp8(None, 0, 64, None, None, None) == 0            # nothing to do
+
+
+def test_expert_ffn_a8w4_validation(L):
+    def call(G=2, rows=8, d=128, F=128, a8=FAKE, y=FAKE, hs=FAKE):
+        return L.moe_expert_ffn_a8w4(a8, FAKE, FAKE, G, rows, d, F, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, 10.0, 0, FAKE, hs, y, None)
+    assert call(G=0) == ERR_SHAPE
+    assert call(d=64) == ERR_UNSUPPORTED                # d and F multiples of 128
+    assert call(F=192) == ERR_UNSUPPORTED
+    assert call(G=1 << 20) == ERR_UNSUPPORTED
+    assert call(a8=None) == ERR_NULL
+    assert call(y=FAKE + 4) == ERR_ALIGN
+    assert call(hs=FAKE + 2) == ERR_ALIGN
+    assert call(rows=0, a8=None) == 0
+
+
 def test_combine_validation(L):
     def comb(T=4, d=64, k=2, rows=8, out=0, yp=FAKE, y=FAKE):
         return L.moe_combine(yp, FAKE, FAKE, None, T, d, k, rows, out, y, None)
@@ -222,8 +248,14 @@ def test_forward_validation(L):
         setattr(c, field, val)
         assert fwd(c=c) == code, field
     wp = ops.MoeWeights.from_buffer_copy(w)
-    wp.packed = 4
+    wp.packed = 5
     assert fwd(wt=wp) == ERR_UNSUPPORTED
+    wp.packed = ops.WEIGHTS_A8W4                     # A8W4 needs d and F multiples of 128
+    assert fwd(wt=wp) == ERR_UNSUPPORTED
+    c8 = ops.MoeCfg.from_buffer_copy(cfg)
+    c8.F = 128
+    need8 = L.moe_forward_workspace_size(ctypes.byref(c8))
+    assert fwd(c=c8, wt=wp, wsb=need8) == ERR_NULL   # ... and the MXFP4 block scales
     wp.packed = ops.WEIGHTS_FP4                      # MXFP4 weights need their block scales
     assert fwd(wt=wp) == ERR_NULL
     wp.packed = ops.WEIGHTS_FP8                      # MXFP8 weights need their block scales

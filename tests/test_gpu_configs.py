@@ -12,8 +12,9 @@ weights, one moe_forward call):
   - the layer output (fp32 mode) within 1e-2 x RMS of the oracle: every
     token of the 64-expert layer; at the larger ones a token set that covers
     every non-empty expert and, for every m-tile of the expert GEMMs, its
-    first and last row and the rows on both sides of its wave-half split
-    (plus the shared expert's tile boundaries and a seeded random sample);
+    first and last row and the rows on both sides of each 32-row block
+    boundary (plus the shared expert's tile boundaries and a seeded random
+    sample);
     the bf16 output within one bf16 rounding of that bound.
 Near-ties (k-th vs (k+1)-th biased score gap below 1e-6) are counted and
 printed (they are bit-exact here because both sides use the same logits).
@@ -41,34 +42,31 @@ def _opt(inp, key):
     return None if inp[key] is None else host(inp[key])
 
 
-TM = 256   # activation rows per expert-GEMM tile
+FM = 128   # activation rows per expert-GEMM tile
 
 
-def _bf16_tile_split(n):
-    """Rows per m-tile of an expert with n rows for bf16 weights: TM (the
-    last tile shorter)."""
-    return TM
+def flat_tile_split(n):
+    """Rows per m-tile of an expert with n rows in the expert GEMM (every
+    weight mode): the rows split evenly over ceil(n / 128) tiles, rounded up
+    to 32."""
+    mt = -(-n // FM)
+    return (-(-n // mt) + 31) & ~31
 
 
-def _mx_tile_split(n):
-    """Rows per m-tile of an expert with n rows in the MX weight modes: the
-    rows split evenly over ceil(n / 256) tiles, rounded up to 16."""
-    mt = -(-n // TM)
-    return (-(-n // mt) + 15) & ~15
+_bf16_tile_split = _mx_tile_split = flat_tile_split
 
 
 def tile_edge_rows(lo, hi, per):
     """Rows of the expert segment [lo, hi) at the edges of its m-tiles of
     `per` rows: each tile's first and last row and the rows on both sides of
-    the split between its two wave halves (each half takes
-    min(128, ceil(valid / 2) rounded up to 32) rows)."""
+    every 32-row block boundary inside it (each block is one MFMA column
+    block of every wave)."""
     out = []
     for r0 in range(lo, hi, per):
         valid = min(per, hi - r0)
-        mh = min(TM // 2, (((valid + 1) >> 1) + 31) & ~31)
         out += [r0, r0 + valid - 1]
-        if mh < valid:
-            out += [r0 + mh - 1, r0 + mh]
+        for b in range(32, valid, 32):
+            out += [r0 + b - 1, r0 + b]
     return out
 
 
@@ -81,7 +79,7 @@ def coverage_tokens(counts, offsets, src, split, T, rng, n_random=32):
     for e in np.nonzero(counts)[0]:
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         rows += tile_edge_rows(lo, hi, split(hi - lo))
-    toks = [src[np.asarray(rows, np.int64)], np.asarray(tile_edge_rows(0, T, TM), np.int64),
+    toks = [src[np.asarray(rows, np.int64)], np.asarray(tile_edge_rows(0, T, FM), np.int64),
             rng.choice(T, size=min(n_random, T), replace=False)]
     return np.unique(np.concatenate(toks).astype(np.int64))
 
@@ -219,5 +217,54 @@ def test_full_size_mx(cfg, fmt):
     rel = check_rms(host(y)[toks], yref)
     print(f"[{w.name}, {fmt} weights] {len(toks)} of {w.T} tokens, {len(experts)} experts "
           f"(all non-empty): max|y - y_oracle| / rms = {rel:.2e}", flush=True)
+    del layer, inp, y, logits, ids, wts, mats
+    free_cuda()
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_full_size_a8w4(cfg):
+    """The A8W4 mode (MXFP4 routed weights, MXFP8 activations on the scaled
+    MX matrix cores; --weights a8w4) at full size: routes bit-exact, and the
+    outputs of a token set covering every non-empty expert and every m-tile
+    edge within tolerance of the oracle's A8W4 layer on its own
+    quantisation of x, h and every covered expert's weights (tolerance as in
+    test_gpu_a8w4: 5e-2 x RMS elementwise, 5e-3 relative Frobenius)."""
+    w = wl.WORKLOADS[cfg]
+    print(f"\n[{w.name}, a8w4] generating inputs", flush=True)
+    inp = wl.make_inputs(w, DEV)
+    layer = ops.MoeLayer.from_workload(w, inp, out_dtype=ops.OUT_F32, packed="a8w4")
+    logits = torch.empty((w.T, w.E), dtype=torch.float32, device=DEV)
+    ids = torch.empty((w.T, w.k), dtype=torch.int32, device=DEV)
+    wts = torch.empty((w.T, w.k), dtype=torch.float32, device=DEV)
+    y = layer.forward(inp["x"], input_ids=inp["input_ids"], modality=inp["modality"],
+                      logits=logits, ids=ids, w=wts)
+    torch.cuda.synchronize()
+    assert int(layer.flags.item()) == 0
+    rid, rw, _ = oracle.route(host(logits), w.k, w.scale, bias=_opt(inp, "score_bias"),
+                              modality=_opt(inp, "modality"), input_ids=_opt(inp, "input_ids"),
+                              tid2eid=_opt(inp, "tid2eid"), mode=w.mode)
+    assert np.array_equal(host(ids), rid)
+    assert np.array_equal(host(wts).view(np.uint32), rw.view(np.uint32))
+    counts, offsets, _, src, _ = oracle.permute(rid, w.E)
+    rng = np.random.default_rng(78)
+    toks = coverage_tokens(counts, offsets, src, flat_tile_split, w.T, rng)
+    experts = np.unique(rid[toks])
+    assert set(np.nonzero(counts)[0]) <= set(experts.tolist())
+    mats = {}
+    for key in ("w_gate", "w_up", "w_down"):
+        m = bits(inp[key])
+        _dequant_experts(m, experts, oracle.quant_mxfp4, oracle.dequant_mxfp4)
+        mats[key] = m
+    shared = [bits(inp[k]) for k in ("s_gate", "s_up", "s_down")]
+    yref = oracle.tokens_forward_a8w4(bits(inp["x"]), toks, rid, rw, mats["w_gate"],
+                                      mats["w_up"], mats["w_down"], *shared, w.clamp_limit,
+                                      w.clamp_mode)
+    got = host(y)[toks].astype(np.float64)
+    rel = check_rms(got, yref, tol=5e-2)
+    fro = float(np.linalg.norm(got - yref) / np.linalg.norm(yref))
+    assert fro <= 5e-3, fro
+    print(f"[{w.name}, a8w4] {len(toks)} of {w.T} tokens, {len(experts)} experts "
+          f"(all non-empty): max|y - y_oracle| / rms = {rel:.2e}, rel. Frobenius {fro:.2e}",
+          flush=True)
     del layer, inp, y, logits, ids, wts, mats
     free_cuda()
