@@ -457,22 +457,26 @@ __device__ __forceinline__ void read_b8(const unsigned char* slot, const FlatTil
     }
 }
 
-// the 2 x NTB scaled MFMAs of step S: weight scale bytes packed as
-// [block 0 step 0, block 0 step 1, block 1 step 0, block 1 step 1] (byte
-// selected by the operand's byte select), activation scale words shifted so
-// that byte 2 S is this lane's block
+// the 2 x NTB scaled MFMAs of step S.  The weight fragments stay as loaded
+// (the bytes of lanes n and n + 32: two u32x2 per block) until here, where
+// they are interleaved into K order two stages after their loads were
+// issued (interleaving them at load time made the moves wait on the loads
+// just issued); the weight scale bytes sit alone in their registers; the
+// activation scale words are shifted so that byte 2 S is this lane's block.
 template <int NTB, int S>
-__device__ __forceinline__ void mfma_a8w4(const u32x4& w0, const u32x4& w1, uint32_t ws,
+__device__ __forceinline__ void mfma_a8w4(const u32x2 (&w)[2][2], const uint32_t (&ws)[2],
                                           const v8i (&b)[NTB], const uint32_t (&as)[NTB],
                                           f32x16 (&acc)[2][FNTB]) {
-    const v8i a0 = {(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], 0, 0, 0, 0};
-    const v8i a1 = {(int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3], 0, 0, 0, 0};
+    const v8i a0 = {(int)w[0][0][0], (int)w[0][1][0], (int)w[0][0][1], (int)w[0][1][1],
+                    0, 0, 0, 0};
+    const v8i a1 = {(int)w[1][0][0], (int)w[1][1][0], (int)w[1][0][1], (int)w[1][1][1],
+                    0, 0, 0, 0};
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) {
         acc[0][tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            a0, b[tb], acc[0][tb], 4, 0, S, (int)ws, 2 * S, (int)as[tb]);
+            a0, b[tb], acc[0][tb], 4, 0, 0, (int)ws[0], 2 * S, (int)as[tb]);
         acc[1][tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            a1, b[tb], acc[1][tb], 4, 0, 2 + S, (int)ws, 2 * S, (int)as[tb]);
+            a1, b[tb], acc[1][tb], 4, 0, 0, (int)ws[1], 2 * S, (int)as[tb]);
     }
 }
 
@@ -535,32 +539,33 @@ __device__ __forceinline__ void flat_tile_a8(const GemmArgs& args, const FlatTil
     const uint8_t* a8 = args.a8;
     unsigned char* sring = ring + kRingBytes + kEpiBytes;
 
-    u32x4 wq[2][2][2];       // [set][step][block]
-    uint32_t wsc[2];         // [set]: scale bytes (block 0 step 0, 0 1, 1 0, 1 1)
+    u32x2 wq[2][2][2][2];    // [set][step][block][bytes of lane n, lane n + 32]
+    uint32_t wsc[2][2][2];   // [set][step][block] scale byte
     auto load_w = [&](int j, auto set) {
         constexpr int W = decltype(set)::value;
         const int jj = min(j, S - 1);
-        uint32_t sc = 0;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const size_t kb = (size_t)(4 * jj + 2 * s);
             const size_t off = kb * t.cstage;
-            const u32x2 o0 = *(const u32x2*)(t.cp0 + off), p0 = *(const u32x2*)(t.cp0 + off + 256);
-            const u32x2 o1 = *(const u32x2*)(t.cp1 + off), p1 = *(const u32x2*)(t.cp1 + off + 256);
-            wq[W][s][0] = u32x4{o0[0], p0[0], o0[1], p0[1]};
-            wq[W][s][1] = u32x4{o1[0], p1[0], o1[1], p1[1]};
-            sc |= (uint32_t)t.sp0[kb * t.sstep] << (8 * s);
-            sc |= (uint32_t)t.sp1[kb * t.sstep] << (8 * (2 + s));
+            wq[W][s][0][0] = *(const u32x2*)(t.cp0 + off);
+            wq[W][s][0][1] = *(const u32x2*)(t.cp0 + off + 256);
+            wq[W][s][1][0] = *(const u32x2*)(t.cp1 + off);
+            wq[W][s][1][1] = *(const u32x2*)(t.cp1 + off + 256);
+            wsc[W][s][0] = t.sp0[kb * t.sstep];
+            wsc[W][s][1] = t.sp1[kb * t.sstep];
         }
-        wsc[W] = sc;
     };
     u32x4 areg[2][2];
     uint32_t sreg[2];
     auto load_a = [&](int j, u32x4 (&d)[2], uint32_t& sd) {
+        // (unconditional: clamped rows are valid addresses, and the same
+        // load count on every path keeps the compiler's vmcnt waits from
+        // falling to the shortest path's; measured 6% faster)
         const size_t jj = (size_t)min(j, S - 1);
-        if (t.a_rows > 0) d[0] = *(const u32x4*)(a8 + t.a_off[0] + jj * FK8);
-        if (t.a_rows > 1) d[1] = *(const u32x4*)(a8 + t.a_off[1] + jj * FK8);
-        if (t.tid < FM) sd = *(const uint32_t*)(args.a_scale + t.s_off + 4 * jj);
+        d[0] = *(const u32x4*)(a8 + t.a_off[0] + jj * FK8);
+        d[1] = *(const u32x4*)(a8 + t.a_off[1] + jj * FK8);
+        sd = *(const uint32_t*)(args.a_scale + t.s_off + 4 * jj);
     };
     auto store_a = [&](int j, const u32x4 (&d)[2], uint32_t sd) {
         unsigned char* slot = ring + (j & 1) * kSlotBytes;
@@ -576,9 +581,11 @@ __device__ __forceinline__ void flat_tile_a8(const GemmArgs& args, const FlatTil
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
 
+    // (the loads in the order of the loop's own, so that the waits at the
+    // loop head are the steady state's)
     load_w(0, I0());
-    load_w(1, I1());
     load_a(0, areg[0], sreg[0]);
+    load_w(1, I1());
     load_a(1, areg[1], sreg[1]);
     store_a(0, areg[0], sreg[0]);
 
@@ -589,15 +596,15 @@ __device__ __forceinline__ void flat_tile_a8(const GemmArgs& args, const FlatTil
         __syncthreads();
         const unsigned char* slot = ring + P * kSlotBytes;
         const unsigned char* sslot = sring + P * kScaleSlot;
-        load_a(j + 2, areg[P], sreg[P]);
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb)
             as[tb] = *(const uint32_t*)(sslot + (tb * 32 + t.l32) * 4) >> (8 * t.half);
         read_b8<NTB>(slot, t, 0, b);
-        mfma_a8w4<NTB, 0>(wq[P][0][0], wq[P][0][1], wsc[P], b, as, acc);
+        mfma_a8w4<NTB, 0>(wq[P][0], wsc[P][0], b, as, acc);
         read_b8<NTB>(slot, t, 1, b);
-        mfma_a8w4<NTB, 1>(wq[P][1][0], wq[P][1][1], wsc[P], b, as, acc);
+        mfma_a8w4<NTB, 1>(wq[P][1], wsc[P][1], b, as, acc);
         load_w(j + 2, par);
+        load_a(j + 2, areg[P], sreg[P]);
         if (j + 1 < S) store_a(j + 1, areg[P ^ 1], sreg[P ^ 1]);
     };
     for (int j = 0; j < S; j += 2) {
@@ -718,7 +725,8 @@ __device__ __forceinline__ void flat_item(const GemmArgs& args, FlatTile& t, uns
         t.a_off[i] = e;
     }
     if constexpr (WF == 3) {
-        // scale bytes of tile row tid (threads 0 .. FM - 1)
+        // scale bytes of tile row tid (threads 0 .. FM - 1 store them; the
+        // others load a valid row too)
         const size_t grow = (size_t)(t.row0 + min(t.tid, t.valid - 1));
         const size_t src = AM == FA_GATHER ? (size_t)args.gather[grow] : grow;
         t.s_off = src * (size_t)(t.K / 32);
