@@ -583,10 +583,10 @@ __device__ __forceinline__ void flat_tile_a8(const GemmArgs& args, const FlatTil
 
     // (the loads in the order of the loop's own, so that the waits at the
     // loop head are the steady state's)
-    load_w(0, I0());
     load_a(0, areg[0], sreg[0]);
-    load_w(1, I1());
+    load_w(0, I0());
     load_a(1, areg[1], sreg[1]);
+    load_w(1, I1());
     store_a(0, areg[0], sreg[0]);
 
     v8i b[NTB];
@@ -596,6 +596,7 @@ __device__ __forceinline__ void flat_tile_a8(const GemmArgs& args, const FlatTil
         __syncthreads();
         const unsigned char* slot = ring + P * kSlotBytes;
         const unsigned char* sslot = sring + P * kScaleSlot;
+        load_a(j + 2, areg[P], sreg[P]);
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb)
             as[tb] = *(const uint32_t*)(sslot + (tb * 32 + t.l32) * 4) >> (8 * t.half);
@@ -604,7 +605,6 @@ __device__ __forceinline__ void flat_tile_a8(const GemmArgs& args, const FlatTil
         read_b8<NTB>(slot, t, 1, b);
         mfma_a8w4<NTB, 1>(wq[P][1], wsc[P][1], b, as, acc);
         load_w(j + 2, par);
-        load_a(j + 2, areg[P], sreg[P]);
         if (j + 1 < S) store_a(j + 1, areg[P ^ 1], sreg[P ^ 1]);
     };
     for (int j = 0; j < S; j += 2) {
