@@ -163,8 +163,8 @@ int moe_permute(const int32_t* topk_ids, const uint16_t* x, int T, int d, int E,
 /* moe_permute for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments, checks, results and errors as moe_permute, without the
- * workspace: the permutation's scratch (chunk ranks, chunk histogram and
- * bases: moe_permute_workspace_size(T, k, E) bytes) lives in a static
+ * workspace: the permutation's scratch (entry ranks and chunk histogram:
+ * moe_permute_workspace_size(T, k, E) bytes) lives in a static
  * device array of MOE_NOALLOC_SCRATCH_BYTES that each GPU the library runs
  * on holds until the process ends.  The call allocates nothing; a call whose
  * scratch would exceed the array returns MOE_ERR_SCRATCH before any launch.

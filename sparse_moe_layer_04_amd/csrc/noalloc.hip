@@ -1,7 +1,7 @@
 // moe_permute_noalloc: the token-dispatch permutation for callers that
-// cannot allocate device memory.  Its scratch (the chunk ranks, chunk
-// histogram and chunk bases of the permutation kernels) is a static device
-// array of this file instead of a caller workspace.
+// cannot allocate device memory.  Its scratch (the entry ranks and the
+// chunk histogram of the permutation kernels) is a static device array of
+// this file instead of a caller workspace.
 //
 // In host code the array's name stands for a host-side shadow, not a device
 // address, so it is never passed to a kernel or a copy: the first call on a

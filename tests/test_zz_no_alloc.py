@@ -69,8 +69,8 @@ def test_noalloc_invalid_ids_flagged():
 
 
 def test_noalloc_rejects_oversize_on_host():
-    # T k = 2^20 pairs over 1024 experts: the chunk histogram alone is 32 MiB
-    T, k, E = 1 << 17, 8, 1024
+    # T k = 2^21 pairs over 1024 experts: the entry ranks alone are 8 MiB
+    T, k, E = 1 << 18, 8, 1024
     assert ops.permute_workspace_size(T, k, E) > SCRATCH
     L = ops.lib()
     fake = 0x10000   # never dereferenced: the size check returns first
