@@ -812,7 +812,7 @@ __global__ __launch_bounds__(kFThreads) void grouped_gemm_flat_kernel(GemmArgs a
 
     int q;
     if (ctr) {
-        if (tid == 0) next_item = item_lo + (int)atomicAdd(ctr, 1u);
+        if (tid == 0) next_item = claimed_item(item_lo, item_hi, atomicAdd(ctr, 1u));
         __syncthreads();
         q = next_item;
     } else {
@@ -837,7 +837,7 @@ __global__ __launch_bounds__(kFThreads) void grouped_gemm_flat_kernel(GemmArgs a
         // every wave is past its last LDS read of this tile before the next
         // tile's prologue writes slot 0, and the claimed id is visible
         __syncthreads();
-        if (ctr && tid == 0) next_item = item_lo + (int)claimed;
+        if (ctr && tid == 0) next_item = claimed_item(item_lo, item_hi, claimed);
         __syncthreads();
         q = ctr ? next_item : q + per_xcd;
     }

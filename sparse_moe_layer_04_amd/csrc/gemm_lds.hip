@@ -217,6 +217,7 @@ struct LdsTile {
     unsigned* ctr;         // this XCD's item counter (dynamic scheduling) or NULL
     int* next_item;        // LDS slot receiving the claimed next item
     int item_lo;           // first item of this XCD's range
+    int item_hi;           // end of this XCD's range
 };
 
 // DMA of pipeline stage j (KB columns of K) into the LDS slot at byte offset
@@ -495,7 +496,7 @@ __device__ __forceinline__ void run_tile(const LdsTile& t) {
     unsigned claimed = 0;
     if (claim) claimed = atomicAdd(t.ctr, 1u);
     wait_vm<0>();
-    if (claim) *t.next_item = t.item_lo + (int)claimed;
+    if (claim) *t.next_item = claimed_item(t.item_lo, t.item_hi, claimed);
     __syncthreads();
     if constexpr (NTB > 0) epilogue<EPI, AM, NTB, WF>(t, acc);
 }
@@ -677,10 +678,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_lds_kernel(GemmArgs arg
     t.ctr = args.sched ? args.sched + xcd * 32 : nullptr;
     t.next_item = &next_item;
     t.item_lo = item_lo;
+    t.item_hi = item_hi;
 
     int q;
     if (t.ctr) {
-        if (tid == 0) next_item = item_lo + (int)atomicAdd(t.ctr, 1u);
+        if (tid == 0) next_item = claimed_item(item_lo, item_hi, atomicAdd(t.ctr, 1u));
         __syncthreads();
         q = next_item;
     } else {

@@ -167,6 +167,14 @@ struct GemmArgs {
 // per-launch scheduling counters of the LDS-staged expert GEMM
 constexpr int kSchedWords = 8 * 32;
 
+// The item a workgroup claims from its XCD's counter: item_lo plus the
+// counter's previous value, or item_hi (no item) when that value is past the
+// XCD's range, so a counter that was not cleared before the launch cannot
+// send a workgroup outside its items.
+__device__ __forceinline__ int claimed_item(int item_lo, int item_hi, unsigned claimed) {
+    return claimed < (unsigned)(item_hi - item_lo) ? item_lo + (int)claimed : item_hi;
+}
+
 // Blocked activation layout (internal to moe_forward): a [rows, K] bf16
 // matrix stored as 1 KB blocks of 16 rows x 32 columns, blocks ordered by row
 // block then column block, each block row-major:
