@@ -53,7 +53,8 @@ def _check(lg, ids, dw, scale):
 
 @pytest.mark.parametrize("T,E,k,scale,spread", [(300, 384, 6, 2.5, 1.5), (100, 1024, 8, 1.0, 1.5),
                                                 (1, 8, 2, 1.0, 1.5), (64, 16, 4, 2.5, 30.0),
-                                                (8192, 384, 6, 2.5, 1.0)])
+                                                (8192, 384, 6, 2.5, 1.0), (77, 50, 3, 2.5, 1.5),
+                                                (129, 130, 5, 1.0, 1.5), (65, 7, 7, 2.5, 1.5)])
 def test_route_backward_topk(T, E, k, scale, spread):
     """Routes from the GPU's top-k routing of the same logits (the last case
     is the 384-expert layer's routing shape, T = 8192)."""
@@ -84,3 +85,16 @@ def test_route_backward_hash_routes_and_special_cases():
     bad[100, 0] = E
     got, _ = _check(lg, bad, dw, 2.5)
     assert np.all(got[5] == 0.0) and np.all(got[100] == 0.0)
+
+
+def test_route_backward_duplicate_slots():
+    """An expert listed in two slots of a token (a hash table row may repeat
+    one) gets the sum of both slots' gradients; rows of tokens that fill
+    several waves, E not a multiple of 4."""
+    rng = np.random.default_rng(11)
+    T, E, k = 200, 30, 6
+    lg = rng.normal(0, 1, (T, E)).astype(np.float32)
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    ids[:, 3] = ids[:, 1]
+    dw = rng.normal(0, 1, (T, k)).astype(np.float32)
+    _check(lg, ids, dw, 2.5)

@@ -114,6 +114,31 @@ def test_permute(T, E, k, d):
     assert int(flags.item()) == rf == 0
 
 
+# T k entries across every chunking of the permutation kernels: one 64-entry
+# step per wave up to 2^16 entries, then 2, 4, 8 and 16 steps, and past 64
+# chunks (the scatter reads the chunk histogram in two passes); expert counts
+# that are not a multiple of 4; a few invalid ids
+@pytest.mark.parametrize("T,E,k", [(16000, 384, 6), (40000, 61, 6), (80000, 384, 6),
+                                   (150000, 1021, 8)])
+def test_permute_chunking(T, E, k):
+    rng = np.random.default_rng(T + E + k)
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    bad = rng.integers(0, T * k, 5)
+    ids.reshape(-1)[bad] = np.array([-1, E, E + 7, -100, 1 << 30], np.int32)
+    x = _bf16(rng, (T, 8), 1.0)
+    print(f"\npermute T={T} E={E} k={k} N={T * k}", flush=True)
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = ops.permute(torch.from_numpy(ids).to(DEV), x, E, flags=flags)
+    counts, offsets, dest, src, rf = oracle.permute(ids, E)
+    assert np.array_equal(host(out["counts"]), counts)
+    assert np.array_equal(host(out["offsets"]), offsets)
+    assert np.array_equal(host(out["dest"]), dest)
+    assert np.array_equal(host(out["src"]), src)
+    n = offsets[-1]
+    assert np.array_equal(bits(out["x_perm"])[:n], oracle.gather(bits(x), src)[:n])
+    assert int(flags.item()) == rf == oracle.FLAG_BAD_EXPERT_ID
+
+
 def test_permute_invalid_and_duplicate_ids():
     E, k, d = 8, 3, 64
     rng = np.random.default_rng(9)
