@@ -15,14 +15,23 @@
 // on one XCD (see the order below), so x comes from memory once.
 //   - workgroup: 4 waves (one per SIMD); wave w owns tokens 32 w .. 32 w + 31
 //     of the tile and all of its (up to) three weight blocks;
-//   - per 16-wide K substep: one activation fragment (16 bytes per lane,
-//     straight from x) and three weight fragments (1 KB contiguous each in
-//     the moe_pack_weights panel layout, shared by the four waves through
-//     L1), loaded kRing substeps ahead into a register ring; one
-//     v_mfma_f32_32x32x16_bf16 per weight block.
+//   - per 16-wide K substep: one activation fragment and three weight
+//     fragments (1 KB contiguous each in the moe_pack_weights panel layout,
+//     shared by the four waves through L1, loaded kRing substeps ahead into
+//     a register ring); one v_mfma_f32_32x32x16_bf16 per weight block;
+//   - the activation fragments (lane l: row l % 32, 8 consecutive K) would
+//     touch 32 cache lines per load instruction straight from x, and the L1
+//     lookups of those loads bounded the kernel; instead each wave loads its
+//     32 rows 64 columns at a time (8 lanes per 128-byte row segment, so 8
+//     lines per instruction), two stages ahead, into a private 2-slot LDS
+//     ring (XOR-swizzled 16-byte chunks), and reads the fragments from
+//     there.  The wave's LDS is its own, so its in-order LDS accesses need
+//     no barrier.
 // Each output accumulates its K substeps in ascending order with the same
 // instruction and operand order as the plain-layout kernel, so both layouts
 // give the same bits.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -32,6 +41,7 @@ constexpr int kRouterPanel = 256;   // panel rows of the packed router weights
 constexpr int kRing = 8;            // substeps in flight
 constexpr int kBlocks = 3;          // 32-row weight blocks per workgroup
 constexpr int kTokens = 128;        // tokens per workgroup (32 per wave)
+constexpr int kXSlot = 32 * 128;    // LDS bytes per wave per 64-column stage of x
 
 __global__ __launch_bounds__(256, 1) void router_kernel(const uint16_t* __restrict__ x,
                                                         const uint16_t* __restrict__ wg,
@@ -54,8 +64,37 @@ __global__ __launch_bounds__(256, 1) void router_kernel(const uint16_t* __restri
     const int nb = min(kBlocks, NB - eb0);        // its blocks (>= 1)
     const int S = K / 16;                         // 16-wide K substeps
 
-    // activation row of this lane (rows past T read the last row; not stored)
-    const uint16_t* arow = x + (size_t)min(t0 + l32, T - 1) * K + 8 * half;
+    __shared__ __align__(16) unsigned char xs_all[4 * 2 * kXSlot];
+    unsigned char* xs = xs_all + wave * 2 * kXSlot;
+    // x staging: lane l copies 16-byte chunk l % 8 of rows l / 8 + 8 i
+    // (i < 4) of the wave's 32 rows (rows past T read the last row; their
+    // outputs are not stored); chunk c of row r sits at c ^ ((r >> 1) & 7)
+    const int xc = lane & 7;
+    const uint16_t* xrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        xrow[i] = x + (size_t)min(t0 + (lane >> 3) + 8 * i, T - 1) * K + 8 * xc;
+    const int NS = S / 4;                         // 64-wide stages
+    u32x4 xr[2][4];
+    auto load_x = [&](int st, u32x4 (&d)[4]) {
+        const int sc = min(st, NS - 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d[i] = *(const u32x4*)(xrow[i] + 64 * sc);
+    };
+    auto store_x = [&](int slot, const u32x4 (&d)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = (lane >> 3) + 8 * i;
+            *(u32x4*)(xs + slot * kXSlot + r * 128 + ((xc ^ ((r >> 1) & 7)) << 4)) = d[i];
+        }
+    };
+    // the activation fragment of substep ks (stage ks / 4 in slot (ks / 4) % 2):
+    // row l32, K chunk 2 (ks % 4) + half of the stage
+    auto read_a = [&](int ks) {
+        const int c = 2 * (ks & 3) + half;
+        return *(const bf16x8*)(xs + ((ks >> 2) & 1) * kXSlot + l32 * 128 +
+                                ((c ^ ((l32 >> 1) & 7)) << 4));
+    };
     // weight fragment of block eb, substep ks: panel eb / 8, 64-wide stage
     // ks / 4, block eb % 8, substep ks % 4, 8 elements per lane
     const size_t pstride = (size_t)kRouterPanel * K;
@@ -72,40 +111,49 @@ __global__ __launch_bounds__(256, 1) void router_kernel(const uint16_t* __restri
     for (int j = 0; j < kBlocks; ++j)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
-    bf16x8 ar[kRing], wr[kRing][kBlocks];
+    bf16x8 wr[kRing][kBlocks];
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
         const int ks = min(u, S - 1);
-        ar[u] = *(const bf16x8*)(arow + 16 * ks);
 #pragma unroll
         for (int j = 0; j < kBlocks; ++j) wr[u][j] = *(const bf16x8*)(wb[j] + w_off(ks));
     }
+    // x stages 0 and 1 into registers, stage 0 into slot 0, stage 2 into the
+    // freed registers
+    load_x(0, xr[0]);
+    load_x(1, xr[1]);
+    store_x(0, xr[0]);
+    load_x(2, xr[0]);
     // Loads and MFMAs are unconditional (blocks past the last read its
-    // rows again; their outputs are not stored): straight-line code lets the
-    // compiler count the ring's outstanding loads exactly instead of draining
-    // them at every turn.
-    const int S8 = S / kRing * kRing;             // whole ring turns; S % 4 == 0
-    for (int s0 = 0; s0 < S8; s0 += kRing) {
+    // rows again, stages past the end the last stage; those outputs are not
+    // used): straight-line code lets the compiler count the outstanding
+    // loads exactly instead of draining them at every turn.
+    // stage st (4 substeps) from slot st % 2; then stage st + 1 goes from its
+    // registers into the other slot and those registers take stage st + 3
+    auto stage = [&](int st, auto par) {
+        constexpr int P = decltype(par)::value;   // st % 2
 #pragma unroll
-        for (int u = 0; u < kRing; ++u) {
+        for (int uu = 0; uu < 4; ++uu) {
+            const int u = 4 * P + uu;             // ring slot of substep 4 st + uu
+            const bf16x8 a = read_a(4 * st + uu);
 #pragma unroll
             for (int j = 0; j < kBlocks; ++j)
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], ar[u], acc[j], 0, 0, 0);
-            // refill the slot with substep s0 + u + kRing (the last substep
-            // again past the end, so the loads stay in bounds)
-            const int ks = min(s0 + u + kRing, S - 1);
-            ar[u] = *(const bf16x8*)(arow + 16 * ks);
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], a, acc[j], 0, 0, 0);
+            // refill the slot with substep 4 st + uu + kRing (the last
+            // substep again past the end, so the loads stay in bounds)
+            const int ks = min(4 * st + uu + kRing, S - 1);
 #pragma unroll
             for (int j = 0; j < kBlocks; ++j) wr[u][j] = *(const bf16x8*)(wb[j] + w_off(ks));
         }
+        store_x(P ^ 1, xr[P ^ 1]);
+        load_x(st + 3, xr[P ^ 1]);
+    };
+    const int NS2 = NS / 2 * 2;                   // whole ring turns (two stages)
+    for (int st = 0; st < NS2; st += 2) {
+        stage(st, std::integral_constant<int, 0>());
+        stage(st + 1, std::integral_constant<int, 1>());
     }
-    if (S8 < S) {                                 // last 4 substeps: slots 0 .. 3
-#pragma unroll
-        for (int u = 0; u < kRing / 2; ++u)
-#pragma unroll
-            for (int j = 0; j < kBlocks; ++j)
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], ar[u], acc[j], 0, 0, 0);
-    }
+    if (NS2 < NS) stage(NS2, std::integral_constant<int, 0>());   // last 4 substeps
 
     // acc[j] element 4 qq + i of lane l: token t0 + l % 32, expert
     // 32 (eb0 + j) + 8 qq + 4 (l / 32) + i
