@@ -221,7 +221,7 @@ def test_full_size_mx(cfg, fmt):
     free_cuda()
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 4])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_full_size_a8w4(cfg):
     """The A8W4 mode (MXFP4 routed weights, MXFP8 activations on the scaled
     MX matrix cores; --weights a8w4) at full size: routes bit-exact, and the
