@@ -18,9 +18,9 @@
 //     one barrier per chunk;
 //   - the MFMA operands need 8 consecutive rows of one column per lane
 //     (v_mfma_f32_32x32x16_bf16: operand A = a, so each lane's accumulator
-//     holds 4 consecutive k of one m and the stores are 16 bytes), gathered
-//     with 16-bit LDS reads; LDS rows are padded to 272 bytes, so the two
-//     half-waves (rows 8 apart) read distinct banks;
+//     holds 4 consecutive k of one m and the stores are 16 bytes); two LDS
+//     transpose reads (ds_read_b64_tr_b16) give a lane its 8 rows from the
+//     row-major chunk; LDS rows are padded to 272 bytes;
 //   - wave (wm, wk) owns 64 m x 64 k (2 x 2 accumulators);
 //   - the fp32 tile (64 KB, as many bytes as the tile reads at 128 rows, so
 //     the writes dominate the traffic) leaves through LDS in two halves of
@@ -56,17 +56,27 @@ struct WgradArgs {
     float* dw;
 };
 
-// 8 rows (row0 .. row0 + 7) of column `col` of a staged operand chunk as one
-// MFMA operand (bf16x8)
-__device__ __forceinline__ bf16x8 gather8(const unsigned char* chunk, int row0, int col) {
-    u32x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = *(const uint16_t*)(chunk + (row0 + 2 * i) * kWRow + col * 2);
-        const uint32_t hi = *(const uint16_t*)(chunk + (row0 + 2 * i + 1) * kWRow + col * 2);
-        r[i] = lo | (hi << 16);
-    }
-    return __builtin_bit_cast(bf16x8, r);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// The MFMA operand of lane l from a staged row-major chunk: rows row0 +
+// 8 (l / 32) + t (t = 0..7) of column col0 + l % 32, by two LDS transpose
+// reads.  ds_read_b64_tr_b16 works on groups of 16 lanes: lane j of a group
+// receives 16-bit element j % 4 of the 8-byte pieces addressed by lanes
+// 4 m + j / 4 of the group, m = 0..3 (established on the GPU by a one-wave
+// probe).  Lane i of group gp therefore addresses row i / 4 (of the group's
+// 4-row block) and columns 16 (gp % 2) + 4 (i % 4) .. + 3, so lane j's
+// values are 4 consecutive rows of column 16 (gp % 2) + j.
+__device__ __forceinline__ bf16x8 gather8(const unsigned char* chunk, int row0, int col0,
+                                          int lane) {
+    const int gp = lane >> 4, i = lane & 15;
+    const int r = row0 + 8 * (gp >> 1) + (i >> 2);
+    const int c = col0 + 16 * (gp & 1) + 4 * (i & 3);
+    const unsigned char* p = chunk + r * kWRow + c * 2;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * kWRow));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
 }
 
 __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
@@ -143,12 +153,11 @@ void grouped_wgrad_kernel(WgradArgs args) {
         const unsigned char* ac = dyc + kWOperand;
 #pragma unroll
         for (int s = 0; s < WR / 16; ++s) {
-            const int row0 = 16 * s + 8 * half;
             bf16x8 fa[2], fd[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                fa[i] = gather8(ac, row0, 64 * wk + 32 * i + l32);
-                fd[i] = gather8(dyc, row0, 64 * wm + 32 * i + l32);
+                fa[i] = gather8(ac, 16 * s, 64 * wk + 32 * i, lane);
+                fd[i] = gather8(dyc, 16 * s, 64 * wm + 32 * i, lane);
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
