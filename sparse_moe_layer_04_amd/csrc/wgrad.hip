@@ -20,7 +20,7 @@
 //     (v_mfma_f32_32x32x16_bf16: operand A = a, so each lane's accumulator
 //     holds 4 consecutive k of one m and the stores are 16 bytes); two LDS
 //     transpose reads (ds_read_b64_tr_b16) give a lane its 8 rows from the
-//     row-major chunk; LDS rows are padded to 272 bytes;
+//     row-major chunk; LDS rows are padded to 288 bytes;
 //   - wave (wm, wk) owns 64 m x 64 k (2 x 2 accumulators);
 //   - the fp32 tile (64 KB, as many bytes as the tile reads at 128 rows, so
 //     the writes dominate the traffic) leaves through LDS in two halves of
@@ -41,7 +41,7 @@ namespace {
 constexpr int WT = 128;                 // tile: m and k extent
 constexpr int WR = 32;                  // rows per chunk
 constexpr int kWThreads = 256;
-constexpr int kWRow = WT * 2 + 16;      // LDS bytes per staged row (padded)
+constexpr int kWRow = WT * 2 + 32;      // LDS bytes per staged row (padded)
 constexpr int kWOperand = WR * kWRow;   // one operand chunk
 constexpr int kWSlot = 2 * kWOperand;   // dy + a chunk
 
