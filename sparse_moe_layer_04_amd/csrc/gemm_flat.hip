@@ -138,8 +138,10 @@ __device__ __forceinline__ void mfma_step(const bf16x8& w0, const bf16x8& w1, co
 // fp32 outputs (down projection): each 32-row block goes through LDS so that
 // every store instruction writes 1 KB of one output row (the accumulator
 // layout gives each lane 16 bytes in each of 32 rows 4 * N bytes apart).
-// Barrier-uniform: every wave runs it whatever its columns.
-template <int NTB>
+// Barrier-uniform: every wave runs it whatever its columns.  NT_OUT: stores
+// with the streaming hint (the routed expert outputs, larger than the caches
+// and read once by the combine).
+template <int NTB, bool NT_OUT>
 __device__ __forceinline__ void flat_epilogue_f32(const GemmArgs& args, const FlatTile& t,
                                                   const f32x16 (&acc)[2][FNTB],
                                                   unsigned char* stg) {
@@ -171,8 +173,14 @@ __device__ __forceinline__ void flat_epilogue_f32(const GemmArgs& args, const Fl
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int c = 256 * h + 4 * t.lane;
-                if (nbase + c < N)
-                    *(f32x4*)(orow + c) = *(const f32x4*)(stg + row * kEpiRow + c * 4);
+                if (nbase + c < N) {
+                    const f32x4 v = *(const f32x4*)(stg + row * kEpiRow + c * 4);
+                    if constexpr (NT_OUT) {
+                        __builtin_nontemporal_store(v, (f32x4*)(orow + c));
+                    } else {
+                        *(f32x4*)(orow + c) = v;
+                    }
+                }
             }
         }
     }
@@ -418,7 +426,8 @@ __device__ __forceinline__ void flat_tile(const GemmArgs& args, const FlatTile& 
         if (j + 1 < S) stage(j + 1, std::integral_constant<int, 1>());
     }
     if constexpr (EPI == EPI_F32) {
-        flat_epilogue_f32<NTB>(args, t, acc, ring + kRingBytes);
+        // (the blocked activations are the routed h of the forward)
+        flat_epilogue_f32<NTB, AM == FA_BLK>(args, t, acc, ring + kRingBytes);
     } else {
         flat_epilogue<EPI, AM, NTB>(args, t, acc);
     }
@@ -612,7 +621,7 @@ __device__ __forceinline__ void flat_tile_a8(const GemmArgs& args, const FlatTil
         if (j + 1 < S) stage(j + 1, I1());
     }
     if constexpr (EPI == EPI_F32) {
-        flat_epilogue_f32<NTB>(args, t, acc, ring + kRingBytes);
+        flat_epilogue_f32<NTB, true>(args, t, acc, ring + kRingBytes);
     } else {
         flat_epilogue_h8<NTB>(args, t, acc);
     }
