@@ -161,7 +161,7 @@ struct BwdWs {
     float* u;           // [N, F] up pre-activations
     uint16_t* h;        // [N, F] bf16
     float* y_perm;      // [N, d]
-    float* dyp;         // [N, d] fp32 expert-output gradient (later: dx_perm)
+    float* dyp;         // [N, d] fp32 dx_perm (the gate/up input gradient rows)
     uint16_t* dyp16;    // [N, d] bf16
     float* dh;          // [N, F]
     uint16_t* dgu;      // [N, 2F] bf16
@@ -936,9 +936,9 @@ int moe_backward(const moe_cfg* c, const moe_weights* w, const moe_bwd_weights* 
         return MOE_ERR_HIP;
 
     // ---- combine -> expert outputs and routing weights
-    if (!ok(launch_combine_backward(dy, L.y_perm, L.dest, L.w, T, d, k, N, L.dyp, L.dtw, s)))
+    if (!ok(launch_combine_backward_bf16(dy, L.y_perm, L.dest, L.w, T, d, k, N, L.dyp16, L.dtw,
+                                         s)))
         return MOE_ERR_HIP;
-    if (!ok(launch_cast_bf16(L.dyp, (long long)N * d, L.dyp16, s))) return MOE_ERR_HIP;
     // ---- down projection: weight and input gradients
     if (!ok(launch_grouped_wgrad(L.dyp16, L.h, L.offsets, E, N, d, F, gr->dw_down, s)))
         return MOE_ERR_HIP;
@@ -952,7 +952,7 @@ int moe_backward(const moe_cfg* c, const moe_weights* w, const moe_bwd_weights* 
         return MOE_ERR_HIP;
     if (!ok(launch_grouped_wgrad(L.dgu + F, L.x_perm, L.offsets, E, N, F, d, gr->dw_up, s, 2 * F)))
         return MOE_ERR_HIP;
-    float* dxp = L.dyp;  // (dy_perm is no longer needed: its rows take dx_perm)
+    float* dxp = L.dyp;
     if (!ok(flat_gemm(EPI_F32, L.dgu, L.offsets, E, N, 2 * F, d, bw->w_gu_t, nullptr, Lc, cm, dxp,
                       nullptr, nullptr, sch + 3 * kSchedWords, s)))
         return MOE_ERR_HIP;

@@ -235,6 +235,11 @@ hipError_t launch_swiglu_backward(const float* gate, const float* up, const floa
 hipError_t launch_combine_backward(const float* dy, const float* y_perm, const int32_t* dest,
                                    const float* w, int T, int d, int k, int rows, float* dy_perm,
                                    float* dw, hipStream_t stream);
+// the same with the gradient rows written as bf16 (d a multiple of 4)
+hipError_t launch_combine_backward_bf16(const float* dy, const float* y_perm,
+                                        const int32_t* dest, const float* w, int T, int d, int k,
+                                        int rows, uint16_t* dy_perm, float* dw,
+                                        hipStream_t stream);
 
 hipError_t launch_route_backward(const float* logits, const int32_t* ids, const float* dw,
                                  int T, int E, int k, float scale, float* dl, uint32_t* flags,
