@@ -85,6 +85,20 @@ __device__ __forceinline__ float fclamp_sym(float v, float L) { return fminf(fma
 
 __device__ __forceinline__ int fswz(int r) { return (r >> 1) & 7; }
 
+// Buffer resource over [base, base + bytes), base and bytes wave-uniform
+// (read from the first lane, so the resource lives in scalar registers):
+// the weight loads address their panel as a scalar base plus the lane's
+// 16-byte offset and a scalar stage offset, which keeps the 64-bit address
+// arithmetic out of the vector registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t flat_rsrc(const void* base, size_t bytes) {
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+    const int n = __builtin_amdgcn_readfirstlane((int)min(bytes, (size_t)0x7fffffff));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), 0, n,
+                                             0x00020000);
+}
+
 // Per-workgroup state of one tile.
 struct FlatTile {
     int lane, wave, half, l32, tid;
@@ -322,12 +336,17 @@ __device__ __forceinline__ void flat_tile(const GemmArgs& args, const FlatTile& 
         }
     };
 
-    // weights of global substep u (stage u / 4, substep u % 4), clamped to K
+    // weights of global substep u (stage u / 4, substep u % 4), clamped to K,
+    // through buffer resources over this wave's two blocks (the launch keeps
+    // a panel under 2 GiB)
+    const size_t wbytes = (size_t)S * t.wstage * 2;
+    const __amdgpu_buffer_rsrc_t wr0 = flat_rsrc(t.wp0 - t.lane * 8, wbytes);
+    const __amdgpu_buffer_rsrc_t wr1 = flat_rsrc(t.wp1 - t.lane * 8, wbytes);
     auto load_w = [&](int u, bf16x8& d0, bf16x8& d1) {
         const int j = min(u >> 2, S - 1);
-        const size_t off = (size_t)j * t.wstage + (size_t)(u & 3) * 512;
-        d0 = *(const bf16x8*)(t.wp0 + off);
-        d1 = *(const bf16x8*)(t.wp1 + off);
+        const int so = (int)(((size_t)j * t.wstage + (size_t)(u & 3) * 512) * 2);
+        d0 = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(wr0, t.lane * 16, so, 0));
+        d1 = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(wr1, t.lane * 16, so, 0));
     };
     auto load_a = [&](int j, u32x4 (&d)[2]) {
         const size_t off = (size_t)min(j, S - 1) * t.a_step;
@@ -886,6 +905,8 @@ int grouped_gemm_flat_max_groups() {
 
 hipError_t launch_grouped_gemm_flat(int epilogue, const GemmArgs& g, hipStream_t stream) {
     if (g.K % FK != 0 || g.G < 1) return hipErrorInvalidValue;
+    // one weight panel (at most 256 rows) within a buffer resource's range
+    if ((long long)g.K * 256 * 2 > 0x7fffffffll) return hipErrorInvalidValue;
     if (g.wfp8 == 3) {
         // A8W4: gate/up on MXFP8 rows (gathered or row-major) into MXFP8 h,
         // down on row-major MXFP8 h; MXFP4 weights
