@@ -73,7 +73,11 @@ extern "C" {
 #define MOE_FLAG_BAD_EXPERT_ID 2u /* an expert id outside [0, E) */
 
 /* Limits: 1 <= k <= 8, k <= E, 1 <= E <= 1024 (route/permute/forward);
- * d, F multiples of 64 (expert FFN, forward); T * k < 2^31; G <= 4096. */
+ * d, F multiples of 64 (expert FFN, forward); T * k < 2^31; G <= 4096.
+ * The packed-weight expert GEMMs contract over at most 4,194,240 values (a
+ * 256-row weight panel within 2 GiB): d, F, F_shared and K up to that,
+ * 2 F and 2 F_shared too in moe_backward; larger sizes return
+ * MOE_ERR_UNSUPPORTED. */
 #define MOE_MAX_K 8
 #define MOE_MAX_E 1024
 #define MOE_MAX_GROUPS 4096

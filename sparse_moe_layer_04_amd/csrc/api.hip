@@ -49,6 +49,7 @@ int route_checks(const float* logits, const float* bias, const int32_t* input_id
 int ffn_checks(int rows, int d, int F, float clamp_limit, int clamp_mode) {
     if (rows < 0 || d < 64 || F < 64) return MOE_ERR_SHAPE;
     if (d % 64 || F % 64) return MOE_ERR_UNSUPPORTED;
+    if (d > kFlatMaxK || F > kFlatMaxK) return MOE_ERR_UNSUPPORTED;
     if (!(clamp_limit > 0.0f)) return MOE_ERR_SHAPE;  // also rejects NaN
     if (clamp_mode != MOE_CLAMP_SYMMETRIC && clamp_mode != MOE_CLAMP_GATE_UPPER)
         return MOE_ERR_UNSUPPORTED;
@@ -570,7 +571,7 @@ int moe_expert_ffn_a8w4(const uint8_t* a8, const uint8_t* a_scale, const int32_t
 int moe_grouped_gemm_packed(const uint16_t* a, const int32_t* offsets, int G, int rows, int K,
                             int N, const uint16_t* w_packed, float* out, void* stream) {
     if (G < 1 || rows < 0 || K < 64 || N < 64) return MOE_ERR_SHAPE;
-    if (K % 64 || N % 64) return MOE_ERR_UNSUPPORTED;
+    if (K % 64 || N % 64 || K > kFlatMaxK) return MOE_ERR_UNSUPPORTED;
     if (G > MOE_MAX_GROUPS || G > grouped_gemm_lds_max_groups()) return MOE_ERR_UNSUPPORTED;
     if ((long long)rows * K >= (1ll << 40) || (long long)rows * N >= (1ll << 40))
         return MOE_ERR_SHAPE;
@@ -629,7 +630,7 @@ static int forward_checks(const moe_cfg* c, const moe_weights* w) {
     if ((long long)c->T * c->k >= (1ll << 31)) return MOE_ERR_SHAPE;
     int st = ffn_checks(c->T * c->k, c->d, c->F, c->clamp_limit, c->clamp_mode);
     if (st != MOE_OK) return st;
-    if (c->F_shared % 64) return MOE_ERR_UNSUPPORTED;
+    if (c->F_shared % 64 || c->F_shared > kFlatMaxK) return MOE_ERR_UNSUPPORTED;
     if (c->mode != MOE_MODE_TOPK && c->mode != MOE_MODE_HASH) return MOE_ERR_UNSUPPORTED;
     if (c->out_dtype != MOE_OUT_BF16 && c->out_dtype != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
     if (!(c->scale == c->scale)) return MOE_ERR_SHAPE;
@@ -864,6 +865,8 @@ int moe_backward(const moe_cfg* c, const moe_weights* w, const moe_bwd_weights* 
     if (st != MOE_OK) return st;
     if (!bw || !gr) return MOE_ERR_NULL;
     if (w->packed != 1) return MOE_ERR_UNSUPPORTED;   // bf16 packed weights only
+    // (the gate/up input gradient contracts over 2F and 2 F_shared)
+    if (2LL * c->F > kFlatMaxK || 2LL * c->F_shared > kFlatMaxK) return MOE_ERR_UNSUPPORTED;
     if (c->E > grouped_gemm_flat_max_groups()) return MOE_ERR_UNSUPPORTED;
     if (c->T == 0) return MOE_OK;
     const int Fs = c->F_shared;

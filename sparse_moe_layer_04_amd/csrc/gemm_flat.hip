@@ -906,7 +906,7 @@ int grouped_gemm_flat_max_groups() {
 hipError_t launch_grouped_gemm_flat(int epilogue, const GemmArgs& g, hipStream_t stream) {
     if (g.K % FK != 0 || g.G < 1) return hipErrorInvalidValue;
     // one weight panel (at most 256 rows) within a buffer resource's range
-    if ((long long)g.K * 256 * 2 > 0x7fffffffll) return hipErrorInvalidValue;
+    if (g.K > kFlatMaxK) return hipErrorInvalidValue;
     if (g.wfp8 == 3) {
         // A8W4: gate/up on MXFP8 rows (gathered or row-major) into MXFP8 h,
         // down on row-major MXFP8 h; MXFP4 weights

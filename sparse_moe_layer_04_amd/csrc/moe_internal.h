@@ -166,6 +166,9 @@ struct GemmArgs {
 };
 // per-launch scheduling counters of the LDS-staged expert GEMM
 constexpr int kSchedWords = 8 * 32;
+// largest contraction length K of the flat expert GEMM: one 256-row packed
+// weight panel (K 256 bf16 values) stays within a buffer resource's 2 GiB
+constexpr int kFlatMaxK = (0x7fffffff / (256 * 2)) / 64 * 64;
 
 // The item a workgroup claims from its XCD's counter: item_lo plus the
 // counter's previous value, or item_hi (no item) when that value is past the

@@ -107,6 +107,8 @@ def test_expert_ffn_validation(L, entry):
     assert ffn(G=0) == ERR_SHAPE
     assert ffn(G=5000) == ERR_UNSUPPORTED
     assert ffn(d=96) == ERR_UNSUPPORTED
+    assert ffn(d=4194240 + 64) == ERR_UNSUPPORTED
+    assert ffn(F=4194240 + 64) == ERR_UNSUPPORTED
     assert ffn(F=32) == ERR_SHAPE
     assert ffn(L_=0.0) == ERR_SHAPE
     assert ffn(L_=float("nan")) == ERR_SHAPE
@@ -202,6 +204,7 @@ def test_grouped_gemm_packed_validation(L):
     assert gg(K=32) == ERR_SHAPE
     assert gg(K=96) == ERR_UNSUPPORTED
     assert gg(N=100) == ERR_UNSUPPORTED
+    assert gg(K=4194240 + 64) == ERR_UNSUPPORTED   # one weight panel past 2 GiB
     assert gg(G=5000) == ERR_UNSUPPORTED
     assert gg(a=None) == ERR_NULL
     assert gg(w=None) == ERR_NULL
