@@ -11,8 +11,10 @@
 // smallest for a square-ish tile.  Tile: 128 tokens x 96 experts (three
 // 32-row weight blocks), T / 128 x ceil(E / 96) workgroups (256 at the
 // 384-expert layer): ~0.47 GB of operand reads instead of ~1 GB for
-// 32 tokens x all experts.  The workgroups of one token tile run together
-// on one XCD (see the order below), so x comes from memory once.
+// 32 tokens x all experts.  Where that grid would not cover the CUs (few
+// tokens or experts), a workgroup takes 2 or 1 weight blocks instead: more,
+// shorter workgroups.  The workgroups of one token tile run together on one
+// XCD (see the order below), so x comes from memory once.
 //   - workgroup: 4 waves (one per SIMD); wave w owns tokens 32 w .. 32 w + 31
 //     of the tile and all of its (up to) three weight blocks;
 //   - per 16-wide K substep: one activation fragment and three weight
@@ -39,10 +41,12 @@ namespace {
 
 constexpr int kRouterPanel = 256;   // panel rows of the packed router weights
 constexpr int kRing = 8;            // substeps in flight
-constexpr int kBlocks = 3;          // 32-row weight blocks per workgroup
 constexpr int kTokens = 128;        // tokens per workgroup (32 per wave)
 constexpr int kXSlot = 32 * 128;    // LDS bytes per wave per 64-column stage of x
 
+// KB: 32-row weight blocks per workgroup (3, or fewer when the grid would
+// not cover the CUs)
+template <int KB>
 __global__ __launch_bounds__(256, 1) void router_kernel(const uint16_t* __restrict__ x,
                                                         const uint16_t* __restrict__ wg,
                                                         const float* __restrict__ offset, int T,
@@ -55,13 +59,13 @@ __global__ __launch_bounds__(256, 1) void router_kernel(const uint16_t* __restri
     // the tile's rows of x are read from memory once and then hit that
     // XCD's L2 (and every XCD keeps all of W_g in its L2)
     const int NB = (E + 31) / 32;                 // 32-row weight blocks
-    const int groups = (NB + kBlocks - 1) / kBlocks;
+    const int groups = (NB + KB - 1) / KB;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int tile = (slot / groups) * 8 + xcd, group = slot % groups;
     const int t0 = tile * kTokens + wave * 32;
     if (t0 >= T) return;                          // (wave-uniform; no barrier below)
-    const int eb0 = group * kBlocks;              // this workgroup's first block
-    const int nb = min(kBlocks, NB - eb0);        // its blocks (>= 1)
+    const int eb0 = group * KB;              // this workgroup's first block
+    const int nb = min(KB, NB - eb0);        // its blocks (>= 1)
     const int S = K / 16;                         // 16-wide K substeps
 
     __shared__ __align__(16) unsigned char xs_all[4 * 2 * kXSlot];
@@ -98,25 +102,25 @@ __global__ __launch_bounds__(256, 1) void router_kernel(const uint16_t* __restri
     // weight fragment of block eb, substep ks: panel eb / 8, 64-wide stage
     // ks / 4, block eb % 8, substep ks % 4, 8 elements per lane
     const size_t pstride = (size_t)kRouterPanel * K;
-    const uint16_t* wb[kBlocks];
+    const uint16_t* wb[KB];
 #pragma unroll
-    for (int j = 0; j < kBlocks; ++j) {
+    for (int j = 0; j < KB; ++j) {
         const int eb = min(eb0 + j, NB - 1);
         wb[j] = wg + (size_t)(eb / 8) * pstride + (eb % 8) * 2048 + lane * 8;
     }
     auto w_off = [](int ks) { return (size_t)(ks >> 2) * (8 * 2048) + (ks & 3) * 512; };
 
-    f32x16 acc[kBlocks];
+    f32x16 acc[KB];
 #pragma unroll
-    for (int j = 0; j < kBlocks; ++j)
+    for (int j = 0; j < KB; ++j)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
-    bf16x8 wr[kRing][kBlocks];
+    bf16x8 wr[kRing][KB];
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
         const int ks = min(u, S - 1);
 #pragma unroll
-        for (int j = 0; j < kBlocks; ++j) wr[u][j] = *(const bf16x8*)(wb[j] + w_off(ks));
+        for (int j = 0; j < KB; ++j) wr[u][j] = *(const bf16x8*)(wb[j] + w_off(ks));
     }
     // x stages 0 and 1 into registers, stage 0 into slot 0, stage 2 into the
     // freed registers
@@ -137,13 +141,13 @@ __global__ __launch_bounds__(256, 1) void router_kernel(const uint16_t* __restri
             const int u = 4 * P + uu;             // ring slot of substep 4 st + uu
             const bf16x8 a = read_a(4 * st + uu);
 #pragma unroll
-            for (int j = 0; j < kBlocks; ++j)
+            for (int j = 0; j < KB; ++j)
                 acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[u][j], a, acc[j], 0, 0, 0);
             // refill the slot with substep 4 st + uu + kRing (the last
             // substep again past the end, so the loads stay in bounds)
             const int ks = min(4 * st + uu + kRing, S - 1);
 #pragma unroll
-            for (int j = 0; j < kBlocks; ++j) wr[u][j] = *(const bf16x8*)(wb[j] + w_off(ks));
+            for (int j = 0; j < KB; ++j) wr[u][j] = *(const bf16x8*)(wb[j] + w_off(ks));
         }
         store_x(P ^ 1, xr[P ^ 1]);
         load_x(st + 3, xr[P ^ 1]);
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(256, 1) void router_kernel(const uint16_t* __restri
     if (t >= T) return;
     float* out = logits + (size_t)t * E;
 #pragma unroll
-    for (int j = 0; j < kBlocks; ++j) {
+    for (int j = 0; j < KB; ++j) {
         if (j >= nb) continue;
         const int e_blk = 32 * (eb0 + j);
 #pragma unroll
@@ -186,23 +190,45 @@ __global__ __launch_bounds__(256, 1) void router_kernel(const uint16_t* __restri
 
 }  // namespace
 
+namespace {
+// workgroups of the router grid with kb weight blocks per workgroup
+long long router_wgs(int T, int E, int kb) {
+    const long long groups = ((E + 31) / 32 + kb - 1) / kb;
+    return ((T + kTokens - 1) / kTokens + 7) / 8 * 8 * groups;
+}
+// the most weight blocks per workgroup (3, 2, 1) whose grid still covers the
+// CUs, else 1: fewer blocks per workgroup mean more, shorter workgroups
+// (64-expert layer with 4096 tokens: 29 -> 20 us with 1 block)
+int router_blocks(int T, int E) {
+    const long long cus = device_cu_count();
+    for (int kb = 3; kb > 1; --kb)
+        if (router_wgs(T, E, kb) >= cus) return kb;
+    return 1;
+}
+}  // namespace
+
 bool router_packed_preferred(int T, int E) {
     // each workgroup's time is set by its own load latency chain, so the
     // kernel wins while its grid is at most two rounds over the CUs; larger
     // grids go to the persistent grouped GEMM (same bits either way)
-    const long long groups = ((E + 31) / 32 + kBlocks - 1) / kBlocks;
-    const long long wgs = ((T + kTokens - 1) / kTokens + 7) / 8 * 8 * groups;
-    return wgs <= 2LL * device_cu_count();
+    return router_wgs(T, E, router_blocks(T, E)) <= 2LL * device_cu_count();
 }
 
 hipError_t launch_router_packed(const uint16_t* x, const uint16_t* wg_packed, const float* offset,
                                 int T, int K, int E, float* logits, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
     if (K % 64 || E < 1 || E > MOE_MAX_E) return hipErrorInvalidValue;
-    const int groups = ((E + 31) / 32 + kBlocks - 1) / kBlocks;
-    const long long tiles8 = ((T + kTokens - 1) / kTokens + 7) / 8 * 8;   // whole XCD rounds
-    hipLaunchKernelGGL(router_kernel, dim3((unsigned)(tiles8 * groups)), dim3(256), 0, stream, x,
-                       wg_packed, offset, T, K, E, logits);
+    const int kb = router_blocks(T, E);
+    const unsigned grid = (unsigned)router_wgs(T, E, kb);
+    if (kb == 3)
+        hipLaunchKernelGGL(router_kernel<3>, dim3(grid), dim3(256), 0, stream, x, wg_packed,
+                           offset, T, K, E, logits);
+    else if (kb == 2)
+        hipLaunchKernelGGL(router_kernel<2>, dim3(grid), dim3(256), 0, stream, x, wg_packed,
+                           offset, T, K, E, logits);
+    else
+        hipLaunchKernelGGL(router_kernel<1>, dim3(grid), dim3(256), 0, stream, x, wg_packed,
+                           offset, T, K, E, logits);
     return hipGetLastError();
 }
 
