@@ -312,15 +312,28 @@ __device__ __forceinline__ void flat_tile(const GemmArgs& args, const FlatTile& 
     using CodeT = typename std::conditional<WF == 2, u32x2, u32x4>::type;
     CodeT cw0[2], cw1[2];
     uint32_t sc0[2], sc1[2];
+    // (through buffer resources over the blocks' codes and scale bytes, as
+    // the bf16 weights: the lane offsets are t.lane * 16 or 8 bytes of code
+    // and t.l32 scale bytes; a panel of codes stays under 2 GiB for K up to
+    // kFlatMaxK)
+    const int lane_c = t.lane * (WF == 1 ? 16 : 8);
+    const __amdgpu_buffer_rsrc_t cr0 = flat_rsrc(t.cp0 - lane_c, (size_t)0x7fffffff);
+    const __amdgpu_buffer_rsrc_t cr1 = flat_rsrc(t.cp1 - lane_c, (size_t)0x7fffffff);
+    const __amdgpu_buffer_rsrc_t sr0 = flat_rsrc(t.sp0 - t.l32, (size_t)0x7fffffff);
+    const __amdgpu_buffer_rsrc_t sr1 = flat_rsrc(t.sp1 - t.l32, (size_t)0x7fffffff);
     auto load_c = [&](int j, int c) {
         const int jj = min(j, S - 1);
         const int kb = 2 * jj + c;
-        const size_t off = WF == 1 ? (size_t)jj * t.cstage + (size_t)c * 1024
-                                   : (size_t)kb * t.cstage;
-        cw0[c] = *(const CodeT*)(t.cp0 + off);
-        cw1[c] = *(const CodeT*)(t.cp1 + off);
-        sc0[c] = t.sp0[(size_t)kb * t.sstep];
-        sc1[c] = t.sp1[(size_t)kb * t.sstep];
+        const int off = WF == 1 ? jj * (int)t.cstage + c * 1024 : kb * (int)t.cstage;
+        if constexpr (WF == 1) {
+            cw0[c] = __builtin_bit_cast(CodeT, __builtin_amdgcn_raw_buffer_load_b128(cr0, lane_c, off, 0));
+            cw1[c] = __builtin_bit_cast(CodeT, __builtin_amdgcn_raw_buffer_load_b128(cr1, lane_c, off, 0));
+        } else if constexpr (WF == 2) {
+            cw0[c] = __builtin_bit_cast(CodeT, __builtin_amdgcn_raw_buffer_load_b64(cr0, lane_c, off, 0));
+            cw1[c] = __builtin_bit_cast(CodeT, __builtin_amdgcn_raw_buffer_load_b64(cr1, lane_c, off, 0));
+        }
+        sc0[c] = __builtin_amdgcn_raw_buffer_load_b8(sr0, t.l32, kb * t.sstep, 0);
+        sc1[c] = __builtin_amdgcn_raw_buffer_load_b8(sr1, t.l32, kb * t.sstep, 0);
     };
     // the bf16 operands of substep pq of the stage in the code ring: exact
     // (the scaled code is a bf16 value)
