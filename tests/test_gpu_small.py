@@ -247,10 +247,13 @@ def test_pack_weights_layout(G, N, K, P):
 
 @pytest.mark.parametrize("E,d,T,offset", [(8, 128, 70, False), (384, 256, 300, True),
                                           (5, 64, 33, True), (1000, 128, 200, True),
-                                          (1024, 64, 129, False), (97, 192, 1, True)])
+                                          (1024, 64, 129, False), (97, 192, 1, True),
+                                          (384, 256, 6144, True), (384, 256, 8192, False)])
 def test_gate_logits_packed_matches_plain(E, d, T, offset):
     # the router projection through moe_forward with packed weights equals the
-    # plain-layout call (same kernel arithmetic, only the weight layout differs)
+    # plain-layout call (same kernel arithmetic, only the weight layout differs);
+    # on 256 CUs the router kernel takes 1 weight block per workgroup at the
+    # small grids, 2 at 6144 tokens x 384 experts and 3 at 8192
     rng = np.random.default_rng(E + d)
     w = wl.small(T=T, d=d, E=E, k=1, F=64, seed=E, F_shared=0)
     inp = wl.make_inputs(w, DEV)
